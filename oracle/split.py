@@ -1,0 +1,192 @@
+"""Randomized spectral split A = U_k diag(S_k) V_k^T + R, in fp64.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+What the pages say (SII post on Metis, §2.4 item 1; "Metis: Training LLMs
+with FP4 Quantization", abstract and the method summary of its digest page):
+a matrix is split into a dominant part, made of the largest singular values
+and their vectors, and a long-tail residual; the parts are quantized
+separately. The dominant subspace is found cheaply in a low-dimensional space,
+either by a random projection or by sparse random sampling of columns.
+
+The pages give no formulas, so the steps follow the textbook randomized SVD
+(Halko, Martinsson & Tropp, "Finding structure with randomness", SIAM Review
+2011: Alg. 4.1 range finder without power iterations, Alg. 5.1 direct SVD):
+
+  1. sketch    Y = A Omega (Gaussian Omega, n x l), or Y = A[:, J] (sampled columns)
+  2. range     Y = Q R_Y by Householder reflections; keep Q (m x l, orthonormal)
+  3. project   B = Q^T A (l x n)
+  4. small SVD B = Ub diag(sigma) W^T by one-sided (Hestenes) Jacobi rotations
+  5. factors   U_k = Q Ub[:, :k], S_k = sigma[:k], V_k = W[:, :k]
+  6. signs     each column of U_k is flipped (with the same column of V_k) so
+               that its entry of largest magnitude (lowest row on ties) is positive
+  7. residual  R = A - U_k diag(S_k) V_k^T, from the unquantized factors
+
+Pins (tests/test_oracle_split.py): Householder Q and R against
+numpy.linalg.qr (LAPACK) up to column signs; singular values and subspaces
+against numpy.linalg.svd; full rank k = l = min(m, n) gives ||R||/||A|| <= 1e-12;
+an exactly rank-8 matrix returns its planted singular values to 1e-10; the
+invariants Q^T Q = I, sigma_i(B) <= sigma_i(A), U_k^T R = 0,
+||R||^2 = ||A||^2 - sum S_k^2 and the Eckart-Young lower bound on ||R||.
+"""
+import numpy as np
+
+from .formats import f32, quantize
+
+JACOBI_TOL = 1e-15
+JACOBI_MAX_SWEEPS = 60
+
+
+def householder_qr(Y):
+    """Thin QR of a tall matrix by Householder reflections.
+
+    Returns Q (m x l) with orthonormal columns and upper-triangular R (l x l),
+    Y = Q R. A column that is already zero below the diagonal gets no
+    reflection (its R diagonal is 0 and Q still has orthonormal columns)."""
+    A = np.array(Y, dtype=np.float64)
+    m, l = A.shape
+    if l > m:
+        raise ValueError("householder_qr needs rows >= columns")
+    reflectors = []
+    for j in range(l):
+        x = A[j:, j]
+        norm_x = np.sqrt(x @ x)
+        if norm_x == 0.0:
+            reflectors.append(None)
+            continue
+        # reflect x onto -sign(x0) ||x|| e1 (no cancellation in v0)
+        alpha = -norm_x if x[0] >= 0 else norm_x
+        v = x.copy()
+        v[0] -= alpha
+        v /= np.sqrt(v @ v)
+        A[j:, j:] -= 2.0 * np.outer(v, v @ A[j:, j:])
+        reflectors.append(v)
+    # Q = H_0 H_1 ... H_{l-1} applied to the first l columns of the identity
+    Q = np.zeros((m, l))
+    Q[np.arange(l), np.arange(l)] = 1.0
+    for j in reversed(range(l)):
+        v = reflectors[j]
+        if v is None:
+            continue
+        Q[j:, :] -= 2.0 * np.outer(v, v @ Q[j:, :])
+    return Q, np.triu(A[:l, :])
+
+
+def jacobi_svd(B, tol=JACOBI_TOL, max_sweeps=JACOBI_MAX_SWEEPS):
+    """SVD of a wide matrix B (l x n, l <= n) by one-sided Jacobi rotations.
+
+    The rows of B (the columns of B^T) are rotated in pairs, cyclically by
+    row index, until every pair is orthogonal to relative tolerance ``tol``:
+    |g_p . g_q| <= tol * ||g_p|| ||g_q||. With G = J^T B after convergence,
+    B = J G, the row norms of G are the singular values and the normalized
+    rows are the right singular vectors. Returns (Ub, sigma, W) with
+    B = Ub diag(sigma) W^T, sigma in descending order, W n x l.
+    Rows of zero norm give sigma = 0 and a zero column of W."""
+    G = np.array(B, dtype=np.float64)
+    l, n = G.shape
+    J = np.eye(l)
+    sweeps = 0
+    for sweeps in range(1, max_sweeps + 1):
+        rotated = False
+        for p in range(l - 1):
+            for q in range(p + 1, l):
+                gp, gq = G[p], G[q]
+                alpha = gp @ gp
+                beta = gq @ gq
+                gamma = gp @ gq
+                if abs(gamma) <= tol * np.sqrt(alpha * beta) or gamma == 0.0:
+                    continue
+                rotated = True
+                # rotation angle that makes the pair orthogonal (smaller root)
+                zeta = (beta - alpha) / (2.0 * gamma)
+                t = (1.0 if zeta >= 0 else -1.0) / (abs(zeta) + np.sqrt(1.0 + zeta * zeta))
+                c = 1.0 / np.sqrt(1.0 + t * t)
+                s = c * t
+                new_p = c * gp - s * gq
+                new_q = s * gp + c * gq
+                G[p], G[q] = new_p, new_q
+                jp, jq = J[:, p].copy(), J[:, q].copy()
+                J[:, p] = c * jp - s * jq
+                J[:, q] = s * jp + c * jq
+        if not rotated:
+            break
+    sigma = np.sqrt(np.einsum("ij,ij->i", G, G))
+    order = np.argsort(-sigma, kind="stable")
+    sigma = sigma[order]
+    J = J[:, order]
+    G = G[order]
+    W = np.zeros((n, l))
+    live = sigma > 0
+    W[:, live] = (G[live] / sigma[live, None]).T
+    return J, sigma, W
+
+
+def sign_convention(U, V):
+    """Flip column pairs so that each column of U has its largest-magnitude
+    entry (lowest row index on ties) positive."""
+    U = np.array(U, dtype=np.float64)
+    V = np.array(V, dtype=np.float64)
+    for i in range(U.shape[1]):
+        j = int(np.argmax(np.abs(U[:, i])))  # first maximum = lowest index
+        if U[j, i] < 0:
+            U[:, i] = -U[:, i]
+            V[:, i] = -V[:, i]
+    return U, V
+
+
+def sketch(A, omega=None, columns=None):
+    """Y = A Omega (Gaussian projection) or Y = A[:, J] (sampled columns)."""
+    if (omega is None) == (columns is None):
+        raise ValueError("give exactly one of omega or columns")
+    if omega is not None:
+        return np.asarray(A, dtype=np.float64) @ np.asarray(omega, dtype=np.float64)
+    J = np.asarray(columns, dtype=np.int64)
+    return np.asarray(A, dtype=np.float64)[:, J]
+
+
+def spectral_split(A, l, k, omega=None, columns=None):
+    """The seven steps of the module docstring. Returns a dict with the
+    fp64 factors U (m x k), S (k), V (n x k), the residual R and the
+    intermediates Q, B and sigma_B (all l singular values of B)."""
+    A = np.asarray(A, dtype=np.float64)
+    if not np.all(np.isfinite(A)):
+        raise ValueError("split input must be finite")
+    m, n = A.shape
+    if not (1 <= k <= l <= min(m, n)):
+        raise ValueError("need 1 <= k <= l <= min(m, n)")
+    Y = sketch(A, omega, columns)
+    if Y.shape != (m, l):
+        raise ValueError("sketch width must equal l")
+    Q, _ = householder_qr(Y)
+    B = Q.T @ A
+    Ub, sigma, W = jacobi_svd(B)
+    U = Q @ Ub[:, :k]
+    S = sigma[:k].copy()
+    V = W[:, :k]
+    U, V = sign_convention(U, V)
+    R = A - (U * S) @ V.T
+    return {"U": U, "S": S, "V": V, "R": R, "Q": Q, "B": B, "sigma_B": sigma}
+
+
+def quantize_record(fmt, R, U=None, S=None, V=None, orientations=("n", "t")):
+    """Quantized split record of one tensor.
+
+    The quantizers act on fp32 tensors: U, V and R are rounded to fp32 first.
+    Ut_q: U^T (k x m) blocked along m; Vt_q: V^T (k x n) blocked along n;
+    R_q: R (m x n) blocked along n; Rt_q: R^T (n x m) blocked along m.
+    S stays fp32 and is not quantized. With U = None the record is an
+    unsplit operand (k = 0) whose "residual" is the tensor itself."""
+    R32 = f32(R)
+    m, n = R32.shape
+    rec = {"fmt": fmt, "m": m, "n": n, "k": 0, "S": np.zeros(0),
+           "Ut_q": None, "Vt_q": None, "R_q": None, "Rt_q": None}
+    if U is not None:
+        rec["k"] = U.shape[1]
+        rec["S"] = f32(S)
+        rec["Ut_q"] = quantize(f32(U).T, fmt)
+        rec["Vt_q"] = quantize(f32(V).T, fmt)
+    if "n" in orientations:
+        rec["R_q"] = quantize(R32, fmt)
+    if "t" in orientations:
+        rec["Rt_q"] = quantize(R32.T, fmt)
+    return rec

@@ -1,0 +1,148 @@
+"""Pins of the oracle's randomized split against LAPACK and closed forms."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import split as S
+
+
+def _rand(seed, m, n):
+    return np.random.Generator(np.random.PCG64(seed)).standard_normal((m, n))
+
+
+@pytest.mark.parametrize("m,l", [(40, 7), (300, 16), (97, 33)])
+def test_householder_matches_lapack_qr(m, l):
+    Y = _rand(1, m, l)
+    Q, R = S.householder_qr(Y)
+    Qn, Rn = np.linalg.qr(Y)
+    d = np.sign(np.diag(Rn)) * np.sign(np.diag(R))
+    assert np.allclose(Q, Qn * d, atol=1e-12)
+    assert np.allclose(R, (Rn.T * d).T, atol=1e-12)
+    assert np.allclose(Q.T @ Q, np.eye(l), atol=1e-13)
+    assert np.allclose(Q @ R, Y, atol=1e-12)
+
+
+def test_householder_rank_deficient_keeps_orthonormal_q():
+    Y = _rand(2, 50, 6)
+    Y[:, 3] = 0.0
+    Y[:, 5] = Y[:, 0] * 2.0
+    Q, R = S.householder_qr(Y)
+    assert np.allclose(Q.T @ Q, np.eye(6), atol=1e-13)
+    assert np.allclose(Q @ R, Y, atol=1e-12)
+
+
+@pytest.mark.parametrize("l,n", [(8, 40), (16, 300), (33, 97), (12, 12)])
+def test_jacobi_svd_matches_lapack(l, n):
+    B = _rand(3, l, n)
+    Ub, sig, W = S.jacobi_svd(B)
+    Un, sn, Vtn = np.linalg.svd(B, full_matrices=False)
+    assert np.allclose(sig, sn, rtol=1e-12, atol=0)
+    # each singular vector equal up to sign (distinct singular values here)
+    dots = np.abs(np.sum(Ub * Un, axis=0))
+    assert np.allclose(dots, 1.0, atol=1e-10)
+    assert np.allclose((Ub * sig) @ W.T, B, atol=1e-12)
+    assert np.allclose(Ub.T @ Ub, np.eye(l), atol=1e-13)
+
+
+def test_jacobi_svd_zero_row_gives_zero_sigma():
+    B = _rand(4, 6, 30)
+    B[2] = 0.0
+    Ub, sig, W = S.jacobi_svd(B)
+    assert sig[-1] == 0.0
+    assert np.allclose((Ub * sig) @ W.T, B, atol=1e-12)
+
+
+@pytest.mark.parametrize("m,n", [(64, 48), (48, 64)])
+def test_full_rank_split_leaves_no_residual(m, n):
+    A = _rand(5, m, n)
+    k = min(m, n)
+    omega = _rand(6, n, k)
+    r = S.spectral_split(A, k, k, omega=omega)
+    assert np.linalg.norm(r["R"]) / np.linalg.norm(A) <= 1e-12
+
+
+def test_planted_rank8_singular_values_recovered():
+    g = np.random.Generator(np.random.PCG64(8))
+    U = synth.orthonormal(g, 300, 8)
+    V = synth.orthonormal(g, 200, 8)
+    s = np.array([90.0, 41.0, 17.0, 9.0, 5.5, 2.0, 1.25, 0.5])
+    A = (U * s) @ V.T
+    omega = synth.bf16_value(synth.bf16_bits(g.standard_normal((200, 16)))).astype(np.float64)
+    r = S.spectral_split(A, 16, 8, omega=omega)
+    assert np.allclose(r["S"], s, rtol=1e-10, atol=0)
+    # and the planted subspace itself: U_k U_k^T = U U^T
+    assert np.allclose(r["U"] @ r["U"].T, U @ U.T, atol=1e-10)
+
+
+def test_split_invariants_noisy_powerlaw():
+    t = synth.small_case(21, 384, 256, dtype="bf16", kind="powerlaw", k=16, l=24)
+    A = t.values.astype(np.float64)
+    r = S.spectral_split(A, t.l, t.k, omega=t.omega_values().astype(np.float64))
+    Q, U, Sk, V, R = r["Q"], r["U"], r["S"], r["V"], r["R"]
+    sA = np.linalg.svd(A, compute_uv=False)
+    assert np.allclose(Q.T @ Q, np.eye(t.l), atol=1e-13)
+    assert np.all(r["sigma_B"] <= sA[: t.l] * (1 + 1e-12))          # interlacing
+    assert np.abs(U.T @ R).max() <= 1e-10 * np.abs(A).max()          # U_k^T R = 0
+    lhs = np.linalg.norm(R) ** 2
+    assert abs(lhs - (np.linalg.norm(A) ** 2 - np.sum(Sk ** 2))) <= 1e-10 * np.linalg.norm(A) ** 2
+    assert np.linalg.norm(R) >= np.sqrt(np.sum(sA[t.k:] ** 2)) * (1 - 1e-12)  # Eckart-Young
+    assert np.all(np.diff(Sk) <= 0)
+
+
+def test_sign_convention():
+    t = synth.small_case(22, 128, 96, dtype="f32", kind="planted", k=4, l=8, n_dir=4)
+    A = t.values.astype(np.float64)
+    om = t.omega_values().astype(np.float64)
+    r = S.spectral_split(A, t.l, t.k, omega=om)
+    U = r["U"]
+    for i in range(t.k):
+        j = int(np.argmax(np.abs(U[:, i])))
+        assert U[j, i] > 0
+    # the split of -A negates V, not U
+    r2 = S.spectral_split(-A, t.l, t.k, omega=om)
+    assert np.allclose(r2["U"], U, atol=1e-10) and np.allclose(r2["V"], -r["V"], atol=1e-10)
+
+
+def test_column_sampling_sketch_is_a_gather():
+    A = _rand(9, 30, 50)
+    J = np.array([1, 4, 9, 20, 49], dtype=np.int32)
+    assert np.array_equal(S.sketch(A, columns=J), A[:, J])
+    r = S.spectral_split(A, 5, 3, columns=J)
+    # the captured subspace is the span of the sampled columns
+    P = r["Q"] @ r["Q"].T
+    assert np.allclose(P @ A[:, J], A[:, J], atol=1e-12)
+
+
+def test_bad_arguments():
+    A = _rand(10, 20, 10)
+    with pytest.raises(ValueError):
+        S.spectral_split(A, 11, 4, omega=_rand(1, 10, 11))
+    with pytest.raises(ValueError):
+        S.spectral_split(A, 4, 5, omega=_rand(1, 10, 4))
+    with pytest.raises(ValueError):
+        S.sketch(A)
+
+
+# --- planted mistakes: each pin above must notice a plausible slip ---------
+def test_pins_catch_a_planted_mistake_unsorted_sigma(monkeypatch):
+    real = S.jacobi_svd
+
+    def unsorted(B, **kw):
+        Ub, sig, W = real(B, **kw)
+        return Ub[:, ::-1], sig[::-1], W[:, ::-1]
+
+    monkeypatch.setattr(S, "jacobi_svd", unsorted)
+    with pytest.raises(AssertionError):
+        test_planted_rank8_singular_values_recovered()
+
+
+def test_pins_catch_a_planted_mistake_transposed_projection(monkeypatch):
+    real = S.householder_qr
+
+    def bad_qr(Y):
+        Q, R = real(Y)
+        return Q[:, ::-1] * 0.999, R  # slightly non-orthonormal basis
+
+    monkeypatch.setattr(S, "householder_qr", bad_qr)
+    with pytest.raises(AssertionError):
+        test_split_invariants_noisy_powerlaw()
