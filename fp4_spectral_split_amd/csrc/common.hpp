@@ -1,0 +1,172 @@
+// Shared device helpers of libmetis_fp4 (gfx950 only).
+//
+// Number formats follow the public format descriptions (the Metis pages name
+// MXFP4 and NVFP4 but do not define them):
+//   E2M1  -- OCP Microscaling Formats v1.0 §5.3.3: magnitudes 0,.5,1,1.5,2,3,4,6
+//   E8M0  -- OCP MX v1.0 §5.4.1, shared-exponent rule of §6.3
+//   E4M3  -- OCP 8-bit FP "E4M3FN": bias 7, max 448, no infinities
+// Rounding is to nearest with ties to the even code, saturating.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "metis_fp4.h"
+
+namespace metis {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short ushortx8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+// x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): 16 significant bits.
+__device__ __forceinline__ void split_bf16(float x, unsigned short &hi, unsigned short &lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+// Load element i of a row of type T as fp32.
+template <typename T> __device__ __forceinline__ float load_f32(const T *p);
+template <> __device__ __forceinline__ float load_f32<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float load_f32<unsigned short>(const unsigned short *p) {
+  return bf16_to_f32(*p);
+}
+
+// ------------------------------------------------------------------ E2M1
+// Code (sign in bit 3) of the E2M1 value nearest to v. The count of decision
+// points passed gives the magnitude index; at a decision point the even index
+// wins (0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4,
+// 5 -> 4); above 5 everything saturates to 6.
+__device__ __forceinline__ uint32_t e2m1_rne(float v) {
+  const float a = fabsf(v);
+  uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return m | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Magnitude of an E2M1 code times 2 (integers 0,1,2,3,4,6,8,12): value = x2 / 2.
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  const uint32_t m = code & 7u;
+  // 0, .5, 1, 1.5 for m < 4; 2, 3, 4, 6 for m >= 4
+  float mag = (m < 4u) ? 0.5f * (float)m : (float)(2u << ((m - 4u) >> 1)) * ((m & 1u) ? 1.5f : 1.0f);
+  return (code & 8u) ? -mag : mag;
+}
+
+// ------------------------------------------------------------------ E8M0
+// MXFP4 shared exponent of a block with max magnitude amax >= 0:
+// floor(log2 amax) - 2 clamped to [-127, 127]; -127 (byte 0) for amax == 0.
+__device__ __forceinline__ int mx_shared_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  const uint32_t b = __float_as_uint(amax);
+  const int field = (int)((b >> 23) & 0xFFu);
+  int e;
+  if (field == 0) {
+    e = (31 - __clz(b & 0x7FFFFFu)) - 149;  // subnormal: leading bit position
+  } else {
+    e = field - 127;
+  }
+  e -= 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// ------------------------------------------------------------------ E4M3
+// Non-negative fp32 -> E4M3FN byte, nearest even, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float b) {
+  if (!(b > 0.0f)) return 0u;
+  if (b >= 448.0f) return 0x7Eu;
+  const uint32_t u = __float_as_uint(b);
+  const int e = (int)((u >> 23) & 0xFFu) - 127;
+  if (e < -6) {
+    // subnormal E4M3 range: multiples of 2^-9 (rintf rounds half to even);
+    // a result of 8 steps is 2^-6, whose byte 0x08 is the same integer
+    return (uint32_t)rintf(ldexpf(b, 9));
+  }
+  uint32_t keep = (u >> 20) & 7u;  // top three mantissa bits
+  const uint32_t rest = u & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) keep++;
+  uint32_t field = (uint32_t)(e + 7);
+  if (keep == 8u) {
+    keep = 0u;
+    field++;
+  }
+  if (field > 15u || (field == 15u && keep > 6u)) return 0x7Eu;
+  return (field << 3) | keep;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t byte) {
+  const uint32_t field = (byte >> 3) & 15u, mant = byte & 7u;
+  return field == 0u ? ldexpf((float)mant, -9) : ldexpf((float)(8u + mant), (int)field - 10);
+}
+
+// NVFP4 tensor scale from the tensor's max magnitude (fp32 ops, division).
+__device__ __forceinline__ float nv_tensor_scale(float amax_tensor) {
+  if (!(amax_tensor > 0.0f)) return 1.0f;
+  const float s = __fdiv_rn(amax_tensor, 2688.0f);
+  return s < 1.17549435e-38f ? 1.17549435e-38f : s;
+}
+
+// ------------------------------------------------------------------ MFMA
+// 16x16x32 bf16 -> fp32. Lane l supplies row (or column) l % 16 and the eight
+// contraction slots 8*(l/16) .. +7; the result holds rows 4*(l/16) .. +3 of
+// column l % 16.
+__device__ __forceinline__ floatx4 mfma16_bf16(const ushortx8 &a, const ushortx8 &b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// 32x32x16 bf16 -> fp32. Lane l supplies row l % 32, contraction slots
+// 8*(l/32) .. +7; result register r holds row 8*(r/4) + 4*(l/32) + r%4 of
+// column l % 32.
+__device__ __forceinline__ floatx16 mfma32_bf16(const ushortx8 &a, const ushortx8 &b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// ------------------------------------------------------------------ misc
+__host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Max over a wavefront (64 lanes) with cross-lane shuffles.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace metis
+
+// ------------------------------------------------------------------ host
+namespace metis_host {
+
+// Bump allocator over a caller workspace; every carve is 256-byte aligned.
+struct Carver {
+  char *base;
+  size_t off;
+  explicit Carver(void *b) : base((char *)b), off(0) {}
+  template <typename T> T *take(size_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T *p = base ? (T *)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+  size_t bytes() const { return (off + 255) & ~(size_t)255; }
+};
+
+}  // namespace metis_host
+
+#define METIS_LAUNCH_CHECK()                                \
+  do {                                                      \
+    if (hipGetLastError() != hipSuccess) return METIS_ERR_HIP; \
+  } while (0)

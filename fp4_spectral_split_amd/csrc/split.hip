@@ -1,0 +1,1118 @@
+// metis_split: randomized spectral split A = U_k diag(S_k) V_k^T + R with
+// block FP4 quantization of the parts.
+//
+// Method: SII open-source-week post on Metis §2.4 item 1 (dominant part +
+// long-tail residual, decomposition in a low-dimensional space); "Metis:
+// Training LLMs with FP4 Quantization", abstract (random projection / sparse
+// random sampling). The steps are the randomized SVD of Halko, Martinsson &
+// Tropp (SIAM Review 2011) Alg. 4.1 (range finder, no power iteration) and
+// Alg. 5.1 (direct SVD):
+//
+//   pass 1 over A  sketch        Y = A Omega  (bf16 MFMA, fp32 accumulate;
+//                                 split-K partials)       or Y = A[:, J]
+//                  range         CholeskyQR2 on Y: fp64 Gram, one-workgroup
+//                                 Cholesky + triangular inverse, Y R^-1, twice
+//   pass 2 over A  projection    B^T = A^T Q  (Q as bf16 hi + lo: fp32-accurate)
+//                  small SVD     eigen-decomposition of B B^T (fp64, l x l) by
+//                                 parallel cyclic Jacobi in one workgroup
+//                  assemble      U = Q E_k, S = sqrt(lambda_k), V = B^T E_k / S
+//                  signs         largest-|entry| of each U column made positive
+//                  factors       U^T, V^T block-quantized along their length
+//   pass 3 over A  residual      R = A - U S V^T via bf16 hi/lo MFMA, then block
+//                                 absmax, scale, E2M1 rounding and nibble packing
+//                                 in both orientations from one LDS tile
+//
+// Every reduction runs in a fixed order (no atomics except the order-free
+// integer max of NVFP4 tensor scales), so results are bitwise reproducible.
+#include <algorithm>
+
+#include "common.hpp"
+
+using namespace metis;
+
+namespace {
+
+constexpr int kLpMax = 96;  // Gaussian / sampled sketch width handled in LDS
+constexpr int kThreads = 256;
+
+// ===================================================================== plan
+struct SplitPlan {
+  int64_t m, n;
+  int l, lp, k, kp;
+  int kind, fmt;
+  int elem;  // bytes per input element
+  // sketch
+  int sk;
+  int64_t sk_chunk;
+  // gram over rows of Y (and Q1)
+  int64_t gy_rows;
+  int gy_parts;
+  // projection
+  int pk;
+  int64_t pk_rows;
+  // gram over rows of B^T
+  int64_t gb_rows;
+  int gb_parts;
+  // assemble U argmax chunks
+  int64_t am_rows;
+  int am_parts;
+  // workspace
+  unsigned short *omt;   // lp x n bf16 (Omega^T, zero padded)
+  float *ysk;            // sk x m x l
+  float *y;              // m x l
+  float *q1;             // m x l
+  float *q;              // m x l
+  unsigned short *qt;    // 2 x lp x m bf16 (hi, lo) transposed, zero padded rows
+  float *btp;            // pk x n x l
+  float *bt;             // n x l
+  double *gpart;         // max(gy_parts, gb_parts) x lp x lp
+  double *gram;          // lp x lp
+  double *rinv;          // lp x lp
+  double *evec;          // lp x lp
+  double *sig_inv;       // lp (1/sigma, 0 for dropped)
+  float *am_val;         // am_parts x k (value at argmax)
+  int *am_idx;           // am_parts x k
+  float *sign;           // k
+  unsigned short *uhl;   // 2 x m x kp bf16 (U hi, lo)
+  unsigned short *whl;   // 2 x n x kp bf16 ((V S) hi, lo)
+  uint32_t *amax;        // 8 words: NVFP4 tensor maxima (U^T, V^T, R)
+  int *info_ws;          // 1 word
+  size_t bytes;
+};
+
+int64_t pick_rows_per_part(int64_t rows, int64_t want_parts, int64_t quantum) {
+  int64_t per = round_up(cdiv(rows, std::max<int64_t>(1, want_parts)), quantum);
+  return std::max<int64_t>(per, quantum);
+}
+
+SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int elem, void *ws) {
+  SplitPlan p;
+  p.m = m; p.n = n; p.l = l; p.k = k; p.kind = kind; p.fmt = fmt; p.elem = elem;
+  p.lp = (int)round_up(l, 16);
+  p.kp = (int)round_up(k, 32);
+  // sketch: 128-row tiles, split-K bounded so partial traffic stays ~10% of A
+  const int64_t m_tiles = cdiv(m, 128);
+  if (kind == METIS_OMEGA_GAUSSIAN) {
+    int64_t want = std::min<int64_t>(cdiv(768, m_tiles), std::max<int64_t>(1, n * elem / (20 * l)));
+    want = std::max<int64_t>(1, std::min<int64_t>(want, n / 128));
+    p.sk_chunk = round_up(cdiv(n, want), 128);
+    p.sk = (int)cdiv(n, p.sk_chunk);
+  } else {
+    p.sk = 1;
+    p.sk_chunk = n;
+  }
+  p.gy_rows = pick_rows_per_part(m, 128, 32);
+  p.gy_parts = (int)cdiv(m, p.gy_rows);
+  const int64_t n_tiles = cdiv(n, 128);
+  int64_t wantp = std::min<int64_t>(cdiv(768, n_tiles), std::max<int64_t>(1, m * elem / (20 * l)));
+  wantp = std::max<int64_t>(1, std::min<int64_t>(wantp, m / 32));
+  p.pk_rows = round_up(cdiv(m, wantp), 32);
+  p.pk = (int)cdiv(m, p.pk_rows);
+  p.gb_rows = pick_rows_per_part(n, 128, 32);
+  p.gb_parts = (int)cdiv(n, p.gb_rows);
+  p.am_rows = 256;
+  p.am_parts = (int)cdiv(m, p.am_rows);
+
+  metis_host::Carver c(ws);
+  p.omt = c.take<unsigned short>((size_t)p.lp * n);
+  p.ysk = c.take<float>((size_t)p.sk * m * l);
+  p.y = c.take<float>((size_t)m * l);
+  p.q1 = c.take<float>((size_t)m * l);
+  p.q = c.take<float>((size_t)m * l);
+  p.qt = c.take<unsigned short>((size_t)2 * p.lp * m);
+  p.btp = c.take<float>((size_t)p.pk * n * l);
+  p.bt = c.take<float>((size_t)n * l);
+  p.gpart = c.take<double>((size_t)std::max(p.gy_parts, p.gb_parts) * p.lp * p.lp);
+  p.gram = c.take<double>((size_t)p.lp * p.lp);
+  p.rinv = c.take<double>((size_t)p.lp * p.lp);
+  p.evec = c.take<double>((size_t)p.lp * p.lp);
+  p.sig_inv = c.take<double>((size_t)p.lp);
+  p.am_val = c.take<float>((size_t)p.am_parts * k);
+  p.am_idx = c.take<int>((size_t)p.am_parts * k);
+  p.sign = c.take<float>((size_t)k);
+  p.uhl = c.take<unsigned short>((size_t)2 * m * p.kp);
+  p.whl = c.take<unsigned short>((size_t)2 * n * p.kp);
+  p.amax = c.take<uint32_t>(8);
+  p.info_ws = c.take<int>(1);
+  p.bytes = c.bytes();
+  return p;
+}
+
+// ============================================================ small kernels
+__global__ void fill_u32(uint32_t *p, uint32_t v, int count) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = v;
+}
+
+// Omega (n x l bf16, row-major) -> Omega^T (lp x n), rows l..lp-1 zero.
+__global__ void omega_transpose_kernel(const unsigned short *__restrict__ om, int64_t n, int l, int lp,
+                                       unsigned short *__restrict__ omt) {
+  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int c = blockIdx.y;
+  if (j >= n) return;
+  omt[(int64_t)c * n + j] = c < l ? om[j * l + c] : (unsigned short)0;
+}
+
+// ================================================================== sketch
+// ysk[s] = A[:, chunk s] * Omega[chunk s, :]. 4 waves x 32 rows; the Omega^T
+// chunk (lp x 128) is staged in LDS and shared by the waves. Lane (r, g) loads
+// 32 consecutive elements of its row (contraction slots permuted consistently
+// with the Omega operand), so each row's 256 bytes per step are read whole.
+template <typename T>
+__global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda,
+                                                          const unsigned short *__restrict__ omt, int l, int lp,
+                                                          int64_t chunk, float *__restrict__ ysk) {
+  constexpr int KS = 128;
+  constexpr int NT = (sizeof(T) == 4) ? 3 : 1;  // bf16 terms per element (fp32 = hi + mid + lo)
+  __shared__ __attribute__((aligned(16))) unsigned short lds[kLpMax][KS + 8];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * 128 + wave * 32;
+  const int s = blockIdx.y;
+  const int64_t c_beg = (int64_t)s * chunk;
+  const int64_t c_end = std::min<int64_t>(n, c_beg + chunk);
+  const int nct = lp >> 4;
+  floatx4 acc[2][kLpMax / 16];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < kLpMax / 16; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t c0 = c_beg; c0 < c_end; c0 += KS) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < lp * (KS / 8); idx += kThreads) {
+      const int rr = idx / (KS / 8), q = idx % (KS / 8);
+      const int64_t cc = c0 + q * 8;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (cc < c_end) v = *(const uint4 *)(omt + (int64_t)rr * n + cc);
+      *(uint4 *)&lds[rr][q * 8] = v;
+    }
+    __syncthreads();
+    ushortx8 a[2][4][NT];
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
+      const int64_t row = row0 + rs * 16 + r16;
+      const int64_t cc = c0 + g * 32;
+      const bool ok = row < m && cc < c_end;
+      if constexpr (sizeof(T) == 2) {
+        const uint4 *src = (const uint4 *)(A + row * lda + cc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint4 v = ok ? src[j] : uint4{0u, 0u, 0u, 0u};
+          a[rs][j][0] = __builtin_bit_cast(ushortx8, v);
+        }
+      } else {
+        const float4 *src = (const float4 *)(A + row * lda + cc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float4 v0 = ok ? src[2 * j] : float4{0.f, 0.f, 0.f, 0.f};
+          float4 v1 = ok ? src[2 * j + 1] : float4{0.f, 0.f, 0.f, 0.f};
+          const float xs[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            // exact three-way split: x = hi + mid + lo, each a bf16 value
+            const unsigned short hi = f32_to_bf16(xs[e]);
+            const float r1 = xs[e] - bf16_to_f32(hi);
+            const unsigned short mid = f32_to_bf16(r1);
+            const unsigned short lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+            a[rs][j][0][e] = hi;
+            a[rs][j][NT > 1 ? 1 : 0][e] = mid;
+            a[rs][j][NT > 2 ? 2 : 0][e] = lo;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < kLpMax / 16; ++ct) {
+      if (ct < nct) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const ushortx8 b = *(const ushortx8 *)&lds[ct * 16 + r16][g * 32 + j * 8];
+#pragma unroll
+          for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[rs][ct] = mfma16_bf16(a[rs][j][t], b, acc[rs][ct]);
+        }
+      }
+    }
+  }
+  float *out = ysk + (int64_t)s * m * l;
+#pragma unroll
+  for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+    for (int ct = 0; ct < kLpMax / 16; ++ct) {
+      if (ct < nct) {
+        const int col = ct * 16 + r16;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t row = row0 + rs * 16 + g * 4 + t;
+          if (row < m && col < l) out[row * l + col] = acc[rs][ct][t];
+        }
+      }
+    }
+}
+
+// Y[:, c] = A[:, J[c]] (exact). Ids outside [0, n) read as zero columns.
+template <typename T>
+__global__ void gather_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda, const int *__restrict__ J,
+                              int l, float *__restrict__ y) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= m * l) return;
+  const int64_t r = idx / l;
+  const int c = (int)(idx - r * l);
+  const int j = J[c];
+  y[idx] = (j >= 0 && j < n) ? load_f32(A + r * lda + j) : 0.0f;
+}
+
+
+// ==================================================================== gram
+// One chunk of rows of a tall matrix X (rows x l, fp32):
+//   rinv == nullptr: X = sum of `parts` slabs of xin (fixed order);
+//   rinv != nullptr: X = xin R^-1 in fp64, rounded to fp32 (R^-1 upper
+//                    triangular, lp x lp);
+// X goes to xout (if given), to xt as bf16 hi/lo transposed (2 x lp x rows,
+// if given), and the fp64 Gram X^T X of the chunk to gpart[chunk] (lp x lp,
+// if given). Thread t owns the RB x RB block (t/16, t%16) of the Gram,
+// RB = lp/16, and accumulates it over the chunk's rows.
+constexpr int kSub = 32;
+
+__global__ void __launch_bounds__(kThreads)
+    gram_kernel(const float *__restrict__ xin, int parts, int64_t part_stride, int64_t rows, int l, int lp,
+                int64_t rows_per_chunk, const double *__restrict__ rinv, float *__restrict__ xout,
+                unsigned short *__restrict__ xt, double *__restrict__ gpart) {
+  __shared__ float xs[kSub][kLpMax + 1];
+  __shared__ float xa[kSub][kLpMax + 1];
+  __shared__ double rl[kLpMax * kLpMax];
+  const int t = threadIdx.x;
+  const int64_t r_beg = blockIdx.x * rows_per_chunk;
+  const int64_t r_end = std::min<int64_t>(rows, r_beg + rows_per_chunk);
+  const int RB = lp >> 4;
+  const int bi = t >> 4, bj = t & 15;
+  if (rinv)
+    for (int i = t; i < lp * lp; i += kThreads) rl[i] = rinv[i];
+  double acc[6][6];
+#pragma unroll
+  for (int a = 0; a < 6; ++a)
+#pragma unroll
+    for (int b = 0; b < 6; ++b) acc[a][b] = 0.0;
+
+  for (int64_t r0 = r_beg; r0 < r_end; r0 += kSub) {
+    __syncthreads();
+    for (int idx = t; idx < kSub * lp; idx += kThreads) {
+      const int rr = idx / lp, c = idx - rr * lp;
+      const int64_t row = r0 + rr;
+      float v = 0.0f;
+      if (row < r_end && c < l) {
+        const float *p = xin + row * l + c;
+        for (int q = 0; q < parts; ++q) v += p[q * part_stride];
+      }
+      if (rinv)
+        xa[rr][c] = v;
+      else
+        xs[rr][c] = v;
+    }
+    __syncthreads();
+    if (rinv) {
+      for (int idx = t; idx < kSub * lp; idx += kThreads) {
+        const int rr = idx / lp, c = idx - rr * lp;
+        double s = 0.0;
+        if (c < l)
+          for (int q = 0; q <= c; ++q) s += (double)xa[rr][q] * rl[q * lp + c];
+        xs[rr][c] = (float)s;
+      }
+      __syncthreads();
+    }
+    if (xout) {
+      for (int idx = t; idx < kSub * l; idx += kThreads) {
+        const int rr = idx / l, c = idx - rr * l;
+        if (r0 + rr < r_end) xout[(r0 + rr) * l + c] = xs[rr][c];
+      }
+    }
+    if (xt) {
+      // 8 consecutive rows of one column per thread (16-byte stores)
+      for (int idx = t; idx < lp * (kSub / 8); idx += kThreads) {
+        const int c = idx >> 2, q = idx & 3;
+        if (r0 + q * 8 >= r_end) continue;
+        ushortx8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          unsigned short h, w;
+          split_bf16(xs[q * 8 + e][c], h, w);
+          hi[e] = h;
+          lo[e] = w;
+        }
+        *(ushortx8 *)(xt + (int64_t)c * rows + r0 + q * 8) = hi;
+        *(ushortx8 *)(xt + ((int64_t)lp + c) * rows + r0 + q * 8) = lo;
+      }
+    }
+    if (gpart) {
+      const int nr = (int)std::min<int64_t>(kSub, r_end - r0);
+#pragma unroll 1
+      for (int rr = 0; rr < nr; ++rr) {
+        double xi[6], xj[6];
+#pragma unroll
+        for (int a = 0; a < 6; ++a) {
+          xi[a] = a < RB ? (double)xs[rr][bi * RB + a] : 0.0;
+          xj[a] = a < RB ? (double)xs[rr][bj * RB + a] : 0.0;
+        }
+#pragma unroll
+        for (int a = 0; a < 6; ++a)
+#pragma unroll
+          for (int b = 0; b < 6; ++b) acc[a][b] += xi[a] * xj[b];
+      }
+    }
+  }
+  if (gpart) {
+    double *g = gpart + (int64_t)blockIdx.x * lp * lp;
+#pragma unroll
+    for (int a = 0; a < 6; ++a)
+#pragma unroll
+      for (int b = 0; b < 6; ++b)
+        if (a < RB && b < RB) g[(bi * RB + a) * lp + bj * RB + b] = acc[a][b];
+  }
+}
+
+// G = sum over parts of gpart (fixed order).
+__global__ void gram_reduce_kernel(const double *__restrict__ gpart, int parts, int lp2, double *__restrict__ g) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= lp2) return;
+  double s = 0.0;
+  for (int p = 0; p < parts; ++p) s += gpart[(int64_t)p * lp2 + e];
+  g[e] = s;
+}
+
+// ========================================================= Cholesky + inverse
+// One workgroup: G = R^T R (upper R, right-looking, fp64 in LDS), then
+// R^-1 by back substitution, one column per thread. A pivot at or below
+// l * 2^-52 * max(diag G) marks that direction as absent: its row of R and
+// its row and column of R^-1 are zero (the orthonormalized column comes out
+// zero) and *info records the first such pivot (1-based).
+__global__ void __launch_bounds__(kThreads)
+    chol_inv_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ rinv, int *info) {
+  __shared__ double a[kLpMax][kLpMax + 1];
+  __shared__ double inv[kLpMax][kLpMax + 1];
+  __shared__ int dead[kLpMax];
+  __shared__ double tol_s;
+  __shared__ int first_dead;
+  const int t = threadIdx.x;
+  for (int i = t; i < lp * lp; i += kThreads) a[i / lp][i % lp] = g[i];
+  if (t == 0) {
+    double md = 0.0;
+    for (int i = 0; i < l; ++i) md = fmax(md, g[i * lp + i]);
+    tol_s = (double)l * 2.220446049250313e-16 * md;
+    first_dead = 0;
+  }
+  __syncthreads();
+  for (int j = 0; j < l; ++j) {
+    if (t == 0) {
+      const double piv = a[j][j];
+      if (piv > tol_s) {
+        a[j][j] = sqrt(piv);
+        dead[j] = 0;
+      } else {
+        a[j][j] = 0.0;
+        dead[j] = 1;
+        if (first_dead == 0) first_dead = j + 1;
+      }
+    }
+    __syncthreads();
+    const double d = a[j][j];
+    const bool dj = dead[j];
+    for (int c = j + 1 + t; c < l; c += kThreads) a[j][c] = dj ? 0.0 : a[j][c] / d;
+    __syncthreads();
+    if (!dj) {
+      const int w = l - j - 1;
+      for (int idx = t; idx < w * w; idx += kThreads) {
+        const int p = j + 1 + idx / w, q = j + 1 + idx % w;
+        if (q >= p) a[p][q] -= a[j][p] * a[j][q];
+      }
+    }
+    __syncthreads();
+  }
+  // column c of R^-1: solve R x = e_c from the bottom up
+  if (t < lp) {
+    const int c = t;
+    for (int i = 0; i < lp; ++i) inv[i][c] = 0.0;
+    if (c < l && !dead[c]) {
+      inv[c][c] = 1.0 / a[c][c];
+      for (int i = c - 1; i >= 0; --i) {
+        if (dead[i]) continue;
+        double s = 0.0;
+        for (int q = i + 1; q <= c; ++q) s += a[i][q] * inv[q][c];
+        inv[i][c] = -s / a[i][i];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < lp * lp; i += kThreads) rinv[i] = inv[i / lp][i % lp];
+  if (t == 0 && info) *info = first_dead;
+}
+
+// ============================================================== projection
+// btp[s] = (A[rows of chunk s, :])^T Q[rows of chunk s, :]   (n x l, fp32)
+// with Q given transposed as bf16 hi + lo (2 x lp x m). WG: 128 columns of A,
+// 4 waves x 32 columns. Per step, 32 rows of A (bf16 or fp32) and the
+// matching 32 columns of Q^T (hi, lo) are staged in LDS.
+template <typename T>
+__global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda,
+                                                           const unsigned short *__restrict__ qt, int l, int lp,
+                                                           int64_t chunk_rows, float *__restrict__ btp) {
+  constexpr int KS = 32;
+  constexpr int TN = 128;
+  constexpr int NT = (sizeof(T) == 4) ? 3 : 1;
+  __shared__ __attribute__((aligned(16))) T at[KS][TN + (sizeof(T) == 2 ? 8 : 4)];
+  __shared__ __attribute__((aligned(16))) unsigned short qs[2][kLpMax][KS + 8];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t col0 = (int64_t)blockIdx.x * TN;
+  const int s = blockIdx.y;
+  const int64_t r_beg = (int64_t)s * chunk_rows;
+  const int64_t r_end = std::min<int64_t>(m, r_beg + chunk_rows);
+  const int nit = lp >> 4;
+  floatx4 acc[2][kLpMax / 16];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < kLpMax / 16; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t r0 = r_beg; r0 < r_end; r0 += KS) {
+    __syncthreads();
+    // A tile: KS rows x TN columns, 16-byte pieces
+    constexpr int PIECE = 16 / sizeof(T);
+    for (int idx = threadIdx.x; idx < KS * (TN / PIECE); idx += kThreads) {
+      const int rr = idx / (TN / PIECE), q = idx % (TN / PIECE);
+      const int64_t row = r0 + rr, col = col0 + q * PIECE;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (row < r_end && col < n) v = *(const uint4 *)(A + row * lda + col);
+      *(uint4 *)&at[rr][q * PIECE] = v;
+    }
+    // Q^T hi/lo: 2 x lp rows of KS bf16 (4 pieces each)
+    for (int idx = threadIdx.x; idx < 2 * lp * (KS / 8); idx += kThreads) {
+      const int h = idx / (lp * 4), rem = idx % (lp * 4);
+      const int i = rem >> 2, q = rem & 3;
+      const int64_t row = r0 + q * 8;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (row < r_end) v = *(const uint4 *)(qt + ((int64_t)h * lp + i) * m + row);
+      *(uint4 *)&qs[h][i][q * 8] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+      const int cl = wave * 32 + cs * 16 + r16;  // A column inside the tile
+      ushortx8 af[NT];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (sizeof(T) == 2) {
+          af[0][e] = at[g * 8 + e][cl];
+        } else {
+          const float x = at[g * 8 + e][cl];
+          const unsigned short hi = f32_to_bf16(x);
+          const float r1 = x - bf16_to_f32(hi);
+          const unsigned short mid = f32_to_bf16(r1);
+          af[0][e] = hi;
+          af[NT > 1 ? 1 : 0][e] = mid;
+          af[NT > 2 ? 2 : 0][e] = f32_to_bf16(r1 - bf16_to_f32(mid));
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < kLpMax / 16; ++it) {
+        if (it < nit) {
+          const ushortx8 qh = *(const ushortx8 *)&qs[0][it * 16 + r16][g * 8];
+          const ushortx8 ql = *(const ushortx8 *)&qs[1][it * 16 + r16][g * 8];
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            acc[cs][it] = mfma16_bf16(af[tt], qh, acc[cs][it]);
+            acc[cs][it] = mfma16_bf16(af[tt], ql, acc[cs][it]);
+          }
+        }
+      }
+    }
+  }
+  float *out = btp + (int64_t)s * n * l;
+#pragma unroll
+  for (int cs = 0; cs < 2; ++cs)
+#pragma unroll
+    for (int it = 0; it < kLpMax / 16; ++it) {
+      if (it < nit) {
+        const int i = it * 16 + r16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = col0 + wave * 32 + cs * 16 + g * 4 + q;
+          if (col < n && i < l) out[col * l + i] = acc[cs][it][q];
+        }
+      }
+    }
+}
+
+// ================================================================== Jacobi
+// Eigen-decomposition of the symmetric lp x lp matrix G (fp64) by cyclic
+// two-sided Jacobi rotations, all lp/2 disjoint pairs of a round at once
+// (round-robin pairing). Rows/columns >= l are zero padding and never rotate.
+// Output: eigenvectors (columns, lp x lp) in descending eigenvalue order,
+// S[c] = sqrt(lambda_c) for c < k (0 below 2^-24 sigma_max) and sig_inv.
+constexpr int kJacThreads = 1024;
+
+__device__ __forceinline__ int rr_player(int pos, int round, int N) {
+  return pos == 0 ? 0 : 1 + (pos - 1 + round) % (N - 1);
+}
+
+__global__ void __launch_bounds__(kJacThreads)
+    jacobi_kernel(const double *__restrict__ gin, int l, int lp, int k, int max_sweeps, double *__restrict__ evec,
+                  double *__restrict__ sig_inv, float *__restrict__ S) {
+  __shared__ double G[kLpMax][kLpMax + 1];
+  __shared__ double V[kLpMax][kLpMax + 1];
+  __shared__ double cs_c[kLpMax / 2], cs_s[kLpMax / 2];
+  __shared__ int pp[kLpMax / 2], qq[kLpMax / 2];
+  __shared__ int rotated;
+  __shared__ double floor_s;
+  __shared__ int rank[kLpMax];
+  const int t = threadIdx.x;
+  const int N = lp, H = lp / 2;
+  for (int i = t; i < N * N; i += kJacThreads) {
+    G[i / N][i % N] = gin[i];
+    V[i / N][i % N] = (i / N == i % N) ? 1.0 : 0.0;
+  }
+  if (t == 0) {
+    double md = 0.0;
+    for (int i = 0; i < l; ++i) md = fmax(md, gin[i * N + i]);
+    floor_s = 4.0 * 2.220446049250313e-16 * md;
+  }
+  __syncthreads();
+  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+    if (t == 0) rotated = 0;
+    __syncthreads();
+    for (int round = 0; round < N - 1; ++round) {
+      if (t < H) {
+        int p = rr_player(t, round, N), q = rr_player(N - 1 - t, round, N);
+        if (p > q) {
+          const int x = p;
+          p = q;
+          q = x;
+        }
+        const double app = G[p][p], aqq = G[q][q], apq = G[p][q];
+        double c = 1.0, s = 0.0;
+        if (apq != 0.0 && fabs(apq) > 1e-14 * sqrt(fabs(app * aqq)) && fabs(apq) > floor_s) {
+          const double zeta = (aqq - app) / (2.0 * apq);
+          const double tt = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+          c = 1.0 / sqrt(1.0 + tt * tt);
+          s = c * tt;
+          rotated = 1;
+        }
+        cs_c[t] = c;
+        cs_s[t] = s;
+        pp[t] = p;
+        qq[t] = q;
+      }
+      __syncthreads();
+      // G <- J^T G J on 2x2 blocks (each block owned by one thread)
+      for (int idx = t; idx < H * H; idx += kJacThreads) {
+        const int P = idx / H, Q = idx % H;
+        const double c1 = cs_c[P], s1 = cs_s[P], c2 = cs_c[Q], s2 = cs_s[Q];
+        if (s1 == 0.0 && s2 == 0.0) continue;
+        const int p1 = pp[P], q1 = qq[P], p2 = pp[Q], q2 = qq[Q];
+        const double b00 = G[p1][p2], b01 = G[p1][q2], b10 = G[q1][p2], b11 = G[q1][q2];
+        const double h00 = c2 * b00 - s2 * b01, h01 = s2 * b00 + c2 * b01;
+        const double h10 = c2 * b10 - s2 * b11, h11 = s2 * b10 + c2 * b11;
+        double n00 = c1 * h00 - s1 * h10, n01 = c1 * h01 - s1 * h11;
+        double n10 = s1 * h00 + c1 * h10, n11 = s1 * h01 + c1 * h11;
+        if (P == Q) {
+          n01 = 0.0;
+          n10 = 0.0;
+        }
+        G[p1][p2] = n00;
+        G[p1][q2] = n01;
+        G[q1][p2] = n10;
+        G[q1][q2] = n11;
+      }
+      // V <- V J
+      for (int idx = t; idx < N * H; idx += kJacThreads) {
+        const int i = idx / H, P = idx % H;
+        const double c = cs_c[P], s = cs_s[P];
+        if (s == 0.0) continue;
+        const int p = pp[P], q = qq[P];
+        const double vp = V[i][p], vq = V[i][q];
+        V[i][p] = c * vp - s * vq;
+        V[i][q] = s * vp + c * vq;
+      }
+      __syncthreads();
+    }
+    if (!rotated) break;
+    __syncthreads();
+  }
+  // rank of each eigenvalue (descending, ties by index); padding ranks last
+  if (t < N) {
+    int r = 0;
+    if (t < l) {
+      const double d = G[t][t];
+      for (int j = 0; j < l; ++j) {
+        const double e = G[j][j];
+        r += (e > d) || (e == d && j < t);
+      }
+    } else {
+      r = t;
+    }
+    rank[t] = r;
+  }
+  __syncthreads();
+  for (int idx = t; idx < N * N; idx += kJacThreads) {
+    const int row = idx / N, col = idx % N;
+    evec[row * N + rank[col]] = V[row][col];
+  }
+  if (t < N) {
+    double smax = sqrt(fmax(G[0][0], 0.0));
+    for (int j = 1; j < l; ++j) smax = fmax(smax, sqrt(fmax(G[j][j], 0.0)));
+    double sg = t < l ? sqrt(fmax(G[t][t], 0.0)) : 0.0;
+    if (!(sg > smax * 5.9604644775390625e-08)) sg = 0.0;
+    const int r = rank[t];
+    sig_inv[r] = sg > 0.0 ? 1.0 / sg : 0.0;
+    if (r < k) S[r] = (float)sg;
+  }
+}
+
+// ================================================================ assemble
+// U[r][c] = sum_t Q[r][t] E[t][c] (fp64 accumulate) for the chunk's rows, and
+// the chunk's argmax of |U[:, c]| (lowest row on ties) with its signed value.
+__global__ void __launch_bounds__(kThreads)
+    assemble_u_kernel(const float *__restrict__ q, int64_t m, int l, int lp, int k, const double *__restrict__ evec,
+                      int64_t chunk_rows, float *__restrict__ U, float *__restrict__ am_val, int *__restrict__ am_idx) {
+  __shared__ double E[kLpMax][kLpMax];
+  __shared__ float qs[64][kLpMax + 1];
+  __shared__ float bv[kThreads];
+  __shared__ float bsv[kThreads];
+  __shared__ int bix[kThreads];
+  const int t = threadIdx.x;
+  for (int i = t; i < l * k; i += kThreads) E[i / k][i % k] = evec[(i / k) * lp + i % k];
+  const int groups = kThreads / k;  // row groups per column
+  const int c = t % k, rg = t / k;
+  const bool active = rg < groups;
+  float best_abs = -1.0f, best_val = 0.0f;
+  int best_idx = 0x7FFFFFFF;
+  const int64_t r_beg = blockIdx.x * chunk_rows;
+  const int64_t r_end = std::min<int64_t>(m, r_beg + chunk_rows);
+  for (int64_t r0 = r_beg; r0 < r_end; r0 += 64) {
+    __syncthreads();
+    for (int idx = t; idx < 64 * l; idx += kThreads) {
+      const int rr = idx / l, cc = idx % l;
+      qs[rr][cc] = (r0 + rr < r_end) ? q[(r0 + rr) * l + cc] : 0.0f;
+    }
+    __syncthreads();
+    if (active) {
+      for (int rr = rg; rr < 64; rr += groups) {
+        const int64_t row = r0 + rr;
+        if (row >= r_end) break;
+        double s = 0.0;
+        for (int q2 = 0; q2 < l; ++q2) s += (double)qs[rr][q2] * E[q2][c];
+        const float u = (float)s;
+        U[row * k + c] = u;
+        const float au = fabsf(u);
+        if (au > best_abs) {
+          best_abs = au;
+          best_val = u;
+          best_idx = (int)row;
+        }
+      }
+    }
+  }
+  bv[t] = active ? best_abs : -1.0f;
+  bsv[t] = active ? best_val : 0.0f;
+  bix[t] = active ? best_idx : 0x7FFFFFFF;
+  __syncthreads();
+  if (t < k) {
+    float ba = -1.0f, bval = 0.0f;
+    int bi = 0x7FFFFFFF;
+    for (int g = 0; g < groups; ++g) {
+      const int w = g * k + t;
+      if (bv[w] > ba || (bv[w] == ba && bix[w] < bi)) {
+        ba = bv[w];
+        bval = bsv[w];
+        bi = bix[w];
+      }
+    }
+    am_val[blockIdx.x * k + t] = bval;
+    am_idx[blockIdx.x * k + t] = bi;
+  }
+}
+
+// V[j][c] = (sum_t B^T[j][t] E[t][c]) / sigma_c   (0 for dropped sigma)
+__global__ void __launch_bounds__(kThreads)
+    assemble_v_kernel(const float *__restrict__ bt, int64_t n, int l, int lp, int k, const double *__restrict__ evec,
+                      const double *__restrict__ sig_inv, float *__restrict__ V) {
+  __shared__ double E[kLpMax][kLpMax];
+  __shared__ float bs[64][kLpMax + 1];
+  const int t = threadIdx.x;
+  for (int i = t; i < l * k; i += kThreads) E[i / k][i % k] = evec[(i / k) * lp + i % k] * sig_inv[i % k];
+  const int64_t r0 = blockIdx.x * 64;
+  for (int idx = t; idx < 64 * l; idx += kThreads) {
+    const int rr = idx / l, cc = idx % l;
+    bs[rr][cc] = (r0 + rr < n) ? bt[(r0 + rr) * l + cc] : 0.0f;
+  }
+  __syncthreads();
+  for (int idx = t; idx < 64 * k; idx += kThreads) {
+    const int rr = idx / k, c = idx % k;
+    if (r0 + rr >= n) continue;
+    double s = 0.0;
+    for (int q = 0; q < l; ++q) s += (double)bs[rr][q] * E[q][c];
+    V[(r0 + rr) * k + c] = (float)s;
+  }
+}
+
+// sign[c] = -1 if the largest-|U[:, c]| entry (lowest row on ties) is negative
+__global__ void sign_kernel(const float *__restrict__ am_val, const int *__restrict__ am_idx, int parts, int k,
+                            float *__restrict__ sign) {
+  const int c = threadIdx.x;
+  if (c >= k) return;
+  float ba = -1.0f, bv = 0.0f;
+  int bi = 0x7FFFFFFF;
+  for (int p = 0; p < parts; ++p) {
+    const float v = am_val[p * k + c];
+    const int i = am_idx[p * k + c];
+    if (fabsf(v) > ba || (fabsf(v) == ba && i < bi)) {
+      ba = fabsf(v);
+      bv = v;
+      bi = i;
+    }
+  }
+  sign[c] = bv < 0.0f ? -1.0f : 1.0f;
+}
+
+// max |x| over a rows x cols fp32 matrix (row stride ld) into *out (bits).
+__global__ void amax_f32_kernel(const float *__restrict__ x, int64_t rows, int64_t cols, uint32_t *out) {
+  float mx = 0.0f;
+  const int64_t total = rows * cols;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x)
+    mx = fmaxf(mx, fabsf(x[i]));
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(mx));
+}
+
+// ================================================================= factors
+// For X = U (m x k, y = 0) or V (n x k, y = 1): flip column signs in place,
+// quantize X^T along its length into (codes, scales), and write the bf16
+// hi/lo panel of X * mult (mult = 1 for U, S for V) for the residual MFMA.
+// Thread = (column c < kp, block of B rows).
+template <bool NV>
+__global__ void __launch_bounds__(kThreads)
+    factor_kernel(float *__restrict__ U, float *__restrict__ V, int64_t m, int64_t n, int k, int kp,
+                  const float *__restrict__ sign, const float *__restrict__ S, uint8_t *__restrict__ ucodes,
+                  uint8_t *__restrict__ uscales, float *__restrict__ uts, uint8_t *__restrict__ vcodes,
+                  uint8_t *__restrict__ vscales, float *__restrict__ vts, const uint32_t *__restrict__ amax,
+                  unsigned short *__restrict__ uhl, unsigned short *__restrict__ whl) {
+  constexpr int B = NV ? 16 : 32;
+  const bool isv = blockIdx.y == 1;
+  float *X = isv ? V : U;
+  const int64_t rows = isv ? n : m;
+  uint8_t *codes = isv ? vcodes : ucodes;
+  uint8_t *scales = isv ? vscales : uscales;
+  unsigned short *hl = isv ? whl : uhl;
+  const int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+  const int c = (int)(idx % kp);
+  const int64_t blk = idx / kp;
+  if (blk >= rows / B) return;
+  float s_t = 1.0f;
+  if (NV) {
+    s_t = nv_tensor_scale(__uint_as_float(amax[isv ? 1 : 0]));
+    if (idx == 0) *(isv ? vts : uts) = s_t;
+  }
+  if (c >= k) {
+    for (int i = 0; i < B; ++i) {
+      hl[(blk * B + i) * kp + c] = 0;
+      hl[rows * kp + (blk * B + i) * kp + c] = 0;
+    }
+    return;
+  }
+  const float sg = sign[c];
+  const float mult = isv ? S[c] : 1.0f;
+  float v[B];
+  for (int i = 0; i < B; ++i) {
+    float* p = X + (blk * B + i) * k + c;
+    v[i] = *p * sg;
+    *p = v[i];
+    unsigned short h, w;
+    split_bf16(v[i] * mult, h, w);
+    hl[(blk * B + i) * kp + c] = h;
+    hl[rows * kp + (blk * B + i) * kp + c] = w;
+  }
+  float amx = 0.0f;
+  for (int i = 0; i < B; ++i) amx = fmaxf(amx, fabsf(v[i]));
+  uint32_t sb, cde[B];
+  if (!NV) {
+    const int se = mx_shared_exponent(amx);
+    sb = (uint32_t)(se + 127);
+    for (int i = 0; i < B; ++i) cde[i] = e2m1_rne(ldexpf(v[i], -se));
+  } else {
+    sb = e4m3_rne_sat(__fdiv_rn(amx, 6.0f * s_t));
+    const float den = e4m3_value(sb) * s_t;
+    for (int i = 0; i < B; ++i) cde[i] = sb ? e2m1_rne(__fdiv_rn(v[i], den)) : ((__float_as_uint(v[i]) >> 28) & 8u);
+  }
+  uint32_t *dst = (uint32_t *)(codes + (int64_t)c * (rows / 2) + blk * (B / 2));
+  for (int w = 0; w < B / 8; ++w) {
+    uint32_t pk = 0;
+    for (int j = 0; j < 8; ++j) pk |= cde[w * 8 + j] << (4 * j);
+    dst[w] = pk;
+  }
+  scales[(int64_t)c * (rows / B) + blk] = (uint8_t)sb;
+}
+
+// ================================================================ residual
+// R = A - U diag(S) V^T on a 128 x 128 tile, then block quantization of R
+// along n (R_q) and along m (Rt_q) from the same LDS copy. L = U W^T with
+// W = V S comes from bf16 MFMA on hi/lo panels: Uh Wh + Uh Wl + Ul Wh.
+// AMAX_ONLY: only the tensor max of |R| (NVFP4 tensor scale) is produced.
+constexpr int kRT = 128;
+
+template <int B, bool NV>
+__device__ __forceinline__ void quant_store(const float (&v)[B], float s_t, uint8_t *codes, uint8_t *scale) {
+  float amx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < B; ++i) amx = fmaxf(amx, fabsf(v[i]));
+  uint32_t sb, c[B];
+  if (!NV) {
+    const int se = mx_shared_exponent(amx);
+    sb = (uint32_t)(se + 127);
+#pragma unroll
+    for (int i = 0; i < B; ++i) c[i] = e2m1_rne(ldexpf(v[i], -se));
+  } else {
+    sb = e4m3_rne_sat(__fdiv_rn(amx, 6.0f * s_t));
+    const float den = e4m3_value(sb) * s_t;
+#pragma unroll
+    for (int i = 0; i < B; ++i) c[i] = sb ? e2m1_rne(__fdiv_rn(v[i], den)) : ((__float_as_uint(v[i]) >> 28) & 8u);
+  }
+  uint32_t pk[B / 8];
+#pragma unroll
+  for (int w = 0; w < B / 8; ++w) {
+    uint32_t p = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p |= c[w * 8 + j] << (4 * j);
+    pk[w] = p;
+  }
+  if constexpr (B == 32) {
+    *(uint4 *)codes = uint4{pk[0], pk[1], pk[2], pk[3]};
+  } else {
+    *(uint2 *)codes = uint2{pk[0], pk[1]};
+  }
+  *scale = (uint8_t)sb;
+}
+
+template <typename T, bool NV, bool AMAX_ONLY>
+__global__ void __launch_bounds__(kThreads)
+    residual_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda, const unsigned short *__restrict__ uhl,
+                    const unsigned short *__restrict__ whl, int kp, uint8_t *__restrict__ rcodes,
+                    uint8_t *__restrict__ rscales, float *__restrict__ rts, uint8_t *__restrict__ tcodes,
+                    uint8_t *__restrict__ tscales, float *__restrict__ tts, uint32_t *__restrict__ amax) {
+  constexpr int B = NV ? 16 : 32;
+  __shared__ __attribute__((aligned(16))) float lt[kRT][kRT + 4];
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t col0 = (int64_t)blockIdx.x * kRT, row0 = (int64_t)blockIdx.y * kRT;
+  // ---- L tile via MFMA: wave owns rows wave*32 .. +32, all 128 columns
+  {
+    floatx4 acc[2][8];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 8; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int64_t um = m * kp, wn = n * kp;
+    for (int kk = 0; kk < kp; kk += 32) {
+      ushortx8 uh[2], ul[2];
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        const int64_t row = row0 + wave * 32 + rs * 16 + r16;
+        const bool ok = row < m;
+        const unsigned short *pu = uhl + row * kp + kk + g * 8;
+        uh[rs] = ok ? *(const ushortx8 *)pu : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
+        ul[rs] = ok ? *(const ushortx8 *)(pu + um) : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int cs = 0; cs < 8; ++cs) {
+        const int64_t col = col0 + cs * 16 + r16;
+        const bool ok = col < n;
+        const unsigned short *pw = whl + col * kp + kk + g * 8;
+        const ushortx8 wh = ok ? *(const ushortx8 *)pw : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
+        const ushortx8 wl = ok ? *(const ushortx8 *)(pw + wn) : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int rs = 0; rs < 2; ++rs) {
+          acc[rs][cs] = mfma16_bf16(uh[rs], wh, acc[rs][cs]);
+          acc[rs][cs] = mfma16_bf16(uh[rs], wl, acc[rs][cs]);
+          acc[rs][cs] = mfma16_bf16(ul[rs], wh, acc[rs][cs]);
+        }
+      }
+    }
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int cs = 0; cs < 8; ++cs)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lt[wave * 32 + rs * 16 + g * 4 + q][cs * 16 + r16] = acc[rs][cs][q];
+  }
+  __syncthreads();
+  float s_t = 1.0f;
+  if (NV && !AMAX_ONLY) s_t = nv_tensor_scale(__uint_as_float(*amax));
+  if (NV && !AMAX_ONLY && blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
+    if (rts) *rts = s_t;
+    if (tts) *tts = s_t;
+  }
+  // ---- row blocks (along n): R = A - L, kept in LDS for the column pass
+  float mx = 0.0f;
+  constexpr int RPB = kRT / B;  // blocks per tile row
+  for (int b = t; b < kRT * RPB; b += kThreads) {
+    const int rr = b / RPB, cb = b % RPB;
+    const int64_t row = row0 + rr, col = col0 + cb * B;
+    float v[B];
+    const bool ok = row < m && col < n;
+    if (ok) {
+      const T *src = A + row * lda + col;
+#pragma unroll
+      for (int i = 0; i < B; ++i) v[i] = load_f32(src + i) - lt[rr][cb * B + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < B; ++i) v[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      lt[rr][cb * B + i] = v[i];
+      mx = fmaxf(mx, fabsf(v[i]));
+    }
+    if (!AMAX_ONLY && ok && rcodes)
+      quant_store<B, NV>(v, s_t, rcodes + row * (n / 2) + col / 2, rscales + row * (n / B) + col / B);
+  }
+  if (AMAX_ONLY) {
+    mx = wave_max(mx);
+    if (lane == 0) atomicMax(amax, __float_as_uint(mx));
+    return;
+  }
+  if (!tcodes) return;
+  __syncthreads();
+  // ---- column blocks (along m) into R^T (n x m)
+  for (int b = t; b < kRT * RPB; b += kThreads) {
+    const int cc = b % kRT, rb = b / kRT;
+    const int64_t col = col0 + cc, row = row0 + rb * B;
+    if (col >= n || row >= m) continue;
+    float v[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) v[i] = lt[rb * B + i][cc];
+    quant_store<B, NV>(v, s_t, tcodes + col * (m / 2) + row / 2, tscales + col * (m / B) + row / B);
+  }
+}
+
+// ==================================================================== host
+template <typename T>
+metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void *omega, metis_split_t *out,
+                         int32_t *info, hipStream_t st) {
+  const int64_t m = p.m, n = p.n;
+  const int l = p.l, lp = p.lp, k = p.k, kp = p.kp;
+  const bool nv = p.fmt == METIS_NVFP4;
+  // ---- pass 1: sketch
+  const float *ysrc;
+  int yparts;
+  if (p.kind == METIS_OMEGA_GAUSSIAN) {
+    omega_transpose_kernel<<<dim3((unsigned)cdiv(n, 256), lp), 256, 0, st>>>((const unsigned short *)omega, n, l, lp,
+                                                                          p.omt);
+    sketch_kernel<T><<<dim3((unsigned)cdiv(m, 128), p.sk), kThreads, 0, st>>>(A, m, n, lda, p.omt, l, lp, p.sk_chunk,
+                                                                             p.ysk);
+    ysrc = p.ysk;
+    yparts = p.sk;
+  } else {
+    gather_kernel<T><<<(unsigned)cdiv(m * l, 256), 256, 0, st>>>(A, m, n, lda, (const int *)omega, l, p.ysk);
+    ysrc = p.ysk;
+    yparts = 1;
+  }
+  // ---- CholeskyQR2
+  gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(ysrc, yparts, m * l, m, l, lp, p.gy_rows, nullptr,
+                                               yparts > 1 ? p.y : nullptr, nullptr, p.gpart);
+  const float *y = yparts > 1 ? p.y : ysrc;
+  gram_reduce_kernel<<<(unsigned)cdiv(lp * lp, 256), 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
+  chol_inv_kernel<<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws);
+  gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(y, 1, 0, m, l, lp, p.gy_rows, p.rinv, p.q1, nullptr, p.gpart);
+  gram_reduce_kernel<<<(unsigned)cdiv(lp * lp, 256), 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
+  chol_inv_kernel<<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws);
+  gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(p.q1, 1, 0, m, l, lp, p.gy_rows, p.rinv, p.q, p.qt, nullptr);
+  // ---- pass 2: projection B^T = A^T Q, then the Gram B B^T
+  project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp, p.pk_rows,
+                                                                           p.btp);
+  gram_kernel<<<p.gb_parts, kThreads, 0, st>>>(p.btp, p.pk, n * l, n, l, lp, p.gb_rows, nullptr, p.bt, nullptr,
+                                               p.gpart);
+  gram_reduce_kernel<<<(unsigned)cdiv(lp * lp, 256), 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
+  // ---- small SVD and factors
+  jacobi_kernel<<<1, kJacThreads, 0, st>>>(p.gram, l, lp, k, 40, p.evec, p.sig_inv, out->S);
+  assemble_u_kernel<<<p.am_parts, kThreads, 0, st>>>(p.q, m, l, lp, k, p.evec, p.am_rows, out->U, p.am_val,
+                                                     p.am_idx);
+  assemble_v_kernel<<<(unsigned)cdiv(n, 64), kThreads, 0, st>>>(p.bt, n, l, lp, k, p.evec, p.sig_inv, out->V);
+  sign_kernel<<<1, 128, 0, st>>>(p.am_val, p.am_idx, p.am_parts, k, p.sign);
+  const int B = nv ? 16 : 32;
+  const unsigned fgrid = (unsigned)cdiv(std::max(m, n) / B * kp, kThreads);
+  if (nv) {
+    fill_u32<<<1, 64, 0, st>>>(p.amax, 0u, 8);
+    amax_f32_kernel<<<64, 256, 0, st>>>(out->U, m, k, p.amax + 0);
+    amax_f32_kernel<<<64, 256, 0, st>>>(out->V, n, k, p.amax + 1);
+    factor_kernel<true><<<dim3(fgrid, 2), kThreads, 0, st>>>(
+        out->U, out->V, m, n, k, kp, p.sign, out->S, out->Ut_q.codes, out->Ut_q.scales, out->Ut_q.tensor_scale,
+        out->Vt_q.codes, out->Vt_q.scales, out->Vt_q.tensor_scale, p.amax, p.uhl, p.whl);
+  } else {
+    factor_kernel<false><<<dim3(fgrid, 2), kThreads, 0, st>>>(
+        out->U, out->V, m, n, k, kp, p.sign, out->S, out->Ut_q.codes, out->Ut_q.scales, nullptr, out->Vt_q.codes,
+        out->Vt_q.scales, nullptr, p.amax, p.uhl, p.whl);
+  }
+  // ---- pass 3: residual + quantization (NVFP4: a max pass first)
+  const dim3 rgrid((unsigned)cdiv(n, kRT), (unsigned)cdiv(m, kRT));
+  if (nv) {
+    residual_kernel<T, true, true><<<rgrid, kThreads, 0, st>>>(A, m, n, lda, p.uhl, p.whl, kp, nullptr, nullptr,
+                                                              nullptr, nullptr, nullptr, nullptr, p.amax + 2);
+    residual_kernel<T, true, false><<<rgrid, kThreads, 0, st>>>(
+        A, m, n, lda, p.uhl, p.whl, kp, out->R_q.codes, out->R_q.scales, out->R_q.tensor_scale, out->Rt_q.codes,
+        out->Rt_q.scales, out->Rt_q.tensor_scale, p.amax + 2);
+  } else {
+    residual_kernel<T, false, false><<<rgrid, kThreads, 0, st>>>(A, m, n, lda, p.uhl, p.whl, kp, out->R_q.codes,
+                                                                out->R_q.scales, nullptr, out->Rt_q.codes,
+                                                                out->Rt_q.scales, nullptr, nullptr);
+  }
+  METIS_LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+bool fp4_ok(const metis_fp4_t &q, int fmt, bool need_ts) {
+  return q.codes && q.scales && q.fmt == fmt && (((uintptr_t)q.codes) & 15) == 0 && (!need_ts || q.tensor_scale);
+}
+
+}  // namespace
+
+extern "C" size_t metis_split_workspace_bytes(int64_t m, int64_t n, int32_t l, int32_t k, metis_omega_t kind,
+                                              metis_fmt_t fmt) {
+  if (m <= 0 || n <= 0 || l <= 0 || k <= 0) return 0;
+  // the plan depends on the element size; cover both input types
+  return std::max(make_plan(m, n, l, k, kind, fmt, 4, nullptr).bytes, make_plan(m, n, l, k, kind, fmt, 2, nullptr).bytes);
+}
+
+extern "C" metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                      const void *omega, metis_omega_t kind, int32_t l, int32_t k, metis_fmt_t fmt,
+                                      metis_split_t *out, int32_t *info, void *ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  if (!A || !omega || !out) return METIS_ERR_INVALID;
+  if (dt != METIS_F32 && dt != METIS_BF16) return METIS_ERR_INVALID;
+  if (fmt != METIS_MXFP4 && fmt != METIS_NVFP4) return METIS_ERR_INVALID;
+  if (kind != METIS_OMEGA_GAUSSIAN && kind != METIS_OMEGA_COLUMNS) return METIS_ERR_INVALID;
+  if (m <= 0 || n <= 0 || m % 32 || n % 32 || lda < n) return METIS_ERR_INVALID;
+  if (k < 1 || l < k || l > m || l > n) return METIS_ERR_INVALID;
+  const int elem = dt == METIS_F32 ? 4 : 2;
+  if (((uintptr_t)A) & 15 || (lda * elem) % 16) return METIS_ERR_INVALID;
+  if (l > kLpMax) return METIS_ERR_UNSUPPORTED;
+  if (!out->U || !out->S || !out->V) return METIS_ERR_INVALID;
+  const bool nv = fmt == METIS_NVFP4;
+  if (!fp4_ok(out->Ut_q, fmt, nv) || !fp4_ok(out->Vt_q, fmt, nv)) return METIS_ERR_INVALID;
+  const bool want_n = out->R_q.codes != nullptr, want_t = out->Rt_q.codes != nullptr;
+  if (want_n && !fp4_ok(out->R_q, fmt, nv)) return METIS_ERR_INVALID;
+  if (want_t && !fp4_ok(out->Rt_q, fmt, nv)) return METIS_ERR_INVALID;
+  if (!ws) return METIS_ERR_WORKSPACE;
+  if (((uintptr_t)ws) & 255) return METIS_ERR_INVALID;
+  SplitPlan p = make_plan(m, n, l, k, kind, fmt, elem, ws);
+  if (ws_bytes < p.bytes) return METIS_ERR_WORKSPACE;
+  out->m = m;
+  out->n = n;
+  out->k = k;
+  out->Ut_q.rows = k; out->Ut_q.cols = m;
+  out->Vt_q.rows = k; out->Vt_q.cols = n;
+  out->R_q.rows = m; out->R_q.cols = n;
+  out->Rt_q.rows = n; out->Rt_q.cols = m;
+  if (dt == METIS_F32) return run_split<float>(p, (const float *)A, lda, omega, out, info, stream);
+  return run_split<unsigned short>(p, (const unsigned short *)A, lda, omega, out, info, stream);
+}
