@@ -78,13 +78,21 @@ def load():
     L.spectral_fp4_linear_fwd.argtypes = [ctypes.POINTER(_Split), ctypes.POINTER(_Split), vp, i64, vp, sz, vp]
     L.spectral_fp4_linear_bwd.restype = i32
     L.spectral_fp4_linear_bwd.argtypes = [ctypes.POINTER(_Split)] * 3 + [vp, i64, vp, i64, vp, sz, vp]
+    sp = ctypes.POINTER(_Split)
+    L.metis_gemm_nt_workspace_bytes.restype = sz
+    L.metis_gemm_nt_workspace_bytes.argtypes = [sp, i32, sp, i32]
+    L.metis_gemm_nt_prepare.restype = i32
+    L.metis_gemm_nt_prepare.argtypes = [sp, i32, sp, i32, vp, sz, vp]
+    L.metis_gemm_nt_main.restype = i32
+    L.metis_gemm_nt_main.argtypes = [sp, i32, sp, i32, vp, i64, vp, sz, vp]
     _lib = L
     return L
 
 
 EXPORTS = ["metis_status_str", "metis_abi_version", "fp4_block_quant_workspace_bytes", "fp4_block_quant",
            "fp4_block_dequant", "metis_split_workspace_bytes", "metis_split", "metis_linear_workspace_bytes",
-           "spectral_fp4_linear_fwd", "spectral_fp4_linear_bwd"]
+           "spectral_fp4_linear_fwd", "spectral_fp4_linear_bwd", "metis_gemm_nt_workspace_bytes",
+           "metis_gemm_nt_prepare", "metis_gemm_nt_main"]
 
 
 def _check(status):
@@ -298,3 +306,43 @@ def spectral_fp4_linear_bwd(dY, X, W, need_dx=True, need_dw=True, dx=None, dw=No
                                      _ptr(dw) if need_dw else None, dw.stride(0) if need_dw else 0,
                                      _ptr(ws), n, _stream(dev)))
     return dx, dw
+
+
+def _dev(rec):
+    q = rec.R_q if rec.R_q is not None else rec.Rt_q
+    return q.codes.device
+
+
+class GemmNT:
+    """One GEMM C = A_hat B_hat^T split into prepare (skinny FP4 products and
+    correction panels) and main (FP4 GEMM + correction), sharing a workspace
+    owned by this object. trans_a / trans_b pick the orientation of each
+    operand (False: R_q, contraction over n; True: Rt_q, over m)."""
+
+    def __init__(self, a, trans_a, b, trans_b):
+        L = load()
+        self.a, self.b = a, b
+        self.ta, self.tb = int(bool(trans_a)), int(bool(trans_b))
+        self.ca, self.cb = a.c(), b.c()
+        self.rows = a.n if trans_a else a.m
+        self.cols = b.n if trans_b else b.m
+        dev = _dev(a)
+        self.nbytes = L.metis_gemm_nt_workspace_bytes(ctypes.byref(self.ca), self.ta, ctypes.byref(self.cb), self.tb)
+        self.ws = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=dev)
+
+    def prepare(self):
+        _check(load().metis_gemm_nt_prepare(ctypes.byref(self.ca), self.ta, ctypes.byref(self.cb), self.tb,
+                                            _ptr(self.ws), self.nbytes, _stream(self.ws.device)))
+
+    def main(self, out):
+        assert out.shape[0] >= self.rows and out.stride(1) == 1
+        _check(load().metis_gemm_nt_main(ctypes.byref(self.ca), self.ta, ctypes.byref(self.cb), self.tb, _ptr(out),
+                                         out.stride(0), _ptr(self.ws), self.nbytes, _stream(out.device)))
+        return out
+
+    def __call__(self, out=None):
+        if out is None:
+            out = torch.empty(self.rows, self.cols, dtype=torch.float32, device=self.ws.device)
+        self.prepare()
+        return self.main(out)
+

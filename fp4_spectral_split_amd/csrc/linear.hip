@@ -1,19 +1,553 @@
-// W4A4G4 linear layer (placeholder entry points; kernels follow).
+// W4A4G4 linear layer on quantized split operands ("Metis: Training LLMs with
+// FP4 Quantization", abstract: FP4 weights, activations and gradients).
+//
+// Each GEMM is C = A_hat B_hat^T with, for a split operand in the orientation
+// it is used in, A_hat = R + G diag(S) F^T (R: residual blocked along the
+// contraction axis T; F: the factor along T, quantized along T; G: the factor
+// along the output axis). Expanding both operands:
+//   C = Ra Rb^T + (Ra Fb Sb) Gb^T + Ga [Sa (Fa^T Rb^T + (Fa^T Fb) Sb Gb^T)]
+//     = Ra Rb^T + L1 L2^T,
+//   L1 = [P_hi  P_lo  Ga  Ga],  L2 = [Gb  Gb  Q_hi  Q_lo],
+//   P  = Ra Fb diag(Sb),        Q  = (Rb Fa + Gb diag(Sb) (Fa^T Fb)^T) diag(Sa).
+// G values are FP4 codes times power-of-two scales, exact in bf16; P and Q are
+// carried as bf16 hi + lo (16 significant bits), so the bf16 MFMA correction
+// is fp32-accurate. Kernels:
+//   skinny_kernel  P, Q and Fa^T Fb on the scaled FP4 MFMA (split-K partials)
+//   panel_kernel   sums the partials and writes the bf16 panels L1, L2
+//   gemm_kernel    Ra Rb^T on v_mfma_scale_f32_32x32x64_f8f6f4 (256 x 256
+//                  tiles, LDS double buffer), then + L1 L2^T on bf16 MFMA into
+//                  the same accumulators, then one fp32 store.
+#include <algorithm>
+
 #include "common.hpp"
+
+using namespace metis;
+
+namespace {
+
+// ---------------------------------------------------------------- operands
+// One side of an NT GEMM: residual R (rows x T) blocked along T, factors.
+struct Side {
+  const metis_fp4_t *R;
+  const metis_fp4_t *F;  // contracted factor, k x T (blocked along T)
+  const metis_fp4_t *G;  // outer factor, k x rows (blocked along rows)
+  const float *S;
+  int64_t rows, T;
+  int k;
+};
+
+bool make_side(const metis_split_t *s, bool transposed, Side &out) {
+  out.R = transposed ? &s->Rt_q : &s->R_q;
+  out.rows = transposed ? s->n : s->m;
+  out.T = transposed ? s->m : s->n;
+  if (out.rows < 0 || out.T < 0) return false;
+  if (out.rows > 0 && out.T > 0 && (!out.R->codes || !out.R->scales)) return false;
+  out.k = s->k;
+  out.S = s->S;
+  out.F = transposed ? &s->Ut_q : &s->Vt_q;
+  out.G = transposed ? &s->Vt_q : &s->Ut_q;
+  if (s->k > 0 && (!s->S || !out.F->codes || !out.F->scales || !out.G->codes || !out.G->scales)) return false;
+  if (s->k > 0 && (out.F->rows != s->k || out.F->cols != out.T || out.G->rows != s->k || out.G->cols != out.rows ||
+                   out.rows % 32 || (((uintptr_t)out.F->codes) & 15)))
+    return false;
+  return true;
+}
+
+struct GemmPlan {
+  int64_t ra, rb, T;
+  int ka, kb, rp;
+  int ks_p, ks_q, ks_c;          // split-K counts of the skinny products
+  int64_t tc_p, tc_q, tc_c;      // T per split (multiple of 128)
+  float *ppart, *qpart, *cpart;  // partials
+  unsigned short *l1, *l2;       // panels
+  size_t bytes;
+};
+
+int64_t pick_split(int64_t row_tiles, int64_t T, int64_t &chunk) {
+  int64_t want = std::max<int64_t>(1, cdiv(512, std::max<int64_t>(1, row_tiles)));
+  want = std::min<int64_t>(want, std::max<int64_t>(1, T / 512));
+  chunk = round_up(cdiv(T, want), 128);
+  return cdiv(T, chunk);
+}
+
+GemmPlan make_gemm_plan(int64_t ra, int64_t rb, int64_t T, int ka, int kb, void *ws) {
+  GemmPlan p;
+  p.ra = ra; p.rb = rb; p.T = T; p.ka = ka; p.kb = kb;
+  p.rp = (int)round_up(2 * ka + 2 * kb, 64);
+  p.ks_p = kb ? (int)pick_split(cdiv(ra, 32), T, p.tc_p) : 0;
+  p.ks_q = ka ? (int)pick_split(cdiv(rb, 32), T, p.tc_q) : 0;
+  p.ks_c = (ka && kb) ? (int)pick_split(1, T, p.tc_c) : 0;
+  metis_host::Carver c(ws);
+  p.ppart = c.take<float>((size_t)p.ks_p * ra * kb);
+  p.qpart = c.take<float>((size_t)p.ks_q * rb * ka);
+  p.cpart = c.take<float>((size_t)p.ks_c * ka * kb);
+  p.l1 = c.take<unsigned short>((size_t)ra * p.rp);
+  p.l2 = c.take<unsigned short>((size_t)rb * p.rp);
+  p.bytes = c.bytes();
+  return p;
+}
+
+// Packed FP4 view of an MFMA operand: 32 codes (16 bytes) in 4 dwords.
+__device__ __forceinline__ intx8 fp4x32(const uint4 v) { return intx8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0}; }
+
+__device__ __forceinline__ floatx16 mfma_fp4(const uint4 a, const uint4 b, int sa, int sb, floatx16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4x32(a), fp4x32(b), c, 4, 4, 0, sa, 0, sb);
+}
+
+// ================================================================== skinny
+// out[s] (rows x cols) = NT(A (rows x T), B (cols x T)) over T-chunk s, both
+// MXFP4. One wave: 32 rows x (32 * NCT) columns. Per 128-element step each
+// lane reads 32 contiguous code bytes (two scale blocks) of its row; the two
+// MFMAs take the first and second 16 bytes, so every lane's K slots line up
+// between the A and B operands.
+template <int NCT>
+__global__ void __launch_bounds__(64)
+    skinny_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t rows,
+                  const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int cols, int64_t T, int64_t chunk,
+                  float *__restrict__ out) {
+  const int lane = threadIdx.x;
+  const int r = lane & 31, h = lane >> 5;
+  const int64_t row = (int64_t)blockIdx.x * 32 + r;
+  const int s = blockIdx.y;
+  const int64_t t_beg = (int64_t)s * chunk, t_end = std::min<int64_t>(T, t_beg + chunk);
+  const int64_t nb = T / 32;  // scale blocks per row
+  floatx16 acc[NCT];
+#pragma unroll
+  for (int j = 0; j < NCT; ++j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[j][q] = 0.0f;
+  const bool rok = row < rows;
+  for (int64_t t0 = t_beg; t0 < t_end; t0 += 128) {
+    const int64_t e0 = t0 + h * 64;  // first element of this lane's two blocks
+    uint4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+    int sa0 = 127, sa1 = 127;
+    if (rok && e0 < t_end) {
+      const uint4 *p = (const uint4 *)(ac + row * (T / 2) + e0 / 2);
+      a0 = p[0];
+      sa0 = as[row * nb + e0 / 32];
+      if (e0 + 32 < t_end) {
+        a1 = p[1];
+        sa1 = as[row * nb + e0 / 32 + 1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int col = j * 32 + r;
+      uint4 b0 = {0u, 0u, 0u, 0u}, b1 = {0u, 0u, 0u, 0u};
+      int sb0 = 127, sb1 = 127;
+      if (col < cols && e0 < t_end) {
+        const uint4 *p = (const uint4 *)(bc + (int64_t)col * (T / 2) + e0 / 2);
+        b0 = p[0];
+        sb0 = bs[(int64_t)col * nb + e0 / 32];
+        if (e0 + 32 < t_end) {
+          b1 = p[1];
+          sb1 = bs[(int64_t)col * nb + e0 / 32 + 1];
+        }
+      }
+      acc[j] = mfma_fp4(a0, b0, sa0, sb0, acc[j]);
+      acc[j] = mfma_fp4(a1, b1, sa1, sb1, acc[j]);
+    }
+  }
+  float *o = out + (int64_t)s * rows * cols;
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) {
+    const int col = j * 32 + r;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int64_t orow = (int64_t)blockIdx.x * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+      if (orow < rows && col < cols) o[orow * cols + col] = acc[j][q];
+    }
+  }
+}
+
+// =================================================================== panels
+// Decoded MXFP4 value of element i of row c of a k x rows factor matrix.
+__device__ __forceinline__ float factor_value(const uint8_t *codes, const uint8_t *scales, int64_t rows, int c,
+                                              int64_t i) {
+  const uint32_t byte = codes[(int64_t)c * (rows / 2) + i / 2];
+  const uint32_t code = (i & 1) ? (byte >> 4) : (byte & 15u);
+  return ldexpf(e2m1_value(code), (int)scales[(int64_t)c * (rows / 32) + i / 32] - 127);
+}
+
+// Rows [0, ra) build L1, rows [ra, ra + rb) build L2 (one 64-thread group per
+// row; columns strided). cross (ka x kb) is summed once per block into LDS.
+__global__ void __launch_bounds__(256)
+    panel_kernel(int64_t ra, int64_t rb, int ka, int kb, int rp, const float *__restrict__ ppart, int ks_p,
+                 const float *__restrict__ qpart, int ks_q, const float *__restrict__ cpart, int ks_c,
+                 const float *__restrict__ Sa, const float *__restrict__ Sb, const uint8_t *__restrict__ ga_c,
+                 const uint8_t *__restrict__ ga_s, const uint8_t *__restrict__ gb_c, const uint8_t *__restrict__ gb_s,
+                 unsigned short *__restrict__ l1, unsigned short *__restrict__ l2) {
+  __shared__ float cross[96][97];
+  __shared__ float gsb[4][96];  // Gb[j][d] * Sb[d] for the 4 rows of this block
+  const int t = threadIdx.x;
+  const int sub = t >> 6, lane = t & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + sub;
+  const bool need_cross = ka && kb && blockIdx.x * 4 + 3 >= ra;
+  if (need_cross) {
+    for (int e = t; e < ka * kb; e += 256) {
+      float v = 0.0f;
+      for (int s = 0; s < ks_c; ++s) v += cpart[(int64_t)s * ka * kb + e];
+      cross[e / kb][e % kb] = v;
+    }
+  }
+  if (row >= ra && row < ra + rb && kb) {
+    const int64_t j = row - ra;
+    for (int d = lane; d < kb; d += 64) gsb[sub][d] = factor_value(gb_c, gb_s, rb, d, j) * Sb[d];
+  }
+  __syncthreads();
+  if (row < ra) {
+    unsigned short *o = l1 + row * rp;
+    for (int c = lane; c < rp; c += 64) {
+      unsigned short v = 0;
+      if (c < 2 * kb) {
+        const int d = c % kb;
+        float p = 0.0f;
+        for (int s = 0; s < ks_p; ++s) p += ppart[((int64_t)s * ra + row) * kb + d];
+        p *= Sb[d];
+        unsigned short hi, lo;
+        split_bf16(p, hi, lo);
+        v = c < kb ? hi : lo;
+      } else if (c < 2 * kb + 2 * ka) {
+        const int cc = (c - 2 * kb) % ka;
+        v = f32_to_bf16(factor_value(ga_c, ga_s, ra, cc, row));
+      }
+      o[c] = v;
+    }
+  } else if (row < ra + rb) {
+    const int64_t j = row - ra;
+    unsigned short *o = l2 + j * rp;
+    for (int c = lane; c < rp; c += 64) {
+      unsigned short v = 0;
+      if (c < 2 * kb) {
+        v = f32_to_bf16(factor_value(gb_c, gb_s, rb, c % kb, j));
+      } else if (c < 2 * kb + 2 * ka) {
+        const int cc = (c - 2 * kb) % ka;
+        float q = 0.0f;
+        for (int s = 0; s < ks_q; ++s) q += qpart[((int64_t)s * rb + j) * ka + cc];
+        for (int d = 0; d < kb; ++d) q += gsb[sub][d] * cross[cc][d];
+        q *= Sa[cc];
+        unsigned short hi, lo;
+        split_bf16(q, hi, lo);
+        v = c < 2 * kb + ka ? hi : lo;
+      }
+      o[c] = v;
+    }
+  }
+}
+
+// ==================================================================== GEMM
+constexpr int BM = 256, BN = 256;
+constexpr int BKB = 64;         // code bytes per row per stage (128 FP4 elements)
+constexpr int ROWB = BKB + 16;  // LDS row stride (bytes), conflict-free b128 reads
+constexpr int STAGE_BYTES = 2 * BM * ROWB + 2 * BM * 4;
+constexpr int EPI_ROWB = 128 + 16;  // bf16 panel chunk: 64 values + pad
+
+__device__ __forceinline__ void tile_coords(int &tm, int &tn, int mt, int nt) {
+  // XCD-aware order: consecutive dispatch ids go round-robin over the 8 XCDs;
+  // regroup so each XCD walks a contiguous range of tiles, grouped 8 tile-rows
+  // at a time (A and B tiles in flight on one XCD share its L2).
+  int w = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) w = (w & 7) * (nwg >> 3) + (w >> 3);
+  constexpr int GM = 8;
+  const int group = GM * nt;
+  const int g = w / group, first = g * GM;
+  const int gm = min(mt - first, GM);
+  const int in = w - g * group;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+__global__ void __launch_bounds__(256, 1)
+    gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
+                const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int64_t N, int64_t T,
+                const unsigned short *__restrict__ l1, const unsigned short *__restrict__ l2, int rp,
+                float *__restrict__ C, int64_t ldc) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(tm, tn, (int)cdiv(M, BM), (int)cdiv(N, BN));
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t nb = T / 32;
+  const int nst = (int)cdiv(T, 128);
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  // global -> register staging: 4 pieces of 16 bytes per operand + 1 scale word
+  uint4 ga[4], gb[4];
+  uint32_t gsa, gsb;
+  auto load_stage = [&](int st) {
+    const int64_t k0 = (int64_t)st * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = (t >> 2) + 64 * i, piece = t & 3;
+      const int64_t e = k0 + piece * 32;
+      const int64_t ar = m0 + rr, br = n0 + rr;
+      ga[i] = (ar < M && e < T) ? *(const uint4 *)(ac + ar * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
+      gb[i] = (br < N && e < T) ? *(const uint4 *)(bc + br * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
+    }
+    const int64_t ar = m0 + t, br = n0 + t;
+    uint32_t wa = 0x7F7F7F7Fu, wb = 0x7F7F7F7Fu;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t blk = k0 / 32 + q;
+      if (blk < nb) {
+        if (ar < M) wa = (wa & ~(0xFFu << (8 * q))) | ((uint32_t)as[ar * nb + blk] << (8 * q));
+        if (br < N) wb = (wb & ~(0xFFu << (8 * q))) | ((uint32_t)bs[br * nb + blk] << (8 * q));
+      }
+    }
+    gsa = wa;
+    gsb = wb;
+  };
+  auto store_stage = [&](int buf) {
+    uint8_t *base = smem + buf * STAGE_BYTES;
+    uint8_t *A_ = base, *B_ = base + BM * ROWB;
+    uint32_t *SA = (uint32_t *)(base + 2 * BM * ROWB), *SB = SA + BM;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = (t >> 2) + 64 * i, piece = t & 3;
+      *(uint4 *)(A_ + rr * ROWB + piece * 16) = ga[i];
+      *(uint4 *)(B_ + rr * ROWB + piece * 16) = gb[i];
+    }
+    SA[t] = gsa;
+    SB[t] = gsb;
+  };
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < nst) load_stage(st + 1);
+    const uint8_t *base = smem + cur * STAGE_BYTES;
+    const uint8_t *A_ = base, *B_ = base + BM * ROWB;
+    const uint8_t *SA = base + 2 * BM * ROWB, *SB = SA + BM * 4;
+    uint4 af[4][2], bf[4][2];
+    int sa[4][2], sb[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = wm * 128 + i * 32 + r32;
+      af[i][0] = *(const uint4 *)(A_ + rr * ROWB + h * 32);
+      af[i][1] = *(const uint4 *)(A_ + rr * ROWB + h * 32 + 16);
+      const uint32_t s2 = *(const unsigned short *)(SA + rr * 4 + h * 2);
+      sa[i][0] = (int)(s2 & 0xFFu);
+      sa[i][1] = (int)(s2 >> 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rr = wn * 128 + j * 32 + r32;
+      bf[j][0] = *(const uint4 *)(B_ + rr * ROWB + h * 32);
+      bf[j][1] = *(const uint4 *)(B_ + rr * ROWB + h * 32 + 16);
+      const uint32_t s2 = *(const unsigned short *)(SB + rr * 4 + h * 2);
+      sb[j][0] = (int)(s2 & 0xFFu);
+      sb[j][1] = (int)(s2 >> 8);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(af[i][ks], bf[j][ks], sa[i][ks], sb[j][ks], acc[i][j]);
+    if (st + 1 < nst) store_stage(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- low-rank correction: acc += L1[m-tile] L2[n-tile]^T (bf16, 64 at a time)
+  if (rp > 0) {
+    uint8_t *L1s = smem, *L2s = smem + BM * EPI_ROWB;
+    for (int c0 = 0; c0 < rp; c0 += 64) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = t + 256 * i;  // 2048 pieces of 16 bytes per panel
+        const int rr = idx >> 3, piece = idx & 7;
+        const int64_t ar = m0 + rr, br = n0 + rr;
+        const uint4 va = ar < M ? *(const uint4 *)(l1 + ar * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
+        const uint4 vb = br < N ? *(const uint4 *)(l2 + br * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
+        *(uint4 *)(L1s + rr * EPI_ROWB + piece * 16) = va;
+        *(uint4 *)(L2s + rr * EPI_ROWB + piece * 16) = vb;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ushortx8 a8[4], b8[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a8[i] = *(const ushortx8 *)(L1s + (wm * 128 + i * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b8[j] = *(const ushortx8 *)(L2s + (wn * 128 + j * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- store (fp32)
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + wn * 128 + j * 32 + r32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + wm * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+        if (row < M) C[row * ldc + col] = acc[i][j][q];
+      }
+    }
+}
+
+static_assert(2 * BM * EPI_ROWB <= 2 * STAGE_BYTES, "epilogue panels must fit the main-loop LDS");
+
+// ====================================================================== host
+void launch_skinny(const metis_fp4_t *A, int64_t rows, const metis_fp4_t *B, int cols, int64_t T, int ks,
+                   int64_t chunk, float *out, hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(rows, 32), ks);
+  if (cols <= 32)
+    skinny_kernel<1><<<grid, 64, 0, st>>>(A->codes, A->scales, rows, B->codes, B->scales, cols, T, chunk, out);
+  else if (cols <= 64)
+    skinny_kernel<2><<<grid, 64, 0, st>>>(A->codes, A->scales, rows, B->codes, B->scales, cols, T, chunk, out);
+  else
+    skinny_kernel<3><<<grid, 64, 0, st>>>(A->codes, A->scales, rows, B->codes, B->scales, cols, T, chunk, out);
+}
+
+metis_status_t check_pair(const Side &a, const Side &b) {
+  if (a.T != b.T) return METIS_ERR_INVALID;
+  if (a.R->fmt != METIS_MXFP4 || b.R->fmt != METIS_MXFP4) return METIS_ERR_UNSUPPORTED;
+  if (a.k > 96 || b.k > 96) return METIS_ERR_UNSUPPORTED;
+  if (a.rows == 0 || b.rows == 0 || a.T == 0) return METIS_OK;
+  if (a.R->rows != a.rows || a.R->cols != a.T || b.R->rows != b.rows || b.R->cols != b.T) return METIS_ERR_INVALID;
+  if (a.T % 32 || (((uintptr_t)a.R->codes) & 15) || (((uintptr_t)b.R->codes) & 15)) return METIS_ERR_INVALID;
+  return METIS_OK;
+}
+
+// Stage 1 + panels: everything the main kernel needs besides the residuals.
+metis_status_t gemm_prepare(const Side &a, const Side &b, void *ws, size_t ws_bytes, hipStream_t st) {
+  metis_status_t s = check_pair(a, b);
+  if (s != METIS_OK) return s;
+  if (a.rows == 0 || b.rows == 0 || a.T == 0 || (a.k == 0 && b.k == 0)) return METIS_OK;
+  GemmPlan p = make_gemm_plan(a.rows, b.rows, a.T, a.k, b.k, ws);
+  if (!ws || ws_bytes < p.bytes) return METIS_ERR_WORKSPACE;
+  if (((uintptr_t)ws) & 255) return METIS_ERR_INVALID;
+  if (b.k) launch_skinny(a.R, a.rows, b.F, b.k, a.T, p.ks_p, p.tc_p, p.ppart, st);
+  if (a.k) launch_skinny(b.R, b.rows, a.F, a.k, a.T, p.ks_q, p.tc_q, p.qpart, st);
+  if (a.k && b.k) launch_skinny(a.F, a.k, b.F, b.k, a.T, p.ks_c, p.tc_c, p.cpart, st);
+  panel_kernel<<<(unsigned)cdiv(a.rows + b.rows, 4), 256, 0, st>>>(
+      a.rows, b.rows, a.k, b.k, p.rp, p.ppart, p.ks_p, p.qpart, p.ks_q, p.cpart, p.ks_c, a.S, b.S,
+      a.k ? a.G->codes : nullptr, a.k ? a.G->scales : nullptr, b.k ? b.G->codes : nullptr,
+      b.k ? b.G->scales : nullptr, p.l1, p.l2);
+  METIS_LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+// Main FP4 GEMM of the residuals plus the low-rank correction from the panels
+// that gemm_prepare left in the same workspace.
+metis_status_t gemm_main(const Side &a, const Side &b, float *C, int64_t ldc, const void *ws, size_t ws_bytes,
+                         hipStream_t st) {
+  metis_status_t s = check_pair(a, b);
+  if (s != METIS_OK) return s;
+  if (ldc < b.rows) return METIS_ERR_INVALID;
+  if (a.rows == 0 || b.rows == 0) return METIS_OK;
+  if (!C) return METIS_ERR_INVALID;
+  int rp = 0;
+  const unsigned short *l1 = nullptr, *l2 = nullptr;
+  if (a.k || b.k) {
+    GemmPlan p = make_gemm_plan(a.rows, b.rows, a.T, a.k, b.k, (void *)ws);
+    if (!ws || ws_bytes < p.bytes) return METIS_ERR_WORKSPACE;
+    if (((uintptr_t)ws) & 255) return METIS_ERR_INVALID;
+    rp = p.rp;
+    l1 = p.l1;
+    l2 = p.l2;
+  }
+  const unsigned tiles = (unsigned)(cdiv(a.rows, BM) * cdiv(b.rows, BN));
+  gemm_kernel<<<tiles, 256, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows, a.T, l1, l2,
+                                    rp, C, ldc);
+  METIS_LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+metis_status_t gemm_nt(const Side &a, const Side &b, float *C, int64_t ldc, void *ws, size_t ws_bytes,
+                       hipStream_t st) {
+  metis_status_t s = gemm_prepare(a, b, ws, ws_bytes, st);
+  if (s != METIS_OK) return s;
+  return gemm_main(a, b, C, ldc, ws, ws_bytes, st);
+}
+
+size_t gemm_bytes(const metis_split_t *a, bool at, const metis_split_t *b, bool bt) {
+  const int64_t ra = at ? a->n : a->m, rb = bt ? b->n : b->m, T = at ? a->m : a->n;
+  return make_gemm_plan(ra, rb, T, a->k, b->k, nullptr).bytes;
+}
+
+}  // namespace
+
+extern "C" size_t metis_gemm_nt_workspace_bytes(const metis_split_t *a, int32_t a_trans, const metis_split_t *b,
+                                                int32_t b_trans) {
+  if (!a || !b) return 0;
+  return gemm_bytes(a, a_trans != 0, b, b_trans != 0);
+}
+
+extern "C" metis_status_t metis_gemm_nt_prepare(const metis_split_t *a, int32_t a_trans, const metis_split_t *b,
+                                                int32_t b_trans, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Side sa, sb;
+  if (!a || !b || !make_side(a, a_trans != 0, sa) || !make_side(b, b_trans != 0, sb)) return METIS_ERR_INVALID;
+  return gemm_prepare(sa, sb, ws, ws_bytes, stream);
+}
+
+extern "C" metis_status_t metis_gemm_nt_main(const metis_split_t *a, int32_t a_trans, const metis_split_t *b,
+                                             int32_t b_trans, float *C, int64_t ldc, const void *ws, size_t ws_bytes,
+                                             hipStream_t stream) {
+  Side sa, sb;
+  if (!a || !b || !make_side(a, a_trans != 0, sa) || !make_side(b, b_trans != 0, sb)) return METIS_ERR_INVALID;
+  return gemm_main(sa, sb, C, ldc, ws, ws_bytes, stream);
+}
 
 extern "C" size_t metis_linear_workspace_bytes(const metis_split_t *X, const metis_split_t *W,
                                                const metis_split_t *dY) {
-  (void)X; (void)W; (void)dY;
-  return 256;
+  if (!X || !W) return 0;
+  size_t n = gemm_bytes(X, false, W, false);
+  if (dY) {
+    n = std::max(n, gemm_bytes(dY, false, W, true));
+    n = std::max(n, gemm_bytes(dY, true, X, true));
+  }
+  return n;
 }
+
 extern "C" metis_status_t spectral_fp4_linear_fwd(const metis_split_t *X, const metis_split_t *W, float *Y,
                                                   int64_t ldy, void *ws, size_t ws_bytes, hipStream_t stream) {
-  (void)X; (void)W; (void)Y; (void)ldy; (void)ws; (void)ws_bytes; (void)stream;
-  return METIS_ERR_UNSUPPORTED;
+  if (!X || !W || X->n != W->n || X->k < 0 || W->k < 0) return METIS_ERR_INVALID;
+  Side a, b;
+  if (!make_side(X, false, a) || !make_side(W, false, b)) return METIS_ERR_INVALID;
+  return gemm_nt(a, b, Y, ldy, ws, ws_bytes, stream);
 }
+
 extern "C" metis_status_t spectral_fp4_linear_bwd(const metis_split_t *dY, const metis_split_t *X,
                                                   const metis_split_t *W, float *dX, int64_t lddx, float *dW,
                                                   int64_t lddw, void *ws, size_t ws_bytes, hipStream_t stream) {
-  (void)dY; (void)X; (void)W; (void)dX; (void)lddx; (void)dW; (void)lddw; (void)ws; (void)ws_bytes; (void)stream;
-  return METIS_ERR_UNSUPPORTED;
+  if (!dY || !X || !W) return METIS_ERR_INVALID;
+  if (dY->m != X->m || dY->n != W->m || X->n != W->n) return METIS_ERR_INVALID;
+  if (dX) {
+    Side a, b;
+    if (!make_side(dY, false, a) || !make_side(W, true, b)) return METIS_ERR_INVALID;
+    const metis_status_t s = gemm_nt(a, b, dX, lddx, ws, ws_bytes, stream);
+    if (s != METIS_OK) return s;
+  }
+  if (dW) {
+    Side a, b;
+    if (!make_side(dY, true, a) || !make_side(X, true, b)) return METIS_ERR_INVALID;
+    const metis_status_t s = gemm_nt(a, b, dW, lddw, ws, ws_bytes, stream);
+    if (s != METIS_OK) return s;
+  }
+  return METIS_OK;
 }

@@ -145,8 +145,9 @@ metis_status_t fp4_block_dequant(const metis_fp4_t *in, float *y, int64_t ldy, h
  *  omega: METIS_OMEGA_GAUSSIAN: n x l bf16 row-major (the bits of bfloat16
  *         values); METIS_OMEGA_COLUMNS: int32[l] distinct ids in [0, n)
  *         (ids out of range give undefined values, never an out-of-bounds read).
- *  1 <= k <= l <= min(m, n); l <= 128 for the Gaussian sketch, l <= 512 for
- *  column sampling; m and n multiples of 32.
+ *  1 <= k <= l <= min(m, n), l <= 96 (wider sketches return
+ *  METIS_ERR_UNSUPPORTED); m and n multiples of 32; A 16-byte aligned and
+ *  lda * sizeof(element) a multiple of 16.
  *  out:   caller provides U, S, V (fp32) and the codes/scales (/tensor_scale)
  *         buffers of Ut_q, Vt_q, R_q and/or Rt_q (each fp4 member's fmt must
  *         equal `fmt`); the library writes m, n, k and the rows/cols fields.
@@ -182,6 +183,25 @@ metis_status_t spectral_fp4_linear_fwd(const metis_split_t *X, const metis_split
 metis_status_t spectral_fp4_linear_bwd(const metis_split_t *dY, const metis_split_t *X, const metis_split_t *W,
                                        float *dX, int64_t lddx, float *dW, int64_t lddw, void *ws,
                                        size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The two halves of one GEMM C = A_hat B_hat^T (rows of C from operand a,
+ * columns from operand b; a_trans / b_trans select the orientation each
+ * operand is used in: 0 -> R_q, contraction over its n; 1 -> Rt_q,
+ * contraction over its m). spectral_fp4_linear_fwd/bwd are prepare + main.
+ *  prepare: the skinny FP4 products R_a F_b, R_b F_a, F_a^T F_b and the bf16
+ *           correction panels, written into ws;
+ *  main:    the FP4 GEMM of the residuals plus the low-rank correction read
+ *           from ws (left there by prepare on the same stream), fp32 output.
+ * Splitting them lets a caller run the next prepare (in another workspace)
+ * while a main runs, or time the main kernel alone. ws holds
+ * metis_gemm_nt_workspace_bytes() bytes, 256-byte aligned. */
+size_t metis_gemm_nt_workspace_bytes(const metis_split_t *a, int32_t a_trans, const metis_split_t *b,
+                                     int32_t b_trans);
+metis_status_t metis_gemm_nt_prepare(const metis_split_t *a, int32_t a_trans, const metis_split_t *b,
+                                     int32_t b_trans, void *ws, size_t ws_bytes, hipStream_t stream);
+metis_status_t metis_gemm_nt_main(const metis_split_t *a, int32_t a_trans, const metis_split_t *b, int32_t b_trans,
+                                  float *C, int64_t ldc, const void *ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,124 @@
+"""GPU parity of spectral_fp4_linear_fwd / _bwd against the oracle's fp64
+GEMM over the same (GPU-produced) quantized records.
+
+Gate: ||C_gpu - C_oracle||_F / ||C_oracle||_F <= 1e-3 (the GPU accumulates
+exact FP4 products in fp32 and carries the low-rank correction with 16
+significant bits, so the measured error is expected near 1e-6)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import linear as OL
+from tests import _glue as G
+
+pytestmark = pytest.mark.gpu
+
+import fp4_spectral_split_amd as M
+
+C_GATE = 1e-3
+
+
+def _rel(got, want):
+    return np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)
+
+
+def _operand(t, orientations):
+    if t.k:
+        return G.split_gpu(t, orientations=orientations)
+    return M.plain_operand(G.to_gpu(t), t.fmt, orientations)
+
+
+def _small(seed, rows, cols, k, l, kind="planted", dtype="bf16"):
+    return synth.small_case(seed, rows, cols, dtype, kind, k=k, l=l, n_dir=4)
+
+
+@pytest.mark.parametrize("kx,kw,kdy", [(8, 8, 8), (0, 8, 0), (8, 0, 8), (0, 0, 0), (16, 8, 4)])
+def test_linear_fwd_bwd_small(kx, kw, kdy):
+    Mt, K, N = 288, 320, 416  # ragged against the 256 x 256 output tile
+    X = _small(201, Mt, K, kx, kx + 8)
+    W = _small(202, N, K, kw, kw + 8, kind="powerlaw")
+    dY = _small(203, Mt, N, kdy, kdy + 8)
+    print("case", kx, kw, kdy, flush=True)
+    rx, rw, rd = _operand(X, ("n", "t")), _operand(W, ("n", "t")), _operand(dY, ("n", "t"))
+    Y = M.spectral_fp4_linear_fwd(rx, rw)
+    dX, dW = M.spectral_fp4_linear_bwd(rd, rx, rw)
+    torch.cuda.synchronize()
+    dx_, dw_, dd_ = G.record_to_dict(rx), G.record_to_dict(rw), G.record_to_dict(rd)
+    for name, got, want in (("Y", Y, OL.linear_fwd(dx_, dw_)), ("dX", dX, OL.linear_bwd_dx(dd_, dw_)),
+                            ("dW", dW, OL.linear_bwd_dw(dd_, dx_))):
+        err = _rel(got.cpu().numpy().astype(np.float64), want)
+        print("%s rel err %.3e" % (name, err), flush=True)
+        assert err <= C_GATE, name
+        assert err <= 1e-5, name  # far inside the gate: fp32-accurate everywhere
+
+
+def test_linear_unsplit_is_a_plain_fp4_gemm_and_handles_empty():
+    X = _small(204, 64, 256, 0, 0, kind="normal")
+    W = _small(205, 96, 256, 0, 0, kind="normal")
+    rx, rw = _operand(X, ("n",)), _operand(W, ("n",))
+    Y = M.spectral_fp4_linear_fwd(rx, rw).cpu().numpy().astype(np.float64)
+    want = OL.linear_fwd(G.record_to_dict(rx), G.record_to_dict(rw))
+    assert _rel(Y, want) <= 1e-6
+    e = M.plain_operand(torch.empty(0, 256, device="cuda"), "mxfp4", ("n",))
+    out = M.spectral_fp4_linear_fwd(e, rw)
+    assert out.shape == (0, 96)
+
+
+def test_linear_deterministic():
+    X = _small(206, 256, 256, 8, 16)
+    W = _small(207, 256, 256, 8, 16, kind="powerlaw")
+    rx, rw = _operand(X, ("n",)), _operand(W, ("n",))
+    a = M.spectral_fp4_linear_fwd(rx, rw).clone()
+    b = M.spectral_fp4_linear_fwd(rx, rw)
+    assert torch.equal(a, b)
+
+
+def _full(cfg, gemms, nrows=512):
+    names = set()
+    for _, a, _, b, _ in gemms:
+        names |= {a, b}
+    tens = {n: synth.make_tensor(cfg, n) for n in sorted(names)}
+    recs = {n: _operand(t, ("n", "t")) for n, t in tens.items()}
+    torch.cuda.synchronize()
+    dicts = {n: G.record_to_dict(r) for n, r in recs.items()}
+    for out, a, ao, b, bo in gemms:
+        if ao == "n" and bo == "n":
+            C = M.spectral_fp4_linear_fwd(recs[a], recs[b])
+        elif ao == "n":
+            C = _bwd_dx(recs[a], recs[b])
+        else:
+            C = _bwd_dw(recs[a], recs[b])
+        torch.cuda.synchronize()
+        rows = np.sort(np.random.Generator(np.random.PCG64(9)).choice(C.shape[0], min(nrows, C.shape[0]),
+                                                                       replace=False))
+        got = C[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+        want = OL.gemm_nt(dicts[a], ao, dicts[b], bo, rows=rows)
+        err = _rel(got, want)
+        print("cfg %d %s rel err %.3e on %d rows" % (cfg, out, err, len(rows)), flush=True)
+        assert err <= C_GATE
+        del C
+
+
+def _bwd_dx(dY, W):
+    """dX through the public bwd entry point (dW skipped)."""
+    fake_x = M.SplitRecord(dY.m, W.n, 0, W.fmt)
+    return M.spectral_fp4_linear_bwd(dY, fake_x, W, need_dx=True, need_dw=False)[0]
+
+
+def _bwd_dw(dY, X):
+    """dW through the public bwd entry point (dX skipped)."""
+    fake_w = M.SplitRecord(dY.n, X.n, 0, X.fmt)
+    return M.spectral_fp4_linear_bwd(dY, X, fake_w, need_dx=False, need_dw=True)[1]
+
+
+def test_linear_full_size_cfg3():
+    _full(3, synth.GEMMS[3])
+
+
+def test_linear_full_size_cfg4_up():
+    _full(4, [g for g in synth.GEMMS[4] if g[0].endswith("_up")])
+
+
+def test_linear_full_size_cfg4_down():
+    _full(4, [g for g in synth.GEMMS[4] if g[0].endswith("_down")], nrows=256)
