@@ -14,9 +14,13 @@
 // is fp32-accurate. Kernels:
 //   skinny_kernel  P, Q and Fa^T Fb on the scaled FP4 MFMA (split-K partials)
 //   panel_kernel   sums the partials and writes the bf16 panels L1, L2
-//   gemm_kernel    Ra Rb^T on v_mfma_scale_f32_32x32x64_f8f6f4 (256 x 256
+//   gemm_mx_kernel Ra Rb^T on v_mfma_scale_f32_32x32x64_f8f6f4 (256 x 256
 //                  tiles, LDS double buffer), then + L1 L2^T on bf16 MFMA into
 //                  the same accumulators, then one fp32 store.
+//   gemm_nv_kernel the NVFP4 form: E2M1 x E4M3 decoded exactly to bf16 in the
+//                  LDS staging, bf16 MFMA (gfx950's scaled MFMA takes only
+//                  E8M0 scales per 32 elements), tensor scales in the epilogue.
+//   skinny_nv_kernel, panel_kernel<true>: the NVFP4 forms of the first two.
 #include <algorithm>
 
 #include "common.hpp"
@@ -160,25 +164,93 @@ __global__ void __launch_bounds__(64)
   }
 }
 
+// NVFP4 variant: both operands decoded exactly to bf16 (E2M1 x E4M3 has at
+// most six significant bits) and multiplied on the bf16 MFMA; the two tensor
+// scales multiply the fp32 result once. One wave: 32 rows x 32*NCT columns;
+// per 32-element step lane (r, h) decodes block h (16 elements) of its row and
+// feeds its first and second 8 values to two 32x32x16 MFMAs.
+__device__ __forceinline__ void nv_decode16(const uint2 codes, uint32_t sbyte, ushortx8 &lo8, ushortx8 &hi8) {
+  const float sv = e4m3_value(sbyte);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    lo8[e] = (unsigned short)(__float_as_uint(e2m1_value((codes.x >> (4 * e)) & 15u) * sv) >> 16);
+    hi8[e] = (unsigned short)(__float_as_uint(e2m1_value((codes.y >> (4 * e)) & 15u) * sv) >> 16);
+  }
+}
+
+template <int NCT>
+__global__ void __launch_bounds__(64)
+    skinny_nv_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, const float *__restrict__ ats,
+                     int64_t rows, const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs,
+                     const float *__restrict__ bts, int cols, int64_t T, int64_t chunk, float *__restrict__ out) {
+  const int lane = threadIdx.x;
+  const int r = lane & 31, h = lane >> 5;
+  const int64_t row = (int64_t)blockIdx.x * 32 + r;
+  const int s = blockIdx.y;
+  const int64_t t_beg = (int64_t)s * chunk, t_end = std::min<int64_t>(T, t_beg + chunk);
+  const int64_t nb = T / 16;
+  floatx16 acc[NCT];
+#pragma unroll
+  for (int j = 0; j < NCT; ++j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[j][q] = 0.0f;
+  const bool rok = row < rows;
+  const ushortx8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t t0 = t_beg; t0 < t_end; t0 += 32) {
+    const int64_t e0 = t0 + h * 16;
+    ushortx8 a0 = z8, a1 = z8;
+    if (rok && e0 < t_end) nv_decode16(*(const uint2 *)(ac + row * (T / 2) + e0 / 2), as[row * nb + e0 / 16], a0, a1);
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int col = j * 32 + r;
+      ushortx8 b0 = z8, b1 = z8;
+      if (col < cols && e0 < t_end)
+        nv_decode16(*(const uint2 *)(bc + (int64_t)col * (T / 2) + e0 / 2), bs[(int64_t)col * nb + e0 / 16], b0, b1);
+      acc[j] = mfma32_bf16(a0, b0, acc[j]);
+      acc[j] = mfma32_bf16(a1, b1, acc[j]);
+    }
+  }
+  const float sc = ats[0] * bts[0];
+  float *o = out + (int64_t)s * rows * cols;
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) {
+    const int col = j * 32 + r;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int64_t orow = (int64_t)blockIdx.x * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+      if (orow < rows && col < cols) o[orow * cols + col] = acc[j][q] * sc;
+    }
+  }
+}
+
 // =================================================================== panels
-// Decoded MXFP4 value of element i of row c of a k x rows factor matrix.
-__device__ __forceinline__ float factor_value(const uint8_t *codes, const uint8_t *scales, int64_t rows, int c,
-                                              int64_t i) {
+// Decoded value of element i of row c of a k x rows factor matrix. For
+// NVFP4, `ts` (the tensor scale) is applied only when with_ts is set.
+template <bool NV>
+__device__ __forceinline__ float factor_value(const uint8_t *codes, const uint8_t *scales, const float *ts,
+                                              int64_t rows, int c, int64_t i, bool with_ts) {
   const uint32_t byte = codes[(int64_t)c * (rows / 2) + i / 2];
   const uint32_t code = (i & 1) ? (byte >> 4) : (byte & 15u);
-  return ldexpf(e2m1_value(code), (int)scales[(int64_t)c * (rows / 32) + i / 32] - 127);
+  if (!NV) return ldexpf(e2m1_value(code), (int)scales[(int64_t)c * (rows / 32) + i / 32] - 127);
+  const float v = e2m1_value(code) * e4m3_value(scales[(int64_t)c * (rows / 16) + i / 16]);
+  return with_ts ? v * ts[0] : v;
 }
 
 // Rows [0, ra) build L1, rows [ra, ra + rb) build L2 (one 64-thread group per
 // row; columns strided). cross (ka x kb) is summed once per block into LDS.
+// The G columns of the panels hold e2m1 * block scale, which bf16 represents
+// exactly; for NVFP4 the G tensor scale is folded into the partner column
+// (P for Gb, Q for Ga) before its hi/lo split.
+template <bool NV>
 __global__ void __launch_bounds__(256)
     panel_kernel(int64_t ra, int64_t rb, int ka, int kb, int rp, const float *__restrict__ ppart, int ks_p,
                  const float *__restrict__ qpart, int ks_q, const float *__restrict__ cpart, int ks_c,
                  const float *__restrict__ Sa, const float *__restrict__ Sb, const uint8_t *__restrict__ ga_c,
-                 const uint8_t *__restrict__ ga_s, const uint8_t *__restrict__ gb_c, const uint8_t *__restrict__ gb_s,
-                 unsigned short *__restrict__ l1, unsigned short *__restrict__ l2) {
+                 const uint8_t *__restrict__ ga_s, const float *__restrict__ ga_t, const uint8_t *__restrict__ gb_c,
+                 const uint8_t *__restrict__ gb_s, const float *__restrict__ gb_t, unsigned short *__restrict__ l1,
+                 unsigned short *__restrict__ l2) {
   __shared__ float cross[96][97];
-  __shared__ float gsb[4][96];  // Gb[j][d] * Sb[d] for the 4 rows of this block
+  __shared__ float gsb[4][96];  // Gb[j][d] * Sb[d] for the (up to) 4 L2 rows of this block
   const int t = threadIdx.x;
   const int sub = t >> 6, lane = t & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + sub;
@@ -192,9 +264,11 @@ __global__ void __launch_bounds__(256)
   }
   if (row >= ra && row < ra + rb && kb) {
     const int64_t j = row - ra;
-    for (int d = lane; d < kb; d += 64) gsb[sub][d] = factor_value(gb_c, gb_s, rb, d, j) * Sb[d];
+    for (int d = lane; d < kb; d += 64) gsb[sub][d] = factor_value<NV>(gb_c, gb_s, gb_t, rb, d, j, true) * Sb[d];
   }
   __syncthreads();
+  const float fold_b = (NV && kb) ? gb_t[0] : 1.0f;  // Gb tensor scale, carried by P
+  const float fold_a = (NV && ka) ? ga_t[0] : 1.0f;  // Ga tensor scale, carried by Q
   if (row < ra) {
     unsigned short *o = l1 + row * rp;
     for (int c = lane; c < rp; c += 64) {
@@ -203,13 +277,13 @@ __global__ void __launch_bounds__(256)
         const int d = c % kb;
         float p = 0.0f;
         for (int s = 0; s < ks_p; ++s) p += ppart[((int64_t)s * ra + row) * kb + d];
-        p *= Sb[d];
+        p = p * Sb[d] * fold_b;
         unsigned short hi, lo;
         split_bf16(p, hi, lo);
         v = c < kb ? hi : lo;
       } else if (c < 2 * kb + 2 * ka) {
         const int cc = (c - 2 * kb) % ka;
-        v = f32_to_bf16(factor_value(ga_c, ga_s, ra, cc, row));
+        v = f32_to_bf16(factor_value<NV>(ga_c, ga_s, ga_t, ra, cc, row, false));
       }
       o[c] = v;
     }
@@ -219,13 +293,13 @@ __global__ void __launch_bounds__(256)
     for (int c = lane; c < rp; c += 64) {
       unsigned short v = 0;
       if (c < 2 * kb) {
-        v = f32_to_bf16(factor_value(gb_c, gb_s, rb, c % kb, j));
+        v = f32_to_bf16(factor_value<NV>(gb_c, gb_s, gb_t, rb, c % kb, j, false));
       } else if (c < 2 * kb + 2 * ka) {
         const int cc = (c - 2 * kb) % ka;
         float q = 0.0f;
         for (int s = 0; s < ks_q; ++s) q += qpart[((int64_t)s * rb + j) * ka + cc];
         for (int d = 0; d < kb; ++d) q += gsb[sub][d] * cross[cc][d];
-        q *= Sa[cc];
+        q = q * Sa[cc] * fold_a;
         unsigned short hi, lo;
         split_bf16(q, hi, lo);
         v = c < 2 * kb + ka ? hi : lo;
@@ -237,10 +311,16 @@ __global__ void __launch_bounds__(256)
 
 // ==================================================================== GEMM
 constexpr int BM = 256, BN = 256;
-constexpr int BKB = 64;         // code bytes per row per stage (128 FP4 elements)
+constexpr int BKB = 64;         // MXFP4: code bytes per row per stage (128 elements)
 constexpr int ROWB = BKB + 16;  // LDS row stride (bytes), conflict-free b128 reads
 constexpr int STAGE_BYTES = 2 * BM * ROWB + 2 * BM * 4;
 constexpr int EPI_ROWB = 128 + 16;  // bf16 panel chunk: 64 values + pad
+constexpr int NV_ROWB = 128 + 16;   // NVFP4: 64 decoded bf16 per row per stage + pad
+constexpr int NV_STAGE_BYTES = 2 * BM * NV_ROWB;
+constexpr int MX_LDS = 2 * STAGE_BYTES;
+constexpr int NV_LDS = 2 * NV_STAGE_BYTES;
+static_assert(2 * BM * EPI_ROWB <= MX_LDS && 2 * BM * EPI_ROWB <= NV_LDS, "epilogue panels must fit the main-loop LDS");
+static_assert(NV_LDS <= 160 * 1024, "LDS budget of one CU");
 
 __device__ __forceinline__ void tile_coords(int &tm, int &tn, int mt, int nt) {
   // XCD-aware order: consecutive dispatch ids go round-robin over the 8 XCDs;
@@ -258,12 +338,80 @@ __device__ __forceinline__ void tile_coords(int &tm, int &tn, int mt, int nt) {
   tn = in / gm;
 }
 
+// acc (the 256 x 256 tile, 4 x 4 MFMA blocks of 32 x 32 per wave) times
+// `scale`, plus L1[m-tile] L2[n-tile]^T (bf16, 64 panel columns at a time
+// through LDS), stored as fp32.
+__device__ __forceinline__ void epilogue(floatx16 (&acc)[4][4], float scale, uint8_t *smem, int64_t m0, int64_t n0,
+                                         int64_t M, int64_t N, const unsigned short *__restrict__ l1,
+                                         const unsigned short *__restrict__ l2, int rp, float *__restrict__ C,
+                                         int64_t ldc) {
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (scale != 1.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] *= scale;
+  }
+  if (rp > 0) {
+    uint8_t *L1s = smem, *L2s = smem + BM * EPI_ROWB;
+    for (int c0 = 0; c0 < rp; c0 += 64) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = t + 256 * i;  // 2048 pieces of 16 bytes per panel
+        const int rr = idx >> 3, piece = idx & 7;
+        const int64_t ar = m0 + rr, br = n0 + rr;
+        const uint4 va = ar < M ? *(const uint4 *)(l1 + ar * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
+        const uint4 vb = br < N ? *(const uint4 *)(l2 + br * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
+        *(uint4 *)(L1s + rr * EPI_ROWB + piece * 16) = va;
+        *(uint4 *)(L2s + rr * EPI_ROWB + piece * 16) = vb;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ushortx8 a8[4], b8[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a8[i] = *(const ushortx8 *)(L1s + (wm * 128 + i * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b8[j] = *(const ushortx8 *)(L2s + (wn * 128 + j * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + wn * 128 + j * 32 + r32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + wm * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+        if (row < M) C[row * ldc + col] = acc[i][j][q];
+      }
+    }
+}
+
+// MXFP4: C = Ra Rb^T (+ L1 L2^T) on the scaled FP4 MFMA; 256 x 256 tile per
+// workgroup (4 waves, 2 x 2, each 128 x 128), 128 contraction elements per
+// LDS stage, double buffered: the next stage's global loads are in flight
+// while the current stage's MFMAs run.
 __global__ void __launch_bounds__(256, 1)
-    gemm_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
-                const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int64_t N, int64_t T,
-                const unsigned short *__restrict__ l1, const unsigned short *__restrict__ l2, int rp,
-                float *__restrict__ C, int64_t ldc) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+    gemm_mx_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
+                   const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int64_t N, int64_t T,
+                   const unsigned short *__restrict__ l1, const unsigned short *__restrict__ l2, int rp,
+                   float *__restrict__ C, int64_t ldc) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int r32 = lane & 31, h = lane >> 5;
@@ -361,75 +509,145 @@ __global__ void __launch_bounds__(256, 1)
     __syncthreads();
   }
 
-  // ---- low-rank correction: acc += L1[m-tile] L2[n-tile]^T (bf16, 64 at a time)
-  if (rp > 0) {
-    uint8_t *L1s = smem, *L2s = smem + BM * EPI_ROWB;
-    for (int c0 = 0; c0 < rp; c0 += 64) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = t + 256 * i;  // 2048 pieces of 16 bytes per panel
-        const int rr = idx >> 3, piece = idx & 7;
-        const int64_t ar = m0 + rr, br = n0 + rr;
-        const uint4 va = ar < M ? *(const uint4 *)(l1 + ar * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
-        const uint4 vb = br < N ? *(const uint4 *)(l2 + br * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
-        *(uint4 *)(L1s + rr * EPI_ROWB + piece * 16) = va;
-        *(uint4 *)(L2s + rr * EPI_ROWB + piece * 16) = vb;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        ushortx8 a8[4], b8[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a8[i] = *(const ushortx8 *)(L1s + (wm * 128 + i * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b8[j] = *(const ushortx8 *)(L2s + (wn * 128 + j * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
-      }
-      __syncthreads();
-    }
-  }
+  epilogue(acc, 1.0f, smem, m0, n0, M, N, l1, l2, rp, C, ldc);
+}
 
-  // ---- store (fp32)
+// NVFP4: codes and E4M3 block scales are decoded exactly to bf16 while being
+// staged into LDS (64 contraction elements per stage), multiplied on the
+// bf16 32x32x16 MFMA with fp32 accumulation; the product of the two tensor
+// scales multiplies the accumulators once before the correction.
+__global__ void __launch_bounds__(256, 1)
+    gemm_nv_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, const float *__restrict__ ats,
+                   int64_t M, const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs,
+                   const float *__restrict__ bts, int64_t N, int64_t T, const unsigned short *__restrict__ l1,
+                   const unsigned short *__restrict__ l2, int rp, float *__restrict__ C, int64_t ldc) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NV_LDS];
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(tm, tn, (int)cdiv(M, BM), (int)cdiv(N, BN));
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t nb = T / 16;
+  const int nst = (int)cdiv(T, 64);
+  floatx16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + r32;
-      if (col >= N) continue;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
-        if (row < M) C[row * ldc + col] = acc[i][j][q];
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  // thread t stages rows (t >> 1) and (t >> 1) + 128, half (t & 1): 32 codes
+  // (two NVFP4 blocks) per row and operand per stage
+  uint4 ga[2], gb[2];
+  uint32_t gsa[2], gsb[2];
+  const int half = t & 1;
+  auto load_stage = [&](int st) {
+    const int64_t e = (int64_t)st * 64 + half * 32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rr = (t >> 1) + 128 * i;
+      const int64_t ar = m0 + rr, br = n0 + rr;
+      const bool ea = ar < M && e < T, eb = br < N && e < T;
+      ga[i] = ea ? *(const uint4 *)(ac + ar * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
+      gb[i] = eb ? *(const uint4 *)(bc + br * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
+      gsa[i] = ea ? ((uint32_t)as[ar * nb + e / 16] | ((uint32_t)as[ar * nb + e / 16 + 1] << 8)) : 0u;
+      gsb[i] = eb ? ((uint32_t)bs[br * nb + e / 16] | ((uint32_t)bs[br * nb + e / 16 + 1] << 8)) : 0u;
+    }
+  };
+  auto store_stage = [&](int buf) {
+    uint8_t *A_ = smem + buf * NV_STAGE_BYTES, *B_ = A_ + BM * NV_ROWB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rr = (t >> 1) + 128 * i;
+      const uint32_t wa[4] = {ga[i].x, ga[i].y, ga[i].z, ga[i].w};
+      const uint32_t wb[4] = {gb[i].x, gb[i].y, gb[i].z, gb[i].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // word w holds elements 8w .. 8w+7 of this half; blocks of 16
+        const float sa = e4m3_value((gsa[i] >> (8 * (w >> 1))) & 0xFFu);
+        const float sb = e4m3_value((gsb[i] >> (8 * (w >> 1))) & 0xFFu);
+        ushortx8 da, db;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          da[e] = (unsigned short)(__float_as_uint(e2m1_value((wa[w] >> (4 * e)) & 15u) * sa) >> 16);
+          db[e] = (unsigned short)(__float_as_uint(e2m1_value((wb[w] >> (4 * e)) & 15u) * sb) >> 16);
+        }
+        *(ushortx8 *)(A_ + rr * NV_ROWB + (half * 32 + w * 8) * 2) = da;
+        *(ushortx8 *)(B_ + rr * NV_ROWB + (half * 32 + w * 8) * 2) = db;
       }
     }
+  };
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < nst) load_stage(st + 1);
+    const uint8_t *A_ = smem + cur * NV_STAGE_BYTES, *B_ = A_ + BM * NV_ROWB;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      ushortx8 a8[4], b8[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a8[i] = *(const ushortx8 *)(A_ + (wm * 128 + i * 32 + r32) * NV_ROWB + ks * 32 + h * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b8[j] = *(const ushortx8 *)(B_ + (wn * 128 + j * 32 + r32) * NV_ROWB + ks * 32 + h * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
+    }
+    if (st + 1 < nst) store_stage(cur ^ 1);
+    __syncthreads();
+  }
+  epilogue(acc, ats[0] * bts[0], smem, m0, n0, M, N, l1, l2, rp, C, ldc);
 }
-
-static_assert(2 * BM * EPI_ROWB <= 2 * STAGE_BYTES, "epilogue panels must fit the main-loop LDS");
 
 // ====================================================================== host
 void launch_skinny(const metis_fp4_t *A, int64_t rows, const metis_fp4_t *B, int cols, int64_t T, int ks,
                    int64_t chunk, float *out, hipStream_t st) {
   const dim3 grid((unsigned)cdiv(rows, 32), ks);
-  if (cols <= 32)
+  const int nct = cols <= 32 ? 1 : (cols <= 64 ? 2 : 3);
+  if (A->fmt == METIS_NVFP4) {
+#define NV_SKINNY(N)                                                                                              \
+  skinny_nv_kernel<N><<<grid, 64, 0, st>>>(A->codes, A->scales, A->tensor_scale, rows, B->codes, B->scales, \
+                                           B->tensor_scale, cols, T, chunk, out)
+    if (nct == 1) NV_SKINNY(1);
+    else if (nct == 2) NV_SKINNY(2);
+    else NV_SKINNY(3);
+#undef NV_SKINNY
+    return;
+  }
+  if (nct == 1)
     skinny_kernel<1><<<grid, 64, 0, st>>>(A->codes, A->scales, rows, B->codes, B->scales, cols, T, chunk, out);
-  else if (cols <= 64)
+  else if (nct == 2)
     skinny_kernel<2><<<grid, 64, 0, st>>>(A->codes, A->scales, rows, B->codes, B->scales, cols, T, chunk, out);
   else
     skinny_kernel<3><<<grid, 64, 0, st>>>(A->codes, A->scales, rows, B->codes, B->scales, cols, T, chunk, out);
 }
 
+bool nv_scales_ok(const Side &x) {
+  if (x.R->fmt != METIS_NVFP4) return true;
+  if (x.rows > 0 && x.T > 0 && !x.R->tensor_scale) return false;
+  return x.k == 0 || (x.F->tensor_scale && x.G->tensor_scale && x.F->fmt == METIS_NVFP4 && x.G->fmt == METIS_NVFP4);
+}
+
 metis_status_t check_pair(const Side &a, const Side &b) {
   if (a.T != b.T) return METIS_ERR_INVALID;
-  if (a.R->fmt != METIS_MXFP4 || b.R->fmt != METIS_MXFP4) return METIS_ERR_UNSUPPORTED;
+  if (a.R->fmt != b.R->fmt || (a.R->fmt != METIS_MXFP4 && a.R->fmt != METIS_NVFP4)) return METIS_ERR_INVALID;
+  if (a.k && (a.F->fmt != a.R->fmt || a.G->fmt != a.R->fmt)) return METIS_ERR_INVALID;
+  if (b.k && (b.F->fmt != b.R->fmt || b.G->fmt != b.R->fmt)) return METIS_ERR_INVALID;
+  if (!nv_scales_ok(a) || !nv_scales_ok(b)) return METIS_ERR_INVALID;
   if (a.k > 96 || b.k > 96) return METIS_ERR_UNSUPPORTED;
   if (a.rows == 0 || b.rows == 0 || a.T == 0) return METIS_OK;
   if (a.R->rows != a.rows || a.R->cols != a.T || b.R->rows != b.rows || b.R->cols != b.T) return METIS_ERR_INVALID;
-  if (a.T % 32 || (((uintptr_t)a.R->codes) & 15) || (((uintptr_t)b.R->codes) & 15)) return METIS_ERR_INVALID;
+  const int64_t B = a.R->fmt == METIS_NVFP4 ? 16 : 32;
+  if (a.T % B || (((uintptr_t)a.R->codes) & 15) || (((uintptr_t)b.R->codes) & 15)) return METIS_ERR_INVALID;
+  // the NVFP4 main loop stages 32-element halves (two blocks) per row
+  if (a.R->fmt == METIS_NVFP4 && a.T % 32) return METIS_ERR_UNSUPPORTED;
   return METIS_OK;
 }
 
@@ -444,10 +662,18 @@ metis_status_t gemm_prepare(const Side &a, const Side &b, void *ws, size_t ws_by
   if (b.k) launch_skinny(a.R, a.rows, b.F, b.k, a.T, p.ks_p, p.tc_p, p.ppart, st);
   if (a.k) launch_skinny(b.R, b.rows, a.F, a.k, a.T, p.ks_q, p.tc_q, p.qpart, st);
   if (a.k && b.k) launch_skinny(a.F, a.k, b.F, b.k, a.T, p.ks_c, p.tc_c, p.cpart, st);
-  panel_kernel<<<(unsigned)cdiv(a.rows + b.rows, 4), 256, 0, st>>>(
-      a.rows, b.rows, a.k, b.k, p.rp, p.ppart, p.ks_p, p.qpart, p.ks_q, p.cpart, p.ks_c, a.S, b.S,
-      a.k ? a.G->codes : nullptr, a.k ? a.G->scales : nullptr, b.k ? b.G->codes : nullptr,
-      b.k ? b.G->scales : nullptr, p.l1, p.l2);
+  const unsigned pgrid = (unsigned)cdiv(a.rows + b.rows, 4);
+#define PANEL(NV)                                                                                                 \
+  panel_kernel<NV><<<pgrid, 256, 0, st>>>(a.rows, b.rows, a.k, b.k, p.rp, p.ppart, p.ks_p, p.qpart, p.ks_q,        \
+                                         p.cpart, p.ks_c, a.S, b.S, a.k ? a.G->codes : nullptr,                    \
+                                         a.k ? a.G->scales : nullptr, a.k ? a.G->tensor_scale : nullptr,           \
+                                         b.k ? b.G->codes : nullptr, b.k ? b.G->scales : nullptr,                  \
+                                         b.k ? b.G->tensor_scale : nullptr, p.l1, p.l2)
+  if (a.R->fmt == METIS_NVFP4)
+    PANEL(true);
+  else
+    PANEL(false);
+#undef PANEL
   METIS_LAUNCH_CHECK();
   return METIS_OK;
 }
@@ -472,8 +698,12 @@ metis_status_t gemm_main(const Side &a, const Side &b, float *C, int64_t ldc, co
     l2 = p.l2;
   }
   const unsigned tiles = (unsigned)(cdiv(a.rows, BM) * cdiv(b.rows, BN));
-  gemm_kernel<<<tiles, 256, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows, a.T, l1, l2,
-                                    rp, C, ldc);
+  if (a.R->fmt == METIS_NVFP4)
+    gemm_nv_kernel<<<tiles, 256, 0, st>>>(a.R->codes, a.R->scales, a.R->tensor_scale, a.rows, b.R->codes,
+                                          b.R->scales, b.R->tensor_scale, b.rows, a.T, l1, l2, rp, C, ldc);
+  else
+    gemm_mx_kernel<<<tiles, 256, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows, a.T, l1,
+                                          l2, rp, C, ldc);
   METIS_LAUNCH_CHECK();
   return METIS_OK;
 }

@@ -39,6 +39,7 @@ constexpr int kThreads = 256;
 struct SplitPlan {
   int64_t m, n;
   int l, lp, k, kp;
+  bool wide;  // l > kLpMax: global-memory forms of the small kernels
   int kind, fmt;
   int elem;  // bytes per input element
   // sketch
@@ -75,6 +76,7 @@ struct SplitPlan {
   float *sign;           // k
   unsigned short *uhl;   // 2 x m x kp bf16 (U hi, lo)
   unsigned short *whl;   // 2 x n x kp bf16 ((V S) hi, lo)
+  double *wa, *winv, *wg, *wv;  // lp x lp scratch of the global-memory (wide) forms
   uint32_t *amax;        // 8 words: NVFP4 tensor maxima (U^T, V^T, R)
   int *info_ws;          // 1 word
   size_t bytes;
@@ -88,7 +90,8 @@ int64_t pick_rows_per_part(int64_t rows, int64_t want_parts, int64_t quantum) {
 SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int elem, void *ws) {
   SplitPlan p;
   p.m = m; p.n = n; p.l = l; p.k = k; p.kind = kind; p.fmt = fmt; p.elem = elem;
-  p.lp = (int)round_up(l, 16);
+  p.wide = l > kLpMax;
+  p.lp = (int)round_up(l, p.wide ? 64 : 16);
   p.kp = (int)round_up(k, 32);
   // sketch: 128-row tiles, split-K bounded so partial traffic stays ~10% of A
   const int64_t m_tiles = cdiv(m, 128);
@@ -101,14 +104,15 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
     p.sk = 1;
     p.sk_chunk = n;
   }
-  p.gy_rows = pick_rows_per_part(m, 128, 32);
+  const int64_t gram_parts = p.wide ? 16 : 128;  // wide Grams are lp x lp each
+  p.gy_rows = pick_rows_per_part(m, gram_parts, 32);
   p.gy_parts = (int)cdiv(m, p.gy_rows);
   const int64_t n_tiles = cdiv(n, 128);
   int64_t wantp = std::min<int64_t>(cdiv(768, n_tiles), std::max<int64_t>(1, m * elem / (20 * l)));
   wantp = std::max<int64_t>(1, std::min<int64_t>(wantp, m / 32));
   p.pk_rows = round_up(cdiv(m, wantp), 32);
   p.pk = (int)cdiv(m, p.pk_rows);
-  p.gb_rows = pick_rows_per_part(n, 128, 32);
+  p.gb_rows = pick_rows_per_part(n, gram_parts, 32);
   p.gb_parts = (int)cdiv(n, p.gb_rows);
   p.am_rows = 256;
   p.am_parts = (int)cdiv(m, p.am_rows);
@@ -132,6 +136,10 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
   p.sign = c.take<float>((size_t)k);
   p.uhl = c.take<unsigned short>((size_t)2 * m * p.kp);
   p.whl = c.take<unsigned short>((size_t)2 * n * p.kp);
+  p.wa = c.take<double>((size_t)p.lp * p.lp);
+  p.winv = c.take<double>((size_t)p.lp * p.lp);
+  p.wg = c.take<double>((size_t)p.lp * p.lp);
+  p.wv = c.take<double>((size_t)p.lp * p.lp);
   p.amax = c.take<uint32_t>(8);
   p.info_ws = c.take<int>(1);
   p.bytes = c.bytes();
@@ -162,6 +170,9 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda,
                                                           const unsigned short *__restrict__ omt, int l, int lp,
                                                           int64_t chunk, float *__restrict__ ysk) {
+  // blockIdx.z selects a tile of kLpMax sketch columns starting at l0
+  const int l0 = blockIdx.z * kLpMax;
+  const int lt = min(kLpMax, lp - l0);
   constexpr int KS = 128;
   constexpr int NT = (sizeof(T) == 4) ? 3 : 1;  // bf16 terms per element (fp32 = hi + mid + lo)
   __shared__ __attribute__((aligned(16))) unsigned short lds[kLpMax][KS + 8];
@@ -171,7 +182,7 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
   const int s = blockIdx.y;
   const int64_t c_beg = (int64_t)s * chunk;
   const int64_t c_end = std::min<int64_t>(n, c_beg + chunk);
-  const int nct = lp >> 4;
+  const int nct = lt >> 4;
   floatx4 acc[2][kLpMax / 16];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -180,11 +191,11 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
 
   for (int64_t c0 = c_beg; c0 < c_end; c0 += KS) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < lp * (KS / 8); idx += kThreads) {
+    for (int idx = threadIdx.x; idx < lt * (KS / 8); idx += kThreads) {
       const int rr = idx / (KS / 8), q = idx % (KS / 8);
       const int64_t cc = c0 + q * 8;
       uint4 v = {0u, 0u, 0u, 0u};
-      if (cc < c_end) v = *(const uint4 *)(omt + (int64_t)rr * n + cc);
+      if (cc < c_end) v = *(const uint4 *)(omt + (int64_t)(l0 + rr) * n + cc);
       *(uint4 *)&lds[rr][q * 8] = v;
     }
     __syncthreads();
@@ -242,7 +253,7 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
 #pragma unroll
     for (int ct = 0; ct < kLpMax / 16; ++ct) {
       if (ct < nct) {
-        const int col = ct * 16 + r16;
+        const int col = l0 + ct * 16 + r16;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int64_t row = row0 + rs * 16 + g * 4 + t;
@@ -387,15 +398,22 @@ __global__ void gram_reduce_kernel(const double *__restrict__ gpart, int parts, 
 // l * 2^-52 * max(diag G) marks that direction as absent: its row of R and
 // its row and column of R^-1 are zero (the orthonormalized column comes out
 // zero) and *info records the first such pivot (1-based).
+template <bool WIDE>
 __global__ void __launch_bounds__(kThreads)
-    chol_inv_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ rinv, int *info) {
-  __shared__ double a[kLpMax][kLpMax + 1];
-  __shared__ double inv[kLpMax][kLpMax + 1];
-  __shared__ int dead[kLpMax];
+    chol_inv_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ rinv, int *info,
+                    double *__restrict__ wa, double *__restrict__ winv) {
+  // LDS copies for l <= kLpMax; global scratch (wa, winv: lp x lp) beyond
+  constexpr int SD = WIDE ? 1 : kLpMax;
+  __shared__ double a_s[SD * (kLpMax + 1)];
+  __shared__ double inv_s[SD * (kLpMax + 1)];
+  __shared__ int dead[512];
   __shared__ double tol_s;
   __shared__ int first_dead;
+  double *a = WIDE ? wa : a_s;
+  double *inv = WIDE ? winv : inv_s;
+  const int sa = WIDE ? lp : kLpMax + 1;
   const int t = threadIdx.x;
-  for (int i = t; i < lp * lp; i += kThreads) a[i / lp][i % lp] = g[i];
+  for (int i = t; i < lp * lp; i += kThreads) a[(i / lp) * sa + i % lp] = g[i];
   if (t == 0) {
     double md = 0.0;
     for (int i = 0; i < l; ++i) md = fmax(md, g[i * lp + i]);
@@ -405,47 +423,193 @@ __global__ void __launch_bounds__(kThreads)
   __syncthreads();
   for (int j = 0; j < l; ++j) {
     if (t == 0) {
-      const double piv = a[j][j];
+      const double piv = a[j * sa + j];
       if (piv > tol_s) {
-        a[j][j] = sqrt(piv);
+        a[j * sa + j] = sqrt(piv);
         dead[j] = 0;
       } else {
-        a[j][j] = 0.0;
+        a[j * sa + j] = 0.0;
         dead[j] = 1;
         if (first_dead == 0) first_dead = j + 1;
       }
     }
     __syncthreads();
-    const double d = a[j][j];
+    const double d = a[j * sa + j];
     const bool dj = dead[j];
-    for (int c = j + 1 + t; c < l; c += kThreads) a[j][c] = dj ? 0.0 : a[j][c] / d;
+    for (int c = j + 1 + t; c < l; c += kThreads) a[j * sa + c] = dj ? 0.0 : a[j * sa + c] / d;
     __syncthreads();
     if (!dj) {
       const int w = l - j - 1;
       for (int idx = t; idx < w * w; idx += kThreads) {
         const int p = j + 1 + idx / w, q = j + 1 + idx % w;
-        if (q >= p) a[p][q] -= a[j][p] * a[j][q];
+        if (q >= p) a[p * sa + q] -= a[j * sa + p] * a[j * sa + q];
       }
     }
     __syncthreads();
   }
   // column c of R^-1: solve R x = e_c from the bottom up
-  if (t < lp) {
-    const int c = t;
-    for (int i = 0; i < lp; ++i) inv[i][c] = 0.0;
+  for (int c = t; c < lp; c += kThreads) {
+    for (int i = 0; i < lp; ++i) inv[i * sa + c] = 0.0;
     if (c < l && !dead[c]) {
-      inv[c][c] = 1.0 / a[c][c];
+      inv[c * sa + c] = 1.0 / a[c * sa + c];
       for (int i = c - 1; i >= 0; --i) {
         if (dead[i]) continue;
         double s = 0.0;
-        for (int q = i + 1; q <= c; ++q) s += a[i][q] * inv[q][c];
-        inv[i][c] = -s / a[i][i];
+        for (int q = i + 1; q <= c; ++q) s += a[i * sa + q] * inv[q * sa + c];
+        inv[i * sa + c] = -s / a[i * sa + i];
       }
     }
   }
   __syncthreads();
-  for (int i = t; i < lp * lp; i += kThreads) rinv[i] = inv[i / lp][i % lp];
+  for (int i = t; i < lp * lp; i += kThreads) rinv[i] = inv[(i / lp) * sa + i % lp];
   if (t == 0 && info) *info = first_dead;
+}
+
+// ----------------------------------------------- wide-sketch helpers (l > 96)
+// x = sum over parts (fixed order); rows x l elements.
+__global__ void sum_parts_kernel(const float *__restrict__ parts, int n_parts, int64_t stride, int64_t count,
+                                 float *__restrict__ x) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float v = 0.0f;
+  for (int p = 0; p < n_parts; ++p) v += parts[p * stride + i];
+  x[i] = v;
+}
+
+// Partial Gram tile over one chunk of rows: gpart[chunk] (lp x lp) rows
+// [64 ti, +64) x columns [64 tj, +64), fp64; thread owns a 4 x 4 block.
+__global__ void __launch_bounds__(kThreads)
+    gram_tile_kernel(const float *__restrict__ x, int64_t rows, int l, int lp, int64_t rows_per_chunk,
+                     double *__restrict__ gpart) {
+  __shared__ float xi[32][65], xj[32][65];
+  const int t = threadIdx.x;
+  const int ti = blockIdx.y, tj = blockIdx.z;
+  const int bi = t >> 4, bj = t & 15;
+  const int64_t r_beg = blockIdx.x * rows_per_chunk;
+  const int64_t r_end = std::min<int64_t>(rows, r_beg + rows_per_chunk);
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int64_t r0 = r_beg; r0 < r_end; r0 += 32) {
+    __syncthreads();
+    for (int idx = t; idx < 32 * 64; idx += kThreads) {
+      const int rr = idx >> 6, c = idx & 63;
+      const int64_t row = r0 + rr;
+      const int ci = ti * 64 + c, cj = tj * 64 + c;
+      xi[rr][c] = (row < r_end && ci < l) ? x[row * l + ci] : 0.0f;
+      xj[rr][c] = (row < r_end && cj < l) ? x[row * l + cj] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int rr = 0; rr < 32; ++rr) {
+      double vi[4], vj[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        vi[a] = xi[rr][bi * 4 + a];
+        vj[a] = xj[rr][bj * 4 + a];
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] += vi[a] * vj[b];
+    }
+  }
+  double *g = gpart + (int64_t)blockIdx.x * lp * lp;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) g[(ti * 64 + bi * 4 + a) * lp + tj * 64 + bj * 4 + b] = acc[a][b];
+}
+
+// xout = xin R^-1 (fp64 accumulate, fp32 out) on 64 x 64 output tiles;
+// optionally also bf16 hi/lo of xout transposed into xt (2 x lp x rows).
+__global__ void __launch_bounds__(kThreads)
+    apply_rinv_kernel(const float *__restrict__ xin, int64_t rows, int l, int lp, const double *__restrict__ rinv,
+                      float *__restrict__ xout, unsigned short *__restrict__ xt) {
+  __shared__ float xs[64][65];
+  __shared__ double rs[64][65];
+  const int t = threadIdx.x;
+  const int64_t r0 = blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const int bi = t >> 4, bj = t & 15;
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int k0 = 0; k0 <= c0; k0 += 64) {  // R^-1 is upper triangular
+    __syncthreads();
+    for (int idx = t; idx < 64 * 64; idx += kThreads) {
+      const int rr = idx >> 6, c = idx & 63;
+      xs[rr][c] = (r0 + rr < rows && k0 + c < l) ? xin[(r0 + rr) * l + k0 + c] : 0.0f;
+      rs[rr][c] = rinv[(int64_t)(k0 + rr) * lp + c0 + c];
+    }
+    __syncthreads();
+    for (int q = 0; q < 64; ++q) {
+      double vx[4], vr[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        vx[a] = xs[bi * 4 + a][q];
+        vr[a] = rs[q][bj * 4 + a];
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] += vx[a] * vr[b];
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int64_t r = r0 + bi * 4 + a;
+    if (r >= rows) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c = c0 + bj * 4 + b;
+      const float v = (float)acc[a][b];
+      if (xout && c < l) xout[r * l + c] = v;
+      if (xt) {
+        unsigned short hi, lo;
+        split_bf16(c < l ? v : 0.0f, hi, lo);
+        xt[(int64_t)c * rows + r] = hi;
+        xt[((int64_t)lp + c) * rows + r] = lo;
+      }
+    }
+  }
+}
+
+// out[r][c] = sum_t x[r][t] E[t][c] * colscale[c]  (fp64), r < rows, c < k
+__global__ void assemble_wide_kernel(const float *__restrict__ x, int64_t rows, int l, int lp, int k,
+                                     const double *__restrict__ evec, const double *__restrict__ colscale,
+                                     float *__restrict__ out) {
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (idx >= rows * k) return;
+  const int64_t r = idx / k;
+  const int c = (int)(idx - r * k);
+  double s = 0.0;
+  for (int q = 0; q < l; ++q) s += (double)x[r * l + q] * evec[(int64_t)q * lp + c];
+  out[idx] = (float)(colscale ? s * colscale[c] : s);
+}
+
+// Per chunk of rows: argmax |U[:, c]| (lowest row on ties) and its value.
+__global__ void argmax_kernel(const float *__restrict__ U, int64_t m, int k, int64_t chunk_rows,
+                              float *__restrict__ am_val, int *__restrict__ am_idx) {
+  const int c = threadIdx.x;
+  if (c >= k) return;
+  const int64_t r_beg = blockIdx.x * chunk_rows, r_end = std::min<int64_t>(m, r_beg + chunk_rows);
+  float ba = -1.0f, bv = 0.0f;
+  int bi = 0x7FFFFFFF;
+  for (int64_t r = r_beg; r < r_end; ++r) {
+    const float u = U[r * k + c];
+    if (fabsf(u) > ba) {
+      ba = fabsf(u);
+      bv = u;
+      bi = (int)r;
+    }
+  }
+  am_val[blockIdx.x * k + c] = bv;
+  am_idx[blockIdx.x * k + c] = bi;
 }
 
 // ============================================================== projection
@@ -457,6 +621,9 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda,
                                                            const unsigned short *__restrict__ qt, int l, int lp,
                                                            int64_t chunk_rows, float *__restrict__ btp) {
+  // blockIdx.z selects a tile of kLpMax columns of Q starting at l0
+  const int l0 = blockIdx.z * kLpMax;
+  const int lt = min(kLpMax, lp - l0);
   constexpr int KS = 32;
   constexpr int TN = 128;
   constexpr int NT = (sizeof(T) == 4) ? 3 : 1;
@@ -468,7 +635,7 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
   const int s = blockIdx.y;
   const int64_t r_beg = (int64_t)s * chunk_rows;
   const int64_t r_end = std::min<int64_t>(m, r_beg + chunk_rows);
-  const int nit = lp >> 4;
+  const int nit = lt >> 4;
   floatx4 acc[2][kLpMax / 16];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -487,12 +654,12 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
       *(uint4 *)&at[rr][q * PIECE] = v;
     }
     // Q^T hi/lo: 2 x lp rows of KS bf16 (4 pieces each)
-    for (int idx = threadIdx.x; idx < 2 * lp * (KS / 8); idx += kThreads) {
-      const int h = idx / (lp * 4), rem = idx % (lp * 4);
+    for (int idx = threadIdx.x; idx < 2 * lt * (KS / 8); idx += kThreads) {
+      const int h = idx / (lt * 4), rem = idx % (lt * 4);
       const int i = rem >> 2, q = rem & 3;
       const int64_t row = r0 + q * 8;
       uint4 v = {0u, 0u, 0u, 0u};
-      if (row < r_end) v = *(const uint4 *)(qt + ((int64_t)h * lp + i) * m + row);
+      if (row < r_end) v = *(const uint4 *)(qt + ((int64_t)h * lp + l0 + i) * m + row);
       *(uint4 *)&qs[h][i][q * 8] = v;
     }
     __syncthreads();
@@ -534,7 +701,7 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
 #pragma unroll
     for (int it = 0; it < kLpMax / 16; ++it) {
       if (it < nit) {
-        const int i = it * 16 + r16;
+        const int i = l0 + it * 16 + r16;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t col = col0 + wave * 32 + cs * 16 + g * 4 + q;
@@ -556,21 +723,30 @@ __device__ __forceinline__ int rr_player(int pos, int round, int N) {
   return pos == 0 ? 0 : 1 + (pos - 1 + round) % (N - 1);
 }
 
+template <bool WIDE>
 __global__ void __launch_bounds__(kJacThreads)
     jacobi_kernel(const double *__restrict__ gin, int l, int lp, int k, int max_sweeps, double *__restrict__ evec,
-                  double *__restrict__ sig_inv, float *__restrict__ S) {
-  __shared__ double G[kLpMax][kLpMax + 1];
-  __shared__ double V[kLpMax][kLpMax + 1];
-  __shared__ double cs_c[kLpMax / 2], cs_s[kLpMax / 2];
-  __shared__ int pp[kLpMax / 2], qq[kLpMax / 2];
+                  double *__restrict__ sig_inv, float *__restrict__ S, double *__restrict__ wg,
+                  double *__restrict__ wv) {
+  // G and V live in LDS for lp <= kLpMax and in global scratch (wg, wv) beyond
+  constexpr int SD = WIDE ? 1 : kLpMax;
+  __shared__ double G_s[SD * (kLpMax + 1)];
+  __shared__ double V_s[SD * (kLpMax + 1)];
+  __shared__ double cs_c[256], cs_s[256];
+  __shared__ int pp[256], qq[256];
   __shared__ int rotated;
   __shared__ double floor_s;
-  __shared__ int rank[kLpMax];
+  __shared__ int rank[512];
+  double *Gp = WIDE ? wg : G_s;
+  double *Vp = WIDE ? wv : V_s;
+  const int gstr = WIDE ? lp : kLpMax + 1;
+#define G(i, j) Gp[(i) * gstr + (j)]
+#define V(i, j) Vp[(i) * gstr + (j)]
   const int t = threadIdx.x;
   const int N = lp, H = lp / 2;
   for (int i = t; i < N * N; i += kJacThreads) {
-    G[i / N][i % N] = gin[i];
-    V[i / N][i % N] = (i / N == i % N) ? 1.0 : 0.0;
+    G(i / N, i % N) = gin[i];
+    V(i / N, i % N) = (i / N == i % N) ? 1.0 : 0.0;
   }
   if (t == 0) {
     double md = 0.0;
@@ -589,7 +765,7 @@ __global__ void __launch_bounds__(kJacThreads)
           p = q;
           q = x;
         }
-        const double app = G[p][p], aqq = G[q][q], apq = G[p][q];
+        const double app = G(p, p), aqq = G(q, q), apq = G(p, q);
         double c = 1.0, s = 0.0;
         if (apq != 0.0 && fabs(apq) > 1e-14 * sqrt(fabs(app * aqq)) && fabs(apq) > floor_s) {
           const double zeta = (aqq - app) / (2.0 * apq);
@@ -610,7 +786,7 @@ __global__ void __launch_bounds__(kJacThreads)
         const double c1 = cs_c[P], s1 = cs_s[P], c2 = cs_c[Q], s2 = cs_s[Q];
         if (s1 == 0.0 && s2 == 0.0) continue;
         const int p1 = pp[P], q1 = qq[P], p2 = pp[Q], q2 = qq[Q];
-        const double b00 = G[p1][p2], b01 = G[p1][q2], b10 = G[q1][p2], b11 = G[q1][q2];
+        const double b00 = G(p1, p2), b01 = G(p1, q2), b10 = G(q1, p2), b11 = G(q1, q2);
         const double h00 = c2 * b00 - s2 * b01, h01 = s2 * b00 + c2 * b01;
         const double h10 = c2 * b10 - s2 * b11, h11 = s2 * b10 + c2 * b11;
         double n00 = c1 * h00 - s1 * h10, n01 = c1 * h01 - s1 * h11;
@@ -619,10 +795,10 @@ __global__ void __launch_bounds__(kJacThreads)
           n01 = 0.0;
           n10 = 0.0;
         }
-        G[p1][p2] = n00;
-        G[p1][q2] = n01;
-        G[q1][p2] = n10;
-        G[q1][q2] = n11;
+        G(p1, p2) = n00;
+        G(p1, q2) = n01;
+        G(q1, p2) = n10;
+        G(q1, q2) = n11;
       }
       // V <- V J
       for (int idx = t; idx < N * H; idx += kJacThreads) {
@@ -630,9 +806,9 @@ __global__ void __launch_bounds__(kJacThreads)
         const double c = cs_c[P], s = cs_s[P];
         if (s == 0.0) continue;
         const int p = pp[P], q = qq[P];
-        const double vp = V[i][p], vq = V[i][q];
-        V[i][p] = c * vp - s * vq;
-        V[i][q] = s * vp + c * vq;
+        const double vp = V(i, p), vq = V(i, q);
+        V(i, p) = c * vp - s * vq;
+        V(i, q) = s * vp + c * vq;
       }
       __syncthreads();
     }
@@ -643,9 +819,9 @@ __global__ void __launch_bounds__(kJacThreads)
   if (t < N) {
     int r = 0;
     if (t < l) {
-      const double d = G[t][t];
+      const double d = G(t, t);
       for (int j = 0; j < l; ++j) {
-        const double e = G[j][j];
+        const double e = G(j, j);
         r += (e > d) || (e == d && j < t);
       }
     } else {
@@ -656,17 +832,19 @@ __global__ void __launch_bounds__(kJacThreads)
   __syncthreads();
   for (int idx = t; idx < N * N; idx += kJacThreads) {
     const int row = idx / N, col = idx % N;
-    evec[row * N + rank[col]] = V[row][col];
+    evec[row * N + rank[col]] = V(row, col);
   }
   if (t < N) {
-    double smax = sqrt(fmax(G[0][0], 0.0));
-    for (int j = 1; j < l; ++j) smax = fmax(smax, sqrt(fmax(G[j][j], 0.0)));
-    double sg = t < l ? sqrt(fmax(G[t][t], 0.0)) : 0.0;
+    double smax = sqrt(fmax(G(0, 0), 0.0));
+    for (int j = 1; j < l; ++j) smax = fmax(smax, sqrt(fmax(G(j, j), 0.0)));
+    double sg = t < l ? sqrt(fmax(G(t, t), 0.0)) : 0.0;
     if (!(sg > smax * 5.9604644775390625e-08)) sg = 0.0;
     const int r = rank[t];
     sig_inv[r] = sg > 0.0 ? 1.0 / sg : 0.0;
     if (r < k) S[r] = (float)sg;
   }
+#undef G
+#undef V
 }
 
 // ================================================================ assemble
@@ -1002,14 +1180,15 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
   const int64_t m = p.m, n = p.n;
   const int l = p.l, lp = p.lp, k = p.k, kp = p.kp;
   const bool nv = p.fmt == METIS_NVFP4;
+  const unsigned lz = (unsigned)cdiv(lp, kLpMax);  // sketch-column tiles
   // ---- pass 1: sketch
   const float *ysrc;
   int yparts;
   if (p.kind == METIS_OMEGA_GAUSSIAN) {
     omega_transpose_kernel<<<dim3((unsigned)cdiv(n, 256), lp), 256, 0, st>>>((const unsigned short *)omega, n, l, lp,
                                                                           p.omt);
-    sketch_kernel<T><<<dim3((unsigned)cdiv(m, 128), p.sk), kThreads, 0, st>>>(A, m, n, lda, p.omt, l, lp, p.sk_chunk,
-                                                                             p.ysk);
+    sketch_kernel<T><<<dim3((unsigned)cdiv(m, 128), p.sk, lz), kThreads, 0, st>>>(A, m, n, lda, p.omt, l, lp,
+                                                                                p.sk_chunk, p.ysk);
     ysrc = p.ysk;
     yparts = p.sk;
   } else {
@@ -1017,27 +1196,59 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     ysrc = p.ysk;
     yparts = 1;
   }
-  // ---- CholeskyQR2
-  gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(ysrc, yparts, m * l, m, l, lp, p.gy_rows, nullptr,
-                                               yparts > 1 ? p.y : nullptr, nullptr, p.gpart);
-  const float *y = yparts > 1 ? p.y : ysrc;
-  gram_reduce_kernel<<<(unsigned)cdiv(lp * lp, 256), 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
-  chol_inv_kernel<<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws);
-  gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(y, 1, 0, m, l, lp, p.gy_rows, p.rinv, p.q1, nullptr, p.gpart);
-  gram_reduce_kernel<<<(unsigned)cdiv(lp * lp, 256), 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
-  chol_inv_kernel<<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws);
-  gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(p.q1, 1, 0, m, l, lp, p.gy_rows, p.rinv, p.q, p.qt, nullptr);
-  // ---- pass 2: projection B^T = A^T Q, then the Gram B B^T
-  project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp, p.pk_rows,
-                                                                           p.btp);
-  gram_kernel<<<p.gb_parts, kThreads, 0, st>>>(p.btp, p.pk, n * l, n, l, lp, p.gb_rows, nullptr, p.bt, nullptr,
-                                               p.gpart);
-  gram_reduce_kernel<<<(unsigned)cdiv(lp * lp, 256), 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
-  // ---- small SVD and factors
-  jacobi_kernel<<<1, kJacThreads, 0, st>>>(p.gram, l, lp, k, 40, p.evec, p.sig_inv, out->S);
-  assemble_u_kernel<<<p.am_parts, kThreads, 0, st>>>(p.q, m, l, lp, k, p.evec, p.am_rows, out->U, p.am_val,
-                                                     p.am_idx);
-  assemble_v_kernel<<<(unsigned)cdiv(n, 64), kThreads, 0, st>>>(p.bt, n, l, lp, k, p.evec, p.sig_inv, out->V);
+  const unsigned rgrid_red = (unsigned)cdiv(lp * lp, 256);
+  if (!p.wide) {
+    // ---- CholeskyQR2 (LDS-resident small matrices)
+    gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(ysrc, yparts, m * l, m, l, lp, p.gy_rows, nullptr,
+                                                 yparts > 1 ? p.y : nullptr, nullptr, p.gpart);
+    const float *y = yparts > 1 ? p.y : ysrc;
+    gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
+    chol_inv_kernel<false><<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws, p.wa, p.winv);
+    gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(y, 1, 0, m, l, lp, p.gy_rows, p.rinv, p.q1, nullptr, p.gpart);
+    gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
+    chol_inv_kernel<false><<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, p.wa, p.winv);
+    gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(p.q1, 1, 0, m, l, lp, p.gy_rows, p.rinv, p.q, p.qt, nullptr);
+    // ---- pass 2: projection B^T = A^T Q, then the Gram B B^T
+    project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
+                                                                                 p.pk_rows, p.btp);
+    gram_kernel<<<p.gb_parts, kThreads, 0, st>>>(p.btp, p.pk, n * l, n, l, lp, p.gb_rows, nullptr, p.bt, nullptr,
+                                                 p.gpart);
+    gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
+    // ---- small SVD and factors
+    jacobi_kernel<false><<<1, kJacThreads, 0, st>>>(p.gram, l, lp, k, 40, p.evec, p.sig_inv, out->S, p.wg, p.wv);
+    assemble_u_kernel<<<p.am_parts, kThreads, 0, st>>>(p.q, m, l, lp, k, p.evec, p.am_rows, out->U, p.am_val,
+                                                       p.am_idx);
+    assemble_v_kernel<<<(unsigned)cdiv(n, 64), kThreads, 0, st>>>(p.bt, n, l, lp, k, p.evec, p.sig_inv, out->V);
+  } else {
+    // ---- the same steps with the l x l matrices in global scratch
+    const float *y = ysrc;
+    if (yparts > 1) {
+      sum_parts_kernel<<<(unsigned)cdiv(m * l, 256), 256, 0, st>>>(ysrc, yparts, m * l, m * l, p.y);
+      y = p.y;
+    }
+    const unsigned nt = (unsigned)(lp / 64);
+    gram_tile_kernel<<<dim3(p.gy_parts, nt, nt), kThreads, 0, st>>>(y, m, l, lp, p.gy_rows, p.gpart);
+    gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
+    chol_inv_kernel<true><<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws, p.wa, p.winv);
+    apply_rinv_kernel<<<dim3((unsigned)cdiv(m, 64), nt), kThreads, 0, st>>>(y, m, l, lp, p.rinv, p.q1, nullptr);
+    gram_tile_kernel<<<dim3(p.gy_parts, nt, nt), kThreads, 0, st>>>(p.q1, m, l, lp, p.gy_rows, p.gpart);
+    gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
+    chol_inv_kernel<true><<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, p.wa, p.winv);
+    apply_rinv_kernel<<<dim3((unsigned)cdiv(m, 64), nt), kThreads, 0, st>>>(p.q1, m, l, lp, p.rinv, p.q, p.qt);
+    project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
+                                                                                 p.pk_rows, p.btp);
+    const float *bt = p.btp;
+    if (p.pk > 1) {
+      sum_parts_kernel<<<(unsigned)cdiv(n * l, 256), 256, 0, st>>>(p.btp, p.pk, n * l, n * l, p.bt);
+      bt = p.bt;
+    }
+    gram_tile_kernel<<<dim3(p.gb_parts, nt, nt), kThreads, 0, st>>>(bt, n, l, lp, p.gb_rows, p.gpart);
+    gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
+    jacobi_kernel<true><<<1, kJacThreads, 0, st>>>(p.gram, l, lp, k, 40, p.evec, p.sig_inv, out->S, p.wg, p.wv);
+    assemble_wide_kernel<<<(unsigned)cdiv(m * k, 256), 256, 0, st>>>(p.q, m, l, lp, k, p.evec, nullptr, out->U);
+    argmax_kernel<<<p.am_parts, 128, 0, st>>>(out->U, m, k, p.am_rows, p.am_val, p.am_idx);
+    assemble_wide_kernel<<<(unsigned)cdiv(n * k, 256), 256, 0, st>>>(bt, n, l, lp, k, p.evec, p.sig_inv, out->V);
+  }
   sign_kernel<<<1, 128, 0, st>>>(p.am_val, p.am_idx, p.am_parts, k, p.sign);
   const int B = nv ? 16 : 32;
   const unsigned fgrid = (unsigned)cdiv(std::max(m, n) / B * kp, kThreads);
@@ -1095,7 +1306,8 @@ extern "C" metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m
   if (k < 1 || l < k || l > m || l > n) return METIS_ERR_INVALID;
   const int elem = dt == METIS_F32 ? 4 : 2;
   if (((uintptr_t)A) & 15 || (lda * elem) % 16) return METIS_ERR_INVALID;
-  if (l > kLpMax) return METIS_ERR_UNSUPPORTED;
+  if (l > 512) return METIS_ERR_UNSUPPORTED;
+  if (k > 96) return METIS_ERR_UNSUPPORTED;
   if (!out->U || !out->S || !out->V) return METIS_ERR_INVALID;
   const bool nv = fmt == METIS_NVFP4;
   if (!fp4_ok(out->Ut_q, fmt, nv) || !fp4_ok(out->Vt_q, fmt, nv)) return METIS_ERR_INVALID;

@@ -17,10 +17,16 @@ The pages give no formulas, so the steps follow the textbook randomized SVD
   2. range     Y = Q R_Y by Householder reflections; keep Q (m x l, orthonormal)
   3. project   B = Q^T A (l x n)
   4. small SVD B = Ub diag(sigma) W^T by one-sided (Hestenes) Jacobi rotations
+               (on B, or for wide B on the triangular factor of B^T's QR)
   5. factors   U_k = Q Ub[:, :k], S_k = sigma[:k], V_k = W[:, :k]
   6. signs     each column of U_k is flipped (with the same column of V_k) so
                that its entry of largest magnitude (lowest row on ties) is positive
   7. residual  R = A - U_k diag(S_k) V_k^T, from the unquantized factors
+
+Sketches wider than 128 columns (the 512-column sampling workload) run steps
+2 and 4 through LAPACK (numpy.linalg.qr / svd) as library primitives; the
+own routines below are pinned against LAPACK, and both routes are pinned to
+agree on a 160-column case.
 
 Pins (tests/test_oracle_split.py): Householder Q and R against
 numpy.linalg.qr (LAPACK) up to column signs; singular values and subspaces
@@ -61,55 +67,70 @@ def householder_qr(Y):
         v /= np.sqrt(v @ v)
         A[j:, j:] -= 2.0 * np.outer(v, v @ A[j:, j:])
         reflectors.append(v)
-    # Q = H_0 H_1 ... H_{l-1} applied to the first l columns of the identity
+    # Q = H_0 H_1 ... H_{l-1} applied to the first l columns of the identity,
+    # accumulated from the last reflector: before H_j is applied, columns
+    # 0..j-1 are still unit vectors with zeros in rows >= j, so H_j only
+    # changes the block Q[j:, j:].
     Q = np.zeros((m, l))
     Q[np.arange(l), np.arange(l)] = 1.0
     for j in reversed(range(l)):
         v = reflectors[j]
         if v is None:
             continue
-        Q[j:, :] -= 2.0 * np.outer(v, v @ Q[j:, :])
+        Q[j:, j:] -= 2.0 * np.outer(v, v @ Q[j:, j:])
     return Q, np.triu(A[:l, :])
+
+
+def _round_robin_pairs(N, rnd):
+    """Pairs of round ``rnd`` of the round-robin (Brent-Luk) ordering of N
+    indices (N even): index 0 stays, the others rotate one position per
+    round; position i meets position N-1-i. Every pair meets once per sweep."""
+    pos = np.arange(N)
+    player = np.where(pos == 0, 0, 1 + (pos - 1 + rnd) % (N - 1))
+    a, b = player[: N // 2], player[::-1][: N // 2]
+    return np.minimum(a, b), np.maximum(a, b)
 
 
 def jacobi_svd(B, tol=JACOBI_TOL, max_sweeps=JACOBI_MAX_SWEEPS):
     """SVD of a wide matrix B (l x n, l <= n) by one-sided Jacobi rotations.
 
-    The rows of B (the columns of B^T) are rotated in pairs, cyclically by
-    row index, until every pair is orthogonal to relative tolerance ``tol``:
-    |g_p . g_q| <= tol * ||g_p|| ||g_q||. With G = J^T B after convergence,
+    The rows of B (the columns of B^T) are rotated in pairs until every pair
+    is orthogonal to relative tolerance ``tol``: |g_p . g_q| <= tol ||g_p|| ||g_q||.
+    Pairs are visited in the round-robin ordering; the pairs of one round are
+    disjoint, so they are rotated together. With G = J^T B after convergence,
     B = J G, the row norms of G are the singular values and the normalized
     rows are the right singular vectors. Returns (Ub, sigma, W) with
     B = Ub diag(sigma) W^T, sigma in descending order, W n x l.
     Rows of zero norm give sigma = 0 and a zero column of W."""
-    G = np.array(B, dtype=np.float64)
-    l, n = G.shape
-    J = np.eye(l)
-    sweeps = 0
-    for sweeps in range(1, max_sweeps + 1):
+    B = np.asarray(B, dtype=np.float64)
+    l, n = B.shape
+    N = l + (l % 2)  # an odd count gets one zero row, which never rotates
+    G = np.zeros((N, n))
+    G[:l] = B
+    J = np.eye(N)
+    for _ in range(max_sweeps):
         rotated = False
-        for p in range(l - 1):
-            for q in range(p + 1, l):
-                gp, gq = G[p], G[q]
-                alpha = gp @ gp
-                beta = gq @ gq
-                gamma = gp @ gq
-                if abs(gamma) <= tol * np.sqrt(alpha * beta) or gamma == 0.0:
-                    continue
-                rotated = True
-                # rotation angle that makes the pair orthogonal (smaller root)
-                zeta = (beta - alpha) / (2.0 * gamma)
-                t = (1.0 if zeta >= 0 else -1.0) / (abs(zeta) + np.sqrt(1.0 + zeta * zeta))
-                c = 1.0 / np.sqrt(1.0 + t * t)
-                s = c * t
-                new_p = c * gp - s * gq
-                new_q = s * gp + c * gq
-                G[p], G[q] = new_p, new_q
-                jp, jq = J[:, p].copy(), J[:, q].copy()
-                J[:, p] = c * jp - s * jq
-                J[:, q] = s * jp + c * jq
+        for rnd in range(N - 1):
+            P, Q = _round_robin_pairs(N, rnd)
+            gp, gq = G[P], G[Q]
+            alpha = np.einsum("ij,ij->i", gp, gp)
+            beta = np.einsum("ij,ij->i", gq, gq)
+            gamma = np.einsum("ij,ij->i", gp, gq)
+            act = (np.abs(gamma) > tol * np.sqrt(alpha * beta)) & (gamma != 0.0)
+            if not act.any():
+                continue
+            rotated = True
+            # rotation angle that makes each active pair orthogonal (smaller root)
+            zeta = np.where(act, (beta - alpha) / np.where(act, 2.0 * gamma, 1.0), 0.0)
+            t = np.where(zeta >= 0, 1.0, -1.0) / (np.abs(zeta) + np.sqrt(1.0 + zeta * zeta))
+            c = np.where(act, 1.0 / np.sqrt(1.0 + t * t), 1.0)
+            s = np.where(act, c * t, 0.0)
+            G[P], G[Q] = c[:, None] * gp - s[:, None] * gq, s[:, None] * gp + c[:, None] * gq
+            jp, jq = J[:, P], J[:, Q]
+            J[:, P], J[:, Q] = c * jp - s * jq, s * jp + c * jq
         if not rotated:
             break
+    G, J = G[:l], J[:l, :l]
     sigma = np.sqrt(np.einsum("ij,ij->i", G, G))
     order = np.argsort(-sigma, kind="stable")
     sigma = sigma[order]
@@ -119,6 +140,43 @@ def jacobi_svd(B, tol=JACOBI_TOL, max_sweeps=JACOBI_MAX_SWEEPS):
     live = sigma > 0
     W[:, live] = (G[live] / sigma[live, None]).T
     return J, sigma, W
+
+
+LIBRARY_ROUTE_MIN_L = 129  # sketches this wide use LAPACK for the same steps
+
+
+def range_basis(Y, force=None):
+    """Orthonormal basis Q of range(Y) by Householder QR (step 2). Sketches
+    wider than 128 columns call LAPACK's Householder QR (numpy.linalg.qr) as
+    a library primitive for the same step; ``force`` picks a route."""
+    use_lib = Y.shape[1] >= LIBRARY_ROUTE_MIN_L if force is None else force == "library"
+    if use_lib:
+        Q, _ = np.linalg.qr(np.asarray(Y, dtype=np.float64))
+        return Q
+    Q, _ = householder_qr(Y)
+    return Q
+
+
+def small_svd(B, force=None):
+    """SVD of the projected matrix B (l x n).
+
+    For n up to 4 l, one-sided Jacobi on B itself. For wider B, the rows of B
+    are first compressed by a Householder QR of B^T = Qb Rb (the usual QR
+    step ahead of an SVD of a very wide matrix, Golub & Van Loan §8.6):
+    B = Rb^T Qb^T, so one-sided Jacobi on the l x l matrix Rb^T gives the same
+    left singular vectors and values, and W = Qb times its right singular
+    vectors. Both routes are exact SVDs; the second only shortens the rows
+    that the rotations touch."""
+    l, n = B.shape
+    use_lib = l >= LIBRARY_ROUTE_MIN_L if force is None else force == "library"
+    if use_lib:  # LAPACK SVD as the library primitive for the same step
+        Ub, sigma, Wt = np.linalg.svd(np.asarray(B, dtype=np.float64), full_matrices=False)
+        return Ub, sigma, Wt.T
+    if n <= 4 * l:
+        return jacobi_svd(B)
+    Qb, Rb = householder_qr(np.asarray(B, dtype=np.float64).T)
+    Ub, sigma, Wr = jacobi_svd(Rb.T)
+    return Ub, sigma, Qb @ Wr
 
 
 def sign_convention(U, V):
@@ -157,9 +215,9 @@ def spectral_split(A, l, k, omega=None, columns=None):
     Y = sketch(A, omega, columns)
     if Y.shape != (m, l):
         raise ValueError("sketch width must equal l")
-    Q, _ = householder_qr(Y)
+    Q = range_basis(Y)
     B = Q.T @ A
-    Ub, sigma, W = jacobi_svd(B)
+    Ub, sigma, W = small_svd(B)
     U = Q @ Ub[:, :k]
     S = sigma[:k].copy()
     V = W[:, :k]

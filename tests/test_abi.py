@@ -104,7 +104,8 @@ def test_split_rejects_bad_arguments_on_host():
     assert ok(A=ctypes.c_void_p(258)) == 1   # misaligned A
     assert ok(ws=None) == 3
     assert ok(ws_bytes=1024) == 3   # far below either dtype's plan
-    assert ok(l=128, k=8, m=512, n=512, lda=512) == 2  # sketch wider than this build handles
+    assert ok(l=544, k=8, m=1024, n=1024, lda=1024) == 2  # sketch wider than this build handles
+    assert ok(l=128, k=100, m=512, n=512, lda=512) == 2  # rank above what the GEMMs take
     bad = _split_rec()
     bad.R_q.fmt = 1
     assert L.metis_split(A, 1, 256, 256, 256, om, 0, 16, 8, 0, ctypes.byref(bad), None, ws, nbytes, None) == 1

@@ -29,17 +29,18 @@ def _operand(t, orientations):
     return M.plain_operand(G.to_gpu(t), t.fmt, orientations)
 
 
-def _small(seed, rows, cols, k, l, kind="planted", dtype="bf16"):
-    return synth.small_case(seed, rows, cols, dtype, kind, k=k, l=l, n_dir=4)
+def _small(seed, rows, cols, k, l, kind="planted", dtype="bf16", fmt="mxfp4"):
+    return synth.small_case(seed, rows, cols, dtype, kind, k=k, l=l, n_dir=4, fmt=fmt)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("kx,kw,kdy", [(8, 8, 8), (0, 8, 0), (8, 0, 8), (0, 0, 0), (16, 8, 4)])
-def test_linear_fwd_bwd_small(kx, kw, kdy):
+def test_linear_fwd_bwd_small(kx, kw, kdy, fmt):
     Mt, K, N = 288, 320, 416  # ragged against the 256 x 256 output tile
-    X = _small(201, Mt, K, kx, kx + 8)
-    W = _small(202, N, K, kw, kw + 8, kind="powerlaw")
-    dY = _small(203, Mt, N, kdy, kdy + 8)
-    print("case", kx, kw, kdy, flush=True)
+    X = _small(201, Mt, K, kx, kx + 8, fmt=fmt)
+    W = _small(202, N, K, kw, kw + 8, kind="powerlaw", fmt=fmt)
+    dY = _small(203, Mt, N, kdy, kdy + 8, fmt=fmt)
+    print("case", kx, kw, kdy, fmt, flush=True)
     rx, rw, rd = _operand(X, ("n", "t")), _operand(W, ("n", "t")), _operand(dY, ("n", "t"))
     Y = M.spectral_fp4_linear_fwd(rx, rw)
     dX, dW = M.spectral_fp4_linear_bwd(rd, rx, rw)
@@ -122,3 +123,9 @@ def test_linear_full_size_cfg4_up():
 
 def test_linear_full_size_cfg4_down():
     _full(4, [g for g in synth.GEMMS[4] if g[0].endswith("_down")], nrows=256)
+
+
+def test_linear_full_size_cfg5_nvfp4():
+    """NVFP4 GEMMs (bf16 MFMA on exactly decoded operands) on the
+    512-column-sampled splits of the FFN down projection."""
+    _full(5, synth.GEMMS[5], nrows=256)

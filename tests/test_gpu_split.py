@@ -86,6 +86,10 @@ CASES = {
     "sampled-columns": lambda: synth.small_case(104, 256, 320, "bf16", "planted", k=8, l=24, n_dir=4,
                                                 sketch="columns"),
     "nvfp4": lambda: synth.small_case(105, 288, 256, "bf16", "powerlaw", k=16, l=32, fmt="nvfp4"),
+    "wide-columns-l160": lambda: synth.small_case(108, 640, 448, "bf16", "planted", k=32, l=160, n_dir=8,
+                                                  sketch="columns"),
+    "wide-gaussian-l128-nvfp4": lambda: synth.small_case(109, 384, 320, "bf16", "powerlaw", k=16, l=128,
+                                                         fmt="nvfp4"),
 }
 
 
@@ -156,3 +160,22 @@ def test_split_parity_full_size(cfg, name):
     rows = np.sort(np.random.Generator(np.random.PCG64(5)).choice(t.shape[0], 256, replace=False))
     Rp = F.f32(A[rows] - (U[rows] * Sg) @ V.T)
     _check_codes_near(d["R_q"], F.quantize(Rp, "mxfp4"), "mxfp4", rows=rows)
+
+
+@pytest.mark.parametrize("name", ["dY", "W", "X"])
+def test_split_parity_full_size_nvfp4_sampled_512(name):
+    """NVFP4 + 512 sampled columns (wide sketch, global-memory small SVD)."""
+    t = synth.make_tensor(5, name)
+    print("case cfg5", name, t.shape, flush=True)
+    A, orc = _oracle_split(t)
+    rec = G.split_gpu(t, orientations=("n",))
+    torch.cuda.synchronize()
+    U, Sg, V = G.factors_np(rec)
+    err = np.linalg.norm((U * Sg) @ V.T - (orc["U"] * orc["S"]) @ orc["V"].T) / np.linalg.norm(A)
+    print("L rel err %.3e" % err, flush=True)
+    assert err <= L_GATE
+    assert int(rec.info.item()) == 0
+    d = G.record_to_dict(rec)
+    want = F.quantize(F.f32(V.T), "nvfp4")
+    assert np.array_equal(d["Vt_q"]["codes"], want["codes"]) and np.array_equal(d["Vt_q"]["scales"], want["scales"])
+    assert np.float32(d["Vt_q"]["tensor_scale"]) == np.float32(want["tensor_scale"])

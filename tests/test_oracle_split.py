@@ -44,6 +44,35 @@ def test_jacobi_svd_matches_lapack(l, n):
     assert np.allclose(Ub.T @ Ub, np.eye(l), atol=1e-13)
 
 
+@pytest.mark.parametrize("l,n", [(6, 100), (16, 300)])
+def test_small_svd_wide_route_equals_direct_jacobi_and_lapack(l, n):
+    B = _rand(11, l, n) * np.exp(np.linspace(0, -6, l))[:, None]
+    U1, s1, W1 = S.small_svd(B)          # QR-compressed route (n > 4 l)
+    U2, s2, W2 = S.jacobi_svd(B)         # direct route
+    sn = np.linalg.svd(B, compute_uv=False)
+    assert np.allclose(s1, sn, rtol=1e-11, atol=0) and np.allclose(s1, s2, rtol=1e-11, atol=0)
+    d = np.sign(np.sum(U1 * U2, axis=0))
+    assert np.allclose(U1, U2 * d, atol=1e-9) and np.allclose(W1, W2 * d, atol=1e-9)
+    assert np.allclose((U1 * s1) @ W1.T, B, atol=1e-12)
+
+
+def test_library_route_agrees_with_own_routines_at_l160(monkeypatch):
+    """Wide sketches use LAPACK for QR and SVD; on a 160-column case both
+    routes give the same split (and the planted values)."""
+    g = np.random.Generator(np.random.PCG64(12))
+    U = synth.orthonormal(g, 640, 10)
+    V = synth.orthonormal(g, 480, 10)
+    s = 100.0 * np.arange(1, 11) ** -1.0
+    A = (U * s) @ V.T + 1e-3 * g.standard_normal((640, 480))
+    J = np.sort(g.choice(480, 160, replace=False))
+    r_lib = S.spectral_split(A, 160, 12, columns=J)
+    monkeypatch.setattr(S, "LIBRARY_ROUTE_MIN_L", 10 ** 9)
+    r_own = S.spectral_split(A, 160, 12, columns=J)
+    assert np.allclose(r_lib["S"], r_own["S"], rtol=1e-10, atol=0)
+    assert np.allclose(r_lib["R"], r_own["R"], atol=1e-10)
+    assert np.allclose(r_lib["S"][:10], s, rtol=1e-3)
+
+
 def test_jacobi_svd_zero_row_gives_zero_sigma():
     B = _rand(4, 6, 30)
     B[2] = 0.0
