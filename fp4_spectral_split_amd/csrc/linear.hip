@@ -338,22 +338,27 @@ __device__ __forceinline__ void tile_coords(int &tm, int &tn, int mt, int nt) {
   tn = in / gm;
 }
 
-// acc (the 256 x 256 tile, 4 x 4 MFMA blocks of 32 x 32 per wave) times
-// `scale`, plus L1[m-tile] L2[n-tile]^T (bf16, 64 panel columns at a time
-// through LDS), stored as fp32.
-__device__ __forceinline__ void epilogue(floatx16 (&acc)[4][4], float scale, uint8_t *smem, int64_t m0, int64_t n0,
-                                         int64_t M, int64_t N, const unsigned short *__restrict__ l1,
+// Both GEMM kernels: 256 x 256 output tile per workgroup of 512 threads,
+// 8 waves in a 2 (rows) x 4 (columns) grid, each wave a 128 x 64 sub-tile of
+// 4 x 2 MFMA blocks of 32 x 32 (128 accumulator registers, two waves per SIMD).
+constexpr int kGemmThreads = 512;
+constexpr int WM = 4, WN = 2;  // 32 x 32 blocks per wave
+
+// acc times `scale`, plus L1[m-tile] L2[n-tile]^T (bf16, 64 panel columns at a
+// time through LDS), stored as fp32.
+__device__ __forceinline__ void epilogue(floatx16 (&acc)[WM][WN], float scale, uint8_t *smem, int64_t m0,
+                                         int64_t n0, int64_t M, int64_t N, const unsigned short *__restrict__ l1,
                                          const unsigned short *__restrict__ l2, int rp, float *__restrict__ C,
                                          int64_t ldc) {
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int r32 = lane & 31, h = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   if (scale != 1.0f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < WN; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] *= scale;
   }
@@ -361,8 +366,8 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[4][4], float scale, uin
     uint8_t *L1s = smem, *L2s = smem + BM * EPI_ROWB;
     for (int c0 = 0; c0 < rp; c0 += 64) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = t + 256 * i;  // 2048 pieces of 16 bytes per panel
+      for (int i = 0; i < 4; ++i) {
+        const int idx = t + kGemmThreads * i;  // 2048 pieces of 16 bytes per panel
         const int rr = idx >> 3, piece = idx & 7;
         const int64_t ar = m0 + rr, br = n0 + rr;
         const uint4 va = ar < M ? *(const uint4 *)(l1 + ar * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
@@ -373,26 +378,26 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[4][4], float scale, uin
       __syncthreads();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        ushortx8 a8[4], b8[4];
+        ushortx8 a8[WM], b8[WN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WM; ++i)
           a8[i] = *(const ushortx8 *)(L1s + (wm * 128 + i * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b8[j] = *(const ushortx8 *)(L2s + (wn * 128 + j * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
+        for (int j = 0; j < WN; ++j)
+          b8[j] = *(const ushortx8 *)(L2s + (wn * 64 + j * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WM; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
+          for (int j = 0; j < WN; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
       }
       __syncthreads();
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + r32;
+    for (int j = 0; j < WN; ++j) {
+      const int64_t col = n0 + wn * 64 + j * 32 + r32;
       if (col >= N) continue;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -402,11 +407,87 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[4][4], float scale, uin
     }
 }
 
-// MXFP4: C = Ra Rb^T (+ L1 L2^T) on the scaled FP4 MFMA; 256 x 256 tile per
-// workgroup (4 waves, 2 x 2, each 128 x 128), 128 contraction elements per
-// LDS stage, double buffered: the next stage's global loads are in flight
-// while the current stage's MFMAs run.
-__global__ void __launch_bounds__(256, 1)
+// MXFP4: C = Ra Rb^T (+ L1 L2^T) on the scaled FP4 MFMA, 128 contraction
+// elements per LDS stage. Global loads run two stages ahead through registers
+// (slot s % 2 holds stage s while it is in flight) and LDS is double
+// buffered, so each load has two stages of MFMA work to land; one barrier
+// per stage. Thread t stages two 16-byte pieces of A and of B per stage and
+// one scale word (rows 0..255 of A for t < 256, of B above).
+template <int SLOT>
+__device__ __forceinline__ void mx_load(uint4 (&ga)[2][2], uint4 (&gb)[2][2], uint32_t (&gs)[2], int st,
+                                        const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
+                                        const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int64_t m0,
+                                        int64_t n0, int64_t M, int64_t N, int64_t T, int64_t nb, bool scale_words) {
+  const int t = threadIdx.x;
+  const int64_t k0 = (int64_t)st * 128;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = (t >> 2) + 128 * i, piece = t & 3;
+    const int64_t e = k0 + piece * 32;
+    const int64_t ar = m0 + rr, br = n0 + rr;
+    ga[SLOT][i] = (ar < M && e < T) ? *(const uint4 *)(ac + ar * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
+    gb[SLOT][i] = (br < N && e < T) ? *(const uint4 *)(bc + br * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
+  }
+  // four scale bytes (blocks k0/32 .. +3) of one row of one operand
+  const bool isb = t >= BM;
+  const int64_t row = (isb ? n0 : m0) + (t & (BM - 1));
+  const bool ok = row < (isb ? N : M);
+  const uint8_t *sc = (isb ? bs : as) + row * nb;
+  const int64_t b0 = k0 / 32;
+  if (scale_words) {  // T % 128 == 0: the four bytes are one aligned word
+    gs[SLOT] = ok ? *(const uint32_t *)(sc + b0) : 0x7F7F7F7Fu;
+  } else {
+    uint32_t w = 0x7F7F7F7Fu;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (ok && b0 + q < nb) w = (w & ~(0xFFu << (8 * q))) | ((uint32_t)sc[b0 + q] << (8 * q));
+    gs[SLOT] = w;
+  }
+}
+
+template <int SLOT>
+__device__ __forceinline__ void mx_store(const uint4 (&ga)[2][2], const uint4 (&gb)[2][2], const uint32_t (&gs)[2],
+                                         uint8_t *base) {
+  const int t = threadIdx.x;
+  uint8_t *A_ = base, *B_ = base + BM * ROWB;
+  uint32_t *S_ = (uint32_t *)(base + 2 * BM * ROWB);  // A scale words then B scale words
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = (t >> 2) + 128 * i, piece = t & 3;
+    *(uint4 *)(A_ + rr * ROWB + piece * 16) = ga[SLOT][i];
+    *(uint4 *)(B_ + rr * ROWB + piece * 16) = gb[SLOT][i];
+  }
+  S_[t] = gs[SLOT];
+}
+
+__device__ __forceinline__ void mx_compute(floatx16 (&acc)[WM][WN], const uint8_t *base, int wm, int wn, int r32,
+                                           int h) {
+  const uint8_t *A_ = base, *B_ = base + BM * ROWB;
+  const uint8_t *SA = base + 2 * BM * ROWB, *SB = SA + BM * 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    uint4 af[WM], bf[WN];
+    int sa[WM], sb[WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const int rr = wm * 128 + i * 32 + r32;
+      af[i] = *(const uint4 *)(A_ + rr * ROWB + h * 32 + ks * 16);
+      sa[i] = SA[rr * 4 + h * 2 + ks];
+    }
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int rr = wn * 64 + j * 32 + r32;
+      bf[j] = *(const uint4 *)(B_ + rr * ROWB + h * 32 + ks * 16);
+      sb[j] = SB[rr * 4 + h * 2 + ks];
+    }
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) acc[i][j] = mfma_fp4(af[i], bf[j], sa[i], sb[j], acc[i][j]);
+  }
+}
+
+__global__ void __launch_bounds__(kGemmThreads, 1)
     gemm_mx_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
                    const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int64_t N, int64_t T,
                    const unsigned short *__restrict__ l1, const unsigned short *__restrict__ l2, int rp,
@@ -415,108 +496,50 @@ __global__ void __launch_bounds__(256, 1)
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int r32 = lane & 31, h = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   int tm, tn;
   tile_coords(tm, tn, (int)cdiv(M, BM), (int)cdiv(N, BN));
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t nb = T / 32;
   const int nst = (int)cdiv(T, 128);
+  const bool words = (T % 128) == 0;
 
-  floatx16 acc[4][4];
+  floatx16 acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // global -> register staging: 4 pieces of 16 bytes per operand + 1 scale word
-  uint4 ga[4], gb[4];
-  uint32_t gsa, gsb;
-  auto load_stage = [&](int st) {
-    const int64_t k0 = (int64_t)st * 128;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = (t >> 2) + 64 * i, piece = t & 3;
-      const int64_t e = k0 + piece * 32;
-      const int64_t ar = m0 + rr, br = n0 + rr;
-      ga[i] = (ar < M && e < T) ? *(const uint4 *)(ac + ar * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
-      gb[i] = (br < N && e < T) ? *(const uint4 *)(bc + br * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
-    }
-    const int64_t ar = m0 + t, br = n0 + t;
-    uint32_t wa = 0x7F7F7F7Fu, wb = 0x7F7F7F7Fu;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t blk = k0 / 32 + q;
-      if (blk < nb) {
-        if (ar < M) wa = (wa & ~(0xFFu << (8 * q))) | ((uint32_t)as[ar * nb + blk] << (8 * q));
-        if (br < N) wb = (wb & ~(0xFFu << (8 * q))) | ((uint32_t)bs[br * nb + blk] << (8 * q));
-      }
-    }
-    gsa = wa;
-    gsb = wb;
-  };
-  auto store_stage = [&](int buf) {
-    uint8_t *base = smem + buf * STAGE_BYTES;
-    uint8_t *A_ = base, *B_ = base + BM * ROWB;
-    uint32_t *SA = (uint32_t *)(base + 2 * BM * ROWB), *SB = SA + BM;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = (t >> 2) + 64 * i, piece = t & 3;
-      *(uint4 *)(A_ + rr * ROWB + piece * 16) = ga[i];
-      *(uint4 *)(B_ + rr * ROWB + piece * 16) = gb[i];
-    }
-    SA[t] = gsa;
-    SB[t] = gsb;
-  };
-
-  load_stage(0);
-  store_stage(0);
+  uint4 ga[2][2], gb[2][2];
+  uint32_t gs[2];
+  mx_load<0>(ga, gb, gs, 0, ac, as, bc, bs, m0, n0, M, N, T, nb, words);
+  if (nst > 1) mx_load<1>(ga, gb, gs, 1, ac, as, bc, bs, m0, n0, M, N, T, nb, words);
+  mx_store<0>(ga, gb, gs, smem);
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < nst) load_stage(st + 1);
-    const uint8_t *base = smem + cur * STAGE_BYTES;
-    const uint8_t *A_ = base, *B_ = base + BM * ROWB;
-    const uint8_t *SA = base + 2 * BM * ROWB, *SB = SA + BM * 4;
-    uint4 af[4][2], bf[4][2];
-    int sa[4][2], sb[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = wm * 128 + i * 32 + r32;
-      af[i][0] = *(const uint4 *)(A_ + rr * ROWB + h * 32);
-      af[i][1] = *(const uint4 *)(A_ + rr * ROWB + h * 32 + 16);
-      const uint32_t s2 = *(const unsigned short *)(SA + rr * 4 + h * 2);
-      sa[i][0] = (int)(s2 & 0xFFu);
-      sa[i][1] = (int)(s2 >> 8);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rr = wn * 128 + j * 32 + r32;
-      bf[j][0] = *(const uint4 *)(B_ + rr * ROWB + h * 32);
-      bf[j][1] = *(const uint4 *)(B_ + rr * ROWB + h * 32 + 16);
-      const uint32_t s2 = *(const unsigned short *)(SB + rr * 4 + h * 2);
-      sb[j][0] = (int)(s2 & 0xFFu);
-      sb[j][1] = (int)(s2 >> 8);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(af[i][ks], bf[j][ks], sa[i][ks], sb[j][ks], acc[i][j]);
-    if (st + 1 < nst) store_stage(cur ^ 1);
+  // stage st: its data is in LDS buffer st % 2; stage st + 1 is in flight in
+  // register slot (st + 1) % 2; stage st + 2 is issued into slot st % 2
+  for (int st = 0; st < nst; st += 2) {
+    if (st + 2 < nst) mx_load<0>(ga, gb, gs, st + 2, ac, as, bc, bs, m0, n0, M, N, T, nb, words);
+    mx_compute(acc, smem, wm, wn, r32, h);
+    if (st + 1 < nst) mx_store<1>(ga, gb, gs, smem + STAGE_BYTES);
+    __syncthreads();
+    if (st + 1 >= nst) break;
+    if (st + 3 < nst) mx_load<1>(ga, gb, gs, st + 3, ac, as, bc, bs, m0, n0, M, N, T, nb, words);
+    mx_compute(acc, smem + STAGE_BYTES, wm, wn, r32, h);
+    if (st + 2 < nst) mx_store<0>(ga, gb, gs, smem);
     __syncthreads();
   }
-
   epilogue(acc, 1.0f, smem, m0, n0, M, N, l1, l2, rp, C, ldc);
 }
 
 // NVFP4: codes and E4M3 block scales are decoded exactly to bf16 while being
 // staged into LDS (64 contraction elements per stage), multiplied on the
 // bf16 32x32x16 MFMA with fp32 accumulation; the product of the two tensor
-// scales multiplies the accumulators once before the correction.
-__global__ void __launch_bounds__(256, 1)
+// scales multiplies the accumulators once before the correction. Thread t
+// stages half (t & 1) of row t >> 1 of each operand: 32 codes, two blocks.
+__global__ void __launch_bounds__(kGemmThreads, 1)
     gemm_nv_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, const float *__restrict__ ats,
                    int64_t M, const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs,
                    const float *__restrict__ bts, int64_t N, int64_t T, const unsigned short *__restrict__ l1,
@@ -525,58 +548,48 @@ __global__ void __launch_bounds__(256, 1)
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int r32 = lane & 31, h = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   int tm, tn;
   tile_coords(tm, tn, (int)cdiv(M, BM), (int)cdiv(N, BN));
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t nb = T / 16;
   const int nst = (int)cdiv(T, 64);
-  floatx16 acc[4][4];
+  floatx16 acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-  // thread t stages rows (t >> 1) and (t >> 1) + 128, half (t & 1): 32 codes
-  // (two NVFP4 blocks) per row and operand per stage
-  uint4 ga[2], gb[2];
-  uint32_t gsa[2], gsb[2];
-  const int half = t & 1;
+  uint4 ga, gb;
+  uint32_t gsa, gsb;
+  const int half = t & 1, rr = t >> 1;
+  const int64_t ar = m0 + rr, br = n0 + rr;
   auto load_stage = [&](int st) {
     const int64_t e = (int64_t)st * 64 + half * 32;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rr = (t >> 1) + 128 * i;
-      const int64_t ar = m0 + rr, br = n0 + rr;
-      const bool ea = ar < M && e < T, eb = br < N && e < T;
-      ga[i] = ea ? *(const uint4 *)(ac + ar * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
-      gb[i] = eb ? *(const uint4 *)(bc + br * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
-      gsa[i] = ea ? ((uint32_t)as[ar * nb + e / 16] | ((uint32_t)as[ar * nb + e / 16 + 1] << 8)) : 0u;
-      gsb[i] = eb ? ((uint32_t)bs[br * nb + e / 16] | ((uint32_t)bs[br * nb + e / 16 + 1] << 8)) : 0u;
-    }
+    const bool ea = ar < M && e < T, eb = br < N && e < T;
+    ga = ea ? *(const uint4 *)(ac + ar * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
+    gb = eb ? *(const uint4 *)(bc + br * (T / 2) + e / 2) : uint4{0u, 0u, 0u, 0u};
+    gsa = ea ? ((uint32_t)as[ar * nb + e / 16] | ((uint32_t)as[ar * nb + e / 16 + 1] << 8)) : 0u;
+    gsb = eb ? ((uint32_t)bs[br * nb + e / 16] | ((uint32_t)bs[br * nb + e / 16 + 1] << 8)) : 0u;
   };
   auto store_stage = [&](int buf) {
     uint8_t *A_ = smem + buf * NV_STAGE_BYTES, *B_ = A_ + BM * NV_ROWB;
+    const uint32_t wa[4] = {ga.x, ga.y, ga.z, ga.w};
+    const uint32_t wb[4] = {gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rr = (t >> 1) + 128 * i;
-      const uint32_t wa[4] = {ga[i].x, ga[i].y, ga[i].z, ga[i].w};
-      const uint32_t wb[4] = {gb[i].x, gb[i].y, gb[i].z, gb[i].w};
+    for (int w = 0; w < 4; ++w) {
+      // word w holds elements 8w .. 8w+7 of this half; blocks of 16
+      const float sa = e4m3_value((gsa >> (8 * (w >> 1))) & 0xFFu);
+      const float sb = e4m3_value((gsb >> (8 * (w >> 1))) & 0xFFu);
+      ushortx8 da, db;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // word w holds elements 8w .. 8w+7 of this half; blocks of 16
-        const float sa = e4m3_value((gsa[i] >> (8 * (w >> 1))) & 0xFFu);
-        const float sb = e4m3_value((gsb[i] >> (8 * (w >> 1))) & 0xFFu);
-        ushortx8 da, db;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          da[e] = (unsigned short)(__float_as_uint(e2m1_value((wa[w] >> (4 * e)) & 15u) * sa) >> 16);
-          db[e] = (unsigned short)(__float_as_uint(e2m1_value((wb[w] >> (4 * e)) & 15u) * sb) >> 16);
-        }
-        *(ushortx8 *)(A_ + rr * NV_ROWB + (half * 32 + w * 8) * 2) = da;
-        *(ushortx8 *)(B_ + rr * NV_ROWB + (half * 32 + w * 8) * 2) = db;
+      for (int e = 0; e < 8; ++e) {
+        da[e] = (unsigned short)(__float_as_uint(e2m1_value((wa[w] >> (4 * e)) & 15u) * sa) >> 16);
+        db[e] = (unsigned short)(__float_as_uint(e2m1_value((wb[w] >> (4 * e)) & 15u) * sb) >> 16);
       }
+      *(ushortx8 *)(A_ + rr * NV_ROWB + (half * 32 + w * 8) * 2) = da;
+      *(ushortx8 *)(B_ + rr * NV_ROWB + (half * 32 + w * 8) * 2) = db;
     }
   };
   load_stage(0);
@@ -588,17 +601,17 @@ __global__ void __launch_bounds__(256, 1)
     const uint8_t *A_ = smem + cur * NV_STAGE_BYTES, *B_ = A_ + BM * NV_ROWB;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      ushortx8 a8[4], b8[4];
+      ushortx8 a8[WM], b8[WN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WM; ++i)
         a8[i] = *(const ushortx8 *)(A_ + (wm * 128 + i * 32 + r32) * NV_ROWB + ks * 32 + h * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b8[j] = *(const ushortx8 *)(B_ + (wn * 128 + j * 32 + r32) * NV_ROWB + ks * 32 + h * 16);
+      for (int j = 0; j < WN; ++j)
+        b8[j] = *(const ushortx8 *)(B_ + (wn * 64 + j * 32 + r32) * NV_ROWB + ks * 32 + h * 16);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
+        for (int j = 0; j < WN; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
     }
     if (st + 1 < nst) store_stage(cur ^ 1);
     __syncthreads();
@@ -699,10 +712,10 @@ metis_status_t gemm_main(const Side &a, const Side &b, float *C, int64_t ldc, co
   }
   const unsigned tiles = (unsigned)(cdiv(a.rows, BM) * cdiv(b.rows, BN));
   if (a.R->fmt == METIS_NVFP4)
-    gemm_nv_kernel<<<tiles, 256, 0, st>>>(a.R->codes, a.R->scales, a.R->tensor_scale, a.rows, b.R->codes,
+    gemm_nv_kernel<<<tiles, kGemmThreads, 0, st>>>(a.R->codes, a.R->scales, a.R->tensor_scale, a.rows, b.R->codes,
                                           b.R->scales, b.R->tensor_scale, b.rows, a.T, l1, l2, rp, C, ldc);
   else
-    gemm_mx_kernel<<<tiles, 256, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows, a.T, l1,
+    gemm_mx_kernel<<<tiles, kGemmThreads, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows, a.T, l1,
                                           l2, rp, C, ldc);
   METIS_LAUNCH_CHECK();
   return METIS_OK;

@@ -34,6 +34,11 @@ namespace {
 
 constexpr int kLpMax = 96;  // Gaussian / sampled sketch width handled in LDS
 constexpr int kThreads = 256;
+// assemble kernels: 16 rows per thread, at most 8 row groups (128 rows) per workgroup
+constexpr int kAsmRows = 16;
+constexpr int kAsmGroups = 8;
+__host__ __device__ __forceinline__ int asm_groups(int k) { return kThreads / k < kAsmGroups ? kThreads / k : kAsmGroups; }
+__host__ __device__ __forceinline__ int asm_chunk_rows(int k) { return kAsmRows * asm_groups(k); }
 
 // ===================================================================== plan
 struct SplitPlan {
@@ -114,7 +119,7 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
   p.pk = (int)cdiv(m, p.pk_rows);
   p.gb_rows = pick_rows_per_part(n, gram_parts, 32);
   p.gb_parts = (int)cdiv(n, p.gb_rows);
-  p.am_rows = 256;
+  p.am_rows = p.wide ? 256 : asm_chunk_rows(k);  // assemble_u's chunk (16 rows per thread)
   p.am_parts = (int)cdiv(m, p.am_rows);
 
   metis_host::Carver c(ws);
@@ -276,6 +281,21 @@ __global__ void gather_kernel(const T *__restrict__ A, int64_t m, int64_t n, int
 }
 
 
+// sum of `parts` values spaced `stride` apart, in a fixed order (four
+// interleaved partial sums so the loads issue together)
+__device__ __forceinline__ float sum_parts(const float *p, int parts, int64_t stride) {
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  int q = 0;
+  for (; q + 4 <= parts; q += 4) {
+    s0 += p[q * stride];
+    s1 += p[(q + 1) * stride];
+    s2 += p[(q + 2) * stride];
+    s3 += p[(q + 3) * stride];
+  }
+  for (; q < parts; ++q) s0 += p[q * stride];
+  return (s0 + s1) + (s2 + s3);
+}
+
 // ==================================================================== gram
 // One chunk of rows of a tall matrix X (rows x l, fp32):
 //   rinv == nullptr: X = sum of `parts` slabs of xin (fixed order);
@@ -313,10 +333,7 @@ __global__ void __launch_bounds__(kThreads)
       const int rr = idx / lp, c = idx - rr * lp;
       const int64_t row = r0 + rr;
       float v = 0.0f;
-      if (row < r_end && c < l) {
-        const float *p = xin + row * l + c;
-        for (int q = 0; q < parts; ++q) v += p[q * part_stride];
-      }
+      if (row < r_end && c < l) v = sum_parts(xin + row * l + c, parts, part_stride);
       if (rinv)
         xa[rr][c] = v;
       else
@@ -383,13 +400,22 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// G = sum over parts of gpart (fixed order).
+// G = sum over parts of gpart (fixed order: four interleaved partial sums,
+// so the loads of a group are independent and issue together).
 __global__ void gram_reduce_kernel(const double *__restrict__ gpart, int parts, int lp2, double *__restrict__ g) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= lp2) return;
-  double s = 0.0;
-  for (int p = 0; p < parts; ++p) s += gpart[(int64_t)p * lp2 + e];
-  g[e] = s;
+  const double *p = gpart + e;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  int q = 0;
+  for (; q + 4 <= parts; q += 4) {
+    s0 += p[(int64_t)q * lp2];
+    s1 += p[(int64_t)(q + 1) * lp2];
+    s2 += p[(int64_t)(q + 2) * lp2];
+    s3 += p[(int64_t)(q + 3) * lp2];
+  }
+  for (; q < parts; ++q) s0 += p[(int64_t)q * lp2];
+  g[e] = (s0 + s1) + (s2 + s3);
 }
 
 // ========================================================= Cholesky + inverse
@@ -465,15 +491,136 @@ __global__ void __launch_bounds__(kThreads)
   if (t == 0 && info) *info = first_dead;
 }
 
+// The same factorization for l <= kLpMax as one elimination on [G | I]:
+// step j subtracts m_p = G'[j][p] / d_j times row j from every later row p,
+// on the upper part of the trailing matrix G' and on the lower-triangular
+// block that starts as I. After the last step the pivots d_j are those of
+// G = L D L^T and the block holds L^-1, so R = D^1/2 L^T and
+// R^-1 = L^-T D^-1/2. Each thread keeps its matrix elements in registers;
+// a row is written to LDS once it is final (after the step before it is
+// used), so one barrier per step suffices. Absent pivots (d_j <= tol) get
+// m_p = 0 and a zero row and column of R^-1, as above.
+// Combined layout of row p: columns x >= p hold G'[p][x], columns x < p hold
+// L^-1[p][x] (its unit diagonal is implicit).
+// FACTOR = true factors G + delta I instead, delta = 4 l eps max(diag G), and
+// writes the Cholesky factor L = R^T column by column (column j of L = row j
+// of R, lp x lp, zero padded) for the one-sided Jacobi below; the shift keeps
+// every column of L nonzero, so every eigenvector comes out of the rotations.
+// shift[0] = delta.
+constexpr int kCholThreads = 1024;
+constexpr int kCholSlots = kLpMax * kLpMax / kCholThreads;  // 9 elements per thread at lp = 96
+
+__device__ __forceinline__ double recip_f64(double d) {
+  double r = __builtin_amdgcn_rcp(d);  // hardware estimate, refined by Newton steps
+  r = fma(r, fma(-d, r, 1.0), r);
+  return fma(r, fma(-d, r, 1.0), r);
+}
+
+template <bool FACTOR>
+__global__ void __launch_bounds__(kCholThreads)
+    chol_small_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ out, int *info,
+                      double *__restrict__ shift) {
+  __shared__ double C[kLpMax][kLpMax + 1];
+  __shared__ double ipiv[kLpMax];  // 1 / d_j, 0 for an absent pivot
+  __shared__ double rs[kLpMax];    // d_j^-1/2, 0 for an absent pivot
+  __shared__ int dead[kLpMax];
+  __shared__ double tol_s;
+  const int t = threadIdx.x;
+  for (int e = t; e < l * l; e += kCholThreads) {
+    const int p = e / l, x = e - (e / l) * l;
+    C[p][x] = x >= p ? g[p * lp + x] : 0.0;
+  }
+  __syncthreads();
+  if (t < 64) {
+    double md = 0.0;
+    for (int i = t; i < l; i += 64) md = fmax(md, C[i][i]);
+    md = wave_max(md);
+    if (t == 0) {
+      const double tol = (double)l * 2.220446049250313e-16 * md;
+      tol_s = tol;
+      if (FACTOR) shift[0] = 4.0 * tol;
+    }
+  }
+  __syncthreads();
+  if (FACTOR)
+    for (int i = t; i < l; i += kCholThreads) C[i][i] += 4.0 * tol_s;
+  __syncthreads();
+  if (t == 0) {
+    const double d = C[0][0];
+    const bool alive = d > tol_s;
+    ipiv[0] = alive ? recip_f64(d) : 0.0;
+    rs[0] = alive ? 1.0 / sqrt(d) : 0.0;
+    dead[0] = !alive;
+  }
+  // owned elements: e = t + s * threads, row p = e / l, column x = e % l
+  double v[kCholSlots];
+  int pr[kCholSlots], xc[kCholSlots];
+#pragma unroll
+  for (int s = 0; s < kCholSlots; ++s) {
+    const int e = t + s * kCholThreads;
+    const bool ok = e < l * l;
+    pr[s] = ok ? e / l : -1;
+    xc[s] = ok ? e - (e / l) * l : 0;
+  }
+  __syncthreads();
+  const double tol = tol_s;
+#pragma unroll
+  for (int s = 0; s < kCholSlots; ++s) v[s] = pr[s] >= 0 ? C[pr[s]][xc[s]] : 0.0;
+  for (int j = 0; j + 1 < l; ++j) {
+    const double ij = ipiv[j];
+#pragma unroll
+    for (int s = 0; s < kCholSlots; ++s) {
+      const int p = pr[s], x = xc[s];
+      if (p > j && ((!FACTOR && x <= j) || x >= p)) {
+        const double w = x == j ? 1.0 : C[j][x];
+        v[s] = fma(-(C[j][p] * ij), w, v[s]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kCholSlots; ++s) {
+      if (pr[s] == j + 1) {
+        C[j + 1][xc[s]] = v[s];
+        if (xc[s] == j + 1) {
+          const double d = v[s];
+          const bool alive = d > tol;
+          ipiv[j + 1] = alive ? recip_f64(d) : 0.0;
+          rs[j + 1] = alive ? 1.0 / sqrt(d) : 0.0;
+          dead[j + 1] = !alive;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (FACTOR) {
+    // column j of L = row j of R: R[j][x] = G'[j][x] * d_j^-1/2 for x >= j
+    for (int e = t; e < lp * lp; e += kCholThreads) {
+      const int j = e / lp, x = e - (e / lp) * lp;
+      out[e] = (j < l && x < l && x >= j) ? C[j][x] * rs[j] : 0.0;
+    }
+  } else {
+    // R^-1[i][c] = L^-1[c][i] * d_c^-1/2 for i <= c < l; zero elsewhere
+    for (int e = t; e < lp * lp; e += kCholThreads) {
+      const int i = e / lp, c = e - (e / lp) * lp;
+      double r = 0.0;
+      if (c < l && i <= c) r = (i == c ? 1.0 : C[c][i]) * rs[c];
+      out[e] = r;
+    }
+  }
+  if (t == 0 && info) {
+    int first = 0;
+    for (int j = l - 1; j >= 0; --j)
+      if (dead[j]) first = j + 1;
+    *info = first;
+  }
+}
+
 // ----------------------------------------------- wide-sketch helpers (l > 96)
 // x = sum over parts (fixed order); rows x l elements.
 __global__ void sum_parts_kernel(const float *__restrict__ parts, int n_parts, int64_t stride, int64_t count,
                                  float *__restrict__ x) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= count) return;
-  float v = 0.0f;
-  for (int p = 0; p < n_parts; ++p) v += parts[p * stride + i];
-  x[i] = v;
+  x[i] = sum_parts(parts + i, n_parts, stride);
 }
 
 // Partial Gram tile over one chunk of rows: gpart[chunk] (lp x lp) rows
@@ -847,46 +994,219 @@ __global__ void __launch_bounds__(kJacThreads)
 #undef V
 }
 
+// One-sided (Hestenes) Jacobi on the columns of the Cholesky factor L of
+// G + delta I (l <= kLpMax). Rotating pairs of columns until all are mutually
+// orthogonal gives L J = U diag(sigma'); then G + delta I = U diag(sigma'^2) U^T,
+// so the normalized columns are the eigenvectors of G and sigma'^2 - delta its
+// eigenvalues (= the squared singular values of B). No rotation is
+// accumulated. Pairs follow the round-robin schedule (position 0 fixed, the
+// others rotate one place per round, position i meets position lp - 1 - i);
+// each pair is handled by 8 lanes that form the three dot products with
+// cross-lane (DPP) sums, so every lane of the group computes the same
+// rotation. One barrier per round; columns live in LDS.
+// LDS layout: lane j of a group owns rows j E .. j E + E - 1 (E = lp / 8) of
+// both columns and reads them as 16-byte pairs. Its chunk starts E2 doubles
+// after lane j - 1's, E2 = E rounded up to 2 mod 4, so the 8 lanes of a group
+// touch 32 distinct banks; the column stride 8 E2 is 16 mod 32 doubles, which
+// puts the chunks of columns of different parity on the other 32 banks.
+constexpr int kOsThreads = 384;           // 8 lanes per column pair, up to 48 pairs
+
+__host__ __device__ constexpr int os_e2(int e) { return (e % 4 == 2) ? e : e + 2; }
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __double2loint(v), hi = __double2hiint(v);
+  return __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false),
+                          __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false));
+}
+
+// Sum over an aligned group of 8 lanes; every lane gets the bitwise same sum.
+__device__ __forceinline__ double group8_sum(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror: lane i with lane 7 - i
+  return v;
+}
+
+// E = lp / 8 is a template parameter so that a round is straight-line code;
+// all rotated values are formed before the first store, so the stores issue
+// back to back instead of each waiting for the previous one's data registers.
+template <int E>
+__global__ void __launch_bounds__(kOsThreads)
+    jacobi_os_kernel(const double *__restrict__ lcol, const double *__restrict__ shift, int l, int k, int max_sweeps,
+                     double *__restrict__ evec, double *__restrict__ sig_inv, float *__restrict__ S) {
+  constexpr int E2 = os_e2(E), CS = 8 * E2, N = 8 * E, H = 4 * E, lp = N, EH = E / 2;
+  __shared__ __align__(16) double X[N * CS];
+  __shared__ double lam[N];
+  __shared__ int rank_s[N];
+  __shared__ int rotated;
+  const int t = threadIdx.x, grp = t >> 3, j = t & 7;
+  for (int i = t; i < lp * lp; i += kOsThreads) {
+    const int c = i / lp, r = i - (i / lp) * lp;
+    X[c * CS + (r / E) * E2 + r % E] = lcol[i];
+  }
+  const double delta = shift[0];
+  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+    if (t == 0) rotated = 0;
+    __syncthreads();
+    for (int round = 0; round < N - 1; ++round) {
+      if (grp < H) {
+        int a = grp - 1 + round, b = N - 2 - grp + round;  // position - 1 + round
+        a = a >= N - 1 ? a - (N - 1) : a;
+        b = b >= N - 1 ? b - (N - 1) : b;
+        a = grp == 0 ? 0 : a + 1;
+        b = b + 1;
+        double2 *xpp = (double2 *)(X + (a < b ? a : b) * CS + j * E2);
+        double2 *xqp = (double2 *)(X + (a < b ? b : a) * CS + j * E2);
+        double2 xp[EH], xq[EH];
+#pragma unroll
+        for (int e = 0; e < EH; ++e) {
+          xp[e] = xpp[e];
+          xq[e] = xqp[e];
+        }
+        double al0 = 0.0, al1 = 0.0, be0 = 0.0, be1 = 0.0, ga0 = 0.0, ga1 = 0.0;
+#pragma unroll
+        for (int e = 0; e < EH; ++e) {
+          al0 = fma(xp[e].x, xp[e].x, al0);
+          al1 = fma(xp[e].y, xp[e].y, al1);
+          be0 = fma(xq[e].x, xq[e].x, be0);
+          be1 = fma(xq[e].y, xq[e].y, be1);
+          ga0 = fma(xp[e].x, xq[e].x, ga0);
+          ga1 = fma(xp[e].y, xq[e].y, ga1);
+        }
+        const double al = group8_sum(al0 + al1), be = group8_sum(be0 + be1), ga = group8_sum(ga0 + ga1);
+        if (ga != 0.0 && ga * ga > 1e-26 * al * be) {
+          // angle from hardware estimates (fp32-level accuracy is ample: a
+          // pair left slightly non-orthogonal is rotated again next sweep);
+          // c and s normalized to fp64 by Newton steps on 1 / sqrt(1 + t^2)
+          const float zeta = (float)((be - al) * (0.5 * __builtin_amdgcn_rcp(ga)));
+          const float az = fabsf(zeta);
+          float tf = az > 1e18f ? 0.5f / az
+                                : __builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.0f)));
+          tf = zeta >= 0.0f ? tf : -tf;
+          const double tt = (double)tf, x = fma(tt, tt, 1.0);
+          double c = __builtin_amdgcn_rsq(x);
+          c = fma(0.5 * c, fma(-x * c, c, 1.0), c);
+          c = fma(0.5 * c, fma(-x * c, c, 1.0), c);
+          const double sn = c * tt;
+          double2 np[EH], nq[EH];
+#pragma unroll
+          for (int e = 0; e < EH; ++e) {
+            np[e] = make_double2(c * xp[e].x - sn * xq[e].x, c * xp[e].y - sn * xq[e].y);
+            nq[e] = make_double2(sn * xp[e].x + c * xq[e].x, sn * xp[e].y + c * xq[e].y);
+          }
+#pragma unroll
+          for (int e = 0; e < EH; ++e) {
+            xpp[e] = np[e];
+            xqp[e] = nq[e];
+          }
+          if (j == 0) rotated = 1;
+        }
+      }
+      __syncthreads();
+    }
+    if (!rotated) break;
+    __syncthreads();
+  }
+  // squared column norms sigma'^2
+  for (int c = grp; c < N; c += kOsThreads / 8) {
+    double s2 = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) s2 = fma(X[c * CS + j * E2 + e], X[c * CS + j * E2 + e], s2);
+    s2 = group8_sum(s2);
+    if (j == 0) lam[c] = s2;
+  }
+  __syncthreads();
+  if (t < N) {
+    int r = 0;
+    if (t < l) {
+      const double d = lam[t];
+      for (int q = 0; q < l; ++q) {
+        const double e = lam[q];
+        r += (e > d) || (e == d && q < t);
+      }
+    } else {
+      r = t;
+    }
+    rank_s[t] = r;
+  }
+  __syncthreads();
+  for (int idx = t; idx < N * N; idx += kOsThreads) {
+    const int row = idx / N, col = idx - (idx / N) * N;
+    const double nrm2 = lam[col];
+    const double v = X[col * CS + (row / E) * E2 + row % E];
+    evec[row * N + rank_s[col]] = (col < l && nrm2 > 0.0) ? v / sqrt(nrm2) : 0.0;
+  }
+  if (t < N) {
+    double smax = 0.0;
+    for (int q = 0; q < l; ++q) smax = fmax(smax, sqrt(fmax(lam[q] - delta, 0.0)));
+    double sg = t < l ? sqrt(fmax(lam[t] - delta, 0.0)) : 0.0;
+    if (!(sg > smax * 5.9604644775390625e-08)) sg = 0.0;
+    const int r = rank_s[t];
+    sig_inv[r] = sg > 0.0 ? 1.0 / sg : 0.0;
+    if (r < k) S[r] = (float)sg;
+  }
+}
+
+void launch_jacobi_os(const double *lcol, const double *shift, int l, int lp, int k, int max_sweeps, double *evec,
+                      double *sig_inv, float *S, hipStream_t st) {
+  switch (lp / 8) {
+    case 2: jacobi_os_kernel<2><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
+    case 4: jacobi_os_kernel<4><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
+    case 6: jacobi_os_kernel<6><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
+    case 8: jacobi_os_kernel<8><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
+    case 10: jacobi_os_kernel<10><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
+    default: jacobi_os_kernel<12><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
+  }
+}
+
 // ================================================================ assemble
-// U[r][c] = sum_t Q[r][t] E[t][c] (fp64 accumulate) for the chunk's rows, and
-// the chunk's argmax of |U[:, c]| (lowest row on ties) with its signed value.
+// U[r][c] = sum_t Q[r][t] E[t][c] (fp64 accumulate) over the workgroup's
+// chunk of rows, and the chunk's argmax of |U[:, c]| (lowest row on ties)
+// with its signed value. Thread (rg, c) owns 16 consecutive rows of column c:
+// one E load feeds 16 FMAs against broadcast reads of the staged Q rows.
+
 __global__ void __launch_bounds__(kThreads)
     assemble_u_kernel(const float *__restrict__ q, int64_t m, int l, int lp, int k, const double *__restrict__ evec,
                       int64_t chunk_rows, float *__restrict__ U, float *__restrict__ am_val, int *__restrict__ am_idx) {
   __shared__ double E[kLpMax][kLpMax];
-  __shared__ float qs[64][kLpMax + 1];
-  __shared__ float bv[kThreads];
-  __shared__ float bsv[kThreads];
+  __shared__ float qs[kAsmRows * kAsmGroups][kLpMax + 1];
+  __shared__ float bv[kThreads], bsv[kThreads];
   __shared__ int bix[kThreads];
   const int t = threadIdx.x;
-  for (int i = t; i < l * k; i += kThreads) E[i / k][i % k] = evec[(i / k) * lp + i % k];
-  const int groups = kThreads / k;  // row groups per column
+  const int groups = asm_groups(k);
   const int c = t % k, rg = t / k;
   const bool active = rg < groups;
+  const int64_t r0 = blockIdx.x * chunk_rows;
+  const int nrows = (int)std::min<int64_t>(chunk_rows, m - r0);
+  for (int i = t; i < l * k; i += kThreads) E[i / k][i % k] = evec[(i / k) * lp + i % k];
+  for (int idx = t; idx < nrows * l; idx += kThreads) {
+    const int rr = idx / l, cc = idx % l;
+    qs[rr][cc] = q[(r0 + rr) * l + cc];
+  }
+  __syncthreads();
   float best_abs = -1.0f, best_val = 0.0f;
   int best_idx = 0x7FFFFFFF;
-  const int64_t r_beg = blockIdx.x * chunk_rows;
-  const int64_t r_end = std::min<int64_t>(m, r_beg + chunk_rows);
-  for (int64_t r0 = r_beg; r0 < r_end; r0 += 64) {
-    __syncthreads();
-    for (int idx = t; idx < 64 * l; idx += kThreads) {
-      const int rr = idx / l, cc = idx % l;
-      qs[rr][cc] = (r0 + rr < r_end) ? q[(r0 + rr) * l + cc] : 0.0f;
+  if (active) {
+    double acc[kAsmRows];
+#pragma unroll
+    for (int r = 0; r < kAsmRows; ++r) acc[r] = 0.0;
+    const int rbase = rg * kAsmRows;
+    for (int q2 = 0; q2 < l; ++q2) {
+      const double e = E[q2][c];
+#pragma unroll
+      for (int r = 0; r < kAsmRows; ++r) acc[r] += (double)qs[rbase + r][q2] * e;
     }
-    __syncthreads();
-    if (active) {
-      for (int rr = rg; rr < 64; rr += groups) {
-        const int64_t row = r0 + rr;
-        if (row >= r_end) break;
-        double s = 0.0;
-        for (int q2 = 0; q2 < l; ++q2) s += (double)qs[rr][q2] * E[q2][c];
-        const float u = (float)s;
-        U[row * k + c] = u;
-        const float au = fabsf(u);
-        if (au > best_abs) {
-          best_abs = au;
+#pragma unroll
+    for (int r = 0; r < kAsmRows; ++r) {
+      const int rr = rbase + r;
+      if (rr < nrows) {
+        const float u = (float)acc[r];
+        U[(r0 + rr) * k + c] = u;
+        if (fabsf(u) > best_abs) {
+          best_abs = fabsf(u);
           best_val = u;
-          best_idx = (int)row;
+          best_idx = (int)(r0 + rr);
         }
       }
     }
@@ -911,27 +1231,38 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// V[j][c] = (sum_t B^T[j][t] E[t][c]) / sigma_c   (0 for dropped sigma)
+// V[j][c] = (sum_t B^T[j][t] E[t][c]) / sigma_c   (0 for dropped sigma), with
+// the same 16-rows-per-thread blocking.
 __global__ void __launch_bounds__(kThreads)
     assemble_v_kernel(const float *__restrict__ bt, int64_t n, int l, int lp, int k, const double *__restrict__ evec,
                       const double *__restrict__ sig_inv, float *__restrict__ V) {
   __shared__ double E[kLpMax][kLpMax];
-  __shared__ float bs[64][kLpMax + 1];
+  __shared__ float bs[kAsmRows * kAsmGroups][kLpMax + 1];
   const int t = threadIdx.x;
+  const int groups = asm_groups(k);
+  const int c = t % k, rg = t / k;
+  const int64_t chunk_rows = asm_chunk_rows(k);
+  const int64_t r0 = blockIdx.x * chunk_rows;
+  const int nrows = (int)std::min<int64_t>(chunk_rows, n - r0);
   for (int i = t; i < l * k; i += kThreads) E[i / k][i % k] = evec[(i / k) * lp + i % k] * sig_inv[i % k];
-  const int64_t r0 = blockIdx.x * 64;
-  for (int idx = t; idx < 64 * l; idx += kThreads) {
+  for (int idx = t; idx < nrows * l; idx += kThreads) {
     const int rr = idx / l, cc = idx % l;
-    bs[rr][cc] = (r0 + rr < n) ? bt[(r0 + rr) * l + cc] : 0.0f;
+    bs[rr][cc] = bt[(r0 + rr) * l + cc];
   }
   __syncthreads();
-  for (int idx = t; idx < 64 * k; idx += kThreads) {
-    const int rr = idx / k, c = idx % k;
-    if (r0 + rr >= n) continue;
-    double s = 0.0;
-    for (int q = 0; q < l; ++q) s += (double)bs[rr][q] * E[q][c];
-    V[(r0 + rr) * k + c] = (float)s;
+  if (rg >= groups) return;
+  double acc[kAsmRows];
+#pragma unroll
+  for (int r = 0; r < kAsmRows; ++r) acc[r] = 0.0;
+  const int rbase = rg * kAsmRows;
+  for (int q2 = 0; q2 < l; ++q2) {
+    const double e = E[q2][c];
+#pragma unroll
+    for (int r = 0; r < kAsmRows; ++r) acc[r] += (double)bs[rbase + r][q2] * e;
   }
+#pragma unroll
+  for (int r = 0; r < kAsmRows; ++r)
+    if (rbase + r < nrows) V[(r0 + rbase + r) * k + c] = (float)acc[r];
 }
 
 // sign[c] = -1 if the largest-|U[:, c]| entry (lowest row on ties) is negative
@@ -1203,10 +1534,10 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
                                                  yparts > 1 ? p.y : nullptr, nullptr, p.gpart);
     const float *y = yparts > 1 ? p.y : ysrc;
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
-    chol_inv_kernel<false><<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws, p.wa, p.winv);
+    chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws, nullptr);
     gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(y, 1, 0, m, l, lp, p.gy_rows, p.rinv, p.q1, nullptr, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
-    chol_inv_kernel<false><<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, p.wa, p.winv);
+    chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
     gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(p.q1, 1, 0, m, l, lp, p.gy_rows, p.rinv, p.q, p.qt, nullptr);
     // ---- pass 2: projection B^T = A^T Q, then the Gram B B^T
     project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
@@ -1215,10 +1546,12 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
                                                  p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
     // ---- small SVD and factors
-    jacobi_kernel<false><<<1, kJacThreads, 0, st>>>(p.gram, l, lp, k, 40, p.evec, p.sig_inv, out->S, p.wg, p.wv);
+    chol_small_kernel<true><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.wg, nullptr, p.wv);
+    launch_jacobi_os(p.wg, p.wv, l, lp, k, 40, p.evec, p.sig_inv, out->S, st);
     assemble_u_kernel<<<p.am_parts, kThreads, 0, st>>>(p.q, m, l, lp, k, p.evec, p.am_rows, out->U, p.am_val,
                                                        p.am_idx);
-    assemble_v_kernel<<<(unsigned)cdiv(n, 64), kThreads, 0, st>>>(p.bt, n, l, lp, k, p.evec, p.sig_inv, out->V);
+    assemble_v_kernel<<<(unsigned)cdiv(n, asm_chunk_rows(k)), kThreads, 0, st>>>(p.bt, n, l, lp, k, p.evec,
+                                                                                 p.sig_inv, out->V);
   } else {
     // ---- the same steps with the l x l matrices in global scratch
     const float *y = ysrc;
