@@ -34,6 +34,8 @@ namespace {
 
 constexpr int kLpMax = 96;  // Gaussian / sampled sketch width handled in LDS
 constexpr int kThreads = 256;
+constexpr int kGramRows = 128;     // rows per Gram chunk (narrow path)
+constexpr int kGramThreads = 512;  // 8 waves, 16 rows each
 // assemble kernels: 16 rows per thread, at most 8 row groups (128 rows) per workgroup
 constexpr int kAsmRows = 16;
 constexpr int kAsmGroups = 8;
@@ -109,15 +111,15 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
     p.sk = 1;
     p.sk_chunk = n;
   }
-  const int64_t gram_parts = p.wide ? 16 : 128;  // wide Grams are lp x lp each
-  p.gy_rows = pick_rows_per_part(m, gram_parts, 32);
+  // narrow Grams: one partial per 128-row chunk; wide Grams: 16 row ranges
+  p.gy_rows = p.wide ? pick_rows_per_part(m, 16, 32) : kGramRows;
   p.gy_parts = (int)cdiv(m, p.gy_rows);
   const int64_t n_tiles = cdiv(n, 128);
   int64_t wantp = std::min<int64_t>(cdiv(768, n_tiles), std::max<int64_t>(1, m * elem / (20 * l)));
   wantp = std::max<int64_t>(1, std::min<int64_t>(wantp, m / 32));
   p.pk_rows = round_up(cdiv(m, wantp), 32);
   p.pk = (int)cdiv(m, p.pk_rows);
-  p.gb_rows = pick_rows_per_part(n, gram_parts, 32);
+  p.gb_rows = p.wide ? pick_rows_per_part(n, 16, 32) : kGramRows;
   p.gb_parts = (int)cdiv(n, p.gb_rows);
   p.am_rows = p.wide ? 256 : asm_chunk_rows(k);  // assemble_u's chunk (16 rows per thread)
   p.am_parts = (int)cdiv(m, p.am_rows);
@@ -297,125 +299,133 @@ __device__ __forceinline__ float sum_parts(const float *p, int parts, int64_t st
 }
 
 // ==================================================================== gram
-// One chunk of rows of a tall matrix X (rows x l, fp32):
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __double2loint(v), hi = __double2hiint(v);
+  return __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false),
+                          __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false));
+}
+
+// Sum over an aligned group of 8 lanes; every lane gets the bitwise same sum.
+__device__ __forceinline__ double group8_sum(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror: lane i with lane 7 - i
+  return v;
+}
+
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+// fp64 MFMA 16x16x4: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16];
+// acc[i] holds C[l / 16 + 4 i][l % 16].
+__device__ __forceinline__ doublex4 mfma16_f64(double a, double b, doublex4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// One 128-row chunk of a tall matrix X (rows x l, fp32, lp = l rounded up to 16):
 //   rinv == nullptr: X = sum of `parts` slabs of xin (fixed order);
-//   rinv != nullptr: X = xin R^-1 in fp64, rounded to fp32 (R^-1 upper
-//                    triangular, lp x lp);
+//   rinv != nullptr: X = xin R^-1 with fp64 products and sums (fp64 MFMA),
+//                    rounded to fp32 (R^-1 upper triangular, lp x lp).
 // X goes to xout (if given), to xt as bf16 hi/lo transposed (2 x lp x rows,
-// if given), and the fp64 Gram X^T X of the chunk to gpart[chunk] (lp x lp,
-// if given). Thread t owns the RB x RB block (t/16, t%16) of the Gram,
-// RB = lp/16, and accumulates it over the chunk's rows.
-constexpr int kSub = 32;
+// if given), and the fp64 Gram X^T X of the chunk (upper 16 x 16 tiles) to
+// gpart[chunk] (lp x lp, if given). Eight waves; the chunk sits in LDS. Wave
+// w applies R^-1 to rows 16 w .. 16 w + 15 in place, column tile by column
+// tile from the last (tile J reads only columns below 16 (J + 1)); then each
+// wave accumulates Gram tiles over the chunk's rows, 4 rows per MFMA.
 
-__global__ void __launch_bounds__(kThreads)
+__host__ __device__ constexpr int gram_ys_stride(int lp) { return lp + 4; }                  // (lp + 4) / 4 odd
+__host__ __device__ constexpr int gram_rl_stride(int lp) { return lp % 32 == 16 ? lp : lp + 16; }  // 16 mod 32
+
+__global__ void __launch_bounds__(kGramThreads)
     gram_kernel(const float *__restrict__ xin, int parts, int64_t part_stride, int64_t rows, int l, int lp,
-                int64_t rows_per_chunk, const double *__restrict__ rinv, float *__restrict__ xout,
-                unsigned short *__restrict__ xt, double *__restrict__ gpart) {
-  __shared__ float xs[kSub][kLpMax + 1];
-  __shared__ float xa[kSub][kLpMax + 1];
-  __shared__ double rl[kLpMax * kLpMax];
-  const int t = threadIdx.x;
-  const int64_t r_beg = blockIdx.x * rows_per_chunk;
-  const int64_t r_end = std::min<int64_t>(rows, r_beg + rows_per_chunk);
-  const int RB = lp >> 4;
-  const int bi = t >> 4, bj = t & 15;
+                const double *__restrict__ rinv, float *__restrict__ xout, unsigned short *__restrict__ xt,
+                double *__restrict__ gpart) {
+  __shared__ float Ys[kGramRows * (kLpMax + 4)];
+  __shared__ double Rl[kLpMax * (kLpMax + 16)];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, lr = lane & 15, lk = lane >> 4;
+  const int S = gram_ys_stride(lp), RS = gram_rl_stride(lp), T = lp >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * kGramRows;
+  for (int idx = t; idx < kGramRows * lp; idx += kGramThreads) {
+    const int r = idx / lp, c = idx - (idx / lp) * lp;
+    const int64_t row = row0 + r;
+    Ys[r * S + c] = (row < rows && c < l) ? sum_parts(xin + row * l + c, parts, part_stride) : 0.0f;
+  }
   if (rinv)
-    for (int i = t; i < lp * lp; i += kThreads) rl[i] = rinv[i];
-  double acc[6][6];
+    for (int idx = t; idx < lp * lp; idx += kGramThreads) {
+      const int r = idx / lp, c = idx - (idx / lp) * lp;
+      Rl[r * RS + c] = rinv[idx];
+    }
+  __syncthreads();
+  if (rinv) {
+    const int rb = 16 * wave;
+    for (int J = T - 1; J >= 0; --J) {
+      doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+      for (int s4 = 0; s4 < 4 * (J + 1); ++s4) {
+        const double a = (double)Ys[(rb + lr) * S + 4 * s4 + lk];
+        const double b = Rl[(4 * s4 + lk) * RS + 16 * J + lr];
+        acc = mfma16_f64(a, b, acc);
+      }
 #pragma unroll
-  for (int a = 0; a < 6; ++a)
-#pragma unroll
-    for (int b = 0; b < 6; ++b) acc[a][b] = 0.0;
-
-  for (int64_t r0 = r_beg; r0 < r_end; r0 += kSub) {
-    __syncthreads();
-    for (int idx = t; idx < kSub * lp; idx += kThreads) {
-      const int rr = idx / lp, c = idx - rr * lp;
-      const int64_t row = r0 + rr;
-      float v = 0.0f;
-      if (row < r_end && c < l) v = sum_parts(xin + row * l + c, parts, part_stride);
-      if (rinv)
-        xa[rr][c] = v;
-      else
-        xs[rr][c] = v;
+      for (int i = 0; i < 4; ++i) Ys[(rb + lk + 4 * i) * S + 16 * J + lr] = (float)acc[i];
     }
     __syncthreads();
-    if (rinv) {
-      for (int idx = t; idx < kSub * lp; idx += kThreads) {
-        const int rr = idx / lp, c = idx - rr * lp;
-        double s = 0.0;
-        if (c < l)
-          for (int q = 0; q <= c; ++q) s += (double)xa[rr][q] * rl[q * lp + c];
-        xs[rr][c] = (float)s;
-      }
-      __syncthreads();
+  }
+  if (xout)
+    for (int idx = t; idx < kGramRows * l; idx += kGramThreads) {
+      const int r = idx / l, c = idx - (idx / l) * l;
+      if (row0 + r < rows) xout[(row0 + r) * l + c] = Ys[r * S + c];
     }
-    if (xout) {
-      for (int idx = t; idx < kSub * l; idx += kThreads) {
-        const int rr = idx / l, c = idx - rr * l;
-        if (r0 + rr < r_end) xout[(r0 + rr) * l + c] = xs[rr][c];
+  if (xt) {
+    // 8 consecutive rows of one column per thread (16-byte stores)
+    for (int idx = t; idx < lp * (kGramRows / 8); idx += kGramThreads) {
+      const int c = idx / (kGramRows / 8), q = idx - c * (kGramRows / 8);
+      if (row0 + q * 8 >= rows) continue;
+      ushortx8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        unsigned short h, w;
+        split_bf16(Ys[(q * 8 + e) * S + c], h, w);
+        hi[e] = h;
+        lo[e] = w;
       }
-    }
-    if (xt) {
-      // 8 consecutive rows of one column per thread (16-byte stores)
-      for (int idx = t; idx < lp * (kSub / 8); idx += kThreads) {
-        const int c = idx >> 2, q = idx & 3;
-        if (r0 + q * 8 >= r_end) continue;
-        ushortx8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          unsigned short h, w;
-          split_bf16(xs[q * 8 + e][c], h, w);
-          hi[e] = h;
-          lo[e] = w;
-        }
-        *(ushortx8 *)(xt + (int64_t)c * rows + r0 + q * 8) = hi;
-        *(ushortx8 *)(xt + ((int64_t)lp + c) * rows + r0 + q * 8) = lo;
-      }
-    }
-    if (gpart) {
-      const int nr = (int)std::min<int64_t>(kSub, r_end - r0);
-#pragma unroll 1
-      for (int rr = 0; rr < nr; ++rr) {
-        double xi[6], xj[6];
-#pragma unroll
-        for (int a = 0; a < 6; ++a) {
-          xi[a] = a < RB ? (double)xs[rr][bi * RB + a] : 0.0;
-          xj[a] = a < RB ? (double)xs[rr][bj * RB + a] : 0.0;
-        }
-#pragma unroll
-        for (int a = 0; a < 6; ++a)
-#pragma unroll
-          for (int b = 0; b < 6; ++b) acc[a][b] += xi[a] * xj[b];
-      }
+      *(ushortx8 *)(xt + (int64_t)c * rows + row0 + q * 8) = hi;
+      *(ushortx8 *)(xt + ((int64_t)lp + c) * rows + row0 + q * 8) = lo;
     }
   }
   if (gpart) {
     double *g = gpart + (int64_t)blockIdx.x * lp * lp;
+    const int ntiles = T * (T + 1) / 2;
+    for (int tile = wave; tile < ntiles; tile += kGramThreads / 64) {
+      int I = 0, rem = tile;  // tile -> (I, J), I <= J, row-major over the upper triangle
+      while (rem >= T - I) {
+        rem -= T - I;
+        ++I;
+      }
+      const int J = I + rem;
+      doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+      for (int r = 0; r < kGramRows; r += 4) {
+        const double a = (double)Ys[(r + lk) * S + 16 * I + lr];
+        const double b = (double)Ys[(r + lk) * S + 16 * J + lr];
+        acc = mfma16_f64(a, b, acc);
+      }
 #pragma unroll
-    for (int a = 0; a < 6; ++a)
-#pragma unroll
-      for (int b = 0; b < 6; ++b)
-        if (a < RB && b < RB) g[(bi * RB + a) * lp + bj * RB + b] = acc[a][b];
+      for (int i = 0; i < 4; ++i) g[(16 * I + lk + 4 * i) * lp + 16 * J + lr] = acc[i];
+    }
   }
 }
 
-// G = sum over parts of gpart (fixed order: four interleaved partial sums,
-// so the loads of a group are independent and issue together).
-__global__ void gram_reduce_kernel(const double *__restrict__ gpart, int parts, int lp2, double *__restrict__ g) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= lp2) return;
-  const double *p = gpart + e;
-  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-  int q = 0;
-  for (; q + 4 <= parts; q += 4) {
-    s0 += p[(int64_t)q * lp2];
-    s1 += p[(int64_t)(q + 1) * lp2];
-    s2 += p[(int64_t)(q + 2) * lp2];
-    s3 += p[(int64_t)(q + 3) * lp2];
-  }
-  for (; q < parts; ++q) s0 += p[(int64_t)q * lp2];
-  g[e] = (s0 + s1) + (s2 + s3);
+// G = sum over parts of gpart (upper triangle is what the consumers read).
+// Eight lanes per element, lane j summing parts j, j + 8, ...; the fixed DPP
+// combine keeps the result independent of scheduling.
+__global__ void __launch_bounds__(256)
+    gram_reduce_kernel(const double *__restrict__ gpart, int parts, int lp2, double *__restrict__ g) {
+  const int e = blockIdx.x * 32 + (threadIdx.x >> 3), j = threadIdx.x & 7;
+  double s = 0.0;
+  if (e < lp2)
+    for (int q = j; q < parts; q += 8) s += gpart[(int64_t)q * lp2 + e];
+  s = group8_sum(s);
+  if (e < lp2 && j == 0) g[e] = s;
 }
 
 // ========================================================= Cholesky + inverse
@@ -1013,20 +1023,6 @@ constexpr int kOsThreads = 384;           // 8 lanes per column pair, up to 48 p
 
 __host__ __device__ constexpr int os_e2(int e) { return (e % 4 == 2) ? e : e + 2; }
 
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const int lo = __double2loint(v), hi = __double2hiint(v);
-  return __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false),
-                          __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false));
-}
-
-// Sum over an aligned group of 8 lanes; every lane gets the bitwise same sum.
-__device__ __forceinline__ double group8_sum(double v) {
-  v += dpp_f64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += dpp_f64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v += dpp_f64<0x141>(v);  // row_half_mirror: lane i with lane 7 - i
-  return v;
-}
 
 // E = lp / 8 is a template parameter so that a round is straight-line code;
 // all rotated values are formed before the first store, so the stores issue
@@ -1527,23 +1523,22 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     ysrc = p.ysk;
     yparts = 1;
   }
-  const unsigned rgrid_red = (unsigned)cdiv(lp * lp, 256);
+  const unsigned rgrid_red = (unsigned)cdiv(lp * lp, 32);  // 8 lanes per element
   if (!p.wide) {
     // ---- CholeskyQR2 (LDS-resident small matrices)
-    gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(ysrc, yparts, m * l, m, l, lp, p.gy_rows, nullptr,
-                                                 yparts > 1 ? p.y : nullptr, nullptr, p.gpart);
+    gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(ysrc, yparts, m * l, m, l, lp, nullptr,
+                                                     yparts > 1 ? p.y : nullptr, nullptr, p.gpart);
     const float *y = yparts > 1 ? p.y : ysrc;
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
     chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws, nullptr);
-    gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(y, 1, 0, m, l, lp, p.gy_rows, p.rinv, p.q1, nullptr, p.gpart);
+    gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(y, 1, 0, m, l, lp, p.rinv, p.q1, nullptr, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
     chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
-    gram_kernel<<<p.gy_parts, kThreads, 0, st>>>(p.q1, 1, 0, m, l, lp, p.gy_rows, p.rinv, p.q, p.qt, nullptr);
+    gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(p.q1, 1, 0, m, l, lp, p.rinv, p.q, p.qt, nullptr);
     // ---- pass 2: projection B^T = A^T Q, then the Gram B B^T
     project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
                                                                                  p.pk_rows, p.btp);
-    gram_kernel<<<p.gb_parts, kThreads, 0, st>>>(p.btp, p.pk, n * l, n, l, lp, p.gb_rows, nullptr, p.bt, nullptr,
-                                                 p.gpart);
+    gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.btp, p.pk, n * l, n, l, lp, nullptr, p.bt, nullptr, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
     // ---- small SVD and factors
     chol_small_kernel<true><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.wg, nullptr, p.wv);
