@@ -407,8 +407,8 @@ __device__ __forceinline__ void epilogue(floatx16 (&acc)[WM][WN], float scale, u
     }
 }
 
-// MXFP4: C = Ra Rb^T (+ L1 L2^T) on the scaled FP4 MFMA, 128 contraction
-// elements per LDS stage. Global loads run two stages ahead through registers
+// MXFP4, any K (the fallback of gemm_mx_kernel): C = Ra Rb^T (+ L1 L2^T) on
+// the scaled FP4 MFMA, 128 contraction elements per LDS stage. Global loads run two stages ahead through registers
 // (slot s % 2 holds stage s while it is in flight) and LDS is double
 // buffered, so each load has two stages of MFMA work to land; one barrier
 // per stage. Thread t stages two 16-byte pieces of A and of B per stage and
@@ -488,7 +488,7 @@ __device__ __forceinline__ void mx_compute(floatx16 (&acc)[WM][WN], const uint8_
 }
 
 __global__ void __launch_bounds__(kGemmThreads, 1)
-    gemm_mx_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
+    gemm_mx8_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
                    const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int64_t N, int64_t T,
                    const unsigned short *__restrict__ l1, const unsigned short *__restrict__ l2, int rp,
                    float *__restrict__ C, int64_t ldc) {
@@ -532,6 +532,249 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     __syncthreads();
   }
   epilogue(acc, 1.0f, smem, m0, n0, M, N, l1, l2, rp, C, ldc);
+}
+
+constexpr int kMxThreads = 256;
+constexpr int MXW = 4;  // 32 x 32 blocks per wave along each dimension
+
+
+// acc plus L1[m-tile] L2[n-tile]^T (bf16, 64 panel columns at a time through
+// LDS), stored as fp32; the 4-wave layout of gemm_mx_kernel.
+__device__ __forceinline__ void epilogue_mx4(floatx16 (&acc)[MXW][MXW], uint8_t *smem, int64_t m0, int64_t n0,
+                                             int64_t M, int64_t N, const unsigned short *__restrict__ l1,
+                                             const unsigned short *__restrict__ l2, int rp, float *__restrict__ C,
+                                             int64_t ldc) {
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (rp > 0) {
+    uint8_t *L1s = smem, *L2s = smem + BM * EPI_ROWB;
+    for (int c0 = 0; c0 < rp; c0 += 64) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = t + kMxThreads * i;  // 2048 pieces of 16 bytes per panel
+        const int rr = idx >> 3, piece = idx & 7;
+        const int64_t ar = m0 + rr, br = n0 + rr;
+        const uint4 va = ar < M ? *(const uint4 *)(l1 + ar * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
+        const uint4 vb = br < N ? *(const uint4 *)(l2 + br * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
+        *(uint4 *)(L1s + rr * EPI_ROWB + piece * 16) = va;
+        *(uint4 *)(L2s + rr * EPI_ROWB + piece * 16) = vb;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ushortx8 a8[MXW], b8[MXW];
+#pragma unroll
+        for (int i = 0; i < MXW; ++i) {
+          a8[i] = *(const ushortx8 *)(L1s + (wm * 128 + i * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
+          b8[i] = *(const ushortx8 *)(L2s + (wn * 128 + i * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < MXW; ++i)
+#pragma unroll
+          for (int j = 0; j < MXW; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MXW; ++i)
+#pragma unroll
+    for (int j = 0; j < MXW; ++j) {
+      const int64_t col = n0 + wn * 128 + j * 32 + r32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + wm * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+        if (row < M) C[row * ldc + col] = acc[i][j][q];
+      }
+    }
+}
+
+// MXFP4 main kernel (K a multiple of 128): C = Ra Rb^T (+ L1 L2^T) on the
+// scaled FP4 MFMA. Four waves, one per SIMD, each a 128 x 128 sub-tile (4 x 4
+// MFMA blocks of 32 x 32; 256 accumulators, kept in AGPRs). Operands go
+// straight from global memory to LDS (global_load_lds, 16 bytes per lane)
+// into a ring of four stages of 128 contraction elements, issued three stages
+// ahead; each wave waits on its own load counter for the stage it needs, then
+// one barrier per stage. A stage holds A and B codes (256 rows x 64 bytes,
+// 16-byte units XOR-swizzled by row so the fragment reads are conflict free:
+// unit u of row r sits at r * 4 + (u ^ ((r / 4) & 3))) and the scale words of
+// the stage (one per row and operand). The LDS reads of the ring are done in
+// asm blocks that wait for their own data, so the compiler never has to order
+// them against the asynchronous loads; their outputs are early-clobber, so no
+// output register doubles as an address of a later read in the same block.
+constexpr int kDmaStages = 4;
+constexpr int DMA_CODE_BYTES = BM * 64;
+constexpr int DMA_STAGE = 2 * DMA_CODE_BYTES + 2 * BM * 4;
+constexpr int DMA_LDS = kDmaStages * DMA_STAGE;
+static_assert(DMA_LDS <= 160 * 1024, "LDS budget of one CU");
+static_assert(2 * BM * EPI_ROWB <= DMA_LDS, "epilogue panels must fit the main-loop LDS");
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Source of the loads for rows past M or N (the ring must still be written).
+__device__ __attribute__((aligned(16))) const uint32_t kZeroPage[4] = {0u, 0u, 0u, 0u};
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void *)p);
+}
+
+// lane i of the wave writes its bytes at lds_wave_base + i * size
+__device__ __forceinline__ void dma_load16(const void *g, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma_load4(const void *g, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)lds_wave_base, 4, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding)
+#define METIS_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+__device__ __forceinline__ intx8 fp4x32v(const u32x4 v) { return intx8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0}; }
+
+__device__ __forceinline__ floatx16 mfma_fp4_ks(const u32x4 a, const u32x4 b, int sa, int sb, floatx16 c, int ks) {
+  // the scale byte is picked by opsel = ks from a word pre-shifted per lane
+  return ks == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4x32v(a), fp4x32v(b), c, 4, 4, 0, sa, 0, sb)
+                 : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4x32v(a), fp4x32v(b), c, 4, 4, 1, sa, 1, sb);
+}
+
+__global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+    gemm_mx_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
+                   const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int64_t N, int64_t T,
+                   const unsigned short *__restrict__ l1, const unsigned short *__restrict__ l2, int rp,
+                   float *__restrict__ C, int64_t ldc) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DMA_LDS];
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_coords(tm, tn, (int)cdiv(M, BM), (int)cdiv(N, BN));
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t nb = T / 32;
+  const int nst = (int)(T / 128);
+
+  // per-lane load sources: code unit of row r = q / 4 of this wave's blocks,
+  // and the scale word of row 64 wave + lane; rows past the end read zeros
+  const uint8_t *srcA[4], *srcB[4];
+  int strideA[4], strideB[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
+    const bool okA = m0 + r < M, okB = n0 + r < N;
+    srcA[i] = okA ? ac + (m0 + r) * (T / 2) + u * 16 : (const uint8_t *)kZeroPage;
+    srcB[i] = okB ? bc + (n0 + r) * (T / 2) + u * 16 : (const uint8_t *)kZeroPage;
+    strideA[i] = okA ? 64 : 0;
+    strideB[i] = okB ? 64 : 0;
+  }
+  const int rs = 64 * wave + lane;
+  const bool okSA = m0 + rs < M, okSB = n0 + rs < N;
+  const uint8_t *srcSA = okSA ? as + (m0 + rs) * nb : (const uint8_t *)kZeroPage;
+  const uint8_t *srcSB = okSB ? bs + (n0 + rs) * nb : (const uint8_t *)kZeroPage;
+  const int strideSA = okSA ? 4 : 0, strideSB = okSB ? 4 : 0;
+
+  auto issue = [&](int st) {  // ten loads per wave
+    uint8_t *sb = smem + (st % kDmaStages) * DMA_STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dma_load16(srcA[i] + (int64_t)st * strideA[i], sb + (4 * wave + i) * 1024);
+      dma_load16(srcB[i] + (int64_t)st * strideB[i], sb + DMA_CODE_BYTES + (4 * wave + i) * 1024);
+    }
+    dma_load4(srcSA + (int64_t)st * strideSA, sb + 2 * DMA_CODE_BYTES + wave * 256);
+    dma_load4(srcSB + (int64_t)st * strideSB, sb + 2 * DMA_CODE_BYTES + BM * 4 + wave * 256);
+  };
+
+  floatx16 acc[MXW][MXW];
+#pragma unroll
+  for (int i = 0; i < MXW; ++i)
+#pragma unroll
+    for (int j = 0; j < MXW; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  const int rA0 = wm * 128 + r32, rB0 = wn * 128 + r32;
+  const int fA = (rA0 >> 2) & 3, fB = (rB0 >> 2) & 3;
+  const uint32_t smem0 = lds_offset(smem);
+  if (nst > 0) issue(0);
+  if (nst > 1) issue(1);
+  if (nst > 2) issue(2);
+  for (int st = 0; st < nst; ++st) {
+    // stage st has landed once at most the later issued stages are pending
+    const int later = min(2, nst - 1 - st);
+    if (later == 2)
+      METIS_WAIT_VMCNT(20);
+    else if (later == 1)
+      METIS_WAIT_VMCNT(10);
+    else
+      METIS_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    // every wave is past stage st - 1: its buffer takes stage st + 3
+    if (st + 3 < nst) issue(st + 3);
+    const uint32_t base = smem0 + (st % kDmaStages) * DMA_STAGE;
+    int sa[MXW], sb[MXW];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t pa = base + rA0 * 64 + (((2 * h + ks) ^ fA) << 4);
+      const uint32_t pb = base + DMA_CODE_BYTES + rB0 * 64 + (((2 * h + ks) ^ fB) << 4);
+      u32x4 a0, a1, a2, a3, b0, b1, b2, b3;
+      if (ks == 0) {
+        const uint32_t psa = base + 2 * DMA_CODE_BYTES + rA0 * 4;
+        const uint32_t psb = base + 2 * DMA_CODE_BYTES + BM * 4 + rB0 * 4;
+        asm volatile(
+            "ds_read_b128 %0, %16\n\t"
+            "ds_read_b128 %1, %16 offset:2048\n\t"
+            "ds_read_b128 %2, %16 offset:4096\n\t"
+            "ds_read_b128 %3, %16 offset:6144\n\t"
+            "ds_read_b128 %4, %17\n\t"
+            "ds_read_b128 %5, %17 offset:2048\n\t"
+            "ds_read_b128 %6, %17 offset:4096\n\t"
+            "ds_read_b128 %7, %17 offset:6144\n\t"
+            "ds_read_b32 %8, %18\n\t"
+            "ds_read_b32 %9, %18 offset:128\n\t"
+            "ds_read_b32 %10, %18 offset:256\n\t"
+            "ds_read_b32 %11, %18 offset:384\n\t"
+            "ds_read_b32 %12, %19\n\t"
+            "ds_read_b32 %13, %19 offset:128\n\t"
+            "ds_read_b32 %14, %19 offset:256\n\t"
+            "ds_read_b32 %15, %19 offset:384\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(sa[0]),
+              "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sb[0]), "=&v"(sb[1]), "=&v"(sb[2]), "=&v"(sb[3])
+            : "v"(pa), "v"(pb), "v"(psa), "v"(psb)
+            : "memory");
+#pragma unroll
+        for (int i = 0; i < MXW; ++i) {
+          sa[i] = (int)((uint32_t)sa[i] >> (16 * h));
+          sb[i] = (int)((uint32_t)sb[i] >> (16 * h));
+        }
+      } else {
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %8 offset:2048\n\t"
+            "ds_read_b128 %2, %8 offset:4096\n\t"
+            "ds_read_b128 %3, %8 offset:6144\n\t"
+            "ds_read_b128 %4, %9\n\t"
+            "ds_read_b128 %5, %9 offset:2048\n\t"
+            "ds_read_b128 %6, %9 offset:4096\n\t"
+            "ds_read_b128 %7, %9 offset:6144\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+            : "v"(pa), "v"(pb)
+            : "memory");
+      }
+      const u32x4 af[MXW] = {a0, a1, a2, a3}, bf[MXW] = {b0, b1, b2, b3};
+#pragma unroll
+      for (int i = 0; i < MXW; ++i)
+#pragma unroll
+        for (int j = 0; j < MXW; ++j) acc[i][j] = mfma_fp4_ks(af[i], bf[j], sa[i], sb[j], acc[i][j], ks);
+    }
+  }
+  __syncthreads();  // the epilogue reuses the ring
+  epilogue_mx4(acc, smem, m0, n0, M, N, l1, l2, rp, C, ldc);
 }
 
 // NVFP4: codes and E4M3 block scales are decoded exactly to bf16 while being
@@ -714,9 +957,13 @@ metis_status_t gemm_main(const Side &a, const Side &b, float *C, int64_t ldc, co
   if (a.R->fmt == METIS_NVFP4)
     gemm_nv_kernel<<<tiles, kGemmThreads, 0, st>>>(a.R->codes, a.R->scales, a.R->tensor_scale, a.rows, b.R->codes,
                                           b.R->scales, b.R->tensor_scale, b.rows, a.T, l1, l2, rp, C, ldc);
+  else if (a.T % 128 == 0 && (((uintptr_t)a.R->codes | (uintptr_t)b.R->codes) & 15) == 0 &&
+           (((uintptr_t)a.R->scales | (uintptr_t)b.R->scales) & 3) == 0)
+    gemm_mx_kernel<<<tiles, kMxThreads, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows,
+                                                 a.T, l1, l2, rp, C, ldc);
   else
-    gemm_mx_kernel<<<tiles, kGemmThreads, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows, a.T, l1,
-                                          l2, rp, C, ldc);
+    gemm_mx8_kernel<<<tiles, kGemmThreads, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales,
+                                                    b.rows, a.T, l1, l2, rp, C, ldc);
   METIS_LAUNCH_CHECK();
   return METIS_OK;
 }

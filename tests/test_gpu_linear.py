@@ -33,14 +33,22 @@ def _small(seed, rows, cols, k, l, kind="planted", dtype="bf16", fmt="mxfp4"):
     return synth.small_case(seed, rows, cols, dtype, kind, k=k, l=l, n_dir=4, fmt=fmt)
 
 
+# (288, 320, 416): contraction lengths that are not multiples of 128 and
+# output tiles that are ragged against 256 x 256; (384, 384, 640): every
+# contraction a multiple of 128 (the MXFP4 kernel with asynchronous LDS loads)
+# and still ragged output tiles.
+SHAPES = {"ragged-k": (288, 320, 416), "k128": (384, 384, 640)}
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("kx,kw,kdy", [(8, 8, 8), (0, 8, 0), (8, 0, 8), (0, 0, 0), (16, 8, 4)])
-def test_linear_fwd_bwd_small(kx, kw, kdy, fmt):
-    Mt, K, N = 288, 320, 416  # ragged against the 256 x 256 output tile
+def test_linear_fwd_bwd_small(kx, kw, kdy, fmt, shape):
+    Mt, K, N = SHAPES[shape]
     X = _small(201, Mt, K, kx, kx + 8, fmt=fmt)
     W = _small(202, N, K, kw, kw + 8, kind="powerlaw", fmt=fmt)
     dY = _small(203, Mt, N, kdy, kdy + 8, fmt=fmt)
-    print("case", kx, kw, kdy, fmt, flush=True)
+    print("case", kx, kw, kdy, fmt, shape, flush=True)
     rx, rw, rd = _operand(X, ("n", "t")), _operand(W, ("n", "t")), _operand(dY, ("n", "t"))
     Y = M.spectral_fp4_linear_fwd(rx, rw)
     dX, dW = M.spectral_fp4_linear_bwd(rd, rx, rw)
