@@ -63,6 +63,7 @@ struct GemmPlan {
   int ks_p, ks_q, ks_c;          // split-K counts of the skinny products
   int64_t tc_p, tc_q, tc_c;      // T per split (multiple of 128)
   float *ppart, *qpart, *cpart;  // partials
+  float *cross;                  // ka x kb, the summed cpart
   unsigned short *l1, *l2;       // panels
   size_t bytes;
 };
@@ -85,6 +86,7 @@ GemmPlan make_gemm_plan(int64_t ra, int64_t rb, int64_t T, int ka, int kb, void 
   p.ppart = c.take<float>((size_t)p.ks_p * ra * kb);
   p.qpart = c.take<float>((size_t)p.ks_q * rb * ka);
   p.cpart = c.take<float>((size_t)p.ks_c * ka * kb);
+  p.cross = c.take<float>((size_t)ka * kb);
   p.l1 = c.take<unsigned short>((size_t)ra * p.rp);
   p.l2 = c.take<unsigned short>((size_t)rb * p.rp);
   p.bytes = c.bytes();
@@ -236,75 +238,97 @@ __device__ __forceinline__ float factor_value(const uint8_t *codes, const uint8_
   return with_ts ? v * ts[0] : v;
 }
 
-// Rows [0, ra) build L1, rows [ra, ra + rb) build L2 (one 64-thread group per
-// row; columns strided). cross (ka x kb) is summed once per block into LDS.
-// The G columns of the panels hold e2m1 * block scale, which bf16 represents
-// exactly; for NVFP4 the G tensor scale is folded into the partner column
-// (P for Gb, Q for Ga) before its hi/lo split.
+// cross = sum of the ks split-K slabs of Fa^T Fb (fixed order).
+__global__ void cross_reduce_kernel(const float *__restrict__ cpart, int ks, int count, float *__restrict__ cross) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= count) return;
+  float v = 0.0f;
+  for (int s = 0; s < ks; ++s) v += cpart[(int64_t)s * count + e];
+  cross[e] = v;
+}
+
+// Blocks [0, ceil(ra / 32)) build 32 rows of L1 each, the following blocks 32
+// rows of L2. The factor values, P and Q of the block's rows are formed in LDS
+// first (factor codes read along the rows, partial sums along the columns),
+// then each panel row is written contiguously. The G columns of the panels
+// hold e2m1 * block scale, which bf16 represents exactly; for NVFP4 the G
+// tensor scale is folded into the partner column (P for Gb, Q for Ga) before
+// its hi/lo split.
+constexpr int kPanelRows = 32;
+
 template <bool NV>
 __global__ void __launch_bounds__(256)
     panel_kernel(int64_t ra, int64_t rb, int ka, int kb, int rp, const float *__restrict__ ppart, int ks_p,
-                 const float *__restrict__ qpart, int ks_q, const float *__restrict__ cpart, int ks_c,
+                 const float *__restrict__ qpart, int ks_q, const float *__restrict__ cross_g,
                  const float *__restrict__ Sa, const float *__restrict__ Sb, const uint8_t *__restrict__ ga_c,
                  const uint8_t *__restrict__ ga_s, const float *__restrict__ ga_t, const uint8_t *__restrict__ gb_c,
                  const uint8_t *__restrict__ gb_s, const float *__restrict__ gb_t, unsigned short *__restrict__ l1,
                  unsigned short *__restrict__ l2) {
+  constexpr int R = kPanelRows;
   __shared__ float cross[96][97];
-  __shared__ float gsb[4][96];  // Gb[j][d] * Sb[d] for the (up to) 4 L2 rows of this block
+  __shared__ float fv[R][97];  // L1: P; L2: Gb values
+  __shared__ float gv[R][97];  // L1: Ga values; L2: Gb * tensor scale * Sb
+  __shared__ float qv[R][97];  // L2: Q
   const int t = threadIdx.x;
-  const int sub = t >> 6, lane = t & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + sub;
-  const bool need_cross = ka && kb && blockIdx.x * 4 + 3 >= ra;
-  if (need_cross) {
-    for (int e = t; e < ka * kb; e += 256) {
-      float v = 0.0f;
-      for (int s = 0; s < ks_c; ++s) v += cpart[(int64_t)s * ka * kb + e];
-      cross[e / kb][e % kb] = v;
-    }
-  }
-  if (row >= ra && row < ra + rb && kb) {
-    const int64_t j = row - ra;
-    for (int d = lane; d < kb; d += 64) gsb[sub][d] = factor_value<NV>(gb_c, gb_s, gb_t, rb, d, j, true) * Sb[d];
-  }
-  __syncthreads();
+  const int64_t l1_blocks = (ra + R - 1) / R;
   const float fold_b = (NV && kb) ? gb_t[0] : 1.0f;  // Gb tensor scale, carried by P
   const float fold_a = (NV && ka) ? ga_t[0] : 1.0f;  // Ga tensor scale, carried by Q
-  if (row < ra) {
-    unsigned short *o = l1 + row * rp;
-    for (int c = lane; c < rp; c += 64) {
+  if ((int64_t)blockIdx.x < l1_blocks) {
+    const int64_t i0 = (int64_t)blockIdx.x * R;
+    const int nr = (int)min<int64_t>(R, ra - i0);
+    for (int e = t; e < nr * kb; e += 256) {
+      const int r = e / kb, d = e - (e / kb) * kb;
+      float pv = 0.0f;
+      for (int s = 0; s < ks_p; ++s) pv += ppart[((int64_t)s * ra + i0 + r) * kb + d];
+      fv[r][d] = pv * Sb[d] * fold_b;
+    }
+    for (int e = t; e < ka * nr; e += 256) {
+      const int c = e / nr, r = e - (e / nr) * nr;
+      gv[r][c] = factor_value<NV>(ga_c, ga_s, ga_t, ra, c, i0 + r, false);
+    }
+    __syncthreads();
+    for (int e = t; e < nr * rp; e += 256) {
+      const int r = e / rp, c = e - (e / rp) * rp;
       unsigned short v = 0;
       if (c < 2 * kb) {
-        const int d = c % kb;
-        float p = 0.0f;
-        for (int s = 0; s < ks_p; ++s) p += ppart[((int64_t)s * ra + row) * kb + d];
-        p = p * Sb[d] * fold_b;
         unsigned short hi, lo;
-        split_bf16(p, hi, lo);
+        split_bf16(fv[r][c % kb], hi, lo);
         v = c < kb ? hi : lo;
       } else if (c < 2 * kb + 2 * ka) {
-        const int cc = (c - 2 * kb) % ka;
-        v = f32_to_bf16(factor_value<NV>(ga_c, ga_s, ga_t, ra, cc, row, false));
+        v = f32_to_bf16(gv[r][(c - 2 * kb) % ka]);
       }
-      o[c] = v;
+      l1[(i0 + r) * rp + c] = v;
     }
-  } else if (row < ra + rb) {
-    const int64_t j = row - ra;
-    unsigned short *o = l2 + j * rp;
-    for (int c = lane; c < rp; c += 64) {
+  } else {
+    const int64_t j0 = ((int64_t)blockIdx.x - l1_blocks) * R;
+    const int nr = (int)min<int64_t>(R, rb - j0);
+    if (ka && kb)
+      for (int e = t; e < ka * kb; e += 256) cross[e / kb][e % kb] = cross_g[e];
+    for (int e = t; e < kb * nr; e += 256) {
+      const int d = e / nr, r = e - (e / nr) * nr;
+      fv[r][d] = factor_value<NV>(gb_c, gb_s, gb_t, rb, d, j0 + r, false);
+      gv[r][d] = factor_value<NV>(gb_c, gb_s, gb_t, rb, d, j0 + r, true) * Sb[d];
+    }
+    __syncthreads();
+    for (int e = t; e < nr * ka; e += 256) {
+      const int r = e / ka, cc = e - (e / ka) * ka;
+      float q = 0.0f;
+      for (int s = 0; s < ks_q; ++s) q += qpart[((int64_t)s * rb + j0 + r) * ka + cc];
+      for (int d = 0; d < kb; ++d) q += gv[r][d] * cross[cc][d];
+      qv[r][cc] = q * Sa[cc] * fold_a;
+    }
+    __syncthreads();
+    for (int e = t; e < nr * rp; e += 256) {
+      const int r = e / rp, c = e - (e / rp) * rp;
       unsigned short v = 0;
       if (c < 2 * kb) {
-        v = f32_to_bf16(factor_value<NV>(gb_c, gb_s, gb_t, rb, c % kb, j, false));
+        v = f32_to_bf16(fv[r][c % kb]);
       } else if (c < 2 * kb + 2 * ka) {
-        const int cc = (c - 2 * kb) % ka;
-        float q = 0.0f;
-        for (int s = 0; s < ks_q; ++s) q += qpart[((int64_t)s * rb + j) * ka + cc];
-        for (int d = 0; d < kb; ++d) q += gsb[sub][d] * cross[cc][d];
-        q = q * Sa[cc] * fold_a;
         unsigned short hi, lo;
-        split_bf16(q, hi, lo);
+        split_bf16(qv[r][(c - 2 * kb) % ka], hi, lo);
         v = c < 2 * kb + ka ? hi : lo;
       }
-      o[c] = v;
+      l2[(j0 + r) * rp + c] = v;
     }
   }
 }
@@ -578,37 +602,59 @@ __device__ __forceinline__ void epilogue_mx4(floatx16 (&acc)[MXW][MXW], uint8_t 
       __syncthreads();
     }
   }
+  // C through LDS, 32 rows of the wave's 128 x 128 tile at a time, so each
+  // lane stores 16 contiguous bytes (two 512-byte row pieces per store)
+  constexpr int CS = 128 + 4;  // floats per staged row
+  float *stage = (float *)smem + wave * 32 * CS;
+  __syncthreads();  // the panels (if any) are no longer read
 #pragma unroll
-  for (int i = 0; i < MXW; ++i)
+  for (int i = 0; i < MXW; ++i) {
 #pragma unroll
-    for (int j = 0; j < MXW; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + r32;
-      if (col >= N) continue;
+    for (int j = 0; j < MXW; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
-        if (row < M) C[row * ldc + col] = acc[i][j][q];
+      for (int q = 0; q < 16; ++q) stage[((q >> 2) * 8 + h * 4 + (q & 3)) * CS + j * 32 + r32] = acc[i][j][q];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int rr = it * 2 + (lane >> 5), c4 = (lane & 31) * 4;
+      const int64_t row = m0 + wm * 128 + i * 32 + rr, col = n0 + wn * 128 + c4;
+      const floatx4 v = *(const floatx4 *)(stage + rr * CS + c4);
+      if (row < M) {
+        float *dst = C + row * ldc + col;
+        if (col + 3 < N && ((uintptr_t)dst & 15) == 0) {
+          __builtin_nontemporal_store(v, (floatx4 *)dst);
+        } else {
+          for (int u = 0; u < 4 && col + u < N; ++u) dst[u] = v[u];
+        }
       }
     }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
 }
 
-// MXFP4 main kernel (K a multiple of 128): C = Ra Rb^T (+ L1 L2^T) on the
+// MXFP4 main kernel (K a multiple of 512): C = Ra Rb^T (+ L1 L2^T) on the
 // scaled FP4 MFMA. Four waves, one per SIMD, each a 128 x 128 sub-tile (4 x 4
 // MFMA blocks of 32 x 32; 256 accumulators, kept in AGPRs). Operands go
 // straight from global memory to LDS (global_load_lds, 16 bytes per lane)
-// into a ring of four stages of 128 contraction elements, issued three stages
-// ahead; each wave waits on its own load counter for the stage it needs, then
-// one barrier per stage. A stage holds A and B codes (256 rows x 64 bytes,
-// 16-byte units XOR-swizzled by row so the fragment reads are conflict free:
-// unit u of row r sits at r * 4 + (u ^ ((r / 4) & 3))) and the scale words of
-// the stage (one per row and operand). The LDS reads of the ring are done in
+// into a ring of four stages of 128 contraction elements (A and B codes, 256
+// rows x 64 bytes each, 16-byte units XOR-swizzled by row so the fragment
+// reads are conflict free: unit u of row r sits at r * 4 + (u ^ ((r / 4) & 3))),
+// issued three stages ahead. The block scales of four stages (16 bytes per row
+// and operand) are loaded together into a double buffer, one group ahead, so
+// a row's scales cost one request per four stages. Each wave waits on its own
+// load counter for the stage it needs, then a barrier; a second barrier after
+// the stage's MFMAs frees its buffer. The LDS reads of the ring are done in
 // asm blocks that wait for their own data, so the compiler never has to order
 // them against the asynchronous loads; their outputs are early-clobber, so no
 // output register doubles as an address of a later read in the same block.
 constexpr int kDmaStages = 4;
-constexpr int DMA_CODE_BYTES = BM * 64;
-constexpr int DMA_STAGE = 2 * DMA_CODE_BYTES + 2 * BM * 4;
-constexpr int DMA_LDS = kDmaStages * DMA_STAGE;
+constexpr int DMA_CODE_BYTES = BM * 64;            // one operand's codes per stage
+constexpr int DMA_STAGE = 2 * DMA_CODE_BYTES;      // A then B
+constexpr int DMA_SCALE_GROUP = 2 * BM * 16;       // A then B scales of four stages
+constexpr int DMA_SCALE_BASE = kDmaStages * DMA_STAGE;
+constexpr int DMA_LDS = DMA_SCALE_BASE + 2 * DMA_SCALE_GROUP;
 static_assert(DMA_LDS <= 160 * 1024, "LDS budget of one CU");
 static_assert(2 * BM * EPI_ROWB <= DMA_LDS, "epilogue panels must fit the main-loop LDS");
 
@@ -675,17 +721,20 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
   const bool okSA = m0 + rs < M, okSB = n0 + rs < N;
   const uint8_t *srcSA = okSA ? as + (m0 + rs) * nb : (const uint8_t *)kZeroPage;
   const uint8_t *srcSB = okSB ? bs + (n0 + rs) * nb : (const uint8_t *)kZeroPage;
-  const int strideSA = okSA ? 4 : 0, strideSB = okSB ? 4 : 0;
+  const int strideSA = okSA ? 16 : 0, strideSB = okSB ? 16 : 0;
 
-  auto issue = [&](int st) {  // ten loads per wave
+  auto issue = [&](int st) {  // eight loads per wave
     uint8_t *sb = smem + (st % kDmaStages) * DMA_STAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       dma_load16(srcA[i] + (int64_t)st * strideA[i], sb + (4 * wave + i) * 1024);
       dma_load16(srcB[i] + (int64_t)st * strideB[i], sb + DMA_CODE_BYTES + (4 * wave + i) * 1024);
     }
-    dma_load4(srcSA + (int64_t)st * strideSA, sb + 2 * DMA_CODE_BYTES + wave * 256);
-    dma_load4(srcSB + (int64_t)st * strideSB, sb + 2 * DMA_CODE_BYTES + BM * 4 + wave * 256);
+  };
+  auto issue_scales = [&](int g) {  // two loads per wave: scales of stages 4 g .. 4 g + 3
+    uint8_t *sg = smem + DMA_SCALE_BASE + (g % 2) * DMA_SCALE_GROUP;
+    dma_load16(srcSA + (int64_t)g * strideSA, sg + wave * 1024);
+    dma_load16(srcSB + (int64_t)g * strideSB, sg + BM * 16 + wave * 1024);
   };
 
   floatx16 acc[MXW][MXW];
@@ -699,22 +748,35 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
   const int rA0 = wm * 128 + r32, rB0 = wn * 128 + r32;
   const int fA = (rA0 >> 2) & 3, fB = (rB0 >> 2) & 3;
   const uint32_t smem0 = lds_offset(smem);
-  if (nst > 0) issue(0);
+  // issue order: scales(0), codes(0), codes(1), codes(2), then per iteration
+  // st: codes(st + 3) and, when st % 4 == 0, scales(st / 4 + 1)
+  issue_scales(0);
+  issue(0);
   if (nst > 1) issue(1);
   if (nst > 2) issue(2);
   for (int st = 0; st < nst; ++st) {
-    // stage st has landed once at most the later issued stages are pending
-    const int later = min(2, nst - 1 - st);
-    if (later == 2)
-      METIS_WAIT_VMCNT(20);
-    else if (later == 1)
-      METIS_WAIT_VMCNT(10);
-    else
-      METIS_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();
-    // every wave is past stage st - 1: its buffer takes stage st + 3
+    // every wave is past stage st - 1 (barrier at the end of the previous
+    // iteration): its buffer takes stage st + 3, and the scale buffer of the
+    // group before this one takes the next group
     if (st + 3 < nst) issue(st + 3);
+    const bool next_group = 4 * (st / 4 + 1) < nst;
+    if (st % 4 == 0 && next_group) issue_scales(st / 4 + 1);
+    // codes(st) (and the scales of its group, issued earlier) have landed once
+    // at most the loads issued after codes(st) are pending
+    const int later = 8 * min(3, nst - 1 - st) + (next_group ? 2 : 0);
+    switch (later) {
+      case 26: METIS_WAIT_VMCNT(26); break;
+      case 24: METIS_WAIT_VMCNT(24); break;
+      case 18: METIS_WAIT_VMCNT(18); break;
+      case 16: METIS_WAIT_VMCNT(16); break;
+      case 10: METIS_WAIT_VMCNT(10); break;
+      case 8: METIS_WAIT_VMCNT(8); break;
+      case 2: METIS_WAIT_VMCNT(2); break;
+      default: METIS_WAIT_VMCNT(0); break;
+    }
+    __builtin_amdgcn_s_barrier();
     const uint32_t base = smem0 + (st % kDmaStages) * DMA_STAGE;
+    const uint32_t sbase = smem0 + DMA_SCALE_BASE + ((st / 4) % 2) * DMA_SCALE_GROUP + (st % 4) * 4;
     int sa[MXW], sb[MXW];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -722,8 +784,8 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
       const uint32_t pb = base + DMA_CODE_BYTES + rB0 * 64 + (((2 * h + ks) ^ fB) << 4);
       u32x4 a0, a1, a2, a3, b0, b1, b2, b3;
       if (ks == 0) {
-        const uint32_t psa = base + 2 * DMA_CODE_BYTES + rA0 * 4;
-        const uint32_t psb = base + 2 * DMA_CODE_BYTES + BM * 4 + rB0 * 4;
+        const uint32_t psa = sbase + rA0 * 16;
+        const uint32_t psb = sbase + BM * 16 + rB0 * 16;
         asm volatile(
             "ds_read_b128 %0, %16\n\t"
             "ds_read_b128 %1, %16 offset:2048\n\t"
@@ -734,13 +796,13 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
             "ds_read_b128 %6, %17 offset:4096\n\t"
             "ds_read_b128 %7, %17 offset:6144\n\t"
             "ds_read_b32 %8, %18\n\t"
-            "ds_read_b32 %9, %18 offset:128\n\t"
-            "ds_read_b32 %10, %18 offset:256\n\t"
-            "ds_read_b32 %11, %18 offset:384\n\t"
+            "ds_read_b32 %9, %18 offset:512\n\t"
+            "ds_read_b32 %10, %18 offset:1024\n\t"
+            "ds_read_b32 %11, %18 offset:1536\n\t"
             "ds_read_b32 %12, %19\n\t"
-            "ds_read_b32 %13, %19 offset:128\n\t"
-            "ds_read_b32 %14, %19 offset:256\n\t"
-            "ds_read_b32 %15, %19 offset:384\n\t"
+            "ds_read_b32 %13, %19 offset:512\n\t"
+            "ds_read_b32 %14, %19 offset:1024\n\t"
+            "ds_read_b32 %15, %19 offset:1536\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(sa[0]),
               "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sb[0]), "=&v"(sb[1]), "=&v"(sb[2]), "=&v"(sb[3])
@@ -772,6 +834,7 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
 #pragma unroll
         for (int j = 0; j < MXW; ++j) acc[i][j] = mfma_fp4_ks(af[i], bf[j], sa[i], sb[j], acc[i][j], ks);
     }
+    __builtin_amdgcn_s_barrier();  // buffer st % 4 is free for stage st + 4
   }
   __syncthreads();  // the epilogue reuses the ring
   epilogue_mx4(acc, smem, m0, n0, M, N, l1, l2, rp, C, ldc);
@@ -918,10 +981,12 @@ metis_status_t gemm_prepare(const Side &a, const Side &b, void *ws, size_t ws_by
   if (b.k) launch_skinny(a.R, a.rows, b.F, b.k, a.T, p.ks_p, p.tc_p, p.ppart, st);
   if (a.k) launch_skinny(b.R, b.rows, a.F, a.k, a.T, p.ks_q, p.tc_q, p.qpart, st);
   if (a.k && b.k) launch_skinny(a.F, a.k, b.F, b.k, a.T, p.ks_c, p.tc_c, p.cpart, st);
-  const unsigned pgrid = (unsigned)cdiv(a.rows + b.rows, 4);
+  if (a.k && b.k)
+    cross_reduce_kernel<<<(unsigned)cdiv(a.k * b.k, 256), 256, 0, st>>>(p.cpart, p.ks_c, a.k * b.k, p.cross);
+  const unsigned pgrid = (unsigned)(cdiv(a.rows, kPanelRows) + cdiv(b.rows, kPanelRows));
 #define PANEL(NV)                                                                                                 \
   panel_kernel<NV><<<pgrid, 256, 0, st>>>(a.rows, b.rows, a.k, b.k, p.rp, p.ppart, p.ks_p, p.qpart, p.ks_q,        \
-                                         p.cpart, p.ks_c, a.S, b.S, a.k ? a.G->codes : nullptr,                    \
+                                         p.cross, a.S, b.S, a.k ? a.G->codes : nullptr,                            \
                                          a.k ? a.G->scales : nullptr, a.k ? a.G->tensor_scale : nullptr,           \
                                          b.k ? b.G->codes : nullptr, b.k ? b.G->scales : nullptr,                  \
                                          b.k ? b.G->tensor_scale : nullptr, p.l1, p.l2)
@@ -957,8 +1022,8 @@ metis_status_t gemm_main(const Side &a, const Side &b, float *C, int64_t ldc, co
   if (a.R->fmt == METIS_NVFP4)
     gemm_nv_kernel<<<tiles, kGemmThreads, 0, st>>>(a.R->codes, a.R->scales, a.R->tensor_scale, a.rows, b.R->codes,
                                           b.R->scales, b.R->tensor_scale, b.rows, a.T, l1, l2, rp, C, ldc);
-  else if (a.T % 128 == 0 && (((uintptr_t)a.R->codes | (uintptr_t)b.R->codes) & 15) == 0 &&
-           (((uintptr_t)a.R->scales | (uintptr_t)b.R->scales) & 3) == 0)
+  else if (a.T % 512 == 0 && ((uintptr_t)a.R->codes | (uintptr_t)b.R->codes | (uintptr_t)a.R->scales |
+                              (uintptr_t)b.R->scales) % 16 == 0)
     gemm_mx_kernel<<<tiles, kMxThreads, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows,
                                                  a.T, l1, l2, rp, C, ldc);
   else

@@ -34,10 +34,11 @@ def _small(seed, rows, cols, k, l, kind="planted", dtype="bf16", fmt="mxfp4"):
 
 
 # (288, 320, 416): contraction lengths that are not multiples of 128 and
-# output tiles that are ragged against 256 x 256; (384, 384, 640): every
-# contraction a multiple of 128 (the MXFP4 kernel with asynchronous LDS loads)
-# and still ragged output tiles.
-SHAPES = {"ragged-k": (288, 320, 416), "k128": (384, 384, 640)}
+# output tiles that are ragged against 256 x 256; (288, 512, 416): the forward
+# contraction a multiple of 512 (the MXFP4 kernel with asynchronous LDS loads)
+# with ragged output tiles; (512, 512, 1024): every contraction a multiple of
+# 512, several stage groups deep.
+SHAPES = {"ragged-k": (288, 320, 416), "fwd-k512": (288, 512, 416), "k512": (512, 512, 1024)}
 
 
 @pytest.mark.parametrize("shape", list(SHAPES))
