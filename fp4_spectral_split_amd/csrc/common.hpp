@@ -56,6 +56,23 @@ __device__ __forceinline__ uint32_t e2m1_rne(float v) {
   return m | ((__float_as_uint(v) >> 28) & 8u);
 }
 
+// Eight E2M1 codes (element j in nibble j) by the gfx950 FP4 conversion at
+// scale 1: round to nearest even, saturating at 6, a zero keeping its sign.
+// These are exactly the codes of e2m1_rne (equal on every finite float).
+__device__ __forceinline__ uint32_t e2m1_pack8(const float *v) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+}
+
+// Codes of one block of B pre-scaled values, packed eight to a word.
+template <int B>
+__device__ __forceinline__ void e2m1_pack(const float (&q)[B], uint32_t (&packed)[B / 8]) {
+#pragma unroll
+  for (int w = 0; w < B / 8; ++w) packed[w] = e2m1_pack8(&q[8 * w]);
+}
+
 // Magnitude of an E2M1 code times 2 (integers 0,1,2,3,4,6,8,12): value = x2 / 2.
 __device__ __forceinline__ float e2m1_value(uint32_t code) {
   const uint32_t m = code & 7u;

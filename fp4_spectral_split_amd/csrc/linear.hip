@@ -69,7 +69,7 @@ struct GemmPlan {
 };
 
 int64_t pick_split(int64_t row_tiles, int64_t T, int64_t &chunk) {
-  int64_t want = std::max<int64_t>(1, cdiv(512, std::max<int64_t>(1, row_tiles)));
+  int64_t want = std::max<int64_t>(1, cdiv(1024, std::max<int64_t>(1, row_tiles)));
   want = std::min<int64_t>(want, std::max<int64_t>(1, T / 512));
   chunk = round_up(cdiv(T, want), 128);
   return cdiv(T, chunk);
@@ -105,12 +105,15 @@ __device__ __forceinline__ floatx16 mfma_fp4(const uint4 a, const uint4 b, int s
 // MXFP4. One wave: 32 rows x (32 * NCT) columns. Per 128-element step each
 // lane reads 32 contiguous code bytes (two scale blocks) of its row; the two
 // MFMAs take the first and second 16 bytes, so every lane's K slots line up
-// between the A and B operands.
+// between the A and B operands. The loads of four steps are issued before
+// their MFMAs (T-chunks are multiples of 128; steps past the chunk load
+// zeros).
 template <int NCT>
 __global__ void __launch_bounds__(64)
     skinny_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t rows,
                   const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int cols, int64_t T, int64_t chunk,
                   float *__restrict__ out) {
+  constexpr int U = 4;
   const int lane = threadIdx.x;
   const int r = lane & 31, h = lane >> 5;
   const int64_t row = (int64_t)blockIdx.x * 32 + r;
@@ -123,36 +126,46 @@ __global__ void __launch_bounds__(64)
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[j][q] = 0.0f;
   const bool rok = row < rows;
-  for (int64_t t0 = t_beg; t0 < t_end; t0 += 128) {
-    const int64_t e0 = t0 + h * 64;  // first element of this lane's two blocks
-    uint4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
-    int sa0 = 127, sa1 = 127;
-    if (rok && e0 < t_end) {
-      const uint4 *p = (const uint4 *)(ac + row * (T / 2) + e0 / 2);
-      a0 = p[0];
-      sa0 = as[row * nb + e0 / 32];
-      if (e0 + 32 < t_end) {
-        a1 = p[1];
-        sa1 = as[row * nb + e0 / 32 + 1];
+  for (int64_t t0 = t_beg; t0 < t_end; t0 += 128 * U) {
+    uint4 a[U][2], b[U][NCT][2];
+    int sa[U][2], sb[U][NCT][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e0 = t0 + 128 * u + h * 64;  // first element of this lane's two blocks
+      a[u][0] = a[u][1] = uint4{0u, 0u, 0u, 0u};
+      sa[u][0] = sa[u][1] = 127;
+      if (rok && e0 < t_end) {
+        const uint4 *p = (const uint4 *)(ac + row * (T / 2) + e0 / 2);
+        a[u][0] = p[0];
+        sa[u][0] = as[row * nb + e0 / 32];
+        if (e0 + 32 < t_end) {
+          a[u][1] = p[1];
+          sa[u][1] = as[row * nb + e0 / 32 + 1];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) {
+        const int col = j * 32 + r;
+        b[u][j][0] = b[u][j][1] = uint4{0u, 0u, 0u, 0u};
+        sb[u][j][0] = sb[u][j][1] = 127;
+        if (col < cols && e0 < t_end) {
+          const uint4 *p = (const uint4 *)(bc + (int64_t)col * (T / 2) + e0 / 2);
+          b[u][j][0] = p[0];
+          sb[u][j][0] = bs[(int64_t)col * nb + e0 / 32];
+          if (e0 + 32 < t_end) {
+            b[u][j][1] = p[1];
+            sb[u][j][1] = bs[(int64_t)col * nb + e0 / 32 + 1];
+          }
+        }
       }
     }
 #pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      const int col = j * 32 + r;
-      uint4 b0 = {0u, 0u, 0u, 0u}, b1 = {0u, 0u, 0u, 0u};
-      int sb0 = 127, sb1 = 127;
-      if (col < cols && e0 < t_end) {
-        const uint4 *p = (const uint4 *)(bc + (int64_t)col * (T / 2) + e0 / 2);
-        b0 = p[0];
-        sb0 = bs[(int64_t)col * nb + e0 / 32];
-        if (e0 + 32 < t_end) {
-          b1 = p[1];
-          sb1 = bs[(int64_t)col * nb + e0 / 32 + 1];
-        }
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) {
+        acc[j] = mfma_fp4(a[u][0], b[u][j][0], sa[u][0], sb[u][j][0], acc[j]);
+        acc[j] = mfma_fp4(a[u][1], b[u][j][1], sa[u][1], sb[u][j][1], acc[j]);
       }
-      acc[j] = mfma_fp4(a0, b0, sa0, sb0, acc[j]);
-      acc[j] = mfma_fp4(a1, b1, sa1, sb1, acc[j]);
-    }
   }
   float *o = out + (int64_t)s * rows * cols;
 #pragma unroll

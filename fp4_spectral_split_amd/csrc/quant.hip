@@ -21,31 +21,21 @@ __device__ __forceinline__ uint32_t quant_block(const float (&v)[B], float s_t, 
 #pragma unroll
   for (int i = 0; i < B; ++i) amax = fmaxf(amax, fabsf(v[i]));
   uint32_t scale_byte;
-  uint32_t c[B];
+  float q[B];
   if (!NV) {
     const int se = mx_shared_exponent(amax);
     scale_byte = (uint32_t)(se + 127);
 #pragma unroll
-    for (int i = 0; i < B; ++i) c[i] = e2m1_rne(ldexpf(v[i], -se));
+    for (int i = 0; i < B; ++i) q[i] = ldexpf(v[i], -se);
   } else {
     const float d = 6.0f * s_t;
     scale_byte = e4m3_rne_sat(__fdiv_rn(amax, d));
     const float den = e4m3_value(scale_byte) * s_t;
-    if (scale_byte == 0u) {
+    // a zero scale leaves only the signs (v * 0 keeps the sign of v)
 #pragma unroll
-      for (int i = 0; i < B; ++i) c[i] = (__float_as_uint(v[i]) >> 28) & 8u;
-    } else {
-#pragma unroll
-      for (int i = 0; i < B; ++i) c[i] = e2m1_rne(__fdiv_rn(v[i], den));
-    }
+    for (int i = 0; i < B; ++i) q[i] = scale_byte ? __fdiv_rn(v[i], den) : v[i] * 0.0f;
   }
-#pragma unroll
-  for (int w = 0; w < B / 8; ++w) {
-    uint32_t p = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p |= c[w * 8 + j] << (4 * j);
-    packed[w] = p;
-  }
+  e2m1_pack<B>(q, packed);
   return scale_byte;
 }
 

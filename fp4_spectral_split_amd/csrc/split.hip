@@ -115,9 +115,9 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
   p.gy_rows = p.wide ? pick_rows_per_part(m, 16, 32) : kGramRows;
   p.gy_parts = (int)cdiv(m, p.gy_rows);
   const int64_t n_tiles = cdiv(n, 128);
-  int64_t wantp = std::min<int64_t>(cdiv(768, n_tiles), std::max<int64_t>(1, m * elem / (20 * l)));
-  wantp = std::max<int64_t>(1, std::min<int64_t>(wantp, m / 32));
-  p.pk_rows = round_up(cdiv(m, wantp), 32);
+  int64_t wantp = std::min<int64_t>(cdiv(768, n_tiles), std::max<int64_t>(1, m * elem / (8 * l)));
+  wantp = std::max<int64_t>(1, std::min<int64_t>(wantp, m / 64));
+  p.pk_rows = round_up(cdiv(m, wantp), 64);
   p.pk = (int)cdiv(m, p.pk_rows);
   p.gb_rows = p.wide ? pick_rows_per_part(n, 16, 32) : kGramRows;
   p.gb_parts = (int)cdiv(n, p.gb_rows);
@@ -173,6 +173,8 @@ __global__ void omega_transpose_kernel(const unsigned short *__restrict__ om, in
 // chunk (lp x 128) is staged in LDS and shared by the waves. Lane (r, g) loads
 // 32 consecutive elements of its row (contraction slots permuted consistently
 // with the Omega operand), so each row's 256 bytes per step are read whole.
+// The next step's A elements and Omega^T pieces are loaded into registers
+// while the current step is multiplied.
 template <typename T>
 __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda,
                                                           const unsigned short *__restrict__ omt, int l, int lp,
@@ -182,8 +184,11 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
   const int lt = min(kLpMax, lp - l0);
   constexpr int KS = 128;
   constexpr int NT = (sizeof(T) == 4) ? 3 : 1;  // bf16 terms per element (fp32 = hi + mid + lo)
+  constexpr int AV = 32 * (int)sizeof(T) / 16;   // 16-byte pieces of A per lane and row
+  constexpr int OPR = (kLpMax * (KS / 8) + kThreads - 1) / kThreads;  // Omega^T pieces per thread
   __shared__ __attribute__((aligned(16))) unsigned short lds[kLpMax][KS + 8];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * 128 + wave * 32;
   const int s = blockIdx.y;
@@ -196,35 +201,52 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
 #pragma unroll
     for (int b = 0; b < kLpMax / 16; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t c0 = c_beg; c0 < c_end; c0 += KS) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < lt * (KS / 8); idx += kThreads) {
-      const int rr = idx / (KS / 8), q = idx % (KS / 8);
-      const int64_t cc = c0 + q * 8;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (cc < c_end) v = *(const uint4 *)(omt + (int64_t)(l0 + rr) * n + cc);
-      *(uint4 *)&lds[rr][q * 8] = v;
-    }
-    __syncthreads();
-    ushortx8 a[2][4][NT];
+  uint4 pa[2][AV], ca[2][AV], po[OPR];
+  auto load = [&](int64_t c0) {
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
       const int64_t row = row0 + rs * 16 + r16;
       const int64_t cc = c0 + g * 32;
       const bool ok = row < m && cc < c_end;
+      const uint4 *src = (const uint4 *)(A + row * lda + cc);
+#pragma unroll
+      for (int j = 0; j < AV; ++j) pa[rs][j] = ok ? src[j] : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int p = 0; p < OPR; ++p) {
+      const int idx = t + kThreads * p;
+      const int rr = idx / (KS / 8), q = idx % (KS / 8);
+      const int64_t cc = c0 + q * 8;
+      po[p] = (idx < lt * (KS / 8) && cc < c_end) ? *(const uint4 *)(omt + (int64_t)(l0 + rr) * n + cc)
+                                                  : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  if (c_beg < c_end) load(c_beg);
+  for (int64_t c0 = c_beg; c0 < c_end; c0 += KS) {
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < OPR; ++p) {
+      const int idx = t + kThreads * p;
+      if (idx < lt * (KS / 8)) *(uint4 *)&lds[idx / (KS / 8)][(idx % (KS / 8)) * 8] = po[p];
+    }
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int j = 0; j < AV; ++j) ca[rs][j] = pa[rs][j];
+    if (c0 + KS < c_end) load(c0 + KS);  // in flight while this step is multiplied
+    __syncthreads();
+    ushortx8 a[2][4][NT];
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs) {
       if constexpr (sizeof(T) == 2) {
-        const uint4 *src = (const uint4 *)(A + row * lda + cc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint4 v = ok ? src[j] : uint4{0u, 0u, 0u, 0u};
-          a[rs][j][0] = __builtin_bit_cast(ushortx8, v);
-        }
+        for (int j = 0; j < 4; ++j) a[rs][j][0] = __builtin_bit_cast(ushortx8, ca[rs][j]);
       } else {
-        const float4 *src = (const float4 *)(A + row * lda + cc);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float4 v0 = ok ? src[2 * j] : float4{0.f, 0.f, 0.f, 0.f};
-          float4 v1 = ok ? src[2 * j + 1] : float4{0.f, 0.f, 0.f, 0.f};
+          const float4 v0 = __builtin_bit_cast(float4, ca[rs][2 * j]);
+          const float4 v1 = __builtin_bit_cast(float4, ca[rs][2 * j + 1]);
           const float xs[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -249,7 +271,7 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
 #pragma unroll
           for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc[rs][ct] = mfma16_bf16(a[rs][j][t], b, acc[rs][ct]);
+            for (int tt = 0; tt < NT; ++tt) acc[rs][ct] = mfma16_bf16(a[rs][j][tt], b, acc[rs][ct]);
         }
       }
     }
@@ -772,8 +794,9 @@ __global__ void argmax_kernel(const float *__restrict__ U, int64_t m, int k, int
 // ============================================================== projection
 // btp[s] = (A[rows of chunk s, :])^T Q[rows of chunk s, :]   (n x l, fp32)
 // with Q given transposed as bf16 hi + lo (2 x lp x m). WG: 128 columns of A,
-// 4 waves x 32 columns. Per step, 32 rows of A (bf16 or fp32) and the
-// matching 32 columns of Q^T (hi, lo) are staged in LDS.
+// 4 waves x 32 columns. Per step, 64 rows of A (bf16 or fp32) and the
+// matching 64 columns of Q^T (hi, lo) pass through LDS; the next step's
+// pieces are loaded into registers while the current step is multiplied.
 template <typename T>
 __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda,
                                                            const unsigned short *__restrict__ qt, int l, int lp,
@@ -781,12 +804,16 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
   // blockIdx.z selects a tile of kLpMax columns of Q starting at l0
   const int l0 = blockIdx.z * kLpMax;
   const int lt = min(kLpMax, lp - l0);
-  constexpr int KS = 32;
+  constexpr int KS = 64;
   constexpr int TN = 128;
   constexpr int NT = (sizeof(T) == 4) ? 3 : 1;
+  constexpr int PIECE = 16 / sizeof(T);                      // elements per 16-byte piece
+  constexpr int APR = KS * (TN / PIECE) / kThreads;          // A pieces per thread per step
+  constexpr int QPR = (2 * kLpMax * (KS / 8) + kThreads - 1) / kThreads;  // Q^T pieces
   __shared__ __attribute__((aligned(16))) T at[KS][TN + (sizeof(T) == 2 ? 8 : 4)];
   __shared__ __attribute__((aligned(16))) unsigned short qs[2][kLpMax][KS + 8];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int64_t col0 = (int64_t)blockIdx.x * TN;
   const int s = blockIdx.y;
@@ -799,54 +826,78 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
 #pragma unroll
     for (int b = 0; b < kLpMax / 16; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t r0 = r_beg; r0 < r_end; r0 += KS) {
-    __syncthreads();
-    // A tile: KS rows x TN columns, 16-byte pieces
-    constexpr int PIECE = 16 / sizeof(T);
-    for (int idx = threadIdx.x; idx < KS * (TN / PIECE); idx += kThreads) {
+  uint4 ra[APR], rq[QPR];
+  auto load = [&](int64_t r0) {
+#pragma unroll
+    for (int p = 0; p < APR; ++p) {
+      const int idx = t + kThreads * p;
       const int rr = idx / (TN / PIECE), q = idx % (TN / PIECE);
       const int64_t row = r0 + rr, col = col0 + q * PIECE;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (row < r_end && col < n) v = *(const uint4 *)(A + row * lda + col);
-      *(uint4 *)&at[rr][q * PIECE] = v;
+      ra[p] = (row < r_end && col < n) ? *(const uint4 *)(A + row * lda + col) : uint4{0u, 0u, 0u, 0u};
     }
-    // Q^T hi/lo: 2 x lp rows of KS bf16 (4 pieces each)
-    for (int idx = threadIdx.x; idx < 2 * lt * (KS / 8); idx += kThreads) {
-      const int h = idx / (lt * 4), rem = idx % (lt * 4);
-      const int i = rem >> 2, q = rem & 3;
+#pragma unroll
+    for (int p = 0; p < QPR; ++p) {
+      const int idx = t + kThreads * p;
+      const int h = idx / (lt * (KS / 8)), rem = idx % (lt * (KS / 8));
+      const int i = rem / (KS / 8), q = rem % (KS / 8);
       const int64_t row = r0 + q * 8;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (row < r_end) v = *(const uint4 *)(qt + ((int64_t)h * lp + l0 + i) * m + row);
-      *(uint4 *)&qs[h][i][q * 8] = v;
+      rq[p] = (idx < 2 * lt * (KS / 8) && row < r_end)
+                  ? *(const uint4 *)(qt + ((int64_t)h * lp + l0 + i) * m + row)
+                  : uint4{0u, 0u, 0u, 0u};
     }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int p = 0; p < APR; ++p) {
+      const int idx = t + kThreads * p;
+      *(uint4 *)&at[idx / (TN / PIECE)][(idx % (TN / PIECE)) * PIECE] = ra[p];
+    }
+#pragma unroll
+    for (int p = 0; p < QPR; ++p) {
+      const int idx = t + kThreads * p;
+      if (idx < 2 * lt * (KS / 8)) {
+        const int h = idx / (lt * (KS / 8)), rem = idx % (lt * (KS / 8));
+        *(uint4 *)&qs[h][rem / (KS / 8)][(rem % (KS / 8)) * 8] = rq[p];
+      }
+    }
+  };
+
+  if (r_beg < r_end) load(r_beg);
+  for (int64_t r0 = r_beg; r0 < r_end; r0 += KS) {
+    __syncthreads();
+    store();
+    if (r0 + KS < r_end) load(r0 + KS);  // in flight while this step is multiplied
     __syncthreads();
 #pragma unroll
-    for (int cs = 0; cs < 2; ++cs) {
-      const int cl = wave * 32 + cs * 16 + r16;  // A column inside the tile
-      ushortx8 af[NT];
+    for (int kq = 0; kq < KS / 32; ++kq) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (sizeof(T) == 2) {
-          af[0][e] = at[g * 8 + e][cl];
-        } else {
-          const float x = at[g * 8 + e][cl];
-          const unsigned short hi = f32_to_bf16(x);
-          const float r1 = x - bf16_to_f32(hi);
-          const unsigned short mid = f32_to_bf16(r1);
-          af[0][e] = hi;
-          af[NT > 1 ? 1 : 0][e] = mid;
-          af[NT > 2 ? 2 : 0][e] = f32_to_bf16(r1 - bf16_to_f32(mid));
+      for (int cs = 0; cs < 2; ++cs) {
+        const int cl = wave * 32 + cs * 16 + r16;  // A column inside the tile
+        ushortx8 af[NT];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (sizeof(T) == 2) {
+            af[0][e] = at[kq * 32 + g * 8 + e][cl];
+          } else {
+            const float x = at[kq * 32 + g * 8 + e][cl];
+            const unsigned short hi = f32_to_bf16(x);
+            const float r1 = x - bf16_to_f32(hi);
+            const unsigned short mid = f32_to_bf16(r1);
+            af[0][e] = hi;
+            af[NT > 1 ? 1 : 0][e] = mid;
+            af[NT > 2 ? 2 : 0][e] = f32_to_bf16(r1 - bf16_to_f32(mid));
+          }
         }
-      }
 #pragma unroll
-      for (int it = 0; it < kLpMax / 16; ++it) {
-        if (it < nit) {
-          const ushortx8 qh = *(const ushortx8 *)&qs[0][it * 16 + r16][g * 8];
-          const ushortx8 ql = *(const ushortx8 *)&qs[1][it * 16 + r16][g * 8];
+        for (int it = 0; it < kLpMax / 16; ++it) {
+          if (it < nit) {
+            const ushortx8 qh = *(const ushortx8 *)&qs[0][it * 16 + r16][kq * 32 + g * 8];
+            const ushortx8 ql = *(const ushortx8 *)&qs[1][it * 16 + r16][kq * 32 + g * 8];
 #pragma unroll
-          for (int tt = 0; tt < NT; ++tt) {
-            acc[cs][it] = mfma16_bf16(af[tt], qh, acc[cs][it]);
-            acc[cs][it] = mfma16_bf16(af[tt], ql, acc[cs][it]);
+            for (int tt = 0; tt < NT; ++tt) {
+              acc[cs][it] = mfma16_bf16(af[tt], qh, acc[cs][it]);
+              acc[cs][it] = mfma16_bf16(af[tt], ql, acc[cs][it]);
+            }
           }
         }
       }
@@ -1262,22 +1313,42 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // sign[c] = -1 if the largest-|U[:, c]| entry (lowest row on ties) is negative
-__global__ void sign_kernel(const float *__restrict__ am_val, const int *__restrict__ am_idx, int parts, int k,
-                            float *__restrict__ sign) {
-  const int c = threadIdx.x;
-  if (c >= k) return;
+// Column c's sign from the chunk argmax partials: the largest |U[:, c]|,
+// lowest row on ties (an order-independent selection). Eight groups of 128
+// threads scan every eighth partial, then group 0 combines the eight.
+__global__ void __launch_bounds__(1024)
+    sign_kernel(const float *__restrict__ am_val, const int *__restrict__ am_idx, int parts, int k,
+                float *__restrict__ sign) {
+  __shared__ float pa[8][128], pv[8][128];
+  __shared__ int pi[8][128];
+  const int c = threadIdx.x & 127, g = threadIdx.x >> 7;
   float ba = -1.0f, bv = 0.0f;
   int bi = 0x7FFFFFFF;
-  for (int p = 0; p < parts; ++p) {
-    const float v = am_val[p * k + c];
-    const int i = am_idx[p * k + c];
-    if (fabsf(v) > ba || (fabsf(v) == ba && i < bi)) {
-      ba = fabsf(v);
-      bv = v;
-      bi = i;
+  if (c < k) {
+#pragma unroll 4
+    for (int p = g; p < parts; p += 8) {
+      const float v = am_val[p * k + c];
+      const int i = am_idx[p * k + c];
+      if (fabsf(v) > ba || (fabsf(v) == ba && i < bi)) {
+        ba = fabsf(v);
+        bv = v;
+        bi = i;
+      }
     }
   }
-  sign[c] = bv < 0.0f ? -1.0f : 1.0f;
+  pa[g][c] = ba;
+  pv[g][c] = bv;
+  pi[g][c] = bi;
+  __syncthreads();
+  if (g == 0 && c < k) {
+    for (int q = 1; q < 8; ++q)
+      if (pa[q][c] > ba || (pa[q][c] == ba && pi[q][c] < bi)) {
+        ba = pa[q][c];
+        bv = pv[q][c];
+        bi = pi[q][c];
+      }
+    sign[c] = bv < 0.0f ? -1.0f : 1.0f;
+  }
 }
 
 // max |x| over a rows x cols fp32 matrix (row stride ld) into *out (bits).
@@ -1339,22 +1410,21 @@ __global__ void __launch_bounds__(kThreads)
   }
   float amx = 0.0f;
   for (int i = 0; i < B; ++i) amx = fmaxf(amx, fabsf(v[i]));
-  uint32_t sb, cde[B];
+  uint32_t sb;
+  float q[B];
   if (!NV) {
     const int se = mx_shared_exponent(amx);
     sb = (uint32_t)(se + 127);
-    for (int i = 0; i < B; ++i) cde[i] = e2m1_rne(ldexpf(v[i], -se));
+    for (int i = 0; i < B; ++i) q[i] = ldexpf(v[i], -se);
   } else {
     sb = e4m3_rne_sat(__fdiv_rn(amx, 6.0f * s_t));
     const float den = e4m3_value(sb) * s_t;
-    for (int i = 0; i < B; ++i) cde[i] = sb ? e2m1_rne(__fdiv_rn(v[i], den)) : ((__float_as_uint(v[i]) >> 28) & 8u);
+    for (int i = 0; i < B; ++i) q[i] = sb ? __fdiv_rn(v[i], den) : v[i] * 0.0f;  // zero scale: signs only
   }
+  uint32_t pk[B / 8];
+  e2m1_pack<B>(q, pk);
   uint32_t *dst = (uint32_t *)(codes + (int64_t)c * (rows / 2) + blk * (B / 2));
-  for (int w = 0; w < B / 8; ++w) {
-    uint32_t pk = 0;
-    for (int j = 0; j < 8; ++j) pk |= cde[w * 8 + j] << (4 * j);
-    dst[w] = pk;
-  }
+  for (int w = 0; w < B / 8; ++w) dst[w] = pk[w];
   scales[(int64_t)c * (rows / B) + blk] = (uint8_t)sb;
 }
 
@@ -1370,26 +1440,21 @@ __device__ __forceinline__ void quant_store(const float (&v)[B], float s_t, uint
   float amx = 0.0f;
 #pragma unroll
   for (int i = 0; i < B; ++i) amx = fmaxf(amx, fabsf(v[i]));
-  uint32_t sb, c[B];
+  uint32_t sb;
+  float q[B];
   if (!NV) {
     const int se = mx_shared_exponent(amx);
     sb = (uint32_t)(se + 127);
 #pragma unroll
-    for (int i = 0; i < B; ++i) c[i] = e2m1_rne(ldexpf(v[i], -se));
+    for (int i = 0; i < B; ++i) q[i] = ldexpf(v[i], -se);
   } else {
     sb = e4m3_rne_sat(__fdiv_rn(amx, 6.0f * s_t));
     const float den = e4m3_value(sb) * s_t;
 #pragma unroll
-    for (int i = 0; i < B; ++i) c[i] = sb ? e2m1_rne(__fdiv_rn(v[i], den)) : ((__float_as_uint(v[i]) >> 28) & 8u);
+    for (int i = 0; i < B; ++i) q[i] = sb ? __fdiv_rn(v[i], den) : v[i] * 0.0f;  // zero scale: signs only
   }
   uint32_t pk[B / 8];
-#pragma unroll
-  for (int w = 0; w < B / 8; ++w) {
-    uint32_t p = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p |= c[w * 8 + j] << (4 * j);
-    pk[w] = p;
-  }
+  e2m1_pack<B>(q, pk);
   if constexpr (B == 32) {
     *(uint4 *)codes = uint4{pk[0], pk[1], pk[2], pk[3]};
   } else {
@@ -1410,39 +1475,73 @@ __global__ void __launch_bounds__(kThreads)
   const int wave = t >> 6, lane = t & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int64_t col0 = (int64_t)blockIdx.x * kRT, row0 = (int64_t)blockIdx.y * kRT;
-  // ---- L tile via MFMA: wave owns rows wave*32 .. +32, all 128 columns
+  // ---- this thread's row blocks of A are loaded first, in flight while L is
+  // formed: block b = t + 256 j is row b / RPB, columns (b % RPB) * B ..
+  constexpr int RPB = kRT / B;                 // blocks per tile row
+  constexpr int NJ = kRT * RPB / kThreads;     // row blocks per thread
+  constexpr int VEC = B * (int)sizeof(T) / 16;  // 16-byte pieces per block
+  static_assert(NJ * kThreads == kRT * RPB, "row blocks must divide over the threads");
+  uint4 apre[NJ][VEC];
+#pragma unroll
+  for (int jb = 0; jb < NJ; ++jb) {
+    const int b = t + kThreads * jb, rr = b / RPB, cb = b % RPB;
+    const int64_t row = row0 + rr, col = col0 + cb * B;
+    const bool ok = row < m && col < n;
+    const uint4 *src = (const uint4 *)(A + row * lda + col);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) apre[jb][q] = ok ? src[q] : uint4{0u, 0u, 0u, 0u};
+  }
+  // ---- L tile via MFMA: wave owns rows wave*32 .. +32, all 128 columns.
+  // This wave's U operands (hi, lo) are loaded into registers up front; the W
+  // panel (hi, lo) of the tile's 128 columns is shared by the four waves and
+  // staged once in LDS, in the space the R tile takes later (row stride
+  // kp + 8 bf16 keeps the fragment reads conflict free).
   {
+    constexpr int KPM = 96;  // largest kp (k <= 96)
+    unsigned short *wst = (unsigned short *)&lt[0][0];  // [2][kRT][kp + 8]
+    const int wstride = kp + 8;
+    const int64_t um = m * kp, wn = n * kp;
+    ushortx8 uh[KPM / 32][2], ul[KPM / 32][2];
+#pragma unroll
+    for (int ks = 0; ks < KPM / 32; ++ks)
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs) {
+        const int64_t row = row0 + wave * 32 + rs * 16 + r16;
+        const bool ok = row < m && ks * 32 < kp;
+        const unsigned short *pu = uhl + row * kp + ks * 32 + g * 8;
+        uh[ks][rs] = ok ? *(const ushortx8 *)pu : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
+        ul[ks][rs] = ok ? *(const ushortx8 *)(pu + um) : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    for (int idx = t; idx < 2 * kRT * (kp / 8); idx += kThreads) {
+      const int h = idx / (kRT * (kp / 8)), rem = idx % (kRT * (kp / 8));
+      const int c = rem / (kp / 8), q = rem % (kp / 8);
+      const int64_t col = col0 + c;
+      const uint4 v = col < n ? *(const uint4 *)(whl + h * wn + col * kp + q * 8) : uint4{0u, 0u, 0u, 0u};
+      *(uint4 *)(wst + (h * kRT + c) * wstride + q * 8) = v;
+    }
+    __syncthreads();
     floatx4 acc[2][8];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int b = 0; b < 8; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int64_t um = m * kp, wn = n * kp;
-    for (int kk = 0; kk < kp; kk += 32) {
-      ushortx8 uh[2], ul[2];
 #pragma unroll
-      for (int rs = 0; rs < 2; ++rs) {
-        const int64_t row = row0 + wave * 32 + rs * 16 + r16;
-        const bool ok = row < m;
-        const unsigned short *pu = uhl + row * kp + kk + g * 8;
-        uh[rs] = ok ? *(const ushortx8 *)pu : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
-        ul[rs] = ok ? *(const ushortx8 *)(pu + um) : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+    for (int ks = 0; ks < KPM / 32; ++ks) {
+      if (ks * 32 >= kp) break;
 #pragma unroll
       for (int cs = 0; cs < 8; ++cs) {
-        const int64_t col = col0 + cs * 16 + r16;
-        const bool ok = col < n;
-        const unsigned short *pw = whl + col * kp + kk + g * 8;
-        const ushortx8 wh = ok ? *(const ushortx8 *)pw : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
-        const ushortx8 wl = ok ? *(const ushortx8 *)(pw + wn) : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
+        const int c = cs * 16 + r16;
+        const ushortx8 wh = *(const ushortx8 *)(wst + c * wstride + ks * 32 + g * 8);
+        const ushortx8 wl = *(const ushortx8 *)(wst + (kRT + c) * wstride + ks * 32 + g * 8);
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
-          acc[rs][cs] = mfma16_bf16(uh[rs], wh, acc[rs][cs]);
-          acc[rs][cs] = mfma16_bf16(uh[rs], wl, acc[rs][cs]);
-          acc[rs][cs] = mfma16_bf16(ul[rs], wh, acc[rs][cs]);
+          acc[rs][cs] = mfma16_bf16(uh[ks][rs], wh, acc[rs][cs]);
+          acc[rs][cs] = mfma16_bf16(uh[ks][rs], wl, acc[rs][cs]);
+          acc[rs][cs] = mfma16_bf16(ul[ks][rs], wh, acc[rs][cs]);
         }
       }
     }
+    __syncthreads();  // the W panel is no longer read
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
@@ -1459,20 +1558,15 @@ __global__ void __launch_bounds__(kThreads)
   }
   // ---- row blocks (along n): R = A - L, kept in LDS for the column pass
   float mx = 0.0f;
-  constexpr int RPB = kRT / B;  // blocks per tile row
-  for (int b = t; b < kRT * RPB; b += kThreads) {
-    const int rr = b / RPB, cb = b % RPB;
+#pragma unroll
+  for (int jb = 0; jb < NJ; ++jb) {
+    const int b = t + kThreads * jb, rr = b / RPB, cb = b % RPB;
     const int64_t row = row0 + rr, col = col0 + cb * B;
     float v[B];
     const bool ok = row < m && col < n;
-    if (ok) {
-      const T *src = A + row * lda + col;
+    const T *pa = (const T *)&apre[jb][0];
 #pragma unroll
-      for (int i = 0; i < B; ++i) v[i] = load_f32(src + i) - lt[rr][cb * B + i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < B; ++i) v[i] = 0.0f;
-    }
+    for (int i = 0; i < B; ++i) v[i] = ok ? load_f32(pa + i) - lt[rr][cb * B + i] : 0.0f;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
       lt[rr][cb * B + i] = v[i];
@@ -1577,7 +1671,7 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     argmax_kernel<<<p.am_parts, 128, 0, st>>>(out->U, m, k, p.am_rows, p.am_val, p.am_idx);
     assemble_wide_kernel<<<(unsigned)cdiv(n * k, 256), 256, 0, st>>>(bt, n, l, lp, k, p.evec, p.sig_inv, out->V);
   }
-  sign_kernel<<<1, 128, 0, st>>>(p.am_val, p.am_idx, p.am_parts, k, p.sign);
+  sign_kernel<<<1, 1024, 0, st>>>(p.am_val, p.am_idx, p.am_parts, k, p.sign);
   const int B = nv ? 16 : 32;
   const unsigned fgrid = (unsigned)cdiv(std::max(m, n) / B * kp, kThreads);
   if (nv) {
