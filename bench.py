@@ -8,12 +8,23 @@ A step is the whole hot path over one batch of synthetic, HBM-resident input:
     dY_down; k = 64, l = 80, Gaussian sketch; residual in both orientations);
   * six GEMMs with their low-rank corrections: Y = X W^T, dX = dY W,
     dW = dY^T X for both layers (6 x 962.07 GFLOP).
-value = sum(2 M N K) / step time. Splits run on three streams and the GEMMs on
-a fourth; a GEMM starts when the splits it reads are done.
+value = sum(2 M N K) / step time. The work runs on three streams (lanes); each
+GEMM sits in a lane behind a split of its own and waits for the splits it
+reads from the other lanes, so GEMMs overlap the splits still running. Work
+is enqueued in dependency order (every GEMM after the splits it reads), and a
+step starts when every lane has finished the previous one.
 
 Prints one JSON line. Usage: python bench.py [--steps K] [--warmup W]
+
+roofline.traffic is the main GEMM kernel's HBM bytes per launch, read from the
+committed counter summary in profiles/ (FETCH_SIZE and WRITE_SIZE, scaled by
+what the same counters read for a plain copy of known size); it is null when
+that summary was taken on a different version of the GEMM source. The copy
+that calibrates the counters runs with --calibrate-copy MIB, ahead of the
+steps, in the same profiled process.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +36,8 @@ sys.path.insert(0, ROOT)
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
 HBM_PEAK_GBS = 8000.0
 CFG = 4
+GEMM_SOURCE = os.path.join(ROOT, "fp4_spectral_split_amd", "csrc", "linear.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_mx_kernel_llama3-8b-ffn_traffic.md")
 
 
 def log(*a):
@@ -39,6 +52,32 @@ def gemm_flops(cfg_shapes, gemms):
         rb = cfg_shapes[b][1] if bo == "t" else cfg_shapes[b][0]
         total += 2 * ra * rb * T
     return total
+
+
+def gemm_traffic():
+    """HBM bytes per main-GEMM launch from the committed counter summary, or
+    None when it is missing or was taken on another version of linear.hip."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_SUMMARY) if line.startswith("- ") and ":" in line)
+    except OSError:
+        return None
+    fields = {k[2:].strip(): v.strip().strip("`") for k, v in fields.items()}
+    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if fields.get("linear.hip sha256") != src or "hbm bytes per launch" not in fields:
+        return None
+    return int(fields["hbm bytes per launch"])
+
+
+def calibrate_copy(torch, dev, mib):
+    """A plain elementwise copy of mib MiB (fp32 in, fp32 out), five times,
+    so that the profiled process holds dispatches of known traffic."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log("calibration copy: 5 x %d MiB read + %d MiB written" % (mib, mib))
 
 
 def cpu_baseline(tensors, gemm_total_flops):
@@ -82,6 +121,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run a plain copy of MIB MiB ahead of the steps (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
@@ -95,6 +136,8 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev, args.calibrate_copy)
     names = synth.TENSOR_NAMES[CFG]
     gemms = synth.GEMMS[CFG]
     t0 = time.perf_counter()
@@ -115,11 +158,16 @@ def main():
         gobj[out] = g
         outs[out] = torch.empty(g.rows, g.cols, dtype=torch.float32, device=dev)
 
-    split_streams = [torch.cuda.Stream(dev) for _ in range(3)]
-    gstream = torch.cuda.Stream(dev)
-    lanes = [["X_up", "X_down"], ["W_up", "W_down"], ["dY_up", "dY_down"]]
+    lanes = [torch.cuda.Stream(dev) for _ in range(3)]
+    # (lane, kind, name) in an order where every GEMM follows the splits it reads
+    order = [(0, "split", "X_up"), (1, "split", "W_up"), (2, "split", "dY_up"), (0, "split", "X_down"),
+             (1, "gemm", "Y_up"), (2, "gemm", "dX_up"), (2, "gemm", "dW_up"), (1, "split", "W_down"),
+             (2, "split", "dY_down"), (0, "gemm", "Y_down"), (1, "gemm", "dX_down"), (2, "gemm", "dW_down")]
+    gemm_of = {g[0]: g for g in gemms}
+    assert sorted(n for _, k, n in order if k == "split") == sorted(names)
+    assert sorted(n for _, k, n in order if k == "gemm") == sorted(gemm_of)
     done = {n: torch.cuda.Event() for n in names}
-    step_end = torch.cuda.Event()
+    lane_end = [torch.cuda.Event() for _ in lanes]
     t = tensors
     ev = lambda: torch.cuda.Event(enable_timing=True)
     split_ev = [{n: (ev(), ev()) for n in names} for _ in range(args.steps)]
@@ -127,27 +175,34 @@ def main():
 
     def step(i):
         rec = i is not None
-        for s, lane in zip(split_streams, lanes):
-            s.wait_event(step_end)
+        for s in lanes:  # the previous step's GEMMs are done with every record
+            for e in lane_end:
+                s.wait_event(e)
+        enqueued = set()
+        for li, kind, n in order:
+            s = lanes[li]
             with torch.cuda.stream(s):
-                for n in lane:
+                if kind == "split":
                     if rec:
                         split_ev[i][n][0].record(s)
                     M.metis_split(A[n], t[n].l, t[n].k, "mxfp4", omega=Om[n], out=recs[n])
                     if rec:
                         split_ev[i][n][1].record(s)
                     done[n].record(s)
-        with torch.cuda.stream(gstream):
-            for out, a, ao, b, bo in gemms:
-                gstream.wait_event(done[a])
-                gstream.wait_event(done[b])
-                gobj[out].prepare()
-                if rec:
-                    main_ev[i][out][0].record(gstream)
-                gobj[out].main(outs[out])
-                if rec:
-                    main_ev[i][out][1].record(gstream)
-            step_end.record(gstream)
+                    enqueued.add(n)
+                else:
+                    _, a, ao, b, bo = gemm_of[n]
+                    assert a in enqueued and b in enqueued
+                    s.wait_event(done[a])
+                    s.wait_event(done[b])
+                    gobj[n].prepare()
+                    if rec:
+                        main_ev[i][n][0].record(s)
+                    gobj[n].main(outs[n])
+                    if rec:
+                        main_ev[i][n][1].record(s)
+        for s, e in zip(lanes, lane_end):
+            e.record(s)
 
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -178,9 +233,9 @@ def main():
                    round(total_flops / 1e9, 2)},
         "split_ms": {n: round(v / args.steps, 4) for n, v in split_ms.items()},
         "gemm_main_ms": {o: round(v / args.steps, 4) for o, v in main_ms.items()},
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (main MXFP4 GEMM + low-rank correction)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_mx_kernel (main MXFP4 GEMM + low-rank correction)",
                      "achieved": round(achieved, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": gemm_traffic()},
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
