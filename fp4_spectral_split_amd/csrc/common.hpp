@@ -188,6 +188,28 @@ struct Carver {
 
 }  // namespace metis_host
 
+// Copy `count` elements src[si(i)] -> dst[di(i)] (dst usually LDS) with the
+// whole block: each thread issues PER loads before the first of them is
+// used, so a small matrix arrives in count / (PER * blockDim.x) memory round
+// trips instead of one round trip per element a thread handles.
+template <int PER, typename T, typename SrcIdx, typename DstIdx>
+__device__ __forceinline__ void stage_batched(T *dst, const T *__restrict__ src, int count, SrcIdx si, DstIdx di) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  for (int base = 0; base < count; base += PER * nt) {
+    T v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = base + t + u * nt;
+      v[u] = i < count ? src[si(i)] : T(0);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = base + t + u * nt;
+      if (i < count) dst[di(i)] = v[u];
+    }
+  }
+}
+
 #define METIS_LAUNCH_CHECK()                                \
   do {                                                      \
     if (hipGetLastError() != hipSuccess) return METIS_ERR_HIP; \

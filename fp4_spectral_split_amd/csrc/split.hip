@@ -358,25 +358,111 @@ __device__ __forceinline__ doublex4 mfma16_f64(double a, double b, doublex4 c) {
 __host__ __device__ constexpr int gram_ys_stride(int lp) { return lp + 4; }                  // (lp + 4) / 4 odd
 __host__ __device__ constexpr int gram_rl_stride(int lp) { return lp % 32 == 16 ? lp : lp + 16; }  // 16 mod 32
 
+// Rows [row0, row0 + kGramRows) of the sum of `parts` slabs of xin (row
+// stride l, slab stride part_stride) into Ys (row stride S), summed in slab
+// order; columns l .. lp - 1 and rows past `rows` are zero. For l % 4 == 0
+// each thread loads float4s and keeps the loads of four slabs in flight
+// together, so the chunk arrives in a few memory round trips.
+__device__ __forceinline__ void gram_load_chunk(float *Ys, int S, const float *__restrict__ xin, int parts,
+                                                int64_t part_stride, int64_t row0, int64_t rows, int l, int lp) {
+  const int t = threadIdx.x;
+  const int nrows = (int)std::min<int64_t>(kGramRows, rows - row0);
+  if ((l & 3) == 0) {
+    constexpr int NV = kGramRows * kLpMax / 4 / kGramThreads;
+    const int nv = nrows * l / 4;
+    const float4 *src = (const float4 *)(xin + row0 * l);
+    const int64_t ps4 = part_stride / 4;
+    const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float4 acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = z;
+    int q = 0;
+    for (; q + 4 <= parts; q += 4) {
+      float4 x[4][NV];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const int f = t + i * kGramThreads;
+          x[u][i] = f < nv ? src[(q + u) * ps4 + f] : z;
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          acc[i].x += x[u][i].x;
+          acc[i].y += x[u][i].y;
+          acc[i].z += x[u][i].z;
+          acc[i].w += x[u][i].w;
+        }
+    }
+    for (; q < parts; ++q) {
+      float4 x[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int f = t + i * kGramThreads;
+        x[i] = f < nv ? src[q * ps4 + f] : z;
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        acc[i].x += x[i].x;
+        acc[i].y += x[i].y;
+        acc[i].z += x[i].z;
+        acc[i].w += x[i].w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int f = t + i * kGramThreads;
+      if (f < nv) {
+        const int r = (4 * f) / l, c = 4 * f - r * l;
+        *(float4 *)(Ys + r * S + c) = acc[i];
+      }
+    }
+    if (nrows < kGramRows || l < lp)
+      for (int idx = t; idx < kGramRows * lp; idx += kGramThreads) {
+        const int r = idx / lp, c = idx - (idx / lp) * lp;
+        if (r >= nrows || c >= l) Ys[r * S + c] = 0.0f;
+      }
+  } else {
+    for (int idx = t; idx < kGramRows * lp; idx += kGramThreads) {
+      const int r = idx / lp, c = idx - (idx / lp) * lp;
+      Ys[r * S + c] = (r < nrows && c < l) ? sum_parts(xin + (row0 + r) * l + c, parts, part_stride) : 0.0f;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kGramThreads)
     gram_kernel(const float *__restrict__ xin, int parts, int64_t part_stride, int64_t rows, int l, int lp,
                 const double *__restrict__ rinv, float *__restrict__ xout, unsigned short *__restrict__ xt,
                 double *__restrict__ gpart) {
-  __shared__ float Ys[kGramRows * (kLpMax + 4)];
+  __shared__ __attribute__((aligned(16))) float Ys[kGramRows * (kLpMax + 4)];
   __shared__ double Rl[kLpMax * (kLpMax + 16)];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, lr = lane & 15, lk = lane >> 4;
   const int S = gram_ys_stride(lp), RS = gram_rl_stride(lp), T = lp >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * kGramRows;
-  for (int idx = t; idx < kGramRows * lp; idx += kGramThreads) {
-    const int r = idx / lp, c = idx - (idx / lp) * lp;
-    const int64_t row = row0 + r;
-    Ys[r * S + c] = (row < rows && c < l) ? sum_parts(xin + row * l + c, parts, part_stride) : 0.0f;
-  }
-  if (rinv)
-    for (int idx = t; idx < lp * lp; idx += kGramThreads) {
-      const int r = idx / lp, c = idx - (idx / lp) * lp;
-      Rl[r * RS + c] = rinv[idx];
+  gram_load_chunk(Ys, S, xin, parts, part_stride, row0, rows, l, lp);
+  if (rinv) {
+    // R^-1 in pairs of columns, every load of the thread in flight at once
+    constexpr int NR = kLpMax * kLpMax / 2 / kGramThreads;
+    const double2 *src = (const double2 *)rinv;
+    const int nr = lp * lp / 2;
+    double2 v[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int f = t + i * kGramThreads;
+      v[i] = f < nr ? src[f] : make_double2(0.0, 0.0);
     }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int f = t + i * kGramThreads;
+      if (f < nr) {
+        const int r = (2 * f) / lp, c = 2 * f - r * lp;
+        Rl[r * RS + c] = v[i].x;
+        Rl[r * RS + c + 1] = v[i].y;
+      }
+    }
+  }
   __syncthreads();
   if (rinv) {
     const int rb = 16 * wave;
@@ -444,8 +530,18 @@ __global__ void __launch_bounds__(256)
     gram_reduce_kernel(const double *__restrict__ gpart, int parts, int lp2, double *__restrict__ g) {
   const int e = blockIdx.x * 32 + (threadIdx.x >> 3), j = threadIdx.x & 7;
   double s = 0.0;
-  if (e < lp2)
-    for (int q = j; q < parts; q += 8) s += gpart[(int64_t)q * lp2 + e];
+  if (e < lp2) {
+    // parts j, j + 8, ... in order, eight loads in flight per step
+    int q = j;
+    for (; q + 56 < parts; q += 64) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = gpart[(int64_t)(q + 8 * u) * lp2 + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; q < parts; q += 8) s += gpart[(int64_t)q * lp2 + e];
+  }
   s = group8_sum(s);
   if (e < lp2 && j == 0) g[e] = s;
 }
@@ -558,9 +654,21 @@ __global__ void __launch_bounds__(kCholThreads)
   __shared__ int dead[kLpMax];
   __shared__ double tol_s;
   const int t = threadIdx.x;
-  for (int e = t; e < l * l; e += kCholThreads) {
-    const int p = e / l, x = e - (e / l) * l;
-    C[p][x] = x >= p ? g[p * lp + x] : 0.0;
+  {
+    // upper triangle of G (the lower part of C starts as zeros), all of a
+    // thread's loads in flight together
+    constexpr int PER = (kLpMax * kLpMax + kCholThreads - 1) / kCholThreads;
+    double v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = t + u * kCholThreads, p = e / l, x = e - (e / l) * l;
+      v[u] = (e < l * l && x >= p) ? g[p * lp + x] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = t + u * kCholThreads, p = e / l, x = e - (e / l) * l;
+      if (e < l * l) C[p][x] = v[u];
+    }
   }
   __syncthreads();
   if (t < 64) {
@@ -1088,10 +1196,10 @@ __global__ void __launch_bounds__(kOsThreads)
   __shared__ int rank_s[N];
   __shared__ int rotated;
   const int t = threadIdx.x, grp = t >> 3, j = t & 7;
-  for (int i = t; i < lp * lp; i += kOsThreads) {
+  stage_batched<(N * N + kOsThreads - 1) / kOsThreads>(X, lcol, lp * lp, [](int i) { return i; }, [](int i) {
     const int c = i / lp, r = i - (i / lp) * lp;
-    X[c * CS + (r / E) * E2 + r % E] = lcol[i];
-  }
+    return c * CS + (r / E) * E2 + r % E;
+  });
   const double delta = shift[0];
   for (int sweep = 0; sweep < max_sweeps; ++sweep) {
     if (t == 0) rotated = 0;
@@ -1226,11 +1334,10 @@ __global__ void __launch_bounds__(kThreads)
   const bool active = rg < groups;
   const int64_t r0 = blockIdx.x * chunk_rows;
   const int nrows = (int)std::min<int64_t>(chunk_rows, m - r0);
-  for (int i = t; i < l * k; i += kThreads) E[i / k][i % k] = evec[(i / k) * lp + i % k];
-  for (int idx = t; idx < nrows * l; idx += kThreads) {
-    const int rr = idx / l, cc = idx % l;
-    qs[rr][cc] = q[(r0 + rr) * l + cc];
-  }
+  stage_batched<16>(&E[0][0], evec, l * k, [=](int i) { return (i / k) * lp + i % k; },
+                    [=](int i) { return (i / k) * kLpMax + i % k; });
+  stage_batched<16>(&qs[0][0], q + r0 * l, nrows * l, [](int i) { return i; },
+                    [=](int i) { return (i / l) * (kLpMax + 1) + i % l; });
   __syncthreads();
   float best_abs = -1.0f, best_val = 0.0f;
   int best_idx = 0x7FFFFFFF;
@@ -1279,7 +1386,7 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // V[j][c] = (sum_t B^T[j][t] E[t][c]) / sigma_c   (0 for dropped sigma), with
-// the same 16-rows-per-thread blocking.
+// the same 16-rows-per-thread blocking (the fp64 sum is scaled once).
 __global__ void __launch_bounds__(kThreads)
     assemble_v_kernel(const float *__restrict__ bt, int64_t n, int l, int lp, int k, const double *__restrict__ evec,
                       const double *__restrict__ sig_inv, float *__restrict__ V) {
@@ -1291,11 +1398,11 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t chunk_rows = asm_chunk_rows(k);
   const int64_t r0 = blockIdx.x * chunk_rows;
   const int nrows = (int)std::min<int64_t>(chunk_rows, n - r0);
-  for (int i = t; i < l * k; i += kThreads) E[i / k][i % k] = evec[(i / k) * lp + i % k] * sig_inv[i % k];
-  for (int idx = t; idx < nrows * l; idx += kThreads) {
-    const int rr = idx / l, cc = idx % l;
-    bs[rr][cc] = bt[(r0 + rr) * l + cc];
-  }
+  const double sc = rg < groups ? sig_inv[c] : 0.0;
+  stage_batched<16>(&E[0][0], evec, l * k, [=](int i) { return (i / k) * lp + i % k; },
+                    [=](int i) { return (i / k) * kLpMax + i % k; });
+  stage_batched<16>(&bs[0][0], bt + r0 * l, nrows * l, [](int i) { return i; },
+                    [=](int i) { return (i / l) * (kLpMax + 1) + i % l; });
   __syncthreads();
   if (rg >= groups) return;
   double acc[kAsmRows];
@@ -1309,7 +1416,7 @@ __global__ void __launch_bounds__(kThreads)
   }
 #pragma unroll
   for (int r = 0; r < kAsmRows; ++r)
-    if (rbase + r < nrows) V[(r0 + rbase + r) * k + c] = (float)acc[r];
+    if (rbase + r < nrows) V[(r0 + rbase + r) * k + c] = (float)(acc[r] * sc);
 }
 
 // sign[c] = -1 if the largest-|U[:, c]| entry (lowest row on ties) is negative
@@ -1325,14 +1432,26 @@ __global__ void __launch_bounds__(1024)
   float ba = -1.0f, bv = 0.0f;
   int bi = 0x7FFFFFFF;
   if (c < k) {
-#pragma unroll 4
-    for (int p = g; p < parts; p += 8) {
-      const float v = am_val[p * k + c];
-      const int i = am_idx[p * k + c];
-      if (fabsf(v) > ba || (fabsf(v) == ba && i < bi)) {
-        ba = fabsf(v);
-        bv = v;
-        bi = i;
+    // sixteen partials per batch, their loads in flight together
+    constexpr int PER = 16;
+    for (int p0 = g; p0 < parts; p0 += 8 * PER) {
+      float vv[PER];
+      int ii[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int p = p0 + 8 * u;
+        vv[u] = p < parts ? am_val[p * k + c] : 0.0f;
+        ii[u] = p < parts ? am_idx[p * k + c] : 0x7FFFFFFF;
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const float v = vv[u];
+        const int i = ii[u];
+        if (p0 + 8 * u < parts && (fabsf(v) > ba || (fabsf(v) == ba && i < bi))) {
+          ba = fabsf(v);
+          bv = v;
+          bi = i;
+        }
       }
     }
   }
@@ -1399,10 +1518,12 @@ __global__ void __launch_bounds__(kThreads)
   const float sg = sign[c];
   const float mult = isv ? S[c] : 1.0f;
   float v[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) v[i] = X[(blk * B + i) * k + c];  // all loads before the first store
+#pragma unroll
   for (int i = 0; i < B; ++i) {
-    float* p = X + (blk * B + i) * k + c;
-    v[i] = *p * sg;
-    *p = v[i];
+    v[i] *= sg;
+    X[(blk * B + i) * k + c] = v[i];
     unsigned short h, w;
     split_bf16(v[i] * mult, h, w);
     hl[(blk * B + i) * kp + c] = h;
