@@ -8,11 +8,15 @@ A step is the whole hot path over one batch of synthetic, HBM-resident input:
     dY_down; k = 64, l = 80, Gaussian sketch; residual in both orientations);
   * six GEMMs with their low-rank corrections: Y = X W^T, dX = dY W,
     dW = dY^T X for both layers (6 x 962.07 GFLOP).
-value = sum(2 M N K) / step time. The work runs on three streams (lanes); each
-GEMM sits in a lane behind a split of its own and waits for the splits it
-reads from the other lanes, so GEMMs overlap the splits still running. Work
-is enqueued in dependency order (every GEMM after the splits it reads), and a
-step starts when every lane has finished the previous one.
+value = sum(2 M N K) / step time. Each split runs on a stream (lane) of its
+own, so the six splits' latency-bound l x l stages (Cholesky, Jacobi) run
+side by side on six CUs; each GEMM follows one of its operands' splits in
+that lane and waits for the other's, so the up-projection GEMMs overlap the
+down-projection splits. Work is enqueued in dependency order, and a step
+starts when every lane has finished the previous one. Seven streams (six
+lanes and the default stream) each get a hardware queue of their own: the
+HIP runtime is asked for 8 queues (GPU_MAX_HW_QUEUES) before it starts, as
+two streams that share a queue run one after the other.
 
 Prints one JSON line. Usage: python bench.py [--steps K] [--warmup W]
 
@@ -36,6 +40,7 @@ sys.path.insert(0, ROOT)
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 MFMA
 HBM_PEAK_GBS = 8000.0
 CFG = 4
+HW_QUEUES = 8
 GEMM_SOURCE = os.path.join(ROOT, "fp4_spectral_split_amd", "csrc", "linear.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_mx_kernel_llama3-8b-ffn_traffic.md")
 
@@ -129,6 +134,8 @@ def main():
               "would shard); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    # one hardware queue per lane (read by the HIP runtime when it starts)
+    os.environ["GPU_MAX_HW_QUEUES"] = str(max(HW_QUEUES, int(os.environ.get("GPU_MAX_HW_QUEUES", "4"))))
     import numpy as np
     import torch
 
@@ -158,11 +165,12 @@ def main():
         gobj[out] = g
         outs[out] = torch.empty(g.rows, g.cols, dtype=torch.float32, device=dev)
 
-    lanes = [torch.cuda.Stream(dev) for _ in range(3)]
+    lanes = [torch.cuda.Stream(dev) for _ in range(6)]
     # (lane, kind, name) in an order where every GEMM follows the splits it reads
-    order = [(0, "split", "X_up"), (1, "split", "W_up"), (2, "split", "dY_up"), (0, "split", "X_down"),
-             (1, "gemm", "Y_up"), (2, "gemm", "dX_up"), (2, "gemm", "dW_up"), (1, "split", "W_down"),
-             (2, "split", "dY_down"), (0, "gemm", "Y_down"), (1, "gemm", "dX_down"), (2, "gemm", "dW_down")]
+    order = [(0, "split", "W_up"), (1, "split", "X_up"), (2, "split", "dY_up"),
+             (1, "gemm", "Y_up"), (2, "gemm", "dX_up"), (0, "gemm", "dW_up"),
+             (3, "split", "W_down"), (4, "split", "X_down"), (5, "split", "dY_down"),
+             (4, "gemm", "Y_down"), (5, "gemm", "dX_down"), (3, "gemm", "dW_down")]
     gemm_of = {g[0]: g for g in gemms}
     assert sorted(n for _, k, n in order if k == "split") == sorted(names)
     assert sorted(n for _, k, n in order if k == "gemm") == sorted(gemm_of)

@@ -436,12 +436,12 @@ constexpr int NV_LDS = 2 * NV_STAGE_BYTES;
 static_assert(2 * BM * EPI_ROWB <= MX_LDS && 2 * BM * EPI_ROWB <= NV_LDS, "epilogue panels must fit the main-loop LDS");
 static_assert(NV_LDS <= 160 * 1024, "LDS budget of one CU");
 
-__device__ __forceinline__ void tile_coords(int &tm, int &tn, int mt, int nt) {
+__device__ __forceinline__ void tile_coords_of(int &tm, int &tn, int w, int nwg, int mt, int nt) {
   // XCD-aware order: consecutive dispatch ids go round-robin over the 8 XCDs;
   // regroup so each XCD walks a contiguous range of tiles, grouped 8 tile-rows
-  // at a time (A and B tiles in flight on one XCD share its L2).
-  int w = blockIdx.x;
-  const int nwg = gridDim.x;
+  // at a time (A and B tiles in flight on one XCD share its L2). w is the
+  // tile's dispatch id among nwg; a persistent workgroup b that takes tiles
+  // b, b + G, ... (G a multiple of 8) stays on the XCD of those ids.
   if ((nwg & 7) == 0) w = (w & 7) * (nwg >> 3) + (w >> 3);
   constexpr int GM = 8;
   const int group = GM * nt;
@@ -450,6 +450,10 @@ __device__ __forceinline__ void tile_coords(int &tm, int &tn, int mt, int nt) {
   const int in = w - g * group;
   tm = first + in % gm;
   tn = in / gm;
+}
+
+__device__ __forceinline__ void tile_coords(int &tm, int &tn, int mt, int nt) {
+  tile_coords_of(tm, tn, blockIdx.x, gridDim.x, mt, nt);
 }
 
 // Both GEMM kernels: 256 x 256 output tile per workgroup of 512 threads,
@@ -744,6 +748,7 @@ __device__ __forceinline__ void epilogue_mx4(floatx16 (&acc)[MXW][MXW], uint8_t 
 // per row, the same swizzle), consumed by bf16 32x32x16 MFMAs, so its loads
 // overlap the end of the main product instead of following it.
 constexpr int kDmaStages = 4;
+constexpr unsigned kMxMaxGrid = 1u << 30;  // workgroups of the persistent MXFP4 kernel (a multiple of 8)
 constexpr int DMA_CODE_BYTES = BM * 64;            // one operand's codes per stage
 constexpr int DMA_STAGE = 2 * DMA_CODE_BYTES;      // A then B
 constexpr int DMA_SCALE_GROUP = 2 * BM * 16;       // A then B scales of four stages
@@ -792,8 +797,11 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
   const int wave = t >> 6, lane = t & 63;
   const int r32 = lane & 31, h = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
+  const int mtiles = (int)cdiv(M, BM), ntiles_n = (int)cdiv(N, BN), ntiles = mtiles * ntiles_n;
+  // persistent: workgroup b takes tiles b, b + gridDim.x, ...
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
   int tm, tn;
-  tile_coords(tm, tn, (int)cdiv(M, BM), (int)cdiv(N, BN));
+  tile_coords_of(tm, tn, tile, ntiles, mtiles, ntiles_n);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t nb = T / 32;
   const int nst = (int)(T / 128);
@@ -989,6 +997,8 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
   }
   __syncthreads();  // the epilogue reuses the ring
   epilogue_mx4(acc, smem, m0, n0, M, N, nullptr, nullptr, 0, C, ldc);
+  __syncthreads();  // the next tile's loads overwrite the staging area
+  }
 }
 
 // NVFP4: codes and E4M3 block scales are decoded exactly to bf16 while being
@@ -1175,8 +1185,8 @@ metis_status_t gemm_main(const Side &a, const Side &b, float *C, int64_t ldc, co
                                           b.R->scales, b.R->tensor_scale, b.rows, a.T, l1, l2, rp, C, ldc);
   else if (a.T % 512 == 0 && ((uintptr_t)a.R->codes | (uintptr_t)b.R->codes | (uintptr_t)a.R->scales |
                               (uintptr_t)b.R->scales) % 16 == 0)
-    gemm_mx_kernel<<<tiles, kMxThreads, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows,
-                                                 a.T, l1, l2, rp, C, ldc);
+    gemm_mx_kernel<<<std::min<unsigned>(tiles, kMxMaxGrid), kMxThreads, 0, st>>>(
+        a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows, a.T, l1, l2, rp, C, ldc);
   else
     gemm_mx8_kernel<<<tiles, kGemmThreads, 0, st>>>(a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales,
                                                     b.rows, a.T, l1, l2, rp, C, ldc);
