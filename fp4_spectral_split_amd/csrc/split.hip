@@ -1633,12 +1633,26 @@ __global__ void __launch_bounds__(kThreads)
         uh[ks][rs] = ok ? *(const ushortx8 *)pu : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
         ul[ks][rs] = ok ? *(const ushortx8 *)(pu + um) : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
       }
-    for (int idx = t; idx < 2 * kRT * (kp / 8); idx += kThreads) {
-      const int h = idx / (kRT * (kp / 8)), rem = idx % (kRT * (kp / 8));
-      const int c = rem / (kp / 8), q = rem % (kp / 8);
-      const int64_t col = col0 + c;
-      const uint4 v = col < n ? *(const uint4 *)(whl + h * wn + col * kp + q * 8) : uint4{0u, 0u, 0u, 0u};
-      *(uint4 *)(wst + (h * kRT + c) * wstride + q * 8) = v;
+    {
+      // the panel's 16-byte pieces, all of a thread's loads in flight together
+      constexpr int PW = 2 * kRT * (KPM / 8) / kThreads;
+      const int nw = 2 * kRT * (kp / 8);
+      uint4 v[PW];
+#pragma unroll
+      for (int u = 0; u < PW; ++u) {
+        const int idx = t + u * kThreads;
+        const int h = idx / (kRT * (kp / 8)), rem = idx % (kRT * (kp / 8));
+        const int c = rem / (kp / 8), q = rem % (kp / 8);
+        const int64_t col = col0 + c;
+        v[u] = (idx < nw && col < n) ? *(const uint4 *)(whl + h * wn + col * kp + q * 8) : uint4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < PW; ++u) {
+        const int idx = t + u * kThreads;
+        const int h = idx / (kRT * (kp / 8)), rem = idx % (kRT * (kp / 8));
+        const int c = rem / (kp / 8), q = rem % (kp / 8);
+        if (idx < nw) *(uint4 *)(wst + (h * kRT + c) * wstride + q * 8) = v[u];
+      }
     }
     __syncthreads();
     floatx4 acc[2][8];
@@ -1703,15 +1717,23 @@ __global__ void __launch_bounds__(kThreads)
   }
   if (!tcodes) return;
   __syncthreads();
-  // ---- column blocks (along m) into R^T (n x m)
-  for (int b = t; b < kRT * RPB; b += kThreads) {
-    const int cc = b % kRT, rb = b / kRT;
-    const int64_t col = col0 + cc, row = row0 + rb * B;
-    if (col >= n || row >= m) continue;
-    float v[B];
+  // ---- column blocks (along m) into R^T (n x m): thread t takes
+  // consecutive row blocks of column t % kRT, so its code stores are
+  // adjacent in R^T's row
+  {
+    constexpr int PER = kRT * RPB / kThreads;  // row blocks per thread
+    const int cc = t % kRT, rb0 = (t / kRT) * PER;
+    const int64_t col = col0 + cc;
 #pragma unroll
-    for (int i = 0; i < B; ++i) v[i] = lt[rb * B + i][cc];
-    quant_store<B, NV>(v, s_t, tcodes + col * (m / 2) + row / 2, tscales + col * (m / B) + row / B);
+    for (int u = 0; u < PER; ++u) {
+      const int rb = rb0 + u;
+      const int64_t row = row0 + rb * B;
+      if (col >= n || row >= m) continue;
+      float v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) v[i] = lt[rb * B + i][cc];
+      quant_store<B, NV>(v, s_t, tcodes + col * (m / 2) + row / 2, tscales + col * (m / B) + row / B);
+    }
   }
 }
 
