@@ -106,70 +106,81 @@ __device__ __forceinline__ floatx16 mfma_fp4(const uint4 a, const uint4 b, int s
 
 // ================================================================== skinny
 // out[s] (rows x cols) = NT(A (rows x T), B (cols x T)) over T-chunk s, both
-// MXFP4. One wave: 32 rows x (32 * NCT) columns. Per 128-element step each
-// lane reads 32 contiguous code bytes (two scale blocks) of its row; the two
-// MFMAs take the first and second 16 bytes, so every lane's K slots line up
-// between the A and B operands. The loads of four steps are issued before
-// their MFMAs (T-chunks are multiples of 128; steps past the chunk load
-// zeros).
+// MXFP4. One wave: 32 rows x (32 * NCT) columns, 512 contraction elements
+// per step: lane (r, h) owns elements [t0 + 256 h, t0 + 256 h + 256) of its
+// row, eight scale blocks, read as eight 16-byte code pieces and (when a row's
+// scale count is a multiple of four) two 32-bit scale words. MFMA c of a step
+// takes block c of every lane's span from A and from B alike, so the K slots
+// of the two operands line up; its scale byte is picked from the word by
+// opsel. Blocks past the chunk read zero codes (any scale).
+__device__ __forceinline__ void skinny_load_span(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                                 int64_t row, bool rok, int64_t e0, int64_t t_end, int64_t T,
+                                                 bool word_scales, uint4 (&c)[8], uint32_t (&w)[2]) {
+  const int64_t nb = T / 32;
+  const uint4 *p = (const uint4 *)(codes + row * (T / 2) + e0 / 2);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) c[q] = (rok && e0 + 32 * q < t_end) ? p[q] : uint4{0u, 0u, 0u, 0u};
+  const uint8_t *ps = scales + row * nb + e0 / 32;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (word_scales) {
+      w[q] = (rok && e0 + 128 * q < t_end) ? *(const uint32_t *)(ps + 4 * q) : 0x7F7F7F7Fu;
+    } else {
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = rok && e0 + 32 * (4 * q + i) < t_end;
+        v |= (ok ? (uint32_t)ps[4 * q + i] : 127u) << (8 * i);
+      }
+      w[q] = v;
+    }
+  }
+}
+
+template <int C>
+__device__ __forceinline__ floatx16 skinny_mfma(const uint4 &a, const uint4 &b, uint32_t sa, uint32_t sb, floatx16 acc) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4x32(a), fp4x32(b), acc, 4, 4, C % 4, (int)sa, C % 4,
+                                                          (int)sb);
+}
+
 template <int NCT>
 __global__ void __launch_bounds__(64)
     skinny_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t rows,
                   const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int cols, int64_t T, int64_t chunk,
                   float *__restrict__ out) {
-  constexpr int U = 4;
   const int lane = threadIdx.x;
   const int r = lane & 31, h = lane >> 5;
   const int64_t row = (int64_t)blockIdx.x * 32 + r;
   const int s = blockIdx.y;
   const int64_t t_beg = (int64_t)s * chunk, t_end = std::min<int64_t>(T, t_beg + chunk);
-  const int64_t nb = T / 32;  // scale blocks per row
+  const bool word_scales = ((T / 32) & 3) == 0;
   floatx16 acc[NCT];
 #pragma unroll
   for (int j = 0; j < NCT; ++j)
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[j][q] = 0.0f;
   const bool rok = row < rows;
-  for (int64_t t0 = t_beg; t0 < t_end; t0 += 128 * U) {
-    uint4 a[U][2], b[U][NCT][2];
-    int sa[U][2], sb[U][NCT][2];
+  for (int64_t t0 = t_beg; t0 < t_end; t0 += 512) {
+    const int64_t e0 = t0 + 256 * h;
+    uint4 a[8], b[NCT][8];
+    uint32_t sa[2], sb[NCT][2];
+    skinny_load_span(ac, as, row, rok, e0, t_end, T, word_scales, a, sa);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t e0 = t0 + 128 * u + h * 64;  // first element of this lane's two blocks
-      a[u][0] = a[u][1] = uint4{0u, 0u, 0u, 0u};
-      sa[u][0] = sa[u][1] = 127;
-      if (rok && e0 < t_end) {
-        const uint4 *p = (const uint4 *)(ac + row * (T / 2) + e0 / 2);
-        a[u][0] = p[0];
-        sa[u][0] = as[row * nb + e0 / 32];
-        if (e0 + 32 < t_end) {
-          a[u][1] = p[1];
-          sa[u][1] = as[row * nb + e0 / 32 + 1];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        const int col = j * 32 + r;
-        b[u][j][0] = b[u][j][1] = uint4{0u, 0u, 0u, 0u};
-        sb[u][j][0] = sb[u][j][1] = 127;
-        if (col < cols && e0 < t_end) {
-          const uint4 *p = (const uint4 *)(bc + (int64_t)col * (T / 2) + e0 / 2);
-          b[u][j][0] = p[0];
-          sb[u][j][0] = bs[(int64_t)col * nb + e0 / 32];
-          if (e0 + 32 < t_end) {
-            b[u][j][1] = p[1];
-            sb[u][j][1] = bs[(int64_t)col * nb + e0 / 32 + 1];
-          }
-        }
-      }
+    for (int j = 0; j < NCT; ++j) {
+      const int col = j * 32 + r;
+      skinny_load_span(bc, bs, col, col < cols, e0, t_end, T, word_scales, b[j], sb[j]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        acc[j] = mfma_fp4(a[u][0], b[u][j][0], sa[u][0], sb[u][j][0], acc[j]);
-        acc[j] = mfma_fp4(a[u][1], b[u][j][1], sa[u][1], sb[u][j][1], acc[j]);
-      }
+    for (int j = 0; j < NCT; ++j) {
+      acc[j] = skinny_mfma<0>(a[0], b[j][0], sa[0], sb[j][0], acc[j]);
+      acc[j] = skinny_mfma<1>(a[1], b[j][1], sa[0], sb[j][0], acc[j]);
+      acc[j] = skinny_mfma<2>(a[2], b[j][2], sa[0], sb[j][0], acc[j]);
+      acc[j] = skinny_mfma<3>(a[3], b[j][3], sa[0], sb[j][0], acc[j]);
+      acc[j] = skinny_mfma<0>(a[4], b[j][4], sa[1], sb[j][1], acc[j]);
+      acc[j] = skinny_mfma<1>(a[5], b[j][5], sa[1], sb[j][1], acc[j]);
+      acc[j] = skinny_mfma<2>(a[6], b[j][6], sa[1], sb[j][1], acc[j]);
+      acc[j] = skinny_mfma<3>(a[7], b[j][7], sa[1], sb[j][1], acc[j]);
+    }
   }
   float *o = out + (int64_t)s * rows * cols;
 #pragma unroll
@@ -344,6 +355,20 @@ __device__ __forceinline__ void panel_factor_values(const uint8_t *__restrict__ 
   }
 }
 
+// Rows [0, nr) of a panel (row stride rp, a multiple of 8) from value(r, c),
+// eight columns per 16-byte store.
+template <typename Value>
+__device__ __forceinline__ void panel_write_rows(unsigned short *__restrict__ dst, int nr, int rp, Value value) {
+  const int pieces = rp / 8;
+  for (int e = threadIdx.x; e < nr * pieces; e += kPanelThreads) {
+    const int r = e / pieces, c0 = (e - r * pieces) * 8;
+    ushortx8 v;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = value(r, c0 + u);
+    *(ushortx8 *)(dst + (int64_t)r * rp + c0) = v;
+  }
+}
+
 template <bool NV>
 __global__ void __launch_bounds__(kPanelThreads)
     panel_kernel(int64_t ra, int64_t rb, int ka, int kb, int rp, const float *__restrict__ ppart, int ks_p,
@@ -373,19 +398,16 @@ __global__ void __launch_bounds__(kPanelThreads)
     panel_factor_values<NV>(ga_c, ga_s, ra, ka, i0, nr, [&](int c, int r, float v) { gv[r][c] = v; });
     __syncthreads();
     const float fold_b = ts_s[1];
-    for (int e = t; e < nr * rp; e += kPanelThreads) {
-      const int r = e / rp, c = e - (e / rp) * rp;
-      unsigned short v = 0;
+    panel_write_rows(l1 + i0 * rp, nr, rp, [&](int r, int c) -> unsigned short {
       if (c < 2 * kb) {
         unsigned short hi, lo;
-        const int d = c % kb;
+        const int d = c < kb ? c : c - kb;
         split_bf16(fv[r][d] * sb_s[d] * fold_b, hi, lo);
-        v = c < kb ? hi : lo;
-      } else if (c < 2 * kb + 2 * ka) {
-        v = f32_to_bf16(gv[r][(c - 2 * kb) % ka]);
+        return c < kb ? hi : lo;
       }
-      l1[(i0 + r) * rp + c] = v;
-    }
+      c -= 2 * kb;
+      return c < 2 * ka ? f32_to_bf16(gv[r][c < ka ? c : c - ka]) : (unsigned short)0;
+    });
   } else {
     const int64_t j0 = ((int64_t)blockIdx.x - l1_blocks) * R;
     const int nr = (int)min<int64_t>(R, rb - j0);
@@ -401,25 +423,33 @@ __global__ void __launch_bounds__(kPanelThreads)
       gv[r][d] = fv[r][d] * tsb * sb_s[d];
     }
     __syncthreads();
-    for (int e = t; e < nr * ka; e += kPanelThreads) {
-      const int r = e / ka, cc = e - (e / ka) * ka;
-      float q = qv[r][cc];
-      for (int d = 0; d < kb; ++d) q += gv[r][d] * cross[cc][d];
-      qv[r][cc] = q * sa_s[cc] * fold_a;
+    // Q[r][cc] += sum_d gv[r][d] cross[cc][d]: a thread owns one cc and
+    // eight rows, so each cross value feeds eight FMAs (the gv reads are
+    // broadcasts within the wave)
+    for (int idx = t; idx < ka * (R / 8); idx += kPanelThreads) {
+      const int cc = idx % ka, r0 = (idx / ka) * 8;
+      float q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = qv[r0 + i][cc];
+      for (int d = 0; d < kb; ++d) {
+        const float x = cross[cc][d];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] += gv[r0 + i][d] * x;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[r0 + i][cc] = q[i] * sa_s[cc] * fold_a;
     }
     __syncthreads();
-    for (int e = t; e < nr * rp; e += kPanelThreads) {
-      const int r = e / rp, c = e - (e / rp) * rp;
-      unsigned short v = 0;
-      if (c < 2 * kb) {
-        v = f32_to_bf16(fv[r][c % kb]);
-      } else if (c < 2 * kb + 2 * ka) {
+    panel_write_rows(l2 + j0 * rp, nr, rp, [&](int r, int c) -> unsigned short {
+      if (c < 2 * kb) return f32_to_bf16(fv[r][c < kb ? c : c - kb]);
+      c -= 2 * kb;
+      if (c < 2 * ka) {
         unsigned short hi, lo;
-        split_bf16(qv[r][(c - 2 * kb) % ka], hi, lo);
-        v = c < 2 * kb + ka ? hi : lo;
+        split_bf16(qv[r][c < ka ? c : c - ka], hi, lo);
+        return c < ka ? hi : lo;
       }
-      l2[(j0 + r) * rp + c] = v;
-    }
+      return (unsigned short)0;
+    });
   }
 }
 

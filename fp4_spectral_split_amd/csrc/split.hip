@@ -636,7 +636,9 @@ __global__ void __launch_bounds__(kThreads)
 // every column of L nonzero, so every eigenvector comes out of the rotations.
 // shift[0] = delta.
 constexpr int kCholThreads = 1024;
-constexpr int kCholSlots = kLpMax * kLpMax / kCholThreads;  // 9 elements per thread at lp = 96
+// a row is shared by floor(threads / l) threads; each owns every tpr-th
+// column of it: at most 10 columns (l = 96)
+constexpr int kCholSlots = 10;
 
 __device__ __forceinline__ double recip_f64(double d) {
   double r = __builtin_amdgcn_rcp(d);  // hardware estimate, refined by Newton steps
@@ -687,50 +689,54 @@ __global__ void __launch_bounds__(kCholThreads)
   __syncthreads();
   if (t == 0) {
     const double d = C[0][0];
-    const bool alive = d > tol_s;
-    ipiv[0] = alive ? recip_f64(d) : 0.0;
-    rs[0] = alive ? 1.0 / sqrt(d) : 0.0;
-    dead[0] = !alive;
+    ipiv[0] = d > tol_s ? recip_f64(d) : 0.0;
   }
-  // owned elements: e = t + s * threads, row p = e / l, column x = e % l
+  // owned elements: row p = t / tpr, columns x = q + tpr s (q = t % tpr), so
+  // the multiplier G'[j][p] / d_j is one load per step and the row-j values
+  // C[j][x] read by a wave are a handful of broadcast addresses
+  const int tpr = kCholThreads / l;
+  const int p = t / tpr, q = t - (t / tpr) * tpr;
   double v[kCholSlots];
-  int pr[kCholSlots], xc[kCholSlots];
-#pragma unroll
-  for (int s = 0; s < kCholSlots; ++s) {
-    const int e = t + s * kCholThreads;
-    const bool ok = e < l * l;
-    pr[s] = ok ? e / l : -1;
-    xc[s] = ok ? e - (e / l) * l : 0;
-  }
   __syncthreads();
   const double tol = tol_s;
 #pragma unroll
-  for (int s = 0; s < kCholSlots; ++s) v[s] = pr[s] >= 0 ? C[pr[s]][xc[s]] : 0.0;
+  for (int s = 0; s < kCholSlots; ++s) {
+    const int x = q + tpr * s;
+    v[s] = (p < l && x < l) ? C[p][x] : 0.0;
+  }
   for (int j = 0; j + 1 < l; ++j) {
     const double ij = ipiv[j];
+    if (p > j && p < l) {
+      const double m = C[j][p] * ij;
 #pragma unroll
-    for (int s = 0; s < kCholSlots; ++s) {
-      const int p = pr[s], x = xc[s];
-      if (p > j && ((!FACTOR && x <= j) || x >= p)) {
-        const double w = x == j ? 1.0 : C[j][x];
-        v[s] = fma(-(C[j][p] * ij), w, v[s]);
+      for (int s = 0; s < kCholSlots; ++s) {
+        const int x = q + tpr * s;
+        if (x < l && ((!FACTOR && x <= j) || x >= p)) {
+          const double w = x == j ? 1.0 : C[j][x];
+          v[s] = fma(-m, w, v[s]);
+        }
       }
     }
+    if (p == j + 1) {
 #pragma unroll
-    for (int s = 0; s < kCholSlots; ++s) {
-      if (pr[s] == j + 1) {
-        C[j + 1][xc[s]] = v[s];
-        if (xc[s] == j + 1) {
-          const double d = v[s];
-          const bool alive = d > tol;
-          ipiv[j + 1] = alive ? recip_f64(d) : 0.0;
-          rs[j + 1] = alive ? 1.0 / sqrt(d) : 0.0;
-          dead[j + 1] = !alive;
+      for (int s = 0; s < kCholSlots; ++s) {
+        const int x = q + tpr * s;
+        if (x < l) {
+          C[j + 1][x] = v[s];
+          if (x == j + 1) ipiv[j + 1] = v[s] > tol ? recip_f64(v[s]) : 0.0;
         }
       }
     }
     __syncthreads();
   }
+  // pivots d_j sit on the diagonal of the published rows
+  for (int j = t; j < l; j += kCholThreads) {
+    const double d = C[j][j];
+    const bool alive = d > tol;
+    rs[j] = alive ? 1.0 / sqrt(d) : 0.0;
+    dead[j] = !alive;
+  }
+  __syncthreads();
   if (FACTOR) {
     // column j of L = row j of R: R[j][x] = G'[j][x] * d_j^-1/2 for x >= j
     for (int e = t; e < lp * lp; e += kCholThreads) {
