@@ -1198,6 +1198,7 @@ __global__ void __launch_bounds__(kOsThreads)
                      double *__restrict__ evec, double *__restrict__ sig_inv, float *__restrict__ S) {
   constexpr int E2 = os_e2(E), CS = 8 * E2, N = 8 * E, H = 4 * E, lp = N, EH = E / 2;
   __shared__ __align__(16) double X[N * CS];
+  __shared__ double nrm[N];  // squared column norms, carried from round 0 of a sweep
   __shared__ double lam[N];
   __shared__ int rank_s[N];
   __shared__ int rotated;
@@ -1217,25 +1218,38 @@ __global__ void __launch_bounds__(kOsThreads)
         b = b >= N - 1 ? b - (N - 1) : b;
         a = grp == 0 ? 0 : a + 1;
         b = b + 1;
-        double2 *xpp = (double2 *)(X + (a < b ? a : b) * CS + j * E2);
-        double2 *xqp = (double2 *)(X + (a < b ? b : a) * CS + j * E2);
+        const int cp = a < b ? a : b, cq = a < b ? b : a;
+        double2 *xpp = (double2 *)(X + cp * CS + j * E2);
+        double2 *xqp = (double2 *)(X + cq * CS + j * E2);
         double2 xp[EH], xq[EH];
 #pragma unroll
         for (int e = 0; e < EH; ++e) {
           xp[e] = xpp[e];
           xq[e] = xqp[e];
         }
-        double al0 = 0.0, al1 = 0.0, be0 = 0.0, be1 = 0.0, ga0 = 0.0, ga1 = 0.0;
+        double ga0 = 0.0, ga1 = 0.0;
 #pragma unroll
         for (int e = 0; e < EH; ++e) {
-          al0 = fma(xp[e].x, xp[e].x, al0);
-          al1 = fma(xp[e].y, xp[e].y, al1);
-          be0 = fma(xq[e].x, xq[e].x, be0);
-          be1 = fma(xq[e].y, xq[e].y, be1);
           ga0 = fma(xp[e].x, xq[e].x, ga0);
           ga1 = fma(xp[e].y, xq[e].y, ga1);
         }
-        const double al = group8_sum(al0 + al1), be = group8_sum(be0 + be1), ga = group8_sum(ga0 + ga1);
+        const double ga = group8_sum(ga0 + ga1);
+        double al, be;
+        if (round == 0) {
+          double al0 = 0.0, al1 = 0.0, be0 = 0.0, be1 = 0.0;
+#pragma unroll
+          for (int e = 0; e < EH; ++e) {
+            al0 = fma(xp[e].x, xp[e].x, al0);
+            al1 = fma(xp[e].y, xp[e].y, al1);
+            be0 = fma(xq[e].x, xq[e].x, be0);
+            be1 = fma(xq[e].y, xq[e].y, be1);
+          }
+          al = group8_sum(al0 + al1);
+          be = group8_sum(be0 + be1);
+        } else {
+          al = nrm[cp];
+          be = nrm[cq];
+        }
         if (ga != 0.0 && ga * ga > 1e-26 * al * be) {
           // angle from hardware estimates (fp32-level accuracy is ample: a
           // pair left slightly non-orthogonal is rotated again next sweep);
@@ -1261,7 +1275,16 @@ __global__ void __launch_bounds__(kOsThreads)
             xpp[e] = np[e];
             xqp[e] = nq[e];
           }
-          if (j == 0) rotated = 1;
+          if (j == 0) {
+            // norms after the applied rotation (exact for the t used)
+            const double c2 = c * c;
+            nrm[cp] = c2 * fma(-tt, fma(-tt, be, 2.0 * ga), al);
+            nrm[cq] = c2 * fma(tt, fma(tt, al, 2.0 * ga), be);
+            rotated = 1;
+          }
+        } else if (round == 0 && j == 0) {
+          nrm[cp] = al;
+          nrm[cq] = be;
         }
       }
       __syncthreads();
