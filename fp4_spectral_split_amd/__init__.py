@@ -72,6 +72,10 @@ def load():
     L.metis_split_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
     L.metis_split.restype = i32
     L.metis_split.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, i32, ctypes.POINTER(_Split), vp, vp, sz, vp]
+    L.metis_mean_split_workspace_bytes.restype = sz
+    L.metis_mean_split_workspace_bytes.argtypes = [i64, i64, i32]
+    L.metis_mean_split.restype = i32
+    L.metis_mean_split.argtypes = [vp, i32, i64, i64, i64, i32, ctypes.POINTER(_Split), vp, sz, vp]
     L.metis_linear_workspace_bytes.restype = sz
     L.metis_linear_workspace_bytes.argtypes = [ctypes.POINTER(_Split)] * 3
     L.spectral_fp4_linear_fwd.restype = i32
@@ -90,7 +94,8 @@ def load():
 
 
 EXPORTS = ["metis_status_str", "metis_abi_version", "fp4_block_quant_workspace_bytes", "fp4_block_quant",
-           "fp4_block_dequant", "metis_split_workspace_bytes", "metis_split", "metis_linear_workspace_bytes",
+           "fp4_block_dequant", "metis_split_workspace_bytes", "metis_split", "metis_mean_split_workspace_bytes",
+           "metis_mean_split", "metis_linear_workspace_bytes",
            "spectral_fp4_linear_fwd", "spectral_fp4_linear_bwd", "metis_gemm_nt_workspace_bytes",
            "metis_gemm_nt_prepare", "metis_gemm_nt_main"]
 
@@ -256,6 +261,23 @@ def metis_split(A, l, k, fmt="mxfp4", omega=None, columns=None, orientations=("n
     ws = workspace(nws, A.device)
     _check(L.metis_split(_ptr(A), _dtype_code(A), m, n, A.stride(0), _ptr(om), kind, l, k, fmt, ctypes.byref(c),
                          _ptr(rec.info), _ptr(ws), nws, _stream(A.device)))
+    return rec
+
+
+def metis_mean_split(A, fmt="mxfp4", orientations=("n", "t"), out=None):
+    """Mean-residual split of a 2-D fp32/bf16 CUDA tensor A (m x n): the
+    column mean mu and A - mu, quantized separately, as a rank-1 record
+    (U = 1, S = 1, V = mu) that the GEMMs take like any split operand."""
+    L = load()
+    assert A.dim() == 2 and A.is_cuda and A.stride(1) == 1
+    m, n = A.shape
+    fmt = _FMT[fmt]
+    rec = out if out is not None else empty_split(m, n, 1, fmt, orientations, A.device)
+    c = rec.c()
+    nws = L.metis_mean_split_workspace_bytes(m, n, fmt)
+    ws = workspace(nws, A.device)
+    _check(L.metis_mean_split(_ptr(A), _dtype_code(A), m, n, A.stride(0), fmt, ctypes.byref(c), _ptr(ws), nws,
+                              _stream(A.device)))
     return rec
 
 

@@ -1613,12 +1613,15 @@ __device__ __forceinline__ void quant_store(const float (&v)[B], float s_t, uint
   *scale = (uint8_t)sb;
 }
 
-template <typename T, bool NV, bool AMAX_ONLY>
+// MEAN: the mean-residual split, L[r][c] = mu[c] (fp32, passed as `mu`)
+// instead of the MFMA product, so R = A - mu is one fp32 subtraction.
+template <typename T, bool NV, bool AMAX_ONLY, bool MEAN = false>
 __global__ void __launch_bounds__(kThreads)
     residual_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda, const unsigned short *__restrict__ uhl,
                     const unsigned short *__restrict__ whl, int kp, uint8_t *__restrict__ rcodes,
                     uint8_t *__restrict__ rscales, float *__restrict__ rts, uint8_t *__restrict__ tcodes,
-                    uint8_t *__restrict__ tscales, float *__restrict__ tts, uint32_t *__restrict__ amax) {
+                    uint8_t *__restrict__ tscales, float *__restrict__ tts, uint32_t *__restrict__ amax,
+                    const float *__restrict__ mu = nullptr) {
   constexpr int B = NV ? 16 : 32;
   __shared__ __attribute__((aligned(16))) float lt[kRT][kRT + 4];
   const int t = threadIdx.x;
@@ -1641,6 +1644,13 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
     for (int q = 0; q < VEC; ++q) apre[jb][q] = ok ? src[q] : uint4{0u, 0u, 0u, 0u};
   }
+  if constexpr (MEAN) {
+    // each thread fills half a column of the tile with mu
+    const int c = t % kRT, r0 = (t / kRT) * (kRT / 2);
+    const float v = col0 + c < n ? mu[col0 + c] : 0.0f;
+#pragma unroll 8
+    for (int r = 0; r < kRT / 2; ++r) lt[r0 + r][c] = v;
+  } else
   // ---- L tile via MFMA: wave owns rows wave*32 .. +32, all 128 columns.
   // This wave's U operands (hi, lo) are loaded into registers up front; the W
   // panel (hi, lo) of the tile's 128 columns is shared by the four waves and
@@ -1767,6 +1777,10 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // ==================================================================== host
+template <typename T, bool MEAN>
+metis_status_t run_factors_and_residual(const SplitPlan &p, const T *A, int64_t lda, metis_split_t *out,
+                                        const float *mu, hipStream_t st);
+
 template <typename T>
 metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void *omega, metis_split_t *out,
                          int32_t *info, hipStream_t st) {
@@ -1844,6 +1858,17 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     assemble_wide_kernel<<<(unsigned)cdiv(n * k, 256), 256, 0, st>>>(bt, n, l, lp, k, p.evec, p.sig_inv, out->V);
   }
   sign_kernel<<<1, 1024, 0, st>>>(p.am_val, p.am_idx, p.am_parts, k, p.sign);
+  return run_factors_and_residual<T, false>(p, A, lda, out, nullptr, st);
+}
+
+// Factor quantization (signs applied from p.sign) and the residual pass,
+// shared by the spectral and the mean-residual splits.
+template <typename T, bool MEAN>
+metis_status_t run_factors_and_residual(const SplitPlan &p, const T *A, int64_t lda, metis_split_t *out,
+                                        const float *mu, hipStream_t st) {
+  const int64_t m = p.m, n = p.n;
+  const int k = p.k, kp = p.kp;
+  const bool nv = p.fmt == METIS_NVFP4;
   const int B = nv ? 16 : 32;
   const unsigned fgrid = (unsigned)cdiv(std::max(m, n) / B * kp, kThreads);
   if (nv) {
@@ -1861,18 +1886,109 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
   // ---- pass 3: residual + quantization (NVFP4: a max pass first)
   const dim3 rgrid((unsigned)cdiv(n, kRT), (unsigned)cdiv(m, kRT));
   if (nv) {
-    residual_kernel<T, true, true><<<rgrid, kThreads, 0, st>>>(A, m, n, lda, p.uhl, p.whl, kp, nullptr, nullptr,
-                                                              nullptr, nullptr, nullptr, nullptr, p.amax + 2);
-    residual_kernel<T, true, false><<<rgrid, kThreads, 0, st>>>(
+    residual_kernel<T, true, true, MEAN><<<rgrid, kThreads, 0, st>>>(
+        A, m, n, lda, p.uhl, p.whl, kp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p.amax + 2, mu);
+    residual_kernel<T, true, false, MEAN><<<rgrid, kThreads, 0, st>>>(
         A, m, n, lda, p.uhl, p.whl, kp, out->R_q.codes, out->R_q.scales, out->R_q.tensor_scale, out->Rt_q.codes,
-        out->Rt_q.scales, out->Rt_q.tensor_scale, p.amax + 2);
+        out->Rt_q.scales, out->Rt_q.tensor_scale, p.amax + 2, mu);
   } else {
-    residual_kernel<T, false, false><<<rgrid, kThreads, 0, st>>>(A, m, n, lda, p.uhl, p.whl, kp, out->R_q.codes,
-                                                                out->R_q.scales, nullptr, out->Rt_q.codes,
-                                                                out->Rt_q.scales, nullptr, nullptr);
+    residual_kernel<T, false, false, MEAN><<<rgrid, kThreads, 0, st>>>(
+        A, m, n, lda, p.uhl, p.whl, kp, out->R_q.codes, out->R_q.scales, nullptr, out->Rt_q.codes, out->Rt_q.scales,
+        nullptr, nullptr, mu);
   }
   METIS_LAUNCH_CHECK();
   return METIS_OK;
+}
+
+// ------------------------------------------------------- mean-residual split
+// Mean over all rows of A (Averis, "Averaging-Induced Residual Splitting",
+// as retold on the zhu318.com page, method paragraphs), as a rank-1 split
+// record: U = 1, S = 1, V = mu. Column sums run in fp64, rows in order: chunk
+// c of rows is summed per column (16 bytes of columns per thread, eight rows'
+// loads in flight), then the chunks in order.
+constexpr int kMeanChunkRows = 128;
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+    colsum_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda, double *__restrict__ part) {
+  constexpr int V = 16 / (int)sizeof(T);  // columns per thread
+  const int64_t j0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+  const int c = blockIdx.y;
+  if (j0 >= n) return;
+  const int64_t r0 = (int64_t)c * kMeanChunkRows, r1 = std::min<int64_t>(m, r0 + kMeanChunkRows);
+  double s[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) s[v] = 0.0;
+  int64_t r = r0;
+  for (; r + 8 <= r1; r += 8) {
+    uint4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = *(const uint4 *)(A + (r + u) * lda + j0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const T *e = (const T *)&x[u];
+#pragma unroll
+      for (int v = 0; v < V; ++v) s[v] += (double)load_f32(e + v);
+    }
+  }
+  for (; r < r1; ++r) {
+    const uint4 x = *(const uint4 *)(A + r * lda + j0);
+    const T *e = (const T *)&x;
+#pragma unroll
+    for (int v = 0; v < V; ++v) s[v] += (double)load_f32(e + v);
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) part[(int64_t)c * n + j0 + v] = s[v];
+}
+
+// mu = (sum of the chunk sums in order) / m into V; U = 1, S = 1, sign = 1.
+__global__ void mean_finish_kernel(const double *__restrict__ part, int chunks, int64_t m, int64_t n,
+                                   float *__restrict__ V, float *__restrict__ U, float *__restrict__ S,
+                                   float *__restrict__ sign) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    double s = 0.0;
+    for (int c = 0; c < chunks; ++c) s += part[(int64_t)c * n + i];
+    V[i] = (float)(s / (double)m);
+  }
+  if (i < m) U[i] = 1.0f;
+  if (i == 0) {
+    S[0] = 1.0f;
+    sign[0] = 1.0f;
+  }
+}
+
+struct MeanPlan {
+  SplitPlan sp;  // the fields the factor and residual passes use
+  double *part;  // chunks x n
+  int chunks;
+  size_t bytes;
+};
+
+MeanPlan make_mean_plan(int64_t m, int64_t n, int fmt, int elem, void *ws) {
+  MeanPlan p{};
+  p.sp.m = m; p.sp.n = n; p.sp.l = 1; p.sp.lp = 16; p.sp.k = 1; p.sp.kp = 32;
+  p.sp.fmt = fmt; p.sp.elem = elem; p.sp.wide = false; p.sp.kind = -1;
+  p.chunks = (int)cdiv(m, kMeanChunkRows);
+  metis_host::Carver c(ws);
+  p.part = c.take<double>((size_t)p.chunks * n);
+  p.sp.sign = c.take<float>(1);
+  p.sp.uhl = c.take<unsigned short>((size_t)2 * m * p.sp.kp);
+  p.sp.whl = c.take<unsigned short>((size_t)2 * n * p.sp.kp);
+  p.sp.amax = c.take<uint32_t>(8);
+  p.bytes = c.bytes();
+  p.sp.bytes = p.bytes;
+  return p;
+}
+
+template <typename T>
+metis_status_t run_mean_split(const MeanPlan &p, const T *A, int64_t lda, metis_split_t *out, hipStream_t st) {
+  const int64_t m = p.sp.m, n = p.sp.n;
+  constexpr int V = 16 / (int)sizeof(T);
+  colsum_kernel<T><<<dim3((unsigned)cdiv(n, 256 * V), (unsigned)p.chunks), 256, 0, st>>>(A, m, n, lda, p.part);
+  mean_finish_kernel<<<(unsigned)cdiv(std::max(m, n), 256), 256, 0, st>>>(p.part, p.chunks, m, n, out->V, out->U,
+                                                                           out->S, p.sp.sign);
+  return run_factors_and_residual<T, true>(p.sp, A, lda, out, out->V, st);
 }
 
 bool fp4_ok(const metis_fp4_t &q, int fmt, bool need_ts) {
@@ -1921,4 +2037,38 @@ extern "C" metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m
   out->Rt_q.rows = n; out->Rt_q.cols = m;
   if (dt == METIS_F32) return run_split<float>(p, (const float *)A, lda, omega, out, info, stream);
   return run_split<unsigned short>(p, (const unsigned short *)A, lda, omega, out, info, stream);
+}
+
+extern "C" size_t metis_mean_split_workspace_bytes(int64_t m, int64_t n, metis_fmt_t fmt) {
+  if (m <= 0 || n <= 0) return 0;
+  return make_mean_plan(m, n, fmt, 2, nullptr).bytes;
+}
+
+extern "C" metis_status_t metis_mean_split(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                           metis_fmt_t fmt, metis_split_t *out, void *ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  if (!A || !out) return METIS_ERR_INVALID;
+  if (dt != METIS_F32 && dt != METIS_BF16) return METIS_ERR_INVALID;
+  if (fmt != METIS_MXFP4 && fmt != METIS_NVFP4) return METIS_ERR_INVALID;
+  if (m <= 0 || n <= 0 || m % 32 || n % 32 || lda < n) return METIS_ERR_INVALID;
+  const int elem = dt == METIS_F32 ? 4 : 2;
+  if (((uintptr_t)A) & 15 || (lda * elem) % 16) return METIS_ERR_INVALID;
+  if (!out->U || !out->S || !out->V) return METIS_ERR_INVALID;
+  const bool nv = fmt == METIS_NVFP4;
+  if (!fp4_ok(out->Ut_q, fmt, nv) || !fp4_ok(out->Vt_q, fmt, nv)) return METIS_ERR_INVALID;
+  if (out->R_q.codes && !fp4_ok(out->R_q, fmt, nv)) return METIS_ERR_INVALID;
+  if (out->Rt_q.codes && !fp4_ok(out->Rt_q, fmt, nv)) return METIS_ERR_INVALID;
+  if (!ws) return METIS_ERR_WORKSPACE;
+  if (((uintptr_t)ws) & 255) return METIS_ERR_INVALID;
+  MeanPlan p = make_mean_plan(m, n, fmt, elem, ws);
+  if (ws_bytes < p.bytes) return METIS_ERR_WORKSPACE;
+  out->m = m;
+  out->n = n;
+  out->k = 1;
+  out->Ut_q.rows = 1; out->Ut_q.cols = m;
+  out->Vt_q.rows = 1; out->Vt_q.cols = n;
+  out->R_q.rows = m; out->R_q.cols = n;
+  out->Rt_q.rows = n; out->Rt_q.cols = m;
+  if (dt == METIS_F32) return run_mean_split<float>(p, (const float *)A, lda, out, stream);
+  return run_mean_split<unsigned short>(p, (const unsigned short *)A, lda, out, stream);
 }

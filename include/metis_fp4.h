@@ -166,6 +166,24 @@ metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m, int64_t n
                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Mean-residual split (Averis, "Averaging-Induced Residual Splitting", as
+ * retold on the zhu318.com page, method paragraphs): the mean over all rows,
+ * mu (one value per column), and the residual A - mu broadcast over the rows
+ * are quantized separately. The result is the rank-1 split record
+ *   U = 1 (m x 1), S = {1}, V = mu (n x 1),  R = A - 1 mu^T,
+ * so it enters spectral_fp4_linear_fwd/_bwd and metis_gemm_nt_* like any
+ * split operand (the all-ones U is exact in both FP4 formats).
+ *  A, dt, m, n, lda, fmt, out, ws, stream: as for metis_split, with k = 1
+ *  (out->U holds m floats, S one, V n). mu is summed in fp64 over rows in a
+ *  fixed order and rounded once to fp32; R = A - mu is one fp32 subtraction
+ *  per element. ws: metis_mean_split_workspace_bytes() bytes, 256-byte
+ *  aligned. Errors as for metis_split; bitwise reproducible. */
+size_t metis_mean_split_workspace_bytes(int64_t m, int64_t n, metis_fmt_t fmt);
+metis_status_t metis_mean_split(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                metis_fmt_t fmt, metis_split_t *out, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * W4A4G4 linear layer ("Metis" abstract: FP4 weights, activations and
  * gradients). Each GEMM is C = A_hat B_hat^T with, for a split operand,
  * A_hat = R_hat + U_hat diag(S) V_hat^T in the orientation it is used in

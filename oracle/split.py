@@ -226,6 +226,32 @@ def spectral_split(A, l, k, omega=None, columns=None):
     return {"U": U, "S": S, "V": V, "R": R, "Q": Q, "B": B, "sigma_B": sigma}
 
 
+def mean_split(A):
+    """Mean-residual split (Averis, "Averaging-Induced Residual Splitting", as
+    retold on the zhu318.com page, its method paragraphs): the mean over all
+    rows of A is a vector mu (one value per column); the residual is A minus
+    mu broadcast to every row; the mean vector and the residual are quantized
+    separately, and the operand is their recombination.
+
+    Written as a rank-1 split record so that it enters the GEMMs like any
+    split operand: U = the all-ones column (exact in FP4), S = [1], V = mu,
+    R = A - 1 mu^T (from the unquantized mu, as for the spectral split).
+    Pins (tests/test_oracle_split.py): mu equals numpy's column mean, the
+    residual's column sums vanish, R + 1 mu^T == A."""
+    A = np.asarray(A, dtype=np.float64)
+    if not np.all(np.isfinite(A)):
+        raise ValueError("split input must be finite")
+    m, n = A.shape
+    if m < 1 or n < 1:
+        raise ValueError("empty input")
+    mu = A.sum(axis=0) / m
+    U = np.ones((m, 1))
+    S = np.ones(1)
+    V = mu[:, None].copy()
+    R = A - U @ V.T
+    return {"U": U, "S": S, "V": V, "R": R, "mu": mu}
+
+
 def quantize_record(fmt, R, U=None, S=None, V=None, orientations=("n", "t")):
     """Quantized split record of one tensor.
 

@@ -109,3 +109,24 @@ def test_split_rejects_bad_arguments_on_host():
     bad = _split_rec()
     bad.R_q.fmt = 1
     assert L.metis_split(A, 1, 256, 256, 256, om, 0, 16, 8, 0, ctypes.byref(bad), None, ws, nbytes, None) == 1
+
+
+def test_mean_split_rejects_bad_arguments_on_host():
+    L = M.load()
+    s = _split_rec()
+    A, ws = ctypes.c_void_p(256), ctypes.c_void_p(256)
+    nbytes = L.metis_mean_split_workspace_bytes(256, 256, 0)
+    assert nbytes > 0
+    ok = lambda **kw: L.metis_mean_split(kw.get("A", A), kw.get("dt", 1), kw.get("m", 256), kw.get("n", 256),
+                                          kw.get("lda", 256), kw.get("fmt", 0), ctypes.byref(s), kw.get("ws", ws),
+                                          kw.get("ws_bytes", nbytes), None)
+    assert ok(m=250) == 1            # not a multiple of 32
+    assert ok(lda=128) == 1          # lda < n
+    assert ok(A=None) == 1
+    assert ok(A=ctypes.c_void_p(258)) == 1   # misaligned A
+    assert ok(dt=7) == 1
+    assert ok(ws=None) == 3
+    assert ok(ws_bytes=64) == 3
+    bad = _split_rec()
+    bad.Vt_q.fmt = 1
+    assert L.metis_mean_split(A, 1, 256, 256, 256, 0, ctypes.byref(bad), ws, nbytes, None) == 1

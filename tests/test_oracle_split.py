@@ -152,6 +152,26 @@ def test_bad_arguments():
         S.sketch(A)
 
 
+def test_mean_split_closed_form():
+    """Averis split: mu is the column mean, the residual is de-meaned, and
+    the parts add back to A; U = 1 and S = 1 quantize exactly."""
+    from oracle import formats as F
+    g = np.random.Generator(np.random.PCG64(31))
+    A = g.standard_normal((96, 64)) + np.linspace(-3.0, 5.0, 64)  # columns with distinct offsets
+    r = S.mean_split(A)
+    assert np.allclose(r["mu"], A.mean(axis=0), rtol=0, atol=1e-14)
+    assert np.allclose(r["R"].sum(axis=0), 0.0, atol=1e-12)
+    assert np.array_equal(r["R"] + np.ones((96, 1)) @ r["V"].T, A) or np.allclose(
+        r["R"] + np.ones((96, 1)) @ r["V"].T, A, rtol=0, atol=1e-15)
+    for fmt in ("mxfp4", "nvfp4"):
+        rec = S.quantize_record(fmt, r["R"], r["U"], r["S"], r["V"])
+        Uq = F.dequantize(rec["Ut_q"])
+        assert np.allclose(Uq, 1.0, rtol=2e-7, atol=0)
+    # a constant matrix is all mean: zero residual
+    r0 = S.mean_split(np.full((32, 32), 2.5))
+    assert np.all(r0["R"] == 0.0) and np.all(r0["mu"] == 2.5)
+
+
 # --- planted mistakes: each pin above must notice a plausible slip ---------
 def test_pins_catch_a_planted_mistake_unsorted_sigma(monkeypatch):
     real = S.jacobi_svd
