@@ -85,6 +85,48 @@ def calibrate_copy(torch, dev, mib):
     log("calibration copy: 5 x %d MiB read + %d MiB written" % (mib, mib))
 
 
+def mean_split_leg(torch, M, A, tensors, reps=10):
+    """The mean-residual split (next to the spectral one) timed alone on the
+    activation and gradient inputs, after the timed steps: milliseconds per
+    call and HBM rate against its algorithmic bytes (A read twice, the
+    residual codes and scales of both orientations written)."""
+    out = {}
+    for n in ("X_up", "dY_up"):
+        m_, n_ = tensors[n].shape
+        rec = M.empty_split(m_, n_, 1, "mxfp4", ("n", "t"), A[n].device)
+        M.metis_mean_split(A[n], "mxfp4", out=rec)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            M.metis_mean_split(A[n], "mxfp4", out=rec)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        elems = m_ * n_
+        nbytes = 2 * 2 * elems + 2 * (elems // 2 + elems // 32)
+        out[n] = {"ms": round(ms, 4), "GB/s": round(nbytes / (ms / 1e3) / 1e9, 1), "algorithmic_bytes": nbytes}
+    return out
+
+
+def power_split_leg(torch, M, A, Om, recs, tensors, reps=5):
+    """The spectral split with q = 1 power iteration (two more passes over A)
+    timed alone on X_up, after the timed steps, next to q = 0."""
+    t = tensors["X_up"]
+    out = {}
+    for q in (0, 1):
+        M.metis_split(A["X_up"], t.l, t.k, "mxfp4", omega=Om["X_up"], out=recs["X_up"], q=q)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            M.metis_split(A["X_up"], t.l, t.k, "mxfp4", omega=Om["X_up"], out=recs["X_up"], q=q)
+        e1.record()
+        torch.cuda.synchronize()
+        out["q%d_ms" % q] = round(e0.elapsed_time(e1) / reps, 4)
+    return {"tensor": "X_up 8192x4096 bf16, k 64, l 80", **out}
+
+
 def cpu_baseline(tensors, gemm_total_flops):
     """The fp64 oracle on a bounded sample of the same workload: the split of
     X_up (8192 x 4096) and the forward GEMM Y_up on 256 sampled rows; the
@@ -245,6 +287,8 @@ def main():
                      "achieved": round(achieved, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": gemm_traffic()},
     }
+    line["mean_split"] = mean_split_leg(torch, M, A, tensors)
+    line["power_split"] = power_split_leg(torch, M, A, Om, recs, tensors)
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(tensors, total_flops)

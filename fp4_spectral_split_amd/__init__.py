@@ -72,6 +72,11 @@ def load():
     L.metis_split_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
     L.metis_split.restype = i32
     L.metis_split.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, i32, ctypes.POINTER(_Split), vp, vp, sz, vp]
+    L.metis_split_power_workspace_bytes.restype = sz
+    L.metis_split_power_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32]
+    L.metis_split_power.restype = i32
+    L.metis_split_power.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, i32, i32, ctypes.POINTER(_Split), vp,
+                                    vp, sz, vp]
     L.metis_mean_split_workspace_bytes.restype = sz
     L.metis_mean_split_workspace_bytes.argtypes = [i64, i64, i32]
     L.metis_mean_split.restype = i32
@@ -94,7 +99,8 @@ def load():
 
 
 EXPORTS = ["metis_status_str", "metis_abi_version", "fp4_block_quant_workspace_bytes", "fp4_block_quant",
-           "fp4_block_dequant", "metis_split_workspace_bytes", "metis_split", "metis_mean_split_workspace_bytes",
+           "fp4_block_dequant", "metis_split_workspace_bytes", "metis_split", "metis_split_power_workspace_bytes",
+           "metis_split_power", "metis_mean_split_workspace_bytes",
            "metis_mean_split", "metis_linear_workspace_bytes",
            "spectral_fp4_linear_fwd", "spectral_fp4_linear_bwd", "metis_gemm_nt_workspace_bytes",
            "metis_gemm_nt_prepare", "metis_gemm_nt_main"]
@@ -239,10 +245,11 @@ def empty_split(m, n, k, fmt, orientations, device):
     return rec
 
 
-def metis_split(A, l, k, fmt="mxfp4", omega=None, columns=None, orientations=("n", "t"), out=None):
+def metis_split(A, l, k, fmt="mxfp4", omega=None, columns=None, orientations=("n", "t"), out=None, q=0):
     """Split a 2-D fp32/bf16 CUDA tensor A (m x n) into U diag(S) V^T + R and
     quantize the parts. omega: n x l bf16 tensor (Gaussian sketch) or
-    columns: int32 tensor of l column ids (sampling sketch)."""
+    columns: int32 tensor of l column ids (sampling sketch); q: power
+    iterations after the sketch (metis_split_power)."""
     L = load()
     assert A.dim() == 2 and A.is_cuda and A.stride(1) == 1
     m, n = A.shape
@@ -257,10 +264,16 @@ def metis_split(A, l, k, fmt="mxfp4", omega=None, columns=None, orientations=("n
         kind, om = OMEGA_COLUMNS, columns
     rec = out if out is not None else empty_split(m, n, k, fmt, orientations, A.device)
     c = rec.c()
-    nws = L.metis_split_workspace_bytes(m, n, l, k, kind, fmt)
-    ws = workspace(nws, A.device)
-    _check(L.metis_split(_ptr(A), _dtype_code(A), m, n, A.stride(0), _ptr(om), kind, l, k, fmt, ctypes.byref(c),
-                         _ptr(rec.info), _ptr(ws), nws, _stream(A.device)))
+    if q == 0:
+        nws = L.metis_split_workspace_bytes(m, n, l, k, kind, fmt)
+        ws = workspace(nws, A.device)
+        _check(L.metis_split(_ptr(A), _dtype_code(A), m, n, A.stride(0), _ptr(om), kind, l, k, fmt,
+                             ctypes.byref(c), _ptr(rec.info), _ptr(ws), nws, _stream(A.device)))
+    else:
+        nws = L.metis_split_power_workspace_bytes(m, n, l, k, kind, q, fmt)
+        ws = workspace(nws, A.device)
+        _check(L.metis_split_power(_ptr(A), _dtype_code(A), m, n, A.stride(0), _ptr(om), kind, l, k, q, fmt,
+                                   ctypes.byref(c), _ptr(rec.info), _ptr(ws), nws, _stream(A.device)))
     return rec
 
 

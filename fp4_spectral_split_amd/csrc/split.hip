@@ -32,7 +32,8 @@ using namespace metis;
 
 namespace {
 
-constexpr int kLpMax = 96;  // Gaussian / sampled sketch width handled in LDS
+constexpr int kLpMax = 96;
+constexpr int kMaxPowerIterations = 16;  // Gaussian / sampled sketch width handled in LDS
 constexpr int kThreads = 256;
 constexpr int kGramRows = 128;     // rows per Gram chunk (narrow path)
 constexpr int kGramThreads = 512;  // 8 waves, 16 rows each
@@ -46,6 +47,7 @@ __host__ __device__ __forceinline__ int asm_chunk_rows(int k) { return kAsmRows 
 struct SplitPlan {
   int64_t m, n;
   int l, lp, k, kp;
+  int power;  // power iterations
   bool wide;  // l > kLpMax: global-memory forms of the small kernels
   int kind, fmt;
   int elem;  // bytes per input element
@@ -85,6 +87,8 @@ struct SplitPlan {
   unsigned short *whl;   // 2 x n x kp bf16 ((V S) hi, lo)
   double *wa, *winv, *wg, *wv;  // lp x lp scratch of the global-memory (wide) forms
   uint32_t *amax;        // 8 words: NVFP4 tensor maxima (U^T, V^T, R)
+  float *z1;             // n x l (power iterations: A^T Q after one R^-1)
+  unsigned short *zt;    // 2 x lp x n bf16 (power iterations: orth(A^T Q)^T hi, lo)
   int *info_ws;          // 1 word
   size_t bytes;
 };
@@ -94,15 +98,15 @@ int64_t pick_rows_per_part(int64_t rows, int64_t want_parts, int64_t quantum) {
   return std::max<int64_t>(per, quantum);
 }
 
-SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int elem, void *ws) {
+SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int elem, void *ws, int q = 0) {
   SplitPlan p;
-  p.m = m; p.n = n; p.l = l; p.k = k; p.kind = kind; p.fmt = fmt; p.elem = elem;
+  p.m = m; p.n = n; p.l = l; p.k = k; p.kind = kind; p.fmt = fmt; p.elem = elem; p.power = q;
   p.wide = l > kLpMax;
   p.lp = (int)round_up(l, p.wide ? 64 : 16);
   p.kp = (int)round_up(k, 32);
   // sketch: 128-row tiles, split-K bounded so partial traffic stays ~10% of A
   const int64_t m_tiles = cdiv(m, 128);
-  if (kind == METIS_OMEGA_GAUSSIAN) {
+  if (kind == METIS_OMEGA_GAUSSIAN || q > 0) {
     int64_t want = std::min<int64_t>(cdiv(768, m_tiles), std::max<int64_t>(1, n * elem / (20 * l)));
     want = std::max<int64_t>(1, std::min<int64_t>(want, n / 128));
     p.sk_chunk = round_up(cdiv(n, want), 128);
@@ -149,6 +153,8 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
   p.wv = c.take<double>((size_t)p.lp * p.lp);
   p.amax = c.take<uint32_t>(8);
   p.info_ws = c.take<int>(1);
+  p.z1 = c.take<float>(q > 0 ? (size_t)n * l : 0);
+  p.zt = c.take<unsigned short>(q > 0 ? (size_t)2 * p.lp * n : 0);
   p.bytes = c.bytes();
   return p;
 }
@@ -175,7 +181,10 @@ __global__ void omega_transpose_kernel(const unsigned short *__restrict__ om, in
 // with the Omega operand), so each row's 256 bytes per step are read whole.
 // The next step's A elements and Omega^T pieces are loaded into registers
 // while the current step is multiplied.
-template <typename T>
+// HL: the right-hand factor is an fp32 matrix carried as bf16 hi + lo
+// (omt holds its hi rows 0 .. lp - 1, then its lo rows), both multiplied, so
+// the product is fp32-accurate (the power iterations' Y = A Z).
+template <typename T, bool HL = false>
 __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda,
                                                           const unsigned short *__restrict__ omt, int l, int lp,
                                                           int64_t chunk, float *__restrict__ ysk) {
@@ -186,7 +195,8 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
   constexpr int NT = (sizeof(T) == 4) ? 3 : 1;  // bf16 terms per element (fp32 = hi + mid + lo)
   constexpr int AV = 32 * (int)sizeof(T) / 16;   // 16-byte pieces of A per lane and row
   constexpr int OPR = (kLpMax * (KS / 8) + kThreads - 1) / kThreads;  // Omega^T pieces per thread
-  __shared__ __attribute__((aligned(16))) unsigned short lds[kLpMax][KS + 8];
+  constexpr int NH = HL ? 2 : 1;  // bf16 parts of the right-hand factor
+  __shared__ __attribute__((aligned(16))) unsigned short lds[NH][kLpMax][KS + 8];
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int r16 = lane & 15, g = lane >> 4;
@@ -201,7 +211,7 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
 #pragma unroll
     for (int b = 0; b < kLpMax / 16; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 pa[2][AV], ca[2][AV], po[OPR];
+  uint4 pa[2][AV], ca[2][AV], po[NH][OPR];
   auto load = [&](int64_t c0) {
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs) {
@@ -213,23 +223,28 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
       for (int j = 0; j < AV; ++j) pa[rs][j] = ok ? src[j] : uint4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int p = 0; p < OPR; ++p) {
-      const int idx = t + kThreads * p;
-      const int rr = idx / (KS / 8), q = idx % (KS / 8);
-      const int64_t cc = c0 + q * 8;
-      po[p] = (idx < lt * (KS / 8) && cc < c_end) ? *(const uint4 *)(omt + (int64_t)(l0 + rr) * n + cc)
-                                                  : uint4{0u, 0u, 0u, 0u};
-    }
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int p = 0; p < OPR; ++p) {
+        const int idx = t + kThreads * p;
+        const int rr = idx / (KS / 8), q = idx % (KS / 8);
+        const int64_t cc = c0 + q * 8;
+        po[h][p] = (idx < lt * (KS / 8) && cc < c_end)
+                       ? *(const uint4 *)(omt + ((int64_t)h * lp + l0 + rr) * n + cc)
+                       : uint4{0u, 0u, 0u, 0u};
+      }
   };
 
   if (c_beg < c_end) load(c_beg);
   for (int64_t c0 = c_beg; c0 < c_end; c0 += KS) {
     __syncthreads();
 #pragma unroll
-    for (int p = 0; p < OPR; ++p) {
-      const int idx = t + kThreads * p;
-      if (idx < lt * (KS / 8)) *(uint4 *)&lds[idx / (KS / 8)][(idx % (KS / 8)) * 8] = po[p];
-    }
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int p = 0; p < OPR; ++p) {
+        const int idx = t + kThreads * p;
+        if (idx < lt * (KS / 8)) *(uint4 *)&lds[h][idx / (KS / 8)][(idx % (KS / 8)) * 8] = po[h][p];
+      }
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
@@ -266,13 +281,15 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
     for (int ct = 0; ct < kLpMax / 16; ++ct) {
       if (ct < nct) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const ushortx8 b = *(const ushortx8 *)&lds[ct * 16 + r16][g * 32 + j * 8];
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int rs = 0; rs < 2; ++rs)
+          for (int h = 0; h < NH; ++h) {
+            const ushortx8 b = *(const ushortx8 *)&lds[h][ct * 16 + r16][g * 32 + j * 8];
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) acc[rs][ct] = mfma16_bf16(a[rs][j][tt], b, acc[rs][ct]);
-        }
+            for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+              for (int tt = 0; tt < NT; ++tt) acc[rs][ct] = mfma16_bf16(a[rs][j][tt], b, acc[rs][ct]);
+          }
       }
     }
   }
@@ -1805,16 +1822,37 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
   }
   const unsigned rgrid_red = (unsigned)cdiv(lp * lp, 32);  // 8 lanes per element
   if (!p.wide) {
-    // ---- CholeskyQR2 (LDS-resident small matrices)
-    gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(ysrc, yparts, m * l, m, l, lp, nullptr,
-                                                     yparts > 1 ? p.y : nullptr, nullptr, p.gpart);
-    const float *y = yparts > 1 ? p.y : ysrc;
-    gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
-    chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws, nullptr);
-    gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(y, 1, 0, m, l, lp, p.rinv, p.q1, nullptr, p.gpart);
-    gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
-    chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
-    gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(p.q1, 1, 0, m, l, lp, p.rinv, p.q, p.qt, nullptr);
+    // ---- CholeskyQR2 (LDS-resident small matrices) of the sketch's sum of
+    // parts: Q (m x l) and its bf16 hi/lo transpose
+    auto cholqr2_y = [&](const float *src, int parts) {
+      gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(src, parts, m * l, m, l, lp, nullptr,
+                                                       parts > 1 ? p.y : nullptr, nullptr, p.gpart);
+      const float *y = parts > 1 ? p.y : src;
+      gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
+      chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws, nullptr);
+      gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(y, 1, 0, m, l, lp, p.rinv, p.q1, nullptr, p.gpart);
+      gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
+      chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
+      gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(p.q1, 1, 0, m, l, lp, p.rinv, p.q, p.qt, nullptr);
+    };
+    cholqr2_y(ysrc, yparts);
+    // ---- power iterations: Z = orth(A^T Q) by CholeskyQR2 over the n rows,
+    // then Y = A Z (Z as bf16 hi + lo) and Q = orth(Y) again
+    for (int it = 0; it < p.power; ++it) {
+      project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
+                                                                                   p.pk_rows, p.btp);
+      gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.btp, p.pk, n * l, n, l, lp, nullptr, p.bt, nullptr,
+                                                       p.gpart);
+      gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
+      chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
+      gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.bt, 1, 0, n, l, lp, p.rinv, p.z1, nullptr, p.gpart);
+      gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
+      chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
+      gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.z1, 1, 0, n, l, lp, p.rinv, nullptr, p.zt, nullptr);
+      sketch_kernel<T, true><<<dim3((unsigned)cdiv(m, 128), p.sk, lz), kThreads, 0, st>>>(A, m, n, lda, p.zt, l, lp,
+                                                                                        p.sk_chunk, p.ysk);
+      cholqr2_y(p.ysk, p.sk);
+    }
     // ---- pass 2: projection B^T = A^T Q, then the Gram B B^T
     project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
                                                                                  p.pk_rows, p.btp);
@@ -1997,17 +2035,25 @@ bool fp4_ok(const metis_fp4_t &q, int fmt, bool need_ts) {
 
 }  // namespace
 
-extern "C" size_t metis_split_workspace_bytes(int64_t m, int64_t n, int32_t l, int32_t k, metis_omega_t kind,
-                                              metis_fmt_t fmt) {
-  if (m <= 0 || n <= 0 || l <= 0 || k <= 0) return 0;
+extern "C" size_t metis_split_power_workspace_bytes(int64_t m, int64_t n, int32_t l, int32_t k, metis_omega_t kind,
+                                                    int32_t q, metis_fmt_t fmt) {
+  if (m <= 0 || n <= 0 || l <= 0 || k <= 0 || q < 0) return 0;
   // the plan depends on the element size; cover both input types
-  return std::max(make_plan(m, n, l, k, kind, fmt, 4, nullptr).bytes, make_plan(m, n, l, k, kind, fmt, 2, nullptr).bytes);
+  return std::max(make_plan(m, n, l, k, kind, fmt, 4, nullptr, q).bytes,
+                  make_plan(m, n, l, k, kind, fmt, 2, nullptr, q).bytes);
 }
 
-extern "C" metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
-                                      const void *omega, metis_omega_t kind, int32_t l, int32_t k, metis_fmt_t fmt,
-                                      metis_split_t *out, int32_t *info, void *ws, size_t ws_bytes,
-                                      hipStream_t stream) {
+extern "C" size_t metis_split_workspace_bytes(int64_t m, int64_t n, int32_t l, int32_t k, metis_omega_t kind,
+                                              metis_fmt_t fmt) {
+  return metis_split_power_workspace_bytes(m, n, l, k, kind, 0, fmt);
+}
+
+extern "C" metis_status_t metis_split_power(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                            const void *omega, metis_omega_t kind, int32_t l, int32_t k, int32_t q,
+                                            metis_fmt_t fmt, metis_split_t *out, int32_t *info, void *ws,
+                                            size_t ws_bytes, hipStream_t stream) {
+  if (q < 0) return METIS_ERR_INVALID;
+  if (q > kMaxPowerIterations || (q > 0 && l > kLpMax)) return METIS_ERR_UNSUPPORTED;
   if (!A || !omega || !out) return METIS_ERR_INVALID;
   if (dt != METIS_F32 && dt != METIS_BF16) return METIS_ERR_INVALID;
   if (fmt != METIS_MXFP4 && fmt != METIS_NVFP4) return METIS_ERR_INVALID;
@@ -2026,7 +2072,7 @@ extern "C" metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m
   if (want_t && !fp4_ok(out->Rt_q, fmt, nv)) return METIS_ERR_INVALID;
   if (!ws) return METIS_ERR_WORKSPACE;
   if (((uintptr_t)ws) & 255) return METIS_ERR_INVALID;
-  SplitPlan p = make_plan(m, n, l, k, kind, fmt, elem, ws);
+  SplitPlan p = make_plan(m, n, l, k, kind, fmt, elem, ws, q);
   if (ws_bytes < p.bytes) return METIS_ERR_WORKSPACE;
   out->m = m;
   out->n = n;
@@ -2037,6 +2083,13 @@ extern "C" metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m
   out->Rt_q.rows = n; out->Rt_q.cols = m;
   if (dt == METIS_F32) return run_split<float>(p, (const float *)A, lda, omega, out, info, stream);
   return run_split<unsigned short>(p, (const unsigned short *)A, lda, omega, out, info, stream);
+}
+
+extern "C" metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                      const void *omega, metis_omega_t kind, int32_t l, int32_t k, metis_fmt_t fmt,
+                                      metis_split_t *out, int32_t *info, void *ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  return metis_split_power(A, dt, m, n, lda, omega, kind, l, k, 0, fmt, out, info, ws, ws_bytes, stream);
 }
 
 extern "C" size_t metis_mean_split_workspace_bytes(int64_t m, int64_t n, metis_fmt_t fmt) {

@@ -165,6 +165,23 @@ metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m, int64_t n
                            metis_split_t *out, int32_t *info, void *ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* The same split with q power (subspace) iterations after the sketch
+ * (Halko-Martinsson-Tropp 2011, Alg. 4.4): with Q = orth(Y), each iteration
+ * forms Z = orth(A^T Q) and Y = A Z, Q = orth(Y), every orthonormalization a
+ * CholeskyQR2 in fp64 and Z applied as bf16 hi + lo (fp32-accurate). Each
+ * iteration adds two passes over A. metis_split is q = 0.
+ *  q: 0 <= q <= 16 (beyond: METIS_ERR_UNSUPPORTED); q > 0 needs l <= 96
+ *     (beyond: METIS_ERR_UNSUPPORTED); q < 0: METIS_ERR_INVALID.
+ *  info: the rank status of the last sketch's Cholesky factor.
+ *  ws: metis_split_power_workspace_bytes() bytes (it grows with q > 0).
+ * Everything else as for metis_split. */
+size_t metis_split_power_workspace_bytes(int64_t m, int64_t n, int32_t l, int32_t k, metis_omega_t kind,
+                                         int32_t q, metis_fmt_t fmt);
+metis_status_t metis_split_power(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                 const void *omega, metis_omega_t kind, int32_t l, int32_t k, int32_t q,
+                                 metis_fmt_t fmt, metis_split_t *out, int32_t *info, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Mean-residual split (Averis, "Averaging-Induced Residual Splitting", as
  * retold on the zhu318.com page, method paragraphs): the mean over all rows,

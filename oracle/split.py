@@ -202,20 +202,32 @@ def sketch(A, omega=None, columns=None):
     return np.asarray(A, dtype=np.float64)[:, J]
 
 
-def spectral_split(A, l, k, omega=None, columns=None):
+def spectral_split(A, l, k, omega=None, columns=None, q=0):
     """The seven steps of the module docstring. Returns a dict with the
     fp64 factors U (m x k), S (k), V (n x k), the residual R and the
-    intermediates Q, B and sigma_B (all l singular values of B)."""
+    intermediates Q, B and sigma_B (all l singular values of B).
+
+    q >= 1 adds power (subspace) iterations to step 2, as in Halko,
+    Martinsson & Tropp's randomized subspace iteration (their Alg. 4.4):
+    with Q = orth(Y), each iteration forms Z = orth(A^T Q) and then
+    Y = A Z, Q = orth(Y), re-orthonormalizing after every product so that
+    small singular directions are not lost to rounding. The pages fix no q;
+    the configurations here all use q = 0 (none)."""
     A = np.asarray(A, dtype=np.float64)
     if not np.all(np.isfinite(A)):
         raise ValueError("split input must be finite")
     m, n = A.shape
     if not (1 <= k <= l <= min(m, n)):
         raise ValueError("need 1 <= k <= l <= min(m, n)")
+    if q < 0:
+        raise ValueError("q must be >= 0")
     Y = sketch(A, omega, columns)
     if Y.shape != (m, l):
         raise ValueError("sketch width must equal l")
     Q = range_basis(Y)
+    for _ in range(q):
+        Z = range_basis(A.T @ Q)
+        Q = range_basis(A @ Z)
     B = Q.T @ A
     Ub, sigma, W = small_svd(B)
     U = Q @ Ub[:, :k]

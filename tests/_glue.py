@@ -27,13 +27,13 @@ def columns_gpu(t):
     return torch.from_numpy(t.columns.astype(np.int32)).to(device())
 
 
-def split_gpu(t, orientations=None, fmt=None):
+def split_gpu(t, orientations=None, fmt=None, q=0):
     A = to_gpu(t)
     o = orientations or t.orientations
     f = fmt or t.fmt
     if t.sketch == "gaussian":
-        return M.metis_split(A, t.l, t.k, f, omega=omega_gpu(t), orientations=o)
-    return M.metis_split(A, t.l, t.k, f, columns=columns_gpu(t), orientations=o)
+        return M.metis_split(A, t.l, t.k, f, omega=omega_gpu(t), orientations=o, q=q)
+    return M.metis_split(A, t.l, t.k, f, columns=columns_gpu(t), orientations=o, q=q)
 
 
 def fp4_to_dict(q):

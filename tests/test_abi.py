@@ -130,3 +130,20 @@ def test_mean_split_rejects_bad_arguments_on_host():
     bad = _split_rec()
     bad.Vt_q.fmt = 1
     assert L.metis_mean_split(A, 1, 256, 256, 256, 0, ctypes.byref(bad), ws, nbytes, None) == 1
+
+
+def test_split_power_rejects_bad_arguments_on_host():
+    L = M.load()
+    s = _split_rec()
+    A, om, ws = ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256)
+    n1 = L.metis_split_power_workspace_bytes(256, 256, 16, 8, 0, 1, 0)
+    n0 = L.metis_split_power_workspace_bytes(256, 256, 16, 8, 0, 0, 0)
+    assert n1 > n0 == L.metis_split_workspace_bytes(256, 256, 16, 8, 0, 0)
+    assert L.metis_split_power_workspace_bytes(256, 256, 16, 8, 0, -1, 0) == 0
+    ok = lambda **kw: L.metis_split_power(A, 1, kw.get("m", 256), kw.get("n", 256), kw.get("m", 256), om, 0,
+                                          kw.get("l", 16), 8, kw.get("q", 1), 0, ctypes.byref(s), None, ws,
+                                          kw.get("ws_bytes", n1), None)
+    assert ok(q=-1) == 1
+    assert ok(q=17) == 2                                   # more iterations than this build takes
+    assert ok(q=1, l=128, m=1024, n=1024, ws_bytes=1 << 40) == 2  # wide sketches take no iterations
+    assert ok(q=1, ws_bytes=n0) == 3                       # the q = 0 workspace is too small

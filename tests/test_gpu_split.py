@@ -23,11 +23,11 @@ import fp4_spectral_split_amd as M
 L_GATE = 1e-3
 
 
-def _oracle_split(t):
+def _oracle_split(t, q=0):
     A = t.values.astype(np.float64)
     if t.sketch == "gaussian":
-        return A, S.spectral_split(A, t.l, t.k, omega=t.omega_values().astype(np.float64))
-    return A, S.spectral_split(A, t.l, t.k, columns=t.columns)
+        return A, S.spectral_split(A, t.l, t.k, omega=t.omega_values().astype(np.float64), q=q)
+    return A, S.spectral_split(A, t.l, t.k, columns=t.columns, q=q)
 
 
 def _check_codes_near(got, want, fmt, rows=None):
@@ -179,3 +179,33 @@ def test_split_parity_full_size_nvfp4_sampled_512(name):
     want = F.quantize(F.f32(V.T), "nvfp4")
     assert np.array_equal(d["Vt_q"]["codes"], want["codes"]) and np.array_equal(d["Vt_q"]["scales"], want["scales"])
     assert np.float32(d["Vt_q"]["tensor_scale"]) == np.float32(want["tensor_scale"])
+
+
+@pytest.mark.parametrize("q", [1, 2])
+@pytest.mark.parametrize("name", ["ragged-powerlaw-bf16", "planted-f32", "sampled-columns", "nvfp4", "wide-l96"])
+def test_split_power_iterations_parity_small(name, q):
+    """q power iterations (metis_split_power) against the oracle's subspace
+    iteration with the same q, to the same gates as q = 0."""
+    t = CASES[name]()
+    t.orientations = ("n", "t")
+    print("case", name, "q", q, t.shape, flush=True)
+    A, orc = _oracle_split(t, q=q)
+    rec = G.split_gpu(t, orientations=("n", "t"), q=q)
+    torch.cuda.synchronize()
+    _check_split(t, rec, A, orc, t.fmt)
+
+
+def test_split_power_iterations_full_size():
+    """8192 x 4096 bf16 (LLaMA-3-8B FFN input), k = 64, l = 80, q = 1."""
+    t = synth.make_tensor(4, "X_up")
+    A, orc = _oracle_split(t, q=1)
+    rec = G.split_gpu(t, orientations=("n",), q=1)
+    torch.cuda.synchronize()
+    U, Sg, V = G.factors_np(rec)
+    Lg = (U * Sg) @ V.T
+    err = np.linalg.norm(Lg - (orc["U"] * orc["S"]) @ orc["V"].T) / np.linalg.norm(A)
+    print("L rel err %.3e" % err, flush=True)
+    assert err <= L_GATE
+    rows = np.sort(np.random.Generator(np.random.PCG64(7)).choice(t.shape[0], 256, replace=False))
+    Rp = F.f32(A[rows] - (U[rows] * Sg) @ V.T)
+    _check_codes_near(G.record_to_dict(rec)["R_q"], F.quantize(Rp, "mxfp4"), "mxfp4", rows=rows)

@@ -152,6 +152,30 @@ def test_bad_arguments():
         S.sketch(A)
 
 
+def test_power_iterations_reach_the_exact_top_k():
+    """Subspace iteration (q >= 1): on a slowly decaying spectrum one sketch
+    pass leaves a visible gap to the exact top-k singular values; a few
+    iterations close it to LAPACK precision, monotonically in q."""
+    g = np.random.Generator(np.random.PCG64(41))
+    m, n, k, l = 200, 160, 8, 12
+    U = synth.orthonormal(g, m, 60)
+    V = synth.orthonormal(g, n, 60)
+    A = (U * (np.arange(1, 61) ** -0.5)) @ V.T
+    sA = np.linalg.svd(A, compute_uv=False)
+    om = g.standard_normal((n, l))
+    errs = []
+    for q in range(0, 8):
+        r = S.spectral_split(A, l, k, omega=om, q=q)
+        errs.append(np.max(np.abs(r["S"] - sA[:k]) / sA[0]))
+        # the residual never beats Eckart-Young and is monotone toward it
+        assert np.linalg.norm(r["R"]) >= np.sqrt(np.sum(sA[k:] ** 2)) * (1 - 1e-12)
+    assert errs[0] > 1e-3
+    assert all(b <= a * 1.0001 for a, b in zip(errs, errs[1:]))
+    r = S.spectral_split(A, l, k, omega=om, q=30)
+    assert np.allclose(r["S"], sA[:k], rtol=1e-9, atol=0)
+    assert np.allclose(np.abs(r["U"].T @ np.linalg.svd(A)[0][:, :k]), np.eye(k), atol=1e-6)
+
+
 def test_mean_split_closed_form():
     """Averis split: mu is the column mean, the residual is de-meaned, and
     the parts add back to A; U = 1 and S = 1 quantize exactly."""
