@@ -287,6 +287,18 @@ def main():
                      "achieved": round(achieved, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": gemm_traffic()},
     }
+    # the same kernel alone on an idle GPU (context for the in-step figure,
+    # which shares the CUs with the other lanes' kernels)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(5):
+        gobj["Y_up"].main(outs["Y_up"])
+    e1.record()
+    torch.cuda.synchronize()
+    iso = per_gemm / (e0.elapsed_time(e1) / 5 / 1e3) / 1e12
+    line["roofline"]["isolated_achieved"] = round(iso, 2)
+    line["roofline"]["isolated_frac"] = round(iso / FP4_PEAK_TFLOPS, 4)
     line["mean_split"] = mean_split_leg(torch, M, A, tensors)
     line["power_split"] = power_split_leg(torch, M, A, Om, recs, tensors)
     if not args.no_cpu_baseline:
