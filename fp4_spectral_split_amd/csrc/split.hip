@@ -688,6 +688,35 @@ __global__ void __launch_bounds__(kCholThreads)
       const int e = t + u * kCholThreads, p = e / l, x = e - (e / l) * l;
       if (e < l * l) C[p][x] = v[u];
     }
+    if (!FACTOR) {
+      // the second CholeskyQR pass sees G = I + E with E tiny: then
+      // R = I + F with F = triu(E), diag halved, and R^-1 = I - F up to
+      // O(E^2) (below 1e-10 here), with no elimination at all. A dead
+      // column of the first pass leaves E_jj = -1 and takes the full path.
+      __shared__ double emax_w[kCholThreads / 64];
+      double em = 0.0;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int e = t + u * kCholThreads, p = e / l, x = e - (e / l) * l;
+        if (e < l * l && x >= p) em = fmax(em, fabs(v[u] - (x == p ? 1.0 : 0.0)));
+      }
+      em = wave_max(em);
+      if ((t & 63) == 0) emax_w[t >> 6] = em;
+      __syncthreads();
+      double emax = 0.0;
+#pragma unroll
+      for (int w = 0; w < kCholThreads / 64; ++w) emax = fmax(emax, emax_w[w]);
+      if (emax < 1e-5) {
+        for (int e = t; e < lp * lp; e += kCholThreads) {
+          const int i = e / lp, c = e - (e / lp) * lp;
+          double r = 0.0;
+          if (c < l && i <= c) r = i == c ? 1.0 - 0.5 * (C[i][i] - 1.0) : -C[i][c];
+          out[e] = r;
+        }
+        if (t == 0 && info) *info = 0;
+        return;
+      }
+    }
   }
   __syncthreads();
   if (t < 64) {
