@@ -1629,7 +1629,8 @@ __global__ void __launch_bounds__(kThreads)
 // along n (R_q) and along m (Rt_q) from the same LDS copy. L = U W^T with
 // W = V S comes from bf16 MFMA on hi/lo panels: Uh Wh + Uh Wl + Ul Wh.
 // AMAX_ONLY: only the tensor max of |R| (NVFP4 tensor scale) is produced.
-constexpr int kRT = 128;
+constexpr int kRT = 128;  // residual tile rows
+constexpr int kRC = 64;   // residual tile columns (a 34 KB LDS tile: four workgroups per CU)
 
 template <int B, bool NV>
 __device__ __forceinline__ void quant_store(const float (&v)[B], float s_t, uint8_t *codes, uint8_t *scale) {
@@ -1669,14 +1670,14 @@ __global__ void __launch_bounds__(kThreads)
                     uint8_t *__restrict__ tscales, float *__restrict__ tts, uint32_t *__restrict__ amax,
                     const float *__restrict__ mu = nullptr) {
   constexpr int B = NV ? 16 : 32;
-  __shared__ __attribute__((aligned(16))) float lt[kRT][kRT + 4];
+  __shared__ __attribute__((aligned(16))) float lt[kRT][kRC + 4];
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  const int64_t col0 = (int64_t)blockIdx.x * kRT, row0 = (int64_t)blockIdx.y * kRT;
+  const int64_t col0 = (int64_t)blockIdx.x * kRC, row0 = (int64_t)blockIdx.y * kRT;
   // ---- this thread's row blocks of A are loaded first, in flight while L is
   // formed: block b = t + 256 j is row b / RPB, columns (b % RPB) * B ..
-  constexpr int RPB = kRT / B;                 // blocks per tile row
+  constexpr int RPB = kRC / B;                 // blocks per tile row
   constexpr int NJ = kRT * RPB / kThreads;     // row blocks per thread
   constexpr int VEC = B * (int)sizeof(T) / 16;  // 16-byte pieces per block
   static_assert(NJ * kThreads == kRT * RPB, "row blocks must divide over the threads");
@@ -1691,20 +1692,22 @@ __global__ void __launch_bounds__(kThreads)
     for (int q = 0; q < VEC; ++q) apre[jb][q] = ok ? src[q] : uint4{0u, 0u, 0u, 0u};
   }
   if constexpr (MEAN) {
-    // each thread fills half a column of the tile with mu
-    const int c = t % kRT, r0 = (t / kRT) * (kRT / 2);
+    // each thread fills a quarter of a column of the tile with mu
+    constexpr int RF = kRT * kRC / kThreads;
+    const int c = t % kRC, r0 = (t / kRC) * RF;
     const float v = col0 + c < n ? mu[col0 + c] : 0.0f;
 #pragma unroll 8
-    for (int r = 0; r < kRT / 2; ++r) lt[r0 + r][c] = v;
+    for (int r = 0; r < RF; ++r) lt[r0 + r][c] = v;
   } else
-  // ---- L tile via MFMA: wave owns rows wave*32 .. +32, all 128 columns.
+  // ---- L tile via MFMA: wave owns rows wave*32 .. +32, all kRC columns.
   // This wave's U operands (hi, lo) are loaded into registers up front; the W
   // panel (hi, lo) of the tile's 128 columns is shared by the four waves and
   // staged once in LDS, in the space the R tile takes later (row stride
   // kp + 8 bf16 keeps the fragment reads conflict free).
   {
     constexpr int KPM = 96;  // largest kp (k <= 96)
-    unsigned short *wst = (unsigned short *)&lt[0][0];  // [2][kRT][kp + 8]
+    unsigned short *wst = (unsigned short *)&lt[0][0];  // [2][kRC][kp + 8]
+    static_assert(2 * kRC * (96 + 8) * 2 <= kRT * (kRC + 4) * 4, "the W panel fits the tile's LDS");
     const int wstride = kp + 8;
     const int64_t um = m * kp, wn = n * kp;
     ushortx8 uh[KPM / 32][2], ul[KPM / 32][2];
@@ -1720,13 +1723,13 @@ __global__ void __launch_bounds__(kThreads)
       }
     {
       // the panel's 16-byte pieces, all of a thread's loads in flight together
-      constexpr int PW = 2 * kRT * (KPM / 8) / kThreads;
-      const int nw = 2 * kRT * (kp / 8);
+      constexpr int PW = 2 * kRC * (KPM / 8) / kThreads;
+      const int nw = 2 * kRC * (kp / 8);
       uint4 v[PW];
 #pragma unroll
       for (int u = 0; u < PW; ++u) {
         const int idx = t + u * kThreads;
-        const int h = idx / (kRT * (kp / 8)), rem = idx % (kRT * (kp / 8));
+        const int h = idx / (kRC * (kp / 8)), rem = idx % (kRC * (kp / 8));
         const int c = rem / (kp / 8), q = rem % (kp / 8);
         const int64_t col = col0 + c;
         v[u] = (idx < nw && col < n) ? *(const uint4 *)(whl + h * wn + col * kp + q * 8) : uint4{0u, 0u, 0u, 0u};
@@ -1734,25 +1737,26 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int u = 0; u < PW; ++u) {
         const int idx = t + u * kThreads;
-        const int h = idx / (kRT * (kp / 8)), rem = idx % (kRT * (kp / 8));
+        const int h = idx / (kRC * (kp / 8)), rem = idx % (kRC * (kp / 8));
         const int c = rem / (kp / 8), q = rem % (kp / 8);
-        if (idx < nw) *(uint4 *)(wst + (h * kRT + c) * wstride + q * 8) = v[u];
+        if (idx < nw) *(uint4 *)(wst + (h * kRC + c) * wstride + q * 8) = v[u];
       }
     }
     __syncthreads();
-    floatx4 acc[2][8];
+    constexpr int NCS = kRC / 16;
+    floatx4 acc[2][NCS];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 8; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < NCS; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KPM / 32; ++ks) {
       if (ks * 32 >= kp) break;
 #pragma unroll
-      for (int cs = 0; cs < 8; ++cs) {
+      for (int cs = 0; cs < NCS; ++cs) {
         const int c = cs * 16 + r16;
         const ushortx8 wh = *(const ushortx8 *)(wst + c * wstride + ks * 32 + g * 8);
-        const ushortx8 wl = *(const ushortx8 *)(wst + (kRT + c) * wstride + ks * 32 + g * 8);
+        const ushortx8 wl = *(const ushortx8 *)(wst + (kRC + c) * wstride + ks * 32 + g * 8);
 #pragma unroll
         for (int rs = 0; rs < 2; ++rs) {
           acc[rs][cs] = mfma16_bf16(uh[ks][rs], wh, acc[rs][cs]);
@@ -1765,7 +1769,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
     for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
-      for (int cs = 0; cs < 8; ++cs)
+      for (int cs = 0; cs < NCS; ++cs)
 #pragma unroll
         for (int q = 0; q < 4; ++q) lt[wave * 32 + rs * 16 + g * 4 + q][cs * 16 + r16] = acc[rs][cs][q];
   }
@@ -1803,11 +1807,11 @@ __global__ void __launch_bounds__(kThreads)
   if (!tcodes) return;
   __syncthreads();
   // ---- column blocks (along m) into R^T (n x m): thread t takes
-  // consecutive row blocks of column t % kRT, so its code stores are
+  // consecutive row blocks of column t % kRC, so its code stores are
   // adjacent in R^T's row
   {
-    constexpr int PER = kRT * RPB / kThreads;  // row blocks per thread
-    const int cc = t % kRT, rb0 = (t / kRT) * PER;
+    constexpr int PER = kRC * (kRT / B) / kThreads;  // row blocks per thread
+    const int cc = t % kRC, rb0 = (t / kRC) * PER;
     const int64_t col = col0 + cc;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -1951,7 +1955,7 @@ metis_status_t run_factors_and_residual(const SplitPlan &p, const T *A, int64_t 
         out->Vt_q.scales, nullptr, p.amax, p.uhl, p.whl);
   }
   // ---- pass 3: residual + quantization (NVFP4: a max pass first)
-  const dim3 rgrid((unsigned)cdiv(n, kRT), (unsigned)cdiv(m, kRT));
+  const dim3 rgrid((unsigned)cdiv(n, kRC), (unsigned)cdiv(m, kRT));
   if (nv) {
     residual_kernel<T, true, true, MEAN><<<rgrid, kThreads, 0, st>>>(
         A, m, n, lda, p.uhl, p.whl, kp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p.amax + 2, mu);
