@@ -33,6 +33,7 @@ using namespace metis;
 namespace {
 
 constexpr int kLpMax = 96;
+constexpr int kSketchRS = 2;  // 16-row groups per wave in the sketch (a workgroup: 64 kSketchRS rows)
 constexpr int kMaxPowerIterations = 16;  // Gaussian / sampled sketch width handled in LDS
 constexpr int kThreads = 256;
 constexpr int kGramRows = 128;     // rows per Gram chunk (narrow path)
@@ -184,7 +185,7 @@ __global__ void omega_transpose_kernel(const unsigned short *__restrict__ om, in
 // HL: the right-hand factor is an fp32 matrix carried as bf16 hi + lo
 // (omt holds its hi rows 0 .. lp - 1, then its lo rows), both multiplied, so
 // the product is fp32-accurate (the power iterations' Y = A Z).
-template <typename T, bool HL = false>
+template <typename T, bool HL = false, int RS = kSketchRS>
 __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda,
                                                           const unsigned short *__restrict__ omt, int l, int lp,
                                                           int64_t chunk, float *__restrict__ ysk) {
@@ -200,21 +201,21 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * 128 + wave * 32;
+  const int64_t row0 = (int64_t)blockIdx.x * (64 * RS) + wave * (16 * RS);
   const int s = blockIdx.y;
   const int64_t c_beg = (int64_t)s * chunk;
   const int64_t c_end = std::min<int64_t>(n, c_beg + chunk);
   const int nct = lt >> 4;
-  floatx4 acc[2][kLpMax / 16];
+  floatx4 acc[RS][kLpMax / 16];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < RS; ++a)
 #pragma unroll
     for (int b = 0; b < kLpMax / 16; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 pa[2][AV], ca[2][AV], po[NH][OPR];
+  uint4 pa[RS][AV], ca[RS][AV], po[NH][OPR];
   auto load = [&](int64_t c0) {
 #pragma unroll
-    for (int rs = 0; rs < 2; ++rs) {
+    for (int rs = 0; rs < RS; ++rs) {
       const int64_t row = row0 + rs * 16 + r16;
       const int64_t cc = c0 + g * 32;
       const bool ok = row < m && cc < c_end;
@@ -246,14 +247,14 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
         if (idx < lt * (KS / 8)) *(uint4 *)&lds[h][idx / (KS / 8)][(idx % (KS / 8)) * 8] = po[h][p];
       }
 #pragma unroll
-    for (int rs = 0; rs < 2; ++rs)
+    for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
       for (int j = 0; j < AV; ++j) ca[rs][j] = pa[rs][j];
     if (c0 + KS < c_end) load(c0 + KS);  // in flight while this step is multiplied
     __syncthreads();
-    ushortx8 a[2][4][NT];
+    ushortx8 a[RS][4][NT];
 #pragma unroll
-    for (int rs = 0; rs < 2; ++rs) {
+    for (int rs = 0; rs < RS; ++rs) {
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[rs][j][0] = __builtin_bit_cast(ushortx8, ca[rs][j]);
@@ -286,7 +287,7 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
           for (int h = 0; h < NH; ++h) {
             const ushortx8 b = *(const ushortx8 *)&lds[h][ct * 16 + r16][g * 32 + j * 8];
 #pragma unroll
-            for (int rs = 0; rs < 2; ++rs)
+            for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
               for (int tt = 0; tt < NT; ++tt) acc[rs][ct] = mfma16_bf16(a[rs][j][tt], b, acc[rs][ct]);
           }
@@ -295,7 +296,7 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
   }
   float *out = ysk + (int64_t)s * m * l;
 #pragma unroll
-  for (int rs = 0; rs < 2; ++rs)
+  for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
     for (int ct = 0; ct < kLpMax / 16; ++ct) {
       if (ct < nct) {
@@ -808,6 +809,38 @@ __global__ void __launch_bounds__(kCholThreads)
 
 // ----------------------------------------------- wide-sketch helpers (l > 96)
 // x = sum over parts (fixed order); rows x l elements.
+// x = sum over n_parts slabs (slab order), four elements per thread with
+// the loads of eight slabs in flight: the projection's partials are summed
+// by the whole GPU before their Gram (count % 4 == 0, 16-byte aligned).
+__global__ void __launch_bounds__(256)
+    sum_parts4_kernel(const float *__restrict__ parts, int n_parts, int64_t stride, int64_t count,
+                      float *__restrict__ x) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= count) return;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  int q = 0;
+  for (; q + 8 <= n_parts; q += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *(const float4 *)(parts + (int64_t)(q + u) * stride + i);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc.x += v[u].x;
+      acc.y += v[u].y;
+      acc.z += v[u].z;
+      acc.w += v[u].w;
+    }
+  }
+  for (; q < n_parts; ++q) {
+    const float4 v = *(const float4 *)(parts + (int64_t)q * stride + i);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *(float4 *)(x + i) = acc;
+}
+
 __global__ void sum_parts_kernel(const float *__restrict__ parts, int n_parts, int64_t stride, int64_t count,
                                  float *__restrict__ x) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -1844,7 +1877,7 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
   if (p.kind == METIS_OMEGA_GAUSSIAN) {
     omega_transpose_kernel<<<dim3((unsigned)cdiv(n, 256), lp), 256, 0, st>>>((const unsigned short *)omega, n, l, lp,
                                                                           p.omt);
-    sketch_kernel<T><<<dim3((unsigned)cdiv(m, 128), p.sk, lz), kThreads, 0, st>>>(A, m, n, lda, p.omt, l, lp,
+    sketch_kernel<T><<<dim3((unsigned)cdiv(m, 64 * kSketchRS), p.sk, lz), kThreads, 0, st>>>(A, m, n, lda, p.omt, l, lp,
                                                                                 p.sk_chunk, p.ysk);
     ysrc = p.ysk;
     yparts = p.sk;
@@ -1874,22 +1907,23 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     for (int it = 0; it < p.power; ++it) {
       project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
                                                                                    p.pk_rows, p.btp);
-      gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.btp, p.pk, n * l, n, l, lp, nullptr, p.bt, nullptr,
-                                                       p.gpart);
+      sum_parts4_kernel<<<(unsigned)cdiv(n * l, 1024), 256, 0, st>>>(p.btp, p.pk, n * l, n * l, p.bt);
+      gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.bt, 1, 0, n, l, lp, nullptr, nullptr, nullptr, p.gpart);
       gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
       chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
       gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.bt, 1, 0, n, l, lp, p.rinv, p.z1, nullptr, p.gpart);
       gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
       chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
       gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.z1, 1, 0, n, l, lp, p.rinv, nullptr, p.zt, nullptr);
-      sketch_kernel<T, true><<<dim3((unsigned)cdiv(m, 128), p.sk, lz), kThreads, 0, st>>>(A, m, n, lda, p.zt, l, lp,
+      sketch_kernel<T, true><<<dim3((unsigned)cdiv(m, 64 * kSketchRS), p.sk, lz), kThreads, 0, st>>>(A, m, n, lda, p.zt, l, lp,
                                                                                         p.sk_chunk, p.ysk);
       cholqr2_y(p.ysk, p.sk);
     }
     // ---- pass 2: projection B^T = A^T Q, then the Gram B B^T
     project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
                                                                                  p.pk_rows, p.btp);
-    gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.btp, p.pk, n * l, n, l, lp, nullptr, p.bt, nullptr, p.gpart);
+    sum_parts4_kernel<<<(unsigned)cdiv(n * l, 1024), 256, 0, st>>>(p.btp, p.pk, n * l, n * l, p.bt);
+    gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.bt, 1, 0, n, l, lp, nullptr, nullptr, nullptr, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
     // ---- small SVD and factors
     chol_small_kernel<true><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.wg, nullptr, p.wv);
