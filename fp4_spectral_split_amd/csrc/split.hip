@@ -13,8 +13,10 @@
 //                  range         CholeskyQR2 on Y: fp64 Gram, one-workgroup
 //                                 Cholesky + triangular inverse, Y R^-1, twice
 //   pass 2 over A  projection    B^T = A^T Q  (Q as bf16 hi + lo: fp32-accurate)
-//                  small SVD     eigen-decomposition of B B^T (fp64, l x l) by
-//                                 parallel cyclic Jacobi in one workgroup
+//                  small SVD     eigen-decomposition of B B^T (fp64, l x l) in one
+//                                 workgroup: Householder tridiagonalization,
+//                                 multisection, twisted-factorization vectors
+//                                 (l > 96: parallel cyclic Jacobi)
 //                  assemble      U = Q E_k, S = sqrt(lambda_k), V = B^T E_k / S
 //                  signs         largest-|entry| of each U column made positive
 //                  factors       U^T, V^T block-quantized along their length
@@ -648,11 +650,6 @@ __global__ void __launch_bounds__(kThreads)
 // m_p = 0 and a zero row and column of R^-1, as above.
 // Combined layout of row p: columns x >= p hold G'[p][x], columns x < p hold
 // L^-1[p][x] (its unit diagonal is implicit).
-// FACTOR = true factors G + delta I instead, delta = 4 l eps max(diag G), and
-// writes the Cholesky factor L = R^T column by column (column j of L = row j
-// of R, lp x lp, zero padded) for the one-sided Jacobi below; the shift keeps
-// every column of L nonzero, so every eigenvector comes out of the rotations.
-// shift[0] = delta.
 constexpr int kCholThreads = 1024;
 // a row is shared by floor(threads / l) threads; each owns every tpr-th
 // column of it: at most 10 columns (l = 96)
@@ -664,10 +661,8 @@ __device__ __forceinline__ double recip_f64(double d) {
   return fma(r, fma(-d, r, 1.0), r);
 }
 
-template <bool FACTOR>
 __global__ void __launch_bounds__(kCholThreads)
-    chol_small_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ out, int *info,
-                      double *__restrict__ shift) {
+    chol_small_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ out, int *info) {
   __shared__ double C[kLpMax][kLpMax + 1];
   __shared__ double ipiv[kLpMax];  // 1 / d_j, 0 for an absent pivot
   __shared__ double rs[kLpMax];    // d_j^-1/2, 0 for an absent pivot
@@ -689,7 +684,7 @@ __global__ void __launch_bounds__(kCholThreads)
       const int e = t + u * kCholThreads, p = e / l, x = e - (e / l) * l;
       if (e < l * l) C[p][x] = v[u];
     }
-    if (!FACTOR) {
+    {
       // the second CholeskyQR pass sees G = I + E with E tiny: then
       // R = I + F with F = triu(E), diag halved, and R^-1 = I - F up to
       // O(E^2) (below 1e-10 here), with no elimination at all. A dead
@@ -727,12 +722,8 @@ __global__ void __launch_bounds__(kCholThreads)
     if (t == 0) {
       const double tol = (double)l * 2.220446049250313e-16 * md;
       tol_s = tol;
-      if (FACTOR) shift[0] = 4.0 * tol;
     }
   }
-  __syncthreads();
-  if (FACTOR)
-    for (int i = t; i < l; i += kCholThreads) C[i][i] += 4.0 * tol_s;
   __syncthreads();
   if (t == 0) {
     const double d = C[0][0];
@@ -758,7 +749,7 @@ __global__ void __launch_bounds__(kCholThreads)
 #pragma unroll
       for (int s = 0; s < kCholSlots; ++s) {
         const int x = q + tpr * s;
-        if (x < l && ((!FACTOR && x <= j) || x >= p)) {
+        if (x < l && (x <= j || x >= p)) {
           const double w = x == j ? 1.0 : C[j][x];
           v[s] = fma(-m, w, v[s]);
         }
@@ -784,20 +775,12 @@ __global__ void __launch_bounds__(kCholThreads)
     dead[j] = !alive;
   }
   __syncthreads();
-  if (FACTOR) {
-    // column j of L = row j of R: R[j][x] = G'[j][x] * d_j^-1/2 for x >= j
-    for (int e = t; e < lp * lp; e += kCholThreads) {
-      const int j = e / lp, x = e - (e / lp) * lp;
-      out[e] = (j < l && x < l && x >= j) ? C[j][x] * rs[j] : 0.0;
-    }
-  } else {
-    // R^-1[i][c] = L^-1[c][i] * d_c^-1/2 for i <= c < l; zero elsewhere
-    for (int e = t; e < lp * lp; e += kCholThreads) {
-      const int i = e / lp, c = e - (e / lp) * lp;
-      double r = 0.0;
-      if (c < l && i <= c) r = (i == c ? 1.0 : C[c][i]) * rs[c];
-      out[e] = r;
-    }
+  // R^-1[i][c] = L^-1[c][i] * d_c^-1/2 for i <= c < l; zero elsewhere
+  for (int e = t; e < lp * lp; e += kCholThreads) {
+    const int i = e / lp, c = e - (e / lp) * lp;
+    double r = 0.0;
+    if (c < l && i <= c) r = (i == c ? 1.0 : C[c][i]) * rs[c];
+    out[e] = r;
   }
   if (t == 0 && info) {
     int first = 0;
@@ -1248,178 +1231,415 @@ __global__ void __launch_bounds__(kJacThreads)
 #undef V
 }
 
-// One-sided (Hestenes) Jacobi on the columns of the Cholesky factor L of
-// G + delta I (l <= kLpMax). Rotating pairs of columns until all are mutually
-// orthogonal gives L J = U diag(sigma'); then G + delta I = U diag(sigma'^2) U^T,
-// so the normalized columns are the eigenvectors of G and sigma'^2 - delta its
-// eigenvalues (= the squared singular values of B). No rotation is
-// accumulated. Pairs follow the round-robin schedule (position 0 fixed, the
-// others rotate one place per round, position i meets position lp - 1 - i);
-// each pair is handled by 8 lanes that form the three dot products with
-// cross-lane (DPP) sums, so every lane of the group computes the same
-// rotation. One barrier per round; columns live in LDS.
-// LDS layout: lane j of a group owns rows j E .. j E + E - 1 (E = lp / 8) of
-// both columns and reads them as 16-byte pairs. Its chunk starts E2 doubles
-// after lane j - 1's, E2 = E rounded up to 2 mod 4, so the 8 lanes of a group
-// touch 32 distinct banks; the column stride 8 E2 is 16 mod 32 doubles, which
-// puts the chunks of columns of different parity on the other 32 banks.
-constexpr int kOsThreads = 384;           // 8 lanes per column pair, up to 48 pairs
+// ================================================ tridiagonal eigensolver
+// All wanted eigenpairs of the symmetric l x l matrix G (upper triangle read,
+// fp64) in one workgroup, in four stages:
+//   1. Householder reduction G = H T H^T to tridiagonal T (H = H_0 ... H_{l-3}).
+//      Thread (r, j) holds row r of the active block at columns j, j + 8, ...
+//      in registers; the column being reduced and p = beta A v pass through
+//      LDS, so a reflector costs two barriers. Waves whose rows are all
+//      eliminated (or beyond l) only keep the barriers.
+//   2. Eigenvalues of T by multisection on Sturm counts of the LDL^T form:
+//      eight lanes test eight points of an eigenvalue's bracket at once and
+//      keep the ninth part that holds it; no barriers. When T does not split,
+//      only the k largest are computed.
+//   3. Eigenvectors of T from twisted factorizations T - lambda I = N_r D N_r^T,
+//      the twist r where |gamma_r| is least (one thread per vector; the
+//      factorization's pivots are staged in the vector's own LDS column),
+//      Gram-Schmidt inside chains of eigenvalues closer than 1e-7 ||T||.
+//   4. Back-transformation x = H z, sixteen lanes per vector, no barriers.
+// Off-diagonals at or below 2^-52 ||T|| split T into blocks that are solved
+// separately; an eigenvalue's slot index is its place in its block.
+// Output as the Jacobi kernel: evec[row * lp + rank] (descending eigenvalue,
+// unit columns, zero beyond l rows and k columns), sig_inv[rank] = 1 / sigma
+// with sigma = sqrt(lambda) (0 for sigma <= 2^-24 sigma_max and for ranks
+// whose eigenvalue was not computed), S[rank < k].
+constexpr int kEigThreads = 1024;
+constexpr int kEigCols = kLpMax / 8;  // register columns of a row segment
+constexpr int kEigIters = 16;         // each keeps 1/9 of the bracket: 9^-16 < 2^-50
 
-__host__ __device__ constexpr int os_e2(int e) { return (e % 4 == 2) ? e : e + 2; }
-
-
-// E = lp / 8 is a template parameter so that a round is straight-line code;
-// all rotated values are formed before the first store, so the stores issue
-// back to back instead of each waiting for the previous one's data registers.
-template <int E>
-__global__ void __launch_bounds__(kOsThreads)
-    jacobi_os_kernel(const double *__restrict__ lcol, const double *__restrict__ shift, int l, int k, int max_sweeps,
-                     double *__restrict__ evec, double *__restrict__ sig_inv, float *__restrict__ S) {
-  constexpr int E2 = os_e2(E), CS = 8 * E2, N = 8 * E, H = 4 * E, lp = N, EH = E / 2;
-  __shared__ __align__(16) double X[N * CS];
-  __shared__ double nrm[N];  // squared column norms, carried from round 0 of a sweep
-  __shared__ double lam[N];
-  __shared__ int rank_s[N];
-  __shared__ int rotated;
-  const int t = threadIdx.x, grp = t >> 3, j = t & 7;
-  stage_batched<(N * N + kOsThreads - 1) / kOsThreads>(X, lcol, lp * lp, [](int i) { return i; }, [](int i) {
-    const int c = i / lp, r = i - (i / lp) * lp;
-    return c * CS + (r / E) * E2 + r % E;
-  });
-  const double delta = shift[0];
-  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-    if (t == 0) rotated = 0;
-    __syncthreads();
-    for (int round = 0; round < N - 1; ++round) {
-      if (grp < H) {
-        int a = grp - 1 + round, b = N - 2 - grp + round;  // position - 1 + round
-        a = a >= N - 1 ? a - (N - 1) : a;
-        b = b >= N - 1 ? b - (N - 1) : b;
-        a = grp == 0 ? 0 : a + 1;
-        b = b + 1;
-        const int cp = a < b ? a : b, cq = a < b ? b : a;
-        double2 *xpp = (double2 *)(X + cp * CS + j * E2);
-        double2 *xqp = (double2 *)(X + cq * CS + j * E2);
-        double2 xp[EH], xq[EH];
-#pragma unroll
-        for (int e = 0; e < EH; ++e) {
-          xp[e] = xpp[e];
-          xq[e] = xqp[e];
-        }
-        double ga0 = 0.0, ga1 = 0.0;
-#pragma unroll
-        for (int e = 0; e < EH; ++e) {
-          ga0 = fma(xp[e].x, xq[e].x, ga0);
-          ga1 = fma(xp[e].y, xq[e].y, ga1);
-        }
-        const double ga = group8_sum(ga0 + ga1);
-        double al, be;
-        if (round == 0) {
-          double al0 = 0.0, al1 = 0.0, be0 = 0.0, be1 = 0.0;
-#pragma unroll
-          for (int e = 0; e < EH; ++e) {
-            al0 = fma(xp[e].x, xp[e].x, al0);
-            al1 = fma(xp[e].y, xp[e].y, al1);
-            be0 = fma(xq[e].x, xq[e].x, be0);
-            be1 = fma(xq[e].y, xq[e].y, be1);
-          }
-          al = group8_sum(al0 + al1);
-          be = group8_sum(be0 + be1);
-        } else {
-          al = nrm[cp];
-          be = nrm[cq];
-        }
-        if (ga != 0.0 && ga * ga > 1e-26 * al * be) {
-          // angle from hardware estimates (fp32-level accuracy is ample: a
-          // pair left slightly non-orthogonal is rotated again next sweep);
-          // c and s normalized to fp64 by Newton steps on 1 / sqrt(1 + t^2)
-          const float zeta = (float)((be - al) * (0.5 * __builtin_amdgcn_rcp(ga)));
-          const float az = fabsf(zeta);
-          float tf = az > 1e18f ? 0.5f / az
-                                : __builtin_amdgcn_rcpf(az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.0f)));
-          tf = zeta >= 0.0f ? tf : -tf;
-          const double tt = (double)tf, x = fma(tt, tt, 1.0);
-          double c = __builtin_amdgcn_rsq(x);
-          c = fma(0.5 * c, fma(-x * c, c, 1.0), c);
-          c = fma(0.5 * c, fma(-x * c, c, 1.0), c);
-          const double sn = c * tt;
-          double2 np[EH], nq[EH];
-#pragma unroll
-          for (int e = 0; e < EH; ++e) {
-            np[e] = make_double2(c * xp[e].x - sn * xq[e].x, c * xp[e].y - sn * xq[e].y);
-            nq[e] = make_double2(sn * xp[e].x + c * xq[e].x, sn * xp[e].y + c * xq[e].y);
-          }
-#pragma unroll
-          for (int e = 0; e < EH; ++e) {
-            xpp[e] = np[e];
-            xqp[e] = nq[e];
-          }
-          if (j == 0) {
-            // norms after the applied rotation (exact for the t used)
-            const double c2 = c * c;
-            nrm[cp] = c2 * fma(-tt, fma(-tt, be, 2.0 * ga), al);
-            nrm[cq] = c2 * fma(tt, fma(tt, al, 2.0 * ga), be);
-            rotated = 1;
-          }
-        } else if (round == 0 && j == 0) {
-          nrm[cp] = al;
-          nrm[cq] = be;
-        }
-      }
-      __syncthreads();
-    }
-    if (!rotated) break;
-    __syncthreads();
-  }
-  // squared column norms sigma'^2
-  for (int c = grp; c < N; c += kOsThreads / 8) {
-    double s2 = 0.0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) s2 = fma(X[c * CS + j * E2 + e], X[c * CS + j * E2 + e], s2);
-    s2 = group8_sum(s2);
-    if (j == 0) lam[c] = s2;
-  }
-  __syncthreads();
-  if (t < N) {
-    int r = 0;
-    if (t < l) {
-      const double d = lam[t];
-      for (int q = 0; q < l; ++q) {
-        const double e = lam[q];
-        r += (e > d) || (e == d && q < t);
-      }
-    } else {
-      r = t;
-    }
-    rank_s[t] = r;
-  }
-  __syncthreads();
-  for (int idx = t; idx < N * N; idx += kOsThreads) {
-    const int row = idx / N, col = idx - (idx / N) * N;
-    const double nrm2 = lam[col];
-    const double v = X[col * CS + (row / E) * E2 + row % E];
-    evec[row * N + rank_s[col]] = (col < l && nrm2 > 0.0) ? v / sqrt(nrm2) : 0.0;
-  }
-  if (t < N) {
-    double smax = 0.0;
-    for (int q = 0; q < l; ++q) smax = fmax(smax, sqrt(fmax(lam[q] - delta, 0.0)));
-    double sg = t < l ? sqrt(fmax(lam[t] - delta, 0.0)) : 0.0;
-    if (!(sg > smax * 5.9604644775390625e-08)) sg = 0.0;
-    const int r = rank_s[t];
-    sig_inv[r] = sg > 0.0 ? 1.0 / sg : 0.0;
-    if (r < k) S[r] = (float)sg;
-  }
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
+                          __builtin_amdgcn_readlane(__double2loint(v), lane));
 }
 
-void launch_jacobi_os(const double *lcol, const double *shift, int l, int lp, int k, int max_sweeps, double *evec,
-                      double *sig_inv, float *S, hipStream_t st) {
-  switch (lp / 8) {
-    case 2: jacobi_os_kernel<2><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
-    case 4: jacobi_os_kernel<4><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
-    case 6: jacobi_os_kernel<6><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
-    case 8: jacobi_os_kernel<8><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
-    case 10: jacobi_os_kernel<10><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
-    default: jacobi_os_kernel<12><<<1, kOsThreads, 0, st>>>(lcol, shift, l, k, max_sweeps, evec, sig_inv, S); break;
+// Sum over the whole wave (every lane active), the same bits in every lane:
+// DPP within rows of 16 lanes, then the four row sums read as scalars.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = group8_sum(v);
+  v += dpp_f64<0x140>(v);  // row_mirror: lane i with lane 15 - i
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// Sum over an aligned group of 16 lanes (row_ror:8 pairs the two halves).
+__device__ __forceinline__ double group16_sum(double v) {
+  v = group8_sum(v);
+  return v + dpp_f64<0x128>(v);
+}
+
+// One step of the LDL^T pivot recurrence q' = (d - x) - e^2 / q, a pivot
+// smaller than pivmin replaced by -pivmin. The reciprocal estimate (about
+// 2^-25 relative) gets one Newton step, which leaves about 2^-50.
+__device__ __forceinline__ double ldl_step(double dmx, double e2, double q, double pivmin) {
+  double rq = __builtin_amdgcn_rcp(q);
+  rq = fma(rq, fma(-q, rq, 1.0), rq);
+  q = fma(-e2, rq, dmx);
+  return fabs(q) < pivmin ? -pivmin : q;
+}
+
+__device__ __forceinline__ double ldl_first(double dmx, double pivmin) { return fabs(dmx) < pivmin ? -pivmin : dmx; }
+
+// Highest set position <= p (p < 128) of the 128-bit mask (m1:m0); -1 if none.
+__device__ __forceinline__ int last_set_upto(unsigned long long m0, unsigned long long m1, int p) {
+  if (p >= 64) {
+    const unsigned long long b1 = m1 & ((2ull << (p - 64)) - 1ull);
+    if (b1) return 127 - __builtin_clzll(b1);
+    return m0 ? 63 - __builtin_clzll(m0) : -1;
+  }
+  const unsigned long long b0 = m0 & ((2ull << p) - 1ull);
+  return b0 ? 63 - __builtin_clzll(b0) : -1;
+}
+
+// Lowest set position >= p (p < 128) of (m1:m0); -1 if none.
+__device__ __forceinline__ int first_set_from(unsigned long long m0, unsigned long long m1, int p) {
+  if (p < 64) {
+    const unsigned long long c0 = m0 & ~((1ull << p) - 1ull);
+    if (c0) return __builtin_ctzll(c0);
+    return m1 ? 64 + __builtin_ctzll(m1) : -1;
+  }
+  const unsigned long long c1 = m1 & ~((1ull << (p - 64)) - 1ull);
+  return c1 ? 64 + __builtin_ctzll(c1) : -1;
+}
+
+__global__ void __launch_bounds__(kEigThreads)
+    tridiag_eig_kernel(const double *__restrict__ g, int l, int lp, int k, double *__restrict__ evec,
+                       double *__restrict__ sig_inv, float *__restrict__ S) {
+  __shared__ double V[kLpMax][kLpMax];      // V[j][r]: reflector j at rows j + 1 .. l - 1, zero elsewhere
+  __shared__ double Z[kLpMax][kLpMax + 1];  // Z[row][rank]: eigenvectors of T
+  __shared__ double xb[2][kLpMax];          // column j of the active block (diagonal included)
+  __shared__ double pv[kLpMax], dg[kLpMax], eo[kLpMax], ee[kLpMax], e2[kLpMax], bet[kLpMax], lam[kLpMax];
+  __shared__ double2 de[kLpMax];            // (d_q, e_{q-1}^2) for the Sturm counts
+  __shared__ double dots[kLpMax];
+  __shared__ int blo[kLpMax], bhi[kLpMax], slot_of[kLpMax], chain[kLpMax];
+  __shared__ double nrm_s;
+  __shared__ int any_chain;
+  const int n = l, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = t >> 3, cj = t & 7;
+
+  // ---- stage 1: Householder tridiagonalization
+  double a[kEigCols];
+#pragma unroll
+  for (int u = 0; u < kEigCols; ++u) {
+    const int c = cj + 8 * u;
+    const int lo = r < c ? r : c, hi = r < c ? c : r;
+    a[u] = (r < n && c < n) ? g[lo * lp + hi] : 0.0;
+  }
+  for (int e = t; e < kLpMax * kLpMax; e += kEigThreads) (&V[0][0])[e] = 0.0;
+  if (r < n && cj == 0) xb[0][r] = a[0];
+  __syncthreads();
+  for (int j = 0; j + 2 < n; ++j) {
+    const double *x = xb[j & 1];
+    double *xn = xb[(j + 1) & 1];
+    const bool wact = 8 * wave + 7 > j && 8 * wave < n;  // the wave holds a row of the active block
+    double alpha = 0.0, beta = 0.0;
+    if (wact) {
+      double s2 = 0.0;
+      for (int q = j + 1 + lane; q < n; q += 64) s2 = fma(x[q], x[q], s2);
+      const double a2 = wave_sum_f64(s2);
+      const double x0 = x[j + 1], nrm = sqrt(a2);
+      alpha = x0 >= 0.0 ? -nrm : nrm;
+      beta = a2 > 0.0 ? recip_f64(nrm * (nrm + fabs(x0))) : 0.0;
+      if (r > j && r < n) {
+        // (A v)_r with v = x - alpha e_{j+1}: the alpha term is A[r][j + 1]
+        double sx = 0.0, sc = 0.0;
+#pragma unroll
+        for (int u = 0; u < kEigCols; ++u) {
+          const int c = cj + 8 * u;
+          const bool act = c > j && c < n;
+          sx = fma(a[u], act ? x[c] : 0.0, sx);
+          sc += c == j + 1 ? a[u] : 0.0;
+        }
+        const double s = group8_sum(fma(-alpha, sc, sx));
+        if (cj == 0) pv[r] = beta * s;
+        if (cj == 1) V[j][r] = r == j + 1 ? x[r] - alpha : x[r];
+        if (cj == 2 && r == j + 1) {
+          dg[j] = x[j];
+          eo[j] = alpha;
+          bet[j] = beta;
+        }
+      }
+    }
+    __syncthreads();
+    // A <- A - v w^T - w v^T with w = p - (beta p.v / 2) v
+    if (wact) {
+      double spv = 0.0;
+      for (int q = j + 1 + lane; q < n; q += 64) spv = fma(pv[q], q == j + 1 ? x[q] - alpha : x[q], spv);
+      const double kk = 0.5 * beta * wave_sum_f64(spv);
+      if (r > j && r < n) {
+        const double vr = r == j + 1 ? x[r] - alpha : x[r];
+        const double wr = fma(-kk, vr, pv[r]);
+#pragma unroll
+        for (int u = 0; u < kEigCols; ++u) {
+          const int c = cj + 8 * u;
+          if (c > j && c < n) {
+            const double vc = c == j + 1 ? x[c] - alpha : x[c];
+            const double wc = fma(-kk, vc, pv[c]);
+            a[u] = fma(-vr, wc, fma(-wr, vc, a[u]));
+            if (c == j + 1) xn[r] = a[u];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (n >= 2) {
+    const double *x = xb[(n - 2) & 1];
+    if (t == 0) {
+      dg[n - 2] = x[n - 2];
+      eo[n - 2] = x[n - 1];
+    }
+    if (r == n - 1) {
+#pragma unroll
+      for (int u = 0; u < kEigCols; ++u)
+        if (cj + 8 * u == n - 1) dg[n - 1] = a[u];
+    }
+  } else if (t == 0) {
+    dg[0] = xb[0][0];
+  }
+  __syncthreads();
+
+  // ---- stage 2: Gershgorin bracket, splitting, multisection
+  double glo = 1.0e308, ghi = -1.0e308, tn = 0.0, e2m = 0.0;
+  for (int i = lane; i < n; i += 64) {
+    const double rad = (i > 0 ? fabs(eo[i - 1]) : 0.0) + (i < n - 1 ? fabs(eo[i]) : 0.0);
+    glo = fmin(glo, dg[i] - rad);
+    ghi = fmax(ghi, dg[i] + rad);
+    tn = fmax(tn, fabs(dg[i]) + rad);
+    if (i < n - 1) e2m = fmax(e2m, eo[i] * eo[i]);
+  }
+  glo = -wave_max(-glo);
+  ghi = wave_max(ghi);
+  tn = wave_max(tn);
+  e2m = wave_max(e2m);
+  const double tol_split = 2.220446049250313e-16 * tn;
+  const double pivmin = 2.2250738585072014e-308 * fmax(1.0, e2m);
+  if (t < n) {
+    const double e = t < n - 1 ? (fabs(eo[t]) <= tol_split ? 0.0 : eo[t]) : 0.0;
+    ee[t] = e;
+    e2[t] = e * e;
+    const double ep = t > 0 ? (fabs(eo[t - 1]) <= tol_split ? 0.0 : eo[t - 1]) : 0.0;
+    de[t] = make_double2(dg[t], ep * ep);
+  }
+  if (wave == 0) {
+    // blocks: a split after position s where e_s was zeroed
+    const unsigned long long m0 = __ballot(lane < n - 1 && fabs(eo[lane]) <= tol_split);
+    const unsigned long long m1 = __ballot(lane + 64 < n - 1 && fabs(eo[lane + 64 < kLpMax ? lane + 64 : 0]) <= tol_split);
+    for (int h = 0; h < 2; ++h) {
+      const int i = lane + 64 * h;
+      if (i < n) {
+        const int s = i > 0 ? last_set_upto(m0, m1, i - 1) : -1;
+        const int e = first_set_from(m0, m1, i);
+        blo[i] = s + 1;
+        bhi[i] = e < 0 ? n - 1 : e;
+      }
+    }
+  }
+  __syncthreads();
+  const bool one_block = bhi[0] == n - 1;
+  const int nslot = one_block ? k : n, slot0 = one_block ? n - k : 0;
+  {
+    const int gi = t >> 3, js = t & 7;
+    if (gi < nslot) {
+      const int i = slot0 + gi, b0 = blo[i], b1 = bhi[i], il = i - b0;
+      const double pad = 8.881784197001252e-16 * fmax(fabs(glo), fabs(ghi)) + pivmin;
+      double lo = glo - pad, hi = ghi + pad;
+      const double fj = (double)(js + 1) * (1.0 / 9.0);
+      for (int it = 0; it < kEigIters; ++it) {
+        const double w = hi - lo, xs = fma(w, fj, lo);
+        double q = ldl_first(de[b0].x - xs, pivmin);
+        int cnt = q < 0.0;
+#pragma unroll 4
+        for (int kq = b0 + 1; kq <= b1; ++kq) {
+          const double2 v = de[kq];
+          q = ldl_step(v.x - xs, v.y, q, pivmin);
+          cnt += q < 0.0;
+        }
+        const unsigned long long bal = __ballot(cnt > il);
+        const unsigned m8 = (unsigned)(bal >> (lane & ~7)) & 0xFFu;
+        const int qf = m8 ? __builtin_ctz(m8) : 8;
+        const double nlo = qf > 0 ? fma(w, (double)qf * (1.0 / 9.0), lo) : lo;
+        const double nhi = qf < 8 ? fma(w, (double)(qf + 1) * (1.0 / 9.0), lo) : hi;
+        lo = nlo;
+        hi = nhi;
+      }
+      if (js == 0) lam[i] = 0.5 * (lo + hi);
+    }
+  }
+  __syncthreads();
+  if (t < nslot) {
+    const int i = slot0 + t;
+    int rk;
+    if (one_block) {
+      rk = n - 1 - i;  // slots of one block ascend
+    } else {
+      const double d = lam[i];
+      rk = 0;
+      for (int q = 0; q < n; ++q) {
+        const double e = lam[q];
+        rk += (e > d) || (e == d && q < i);
+      }
+    }
+    slot_of[rk] = i;
+  }
+  __syncthreads();
+  if (t < lp) {
+    double sg = 0.0;
+    if (t < nslot) {
+      const double smax = sqrt(fmax(lam[slot_of[0]], 0.0));
+      sg = sqrt(fmax(lam[slot_of[t]], 0.0));
+      if (!(sg > smax * 5.9604644775390625e-08)) sg = 0.0;
+    }
+    sig_inv[t] = sg > 0.0 ? 1.0 / sg : 0.0;
+    if (t < k) S[t] = (float)sg;
+  }
+  if (wave == kEigThreads / 64 - 1) {
+    // chains of consecutive ranks whose eigenvalues are closer than 1e-7 ||T||
+    bool brk[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = lane + 64 * h;
+      brk[h] = c == 0 || c >= k || !(lam[slot_of[c - 1]] - lam[slot_of[c]] < 1.0e-7 * tn);
+    }
+    const unsigned long long m0 = __ballot(brk[0]), m1 = __ballot(brk[1]);
+    for (int h = 0; h < 2; ++h) {
+      const int c = lane + 64 * h;
+      if (c < k) chain[c] = last_set_upto(m0, m1, c);
+    }
+    if (lane == 0) any_chain = (~m0 | ~m1) != 0ull;
+  }
+
+  // ---- stage 3: eigenvectors of T, one thread per wanted rank
+  if (t < k) {
+    const int c = t, i = slot_of[c], b0 = blo[i], b1 = bhi[i];
+    const double lm = lam[i];
+    for (int q = 0; q < n; ++q)
+      if (q < b0 || q > b1) Z[q][c] = 0.0;
+    // forward pivots D+ into the column
+    double dp = ldl_first(dg[b0] - lm, pivmin);
+    Z[b0][c] = dp;
+    for (int q = b0; q < b1; ++q) {
+      const double2 v = de[q + 1];
+      dp = ldl_step(v.x - lm, v.y, dp, pivmin);
+      Z[q + 1][c] = dp;
+    }
+    // backward pivots D-, twist where |gamma| = |D+ + D- - (d - lambda)| is least
+    double dm = ldl_first(dg[b1] - lm, pivmin);
+    double best = fabs(Z[b1][c] + dm - (dg[b1] - lm));
+    int tw = b1;
+    for (int q = b1 - 1; q >= b0; --q) {
+      dm = ldl_step(dg[q] - lm, e2[q], dm, pivmin);
+      const double gm = fabs(Z[q][c] + dm - (dg[q] - lm));
+      if (gm <= best) {
+        best = gm;
+        tw = q;
+      }
+    }
+    // z_q = -(e_q / D+_q) z_{q+1} above the twist
+    double z = 1.0, nz = 1.0;
+    for (int q = tw - 1; q >= b0; --q) {
+      z = -(ee[q] * recip_f64(Z[q][c])) * z;
+      Z[q][c] = z;
+      nz = fma(z, z, nz);
+    }
+    // D- again below the twist (same operations, same values), then
+    // z_{q+1} = -(e_q / D-_{q+1}) z_q
+    if (b1 > tw) {
+      dm = ldl_first(dg[b1] - lm, pivmin);
+      Z[b1][c] = dm;
+      for (int q = b1 - 1; q > tw; --q) {
+        dm = ldl_step(dg[q] - lm, e2[q], dm, pivmin);
+        Z[q][c] = dm;
+      }
+    }
+    Z[tw][c] = 1.0;
+    z = 1.0;
+    for (int q = tw; q < b1; ++q) {
+      z = -(ee[q] * recip_f64(Z[q + 1][c])) * z;
+      Z[q + 1][c] = z;
+      nz = fma(z, z, nz);
+    }
+    const double sc = 1.0 / sqrt(nz);
+    for (int q = b0; q <= b1; ++q) Z[q][c] *= sc;
+  }
+  __syncthreads();
+  // Gram-Schmidt (twice) of a chained vector against its chain predecessors
+  // of the same block
+  if (any_chain) {
+    for (int c = 1; c < k; ++c) {
+      const int c0 = chain[c];
+      if (c0 == c) continue;
+      const int bc = blo[slot_of[c]];
+      for (int pass = 0; pass < 2; ++pass) {
+        for (int b = c0 + wave; b < c; b += kEigThreads / 64) {
+          double s = 0.0;
+          for (int q = lane; q < n; q += 64) s = fma(Z[q][b], Z[q][c], s);
+          s = wave_sum_f64(s);
+          if (lane == 0) dots[b] = blo[slot_of[b]] == bc ? s : 0.0;
+        }
+        __syncthreads();
+        if (t < n) {
+          double zc = Z[t][c];
+          for (int b = c0; b < c; ++b) zc = fma(-dots[b], Z[t][b], zc);
+          Z[t][c] = zc;
+        }
+        __syncthreads();
+      }
+      if (wave == 0) {
+        double s = 0.0;
+        for (int q = lane; q < n; q += 64) s = fma(Z[q][c], Z[q][c], s);
+        s = wave_sum_f64(s);
+        if (lane == 0) nrm_s = s;
+      }
+      __syncthreads();
+      if (t < n && nrm_s > 0.0) Z[t][c] *= 1.0 / sqrt(nrm_s);
+      __syncthreads();
+    }
+  }
+
+  // ---- stage 4: x = H_0 H_1 ... H_{l-3} z, lanes (vector, rows i16 + 16 u)
+  constexpr int ZR = kLpMax / 16;
+  const int i16 = t & 15;
+  for (int c = t >> 4; c < ((k + 63) & ~63); c += kEigThreads / 16) {
+    const bool act = c < k;
+    double z[ZR];
+#pragma unroll
+    for (int u = 0; u < ZR; ++u) {
+      const int row = i16 + 16 * u;
+      z[u] = (act && row < n) ? Z[row][c] : 0.0;
+    }
+    for (int j = n - 3; j >= 0; --j) {
+      double vj[ZR], s = 0.0;
+#pragma unroll
+      for (int u = 0; u < ZR; ++u) {
+        vj[u] = V[j][i16 + 16 * u];
+        s = fma(vj[u], z[u], s);
+      }
+      const double f = bet[j] * group16_sum(s);
+#pragma unroll
+      for (int u = 0; u < ZR; ++u) z[u] = fma(-f, vj[u], z[u]);
+    }
+    if (act) {
+#pragma unroll
+      for (int u = 0; u < ZR; ++u) {
+        const int row = i16 + 16 * u;
+        if (row < n) evec[row * lp + c] = z[u];
+      }
+    }
+  }
+  // zeros beyond l rows and k columns
+  for (int e = t; e < lp * lp; e += kEigThreads) {
+    const int row = e / lp, col = e - (e / lp) * lp;
+    if (row >= n || col >= k) evec[e] = 0.0;
   }
 }
 
@@ -1895,10 +2115,10 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
                                                        parts > 1 ? p.y : nullptr, nullptr, p.gpart);
       const float *y = parts > 1 ? p.y : src;
       gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
-      chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws, nullptr);
+      chol_small_kernel<<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws);
       gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(y, 1, 0, m, l, lp, p.rinv, p.q1, nullptr, p.gpart);
       gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
-      chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
+      chol_small_kernel<<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws);
       gram_kernel<<<p.gy_parts, kGramThreads, 0, st>>>(p.q1, 1, 0, m, l, lp, p.rinv, p.q, p.qt, nullptr);
     };
     cholqr2_y(ysrc, yparts);
@@ -1910,10 +2130,10 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
       sum_parts4_kernel<<<(unsigned)cdiv(n * l, 1024), 256, 0, st>>>(p.btp, p.pk, n * l, n * l, p.bt);
       gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.bt, 1, 0, n, l, lp, nullptr, nullptr, nullptr, p.gpart);
       gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
-      chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
+      chol_small_kernel<<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws);
       gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.bt, 1, 0, n, l, lp, p.rinv, p.z1, nullptr, p.gpart);
       gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
-      chol_small_kernel<false><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, nullptr);
+      chol_small_kernel<<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws);
       gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.z1, 1, 0, n, l, lp, p.rinv, nullptr, p.zt, nullptr);
       sketch_kernel<T, true><<<dim3((unsigned)cdiv(m, 64 * kSketchRS), p.sk, lz), kThreads, 0, st>>>(A, m, n, lda, p.zt, l, lp,
                                                                                         p.sk_chunk, p.ysk);
@@ -1926,8 +2146,7 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.bt, 1, 0, n, l, lp, nullptr, nullptr, nullptr, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
     // ---- small SVD and factors
-    chol_small_kernel<true><<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.wg, nullptr, p.wv);
-    launch_jacobi_os(p.wg, p.wv, l, lp, k, 40, p.evec, p.sig_inv, out->S, st);
+    tridiag_eig_kernel<<<1, kEigThreads, 0, st>>>(p.gram, l, lp, k, p.evec, p.sig_inv, out->S);
     assemble_u_kernel<<<p.am_parts, kThreads, 0, st>>>(p.q, m, l, lp, k, p.evec, p.am_rows, out->U, p.am_val,
                                                        p.am_idx);
     assemble_v_kernel<<<(unsigned)cdiv(n, asm_chunk_rows(k)), kThreads, 0, st>>>(p.bt, n, l, lp, k, p.evec,
