@@ -1316,7 +1316,8 @@ __global__ void __launch_bounds__(kEigThreads)
                        double *__restrict__ sig_inv, float *__restrict__ S) {
   __shared__ double V[kLpMax][kLpMax];      // V[j][r]: reflector j at rows j + 1 .. l - 1, zero elsewhere
   __shared__ double Z[kLpMax][kLpMax + 1];  // Z[row][rank]: eigenvectors of T
-  __shared__ double xb[2][kLpMax];          // column j of the active block (diagonal included)
+  __shared__ double xb[2][kLpMax], yb[2][kLpMax];  // columns j and j + 1 of the active block
+  __shared__ double nx2[2];                         // squared norm of xb
   __shared__ double pv[kLpMax], dg[kLpMax], eo[kLpMax], ee[kLpMax], e2[kLpMax], bet[kLpMax], lam[kLpMax];
   __shared__ double2 de[kLpMax];            // (d_q, e_{q-1}^2) for the Sturm counts
   __shared__ double dots[kLpMax];
@@ -1326,7 +1327,15 @@ __global__ void __launch_bounds__(kEigThreads)
   const int n = l, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r = t >> 3, cj = t & 7;
 
-  // ---- stage 1: Householder tridiagonalization
+  // ---- stage 1: Householder tridiagonalization. By symmetry the column
+  // being reduced at step j is row j of the active block and the column that
+  // corrects A v for the shift of v's first entry is row j + 1. Those rows'
+  // threads publish them from registers at the end of step j - 1 (x: the
+  // entries right of the diagonal, zero elsewhere, with its squared norm;
+  // y: the whole row).
+  // With x, v (in V[j]) and p zero outside rows j + 1 .. l - 1 no element
+  // needs a mask: products over eliminated columns add zero and leave their
+  // registers as they are.
   double a[kEigCols];
 #pragma unroll
   for (int u = 0; u < kEigCols; ++u) {
@@ -1335,76 +1344,79 @@ __global__ void __launch_bounds__(kEigThreads)
     a[u] = (r < n && c < n) ? g[lo * lp + hi] : 0.0;
   }
   for (int e = t; e < kLpMax * kLpMax; e += kEigThreads) (&V[0][0])[e] = 0.0;
-  if (r < n && cj == 0) xb[0][r] = a[0];
+  if (t < kLpMax) pv[t] = 0.0;
+  // row i's threads (r == i): x = row i right of the diagonal into xb[i & 1],
+  // its squared norm into nx2[i & 1] and the diagonal into dg
+  auto publish_row = [&](int i) {
+    double s2 = 0.0;
+#pragma unroll
+    for (int u = 0; u < kEigCols; ++u) {
+      const int c = cj + 8 * u;
+      const double xv = c > i ? a[u] : 0.0;
+      xb[i & 1][c] = xv;
+      s2 = fma(xv, xv, s2);
+      if (c == i) dg[i] = a[u];
+    }
+    const double a2 = group8_sum(s2);
+    if (cj == 0) nx2[i & 1] = a2;
+  };
+  __syncthreads();
+  if (r == 0) publish_row(0);
+  if (r == 1 && r < n) {
+#pragma unroll
+    for (int u = 0; u < kEigCols; ++u) yb[0][cj + 8 * u] = a[u];
+  }
   __syncthreads();
   for (int j = 0; j + 2 < n; ++j) {
-    const double *x = xb[j & 1];
-    double *xn = xb[(j + 1) & 1];
+    const double *x = xb[j & 1], *y = yb[j & 1];
     const bool wact = 8 * wave + 7 > j && 8 * wave < n;  // the wave holds a row of the active block
     double alpha = 0.0, beta = 0.0;
     if (wact) {
-      double s2 = 0.0;
-      for (int q = j + 1 + lane; q < n; q += 64) s2 = fma(x[q], x[q], s2);
-      const double a2 = wave_sum_f64(s2);
-      const double x0 = x[j + 1], nrm = sqrt(a2);
+      // the reflector: x -> alpha e_{j+1}, v = x - alpha e_{j+1}, beta = 2 / v.v
+      const double a2 = nx2[j & 1], x0 = x[j + 1], nrm = sqrt(a2);
       alpha = x0 >= 0.0 ? -nrm : nrm;
       beta = a2 > 0.0 ? recip_f64(nrm * (nrm + fabs(x0))) : 0.0;
-      if (r > j && r < n) {
-        // (A v)_r with v = x - alpha e_{j+1}: the alpha term is A[r][j + 1]
-        double sx = 0.0, sc = 0.0;
+      // (A v)_r: the alpha term is y_r = A[r][j + 1]
+      double sx = 0.0;
 #pragma unroll
-        for (int u = 0; u < kEigCols; ++u) {
-          const int c = cj + 8 * u;
-          const bool act = c > j && c < n;
-          sx = fma(a[u], act ? x[c] : 0.0, sx);
-          sc += c == j + 1 ? a[u] : 0.0;
-        }
-        const double s = group8_sum(fma(-alpha, sc, sx));
-        if (cj == 0) pv[r] = beta * s;
+      for (int u = 0; u < kEigCols; ++u) sx = fma(a[u], x[cj + 8 * u], sx);
+      const double sp = beta * fma(-alpha, y[r], group8_sum(sx));
+      if (r > j && r < n) {
+        if (cj == 0) pv[r] = sp;
         if (cj == 1) V[j][r] = r == j + 1 ? x[r] - alpha : x[r];
         if (cj == 2 && r == j + 1) {
-          dg[j] = x[j];
           eo[j] = alpha;
           bet[j] = beta;
         }
       }
     }
+    if (t == 0) pv[j] = 0.0;
     __syncthreads();
-    // A <- A - v w^T - w v^T with w = p - (beta p.v / 2) v
+    // A <- A - v w^T - w v^T with w = p - (beta p.v / 2) v; then rows j + 1
+    // and j + 2 publish the next step's x (with alpha, beta) and y
     if (wact) {
-      double spv = 0.0;
-      for (int q = j + 1 + lane; q < n; q += 64) spv = fma(pv[q], q == j + 1 ? x[q] - alpha : x[q], spv);
-      const double kk = 0.5 * beta * wave_sum_f64(spv);
-      if (r > j && r < n) {
-        const double vr = r == j + 1 ? x[r] - alpha : x[r];
-        const double wr = fma(-kk, vr, pv[r]);
+      const double p1 = pv[lane], p2 = lane + 64 < kLpMax ? pv[lane + 64] : 0.0;
+      const double v1 = V[j][lane], v2 = lane + 64 < kLpMax ? V[j][lane + 64] : 0.0;
+      const double kk = 0.5 * beta * wave_sum_f64(fma(p1, v1, p2 * v2));
+      const double vr = V[j][r], wr = fma(-kk, vr, pv[r]);
 #pragma unroll
-        for (int u = 0; u < kEigCols; ++u) {
-          const int c = cj + 8 * u;
-          if (c > j && c < n) {
-            const double vc = c == j + 1 ? x[c] - alpha : x[c];
-            const double wc = fma(-kk, vc, pv[c]);
-            a[u] = fma(-vr, wc, fma(-wr, vc, a[u]));
-            if (c == j + 1) xn[r] = a[u];
-          }
-        }
+      for (int u = 0; u < kEigCols; ++u) {
+        const double vc = V[j][cj + 8 * u], wc = fma(-kk, vc, pv[cj + 8 * u]);
+        a[u] = fma(-vr, wc, fma(-wr, vc, a[u]));
+      }
+      if (r == j + 1) publish_row(j + 1);
+      if (r == j + 2 && r < n) {
+#pragma unroll
+        for (int u = 0; u < kEigCols; ++u) yb[(j + 1) & 1][cj + 8 * u] = a[u];
       }
     }
     __syncthreads();
   }
-  if (n >= 2) {
-    const double *x = xb[(n - 2) & 1];
-    if (t == 0) {
-      dg[n - 2] = x[n - 2];
-      eo[n - 2] = x[n - 1];
-    }
-    if (r == n - 1) {
+  if (n >= 2 && t == 0) eo[n - 2] = xb[(n - 2) & 1][n - 1];  // the last off-diagonal: no reflector
+  if (r == n - 1) {
 #pragma unroll
-      for (int u = 0; u < kEigCols; ++u)
-        if (cj + 8 * u == n - 1) dg[n - 1] = a[u];
-    }
-  } else if (t == 0) {
-    dg[0] = xb[0][0];
+    for (int u = 0; u < kEigCols; ++u)
+      if (cj + 8 * u == n - 1) dg[n - 1] = a[u];
   }
   __syncthreads();
 
