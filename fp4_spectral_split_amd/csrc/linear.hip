@@ -27,6 +27,8 @@
 //   skinny_nv_kernel, panel_kernel<true>: the NVFP4 forms of the first two.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "common.hpp"
 
 using namespace metis;
@@ -686,75 +688,58 @@ constexpr int kMxThreads = 256;
 constexpr int MXW = 4;  // 32 x 32 blocks per wave along each dimension
 
 
-// acc plus L1[m-tile] L2[n-tile]^T (bf16, 64 panel columns at a time through
-// LDS), stored as fp32; the 4-wave layout of gemm_mx_kernel.
-__device__ __forceinline__ void epilogue_mx4(floatx16 (&acc)[MXW][MXW], uint8_t *smem, int64_t m0, int64_t n0,
-                                             int64_t M, int64_t N, const unsigned short *__restrict__ l1,
-                                             const unsigned short *__restrict__ l2, int rp, float *__restrict__ C,
-                                             int64_t ldc) {
+// The accumulators of gemm_mx_kernel stored as fp32 straight from the MFMA
+// layout: lane (r32, h) of block (i, j) holds column r32 at rows
+// 8 (q / 4) + 4 h + q % 4, so one store instruction writes two whole
+// 128-byte row pieces (lanes 0-31 one row, 32-63 the row four below). The
+// stores take their data from the accumulator registers themselves (inline
+// asm with an AGPR operand; the compiler would first copy all 256 values to
+// VGPRs), the four blocks of a row as immediate offsets from one address.
+// Results of the last MFMAs are read only after 24 wait states.
+__device__ __forceinline__ void store4_nt(float *p, float v0, float v1, float v2, float v3) {
+  __asm__ volatile(
+      "global_store_dword %0, %1, off nt\n\t"
+      "global_store_dword %0, %2, off offset:128 nt\n\t"
+      "global_store_dword %0, %3, off offset:256 nt\n\t"
+      "global_store_dword %0, %4, off offset:384 nt"
+      :
+      : "v"(p), "a"(v0), "a"(v1), "a"(v2), "a"(v3)
+      : "memory");
+}
+__device__ __forceinline__ void store1_nt(float *p, float v) {
+  __asm__ volatile("global_store_dword %0, %1, off nt" : : "v"(p), "a"(v) : "memory");
+}
+
+__device__ __forceinline__ void store_acc_mx4(const floatx16 (&acc)[MXW][MXW], int64_t m0, int64_t n0, int64_t M,
+                                              int64_t N, float *__restrict__ C, int64_t ldc) {
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int r32 = lane & 31, h = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
-  if (rp > 0) {
-    uint8_t *L1s = smem, *L2s = smem + BM * EPI_ROWB;
-    for (int c0 = 0; c0 < rp; c0 += 64) {
+  const int lr = wm * 128 + h * 4, lc = wn * 128 + r32;  // the lane's row and column in the tile
+  float *base = C + (m0 + lr) * ldc + n0 + lc;
+  __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  if (m0 + BM <= M && n0 + BN <= N) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = t + kMxThreads * i;  // 2048 pieces of 16 bytes per panel
-        const int rr = idx >> 3, piece = idx & 7;
-        const int64_t ar = m0 + rr, br = n0 + rr;
-        const uint4 va = ar < M ? *(const uint4 *)(l1 + ar * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
-        const uint4 vb = br < N ? *(const uint4 *)(l2 + br * rp + c0 + piece * 8) : uint4{0u, 0u, 0u, 0u};
-        *(uint4 *)(L1s + rr * EPI_ROWB + piece * 16) = va;
-        *(uint4 *)(L2s + rr * EPI_ROWB + piece * 16) = vb;
+    for (int i = 0; i < MXW; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        float *p = base + (int64_t)(i * 32 + (q >> 2) * 8 + (q & 3)) * ldc;
+        store4_nt(p, acc[i][0][q], acc[i][1][q], acc[i][2][q], acc[i][3][q]);
       }
-      __syncthreads();
+  } else {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        ushortx8 a8[MXW], b8[MXW];
+    for (int i = 0; i < MXW; ++i)
 #pragma unroll
-        for (int i = 0; i < MXW; ++i) {
-          a8[i] = *(const ushortx8 *)(L1s + (wm * 128 + i * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
-          b8[i] = *(const ushortx8 *)(L2s + (wn * 128 + i * 32 + r32) * EPI_ROWB + ks * 32 + h * 16);
-        }
+      for (int q = 0; q < 16; ++q) {
+        const int dr = i * 32 + (q >> 2) * 8 + (q & 3);
+        float *p = base + (int64_t)dr * ldc;
+        if (m0 + lr + dr < M) {
 #pragma unroll
-        for (int i = 0; i < MXW; ++i)
-#pragma unroll
-          for (int j = 0; j < MXW; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
-      }
-      __syncthreads();
-    }
-  }
-  // C through LDS, 32 rows of the wave's 128 x 128 tile at a time, so each
-  // lane stores 16 contiguous bytes (two 512-byte row pieces per store)
-  constexpr int CS = 128 + 4;  // floats per staged row
-  float *stage = (float *)smem + wave * 32 * CS;
-  __syncthreads();  // the panels (if any) are no longer read
-#pragma unroll
-  for (int i = 0; i < MXW; ++i) {
-#pragma unroll
-    for (int j = 0; j < MXW; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) stage[((q >> 2) * 8 + h * 4 + (q & 3)) * CS + j * 32 + r32] = acc[i][j][q];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int rr = it * 2 + (lane >> 5), c4 = (lane & 31) * 4;
-      const int64_t row = m0 + wm * 128 + i * 32 + rr, col = n0 + wn * 128 + c4;
-      const floatx4 v = *(const floatx4 *)(stage + rr * CS + c4);
-      if (row < M) {
-        float *dst = C + row * ldc + col;
-        if (col + 3 < N && ((uintptr_t)dst & 15) == 0) {
-          __builtin_nontemporal_store(v, (floatx4 *)dst);
-        } else {
-          for (int u = 0; u < 4 && col + u < N; ++u) dst[u] = v[u];
+          for (int j = 0; j < MXW; ++j)
+            if (n0 + lc + j * 32 < N) store1_nt(p + j * 32, acc[i][j][q]);
         }
       }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   }
 }
 
@@ -789,8 +774,6 @@ static_assert(2 * BM * EPI_ROWB <= DMA_LDS, "epilogue panels must fit the main-l
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// Source of the loads for rows past M or N (the ring must still be written).
-__device__ __attribute__((aligned(16))) const uint32_t kZeroPage[4] = {0u, 0u, 0u, 0u};
 
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void *)p);
@@ -817,6 +800,9 @@ __device__ __forceinline__ floatx16 mfma_fp4_ks(const u32x4 a, const u32x4 b, in
                  : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4x32v(a), fp4x32v(b), c, 4, 4, 1, sa, 1, sb);
 }
 
+// s_waitcnt with the vector-memory count limited and every LDS read done
+#define METIS_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
+
 __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
     gemm_mx_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
                    const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int64_t N, int64_t T,
@@ -828,206 +814,187 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
   const int r32 = lane & 31, h = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
   const int mtiles = (int)cdiv(M, BM), ntiles_n = (int)cdiv(N, BN), ntiles = mtiles * ntiles_n;
-  // persistent: workgroup b takes tiles b, b + gridDim.x, ...
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-  int tm, tn;
-  tile_coords_of(tm, tn, tile, ntiles, mtiles, ntiles_n);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t nb = T / 32;
   const int nst = (int)(T / 128);
-
-  // per-lane load sources: code unit of row r = q / 4 of this wave's blocks,
-  // and the scale word of row 64 wave + lane; rows past the end read zeros
-  const uint8_t *srcA[4], *srcB[4];
-  int strideA[4], strideB[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
-    const bool okA = m0 + r < M, okB = n0 + r < N;
-    srcA[i] = okA ? ac + (m0 + r) * (T / 2) + u * 16 : (const uint8_t *)kZeroPage;
-    srcB[i] = okB ? bc + (n0 + r) * (T / 2) + u * 16 : (const uint8_t *)kZeroPage;
-    strideA[i] = okA ? 64 : 0;
-    strideB[i] = okB ? 64 : 0;
-  }
-  const int rs = 64 * wave + lane;
-  const bool okSA = m0 + rs < M, okSB = n0 + rs < N;
-  const uint8_t *srcSA = okSA ? as + (m0 + rs) * nb : (const uint8_t *)kZeroPage;
-  const uint8_t *srcSB = okSB ? bs + (n0 + rs) * nb : (const uint8_t *)kZeroPage;
-  const int strideSA = okSA ? 16 : 0, strideSB = okSB ? 16 : 0;
-
   // correction stages: 32 bf16 panel columns (64 bytes per row) of L1 rows
   // m0.. and L2 rows n0.., in the same swizzled ring layout as the codes
   const int ncs = rp / 32, ntot = nst + ncs;
-  auto issue = [&](int st) {  // eight loads per wave
-    uint8_t *sb = smem + (st % kDmaStages) * DMA_STAGE;
-    if (st < nst) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dma_load16(srcA[i] + (int64_t)st * strideA[i], sb + (4 * wave + i) * 1024);
-        dma_load16(srcB[i] + (int64_t)st * strideB[i], sb + DMA_CODE_BYTES + (4 * wave + i) * 1024);
-      }
-    } else {
-      const int cs = st - nst;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
-        const uint8_t *pa = m0 + r < M ? (const uint8_t *)l1 + ((m0 + r) * rp + 32 * cs) * 2 + u * 16
-                                       : (const uint8_t *)kZeroPage;
-        const uint8_t *pb = n0 + r < N ? (const uint8_t *)l2 + ((n0 + r) * rp + 32 * cs) * 2 + u * 16
-                                       : (const uint8_t *)kZeroPage;
-        dma_load16(pa, sb + (4 * wave + i) * 1024);
-        dma_load16(pb, sb + DMA_CODE_BYTES + (4 * wave + i) * 1024);
-      }
-    }
-  };
-  auto issue_scales = [&](int g) {  // two loads per wave: scales of stages 4 g .. 4 g + 3
-    uint8_t *sg = smem + DMA_SCALE_BASE + (g % 2) * DMA_SCALE_GROUP;
-    dma_load16(srcSA + (int64_t)g * strideSA, sg + wave * 1024);
-    dma_load16(srcSB + (int64_t)g * strideSB, sg + BM * 16 + wave * 1024);
-  };
-
-  floatx16 acc[MXW][MXW];
-#pragma unroll
-  for (int i = 0; i < MXW; ++i)
-#pragma unroll
-    for (int j = 0; j < MXW; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
   const int rA0 = wm * 128 + r32, rB0 = wn * 128 + r32;
   const int fA = (rA0 >> 2) & 3, fB = (rB0 >> 2) & 3;
-  const uint32_t smem0 = lds_offset(smem);
-  // issue order: scales(0), codes(0), codes(1), codes(2), then per iteration
-  // st: codes(st + 3) and, when st % 4 == 0, scales(st / 4 + 1)
-  issue_scales(0);
-  issue(0);
-  if (ntot > 1) issue(1);
-  if (ntot > 2) issue(2);
-  for (int st = 0; st < nst; ++st) {
-    // every wave is past stage st - 1 (barrier at the end of the previous
-    // iteration): its buffer takes stage st + 3, and the scale buffer of the
-    // group before this one takes the next group
-    if (st + 3 < ntot) issue(st + 3);
-    const bool next_group = 4 * (st / 4 + 1) < nst;
-    if (st % 4 == 0 && next_group) issue_scales(st / 4 + 1);
-    // codes(st) (and the scales of its group, issued earlier) have landed once
-    // at most the loads issued after codes(st) are pending
-    const int later = 8 * min(3, ntot - 1 - st) + (next_group ? 2 : 0);
-    switch (later) {
-      case 26: METIS_WAIT_VMCNT(26); break;
-      case 24: METIS_WAIT_VMCNT(24); break;
-      case 18: METIS_WAIT_VMCNT(18); break;
-      case 16: METIS_WAIT_VMCNT(16); break;
-      case 10: METIS_WAIT_VMCNT(10); break;
-      case 8: METIS_WAIT_VMCNT(8); break;
-      case 2: METIS_WAIT_VMCNT(2); break;
-      default: METIS_WAIT_VMCNT(0); break;
+  // persistent: workgroup b takes tiles b, b + gridDim.x, ...
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    int tm, tn;
+    tile_coords_of(tm, tn, tile, ntiles, mtiles, ntiles_n);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+    // per-lane load offsets (bytes, below 2^31 by the host's check): code unit
+    // of row r = q / 4 of this wave's blocks, and the scale word of row
+    // 64 wave + lane. Rows past M or N read the last row instead: their
+    // products only reach rows and columns of C that are not stored.
+    uint32_t offA[4], offB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
+      offA[i] = (uint32_t)(min(m0 + r, M - 1) * (T / 2) + u * 16);
+      offB[i] = (uint32_t)(min(n0 + r, N - 1) * (T / 2) + u * 16);
     }
-    __builtin_amdgcn_s_barrier();
-    const uint32_t base = smem0 + (st % kDmaStages) * DMA_STAGE;
-    const uint32_t sbase = smem0 + DMA_SCALE_BASE + ((st / 4) % 2) * DMA_SCALE_GROUP + (st % 4) * 4;
-    int sa[MXW], sb[MXW];
+    const int rs = 64 * wave + lane;
+    const uint32_t offSA = (uint32_t)(min(m0 + rs, M - 1) * nb), offSB = (uint32_t)(min(n0 + rs, N - 1) * nb);
+
+    auto issue = [&](int st) {  // eight loads per wave
+      uint8_t *sbuf = smem + (st % kDmaStages) * DMA_STAGE;
+      if (st < nst) {
+        const uint8_t *as_ = ac + (int64_t)st * 64, *bs_ = bc + (int64_t)st * 64;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t pa = base + rA0 * 64 + (((2 * h + ks) ^ fA) << 4);
-      const uint32_t pb = base + DMA_CODE_BYTES + rB0 * 64 + (((2 * h + ks) ^ fB) << 4);
-      u32x4 a0, a1, a2, a3, b0, b1, b2, b3;
-      if (ks == 0) {
-        const uint32_t psa = sbase + rA0 * 16;
-        const uint32_t psb = sbase + BM * 16 + rB0 * 16;
-        asm volatile(
-            "ds_read_b128 %0, %16\n\t"
-            "ds_read_b128 %1, %16 offset:2048\n\t"
-            "ds_read_b128 %2, %16 offset:4096\n\t"
-            "ds_read_b128 %3, %16 offset:6144\n\t"
-            "ds_read_b128 %4, %17\n\t"
-            "ds_read_b128 %5, %17 offset:2048\n\t"
-            "ds_read_b128 %6, %17 offset:4096\n\t"
-            "ds_read_b128 %7, %17 offset:6144\n\t"
-            "ds_read_b32 %8, %18\n\t"
-            "ds_read_b32 %9, %18 offset:512\n\t"
-            "ds_read_b32 %10, %18 offset:1024\n\t"
-            "ds_read_b32 %11, %18 offset:1536\n\t"
-            "ds_read_b32 %12, %19\n\t"
-            "ds_read_b32 %13, %19 offset:512\n\t"
-            "ds_read_b32 %14, %19 offset:1024\n\t"
-            "ds_read_b32 %15, %19 offset:1536\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(sa[0]),
-              "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sb[0]), "=&v"(sb[1]), "=&v"(sb[2]), "=&v"(sb[3])
-            : "v"(pa), "v"(pb), "v"(psa), "v"(psb)
-            : "memory");
-#pragma unroll
-        for (int i = 0; i < MXW; ++i) {
-          sa[i] = (int)((uint32_t)sa[i] >> (16 * h));
-          sb[i] = (int)((uint32_t)sb[i] >> (16 * h));
+        for (int i = 0; i < 4; ++i) {
+          dma_load16(as_ + offA[i], sbuf + (4 * wave + i) * 1024);
+          dma_load16(bs_ + offB[i], sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
         }
       } else {
-        asm volatile(
-            "ds_read_b128 %0, %8\n\t"
-            "ds_read_b128 %1, %8 offset:2048\n\t"
-            "ds_read_b128 %2, %8 offset:4096\n\t"
-            "ds_read_b128 %3, %8 offset:6144\n\t"
-            "ds_read_b128 %4, %9\n\t"
-            "ds_read_b128 %5, %9 offset:2048\n\t"
-            "ds_read_b128 %6, %9 offset:4096\n\t"
-            "ds_read_b128 %7, %9 offset:6144\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
-            : "v"(pa), "v"(pb)
-            : "memory");
+        const uint8_t *l1s = (const uint8_t *)l1 + (int64_t)(st - nst) * 64;
+        const uint8_t *l2s = (const uint8_t *)l2 + (int64_t)(st - nst) * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
+          const uint32_t oa = (uint32_t)(min(m0 + r, M - 1) * rp * 2 + u * 16);
+          const uint32_t ob = (uint32_t)(min(n0 + r, N - 1) * rp * 2 + u * 16);
+          dma_load16(l1s + oa, sbuf + (4 * wave + i) * 1024);
+          dma_load16(l2s + ob, sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
+        }
       }
-      const u32x4 af[MXW] = {a0, a1, a2, a3}, bf[MXW] = {b0, b1, b2, b3};
+    };
+    auto issue_scales = [&](int g) {  // two loads per wave: scales of stages 4 g .. 4 g + 3
+      uint8_t *sg = smem + DMA_SCALE_BASE + (g % 2) * DMA_SCALE_GROUP;
+      dma_load16(as + (int64_t)g * 16 + offSA, sg + wave * 1024);
+      dma_load16(bs + (int64_t)g * 16 + offSB, sg + BM * 16 + wave * 1024);
+    };
+    // Wait until the codes of stage s (and the scales of its group, issued
+    // before them) have landed: at most the 8 loads of each later stage
+    // issued so far (s + 1 .. min(s + 2, ntot - 1)) may still be pending. A
+    // scale group issued among them only makes the wait stricter than needed.
+    // Every LDS read of the wave is also complete afterwards.
+    auto wait_stage = [&](int s) {
+      const int d = min(s + 2, ntot - 1) - s;
+      if (d >= 2) METIS_WAIT_VMCNT_LDS(16);
+      else if (d == 1) METIS_WAIT_VMCNT_LDS(8);
+      else METIS_WAIT_VMCNT_LDS(0);
+    };
+    // fragments of half ks of stage st: 16-byte unit 2 h + ks of the row
+    // (FP4: lane half h takes K 32 h .. of the 64 the MFMA covers) or 2 ks + h
+    // (bf16 panels: 8 consecutive columns), and for FP4 half 0 the stage's
+    // block-scale word of each row (its bytes 2 h + ks serve half ks)
+    auto load_frags = [&](int st, int ks, u32x4 (&af)[MXW], u32x4 (&bf)[MXW], int (&sa)[MXW], int (&sb)[MXW]) {
+      const uint8_t *base = smem + (st % kDmaStages) * DMA_STAGE;
+      const int un = st < nst ? 2 * h + ks : 2 * ks + h;
+      const uint8_t *pa = base + rA0 * 64 + ((un ^ fA) << 4);
+      const uint8_t *pb = base + DMA_CODE_BYTES + rB0 * 64 + ((un ^ fB) << 4);
 #pragma unroll
-      for (int i = 0; i < MXW; ++i)
+      for (int i = 0; i < MXW; ++i) {
+        af[i] = *(const u32x4 *)(pa + i * 2048);
+        bf[i] = *(const u32x4 *)(pb + i * 2048);
+      }
+      if (st < nst && ks == 0) {
+        const uint8_t *sbase = smem + DMA_SCALE_BASE + ((st / 4) % 2) * DMA_SCALE_GROUP + (st % 4) * 4;
 #pragma unroll
-        for (int j = 0; j < MXW; ++j) acc[i][j] = mfma_fp4_ks(af[i], bf[j], sa[i], sb[j], acc[i][j], ks);
-    }
-    __builtin_amdgcn_s_barrier();  // buffer st % 4 is free for stage st + 4
-  }
-  // the low-rank correction L1 L2^T into the same accumulators: bf16
-  // 32x32x16 MFMA, two 16-column steps per stage (lane (r, h) takes 8
-  // consecutive columns: 16-byte unit 2 ks + h of its row)
-  for (int st = nst; st < ntot; ++st) {
-    if (st + 3 < ntot) issue(st + 3);
-    switch (8 * min(3, ntot - 1 - st)) {
-      case 24: METIS_WAIT_VMCNT(24); break;
-      case 16: METIS_WAIT_VMCNT(16); break;
-      case 8: METIS_WAIT_VMCNT(8); break;
-      default: METIS_WAIT_VMCNT(0); break;
-    }
+        for (int i = 0; i < MXW; ++i) {
+          sa[i] = *(const int *)(sbase + (rA0 + 32 * i) * 16);
+          sb[i] = *(const int *)(sbase + BM * 16 + (rB0 + 32 * i) * 16);
+        }
+      }
+    };
+
+    floatx16 acc[MXW][MXW];
+#pragma unroll
+    for (int i = 0; i < MXW; ++i)
+#pragma unroll
+      for (int j = 0; j < MXW; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    auto mfmas = [&](int ks, auto corr, const u32x4 (&af)[MXW], const u32x4 (&bf)[MXW], const int (&sa)[MXW],
+                     const int (&sb)[MXW]) {
+      if constexpr (!decltype(corr)::value) {
+        int xa[MXW], xb[MXW];  // scale words shifted so opsel = ks picks byte 2 h + ks
+#pragma unroll
+        for (int i = 0; i < MXW; ++i) {
+          xa[i] = (int)((uint32_t)sa[i] >> (16 * h));
+          xb[i] = (int)((uint32_t)sb[i] >> (16 * h));
+        }
+#pragma unroll
+        for (int i = 0; i < MXW; ++i)
+#pragma unroll
+          for (int j = 0; j < MXW; ++j) acc[i][j] = mfma_fp4_ks(af[i], bf[j], xa[i], xb[j], acc[i][j], ks);
+      } else {
+#pragma unroll
+        for (int i = 0; i < MXW; ++i)
+#pragma unroll
+          for (int j = 0; j < MXW; ++j)
+            acc[i][j] = mfma32_bf16(__builtin_bit_cast(ushortx8, af[i]), __builtin_bit_cast(ushortx8, bf[j]), acc[i][j]);
+      }
+    };
+
+    // Pipeline: half 1 of stage st is read while the MFMAs of half 0 run; a
+    // barrier (stage st + 1 landed, every read of stage st done) frees buffer
+    // st % 4 for stage st + 4; half 0 of stage st + 1 is read while the MFMAs
+    // of half 1 run. Prologue: scales(0), codes(0 .. 2), then after the first
+    // barrier codes(3) and scales(1); iteration st issues codes(st + 4) and,
+    // right after codes(4 g - 1), scales(g).
+    u32x4 a0f[MXW], b0f[MXW], a1f[MXW], b1f[MXW];
+    int s0a[MXW], s0b[MXW], s1a[MXW], s1b[MXW];
+    issue_scales(0);
+    issue(0);
+    if (ntot > 1) issue(1);
+    if (ntot > 2) issue(2);
+    wait_stage(0);
     __builtin_amdgcn_s_barrier();
-    const uint32_t base = smem0 + (st % kDmaStages) * DMA_STAGE;
+    __asm__ volatile("" ::: "memory");
+    if (ntot > 3) issue(3);
+    if (4 < nst) issue_scales(1);
+    load_frags(0, 0, a0f, b0f, s0a, s0b);
+    // one pipeline step; the FP4 stages and the bf16 correction stages run
+    // in loops of their own so each MFMA kind keeps the accumulators in place
+    // (scheduling barriers keep the four parts in this order: the compiler
+    // would otherwise gather both MFMA halves behind one wait for all reads)
+    auto step = [&](int st, auto corr) {
+      // half 0 (read during the previous MFMA half) is complete before half
+      // 1's reads are issued, so the MFMAs below wait for nothing
+      __asm__ volatile("" : "+v"(a0f[0]), "+v"(a0f[1]), "+v"(a0f[2]), "+v"(a0f[3]), "+v"(b0f[0]), "+v"(b0f[1]),
+                       "+v"(b0f[2]), "+v"(b0f[3]), "+v"(s0a[0]), "+v"(s0a[1]), "+v"(s0a[2]), "+v"(s0a[3]),
+                       "+v"(s0b[0]), "+v"(s0b[1]), "+v"(s0b[2]), "+v"(s0b[3]));
+      load_frags(st, 1, a1f, b1f, s1a, s1b);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t pa = base + rA0 * 64 + (((2 * ks + h) ^ fA) << 4);
-      const uint32_t pb = base + DMA_CODE_BYTES + rB0 * 64 + (((2 * ks + h) ^ fB) << 4);
-      u32x4 a0, a1, a2, a3, b0, b1, b2, b3;
-      asm volatile(
-          "ds_read_b128 %0, %8\n\t"
-          "ds_read_b128 %1, %8 offset:2048\n\t"
-          "ds_read_b128 %2, %8 offset:4096\n\t"
-          "ds_read_b128 %3, %8 offset:6144\n\t"
-          "ds_read_b128 %4, %9\n\t"
-          "ds_read_b128 %5, %9 offset:2048\n\t"
-          "ds_read_b128 %6, %9 offset:4096\n\t"
-          "ds_read_b128 %7, %9 offset:6144\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
-          : "v"(pa), "v"(pb)
-          : "memory");
-      const u32x4 af[MXW] = {a0, a1, a2, a3}, bf[MXW] = {b0, b1, b2, b3};
-#pragma unroll
-      for (int i = 0; i < MXW; ++i)
-#pragma unroll
-        for (int j = 0; j < MXW; ++j)
-          acc[i][j] = mfma32_bf16(__builtin_bit_cast(ushortx8, af[i]), __builtin_bit_cast(ushortx8, bf[j]), acc[i][j]);
-    }
-    __builtin_amdgcn_s_barrier();
-  }
-  __syncthreads();  // the epilogue reuses the ring
-  epilogue_mx4(acc, smem, m0, n0, M, N, nullptr, nullptr, 0, C, ldc);
-  __syncthreads();  // the next tile's loads overwrite the staging area
+      for (int i = 0; i < MXW; ++i) {
+        s1a[i] = s0a[i];
+        s1b[i] = s0b[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(0, corr, a0f, b0f, s0a, s0b);
+      // the MFMAs are pure, so the optimizer may move them across the
+      // barrier; empty asm statements that take the accumulators here and
+      // hand out half 1's fragments after the barrier pin them in place
+      __asm__ volatile("" : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+                       "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]), "+a"(acc[2][0]), "+a"(acc[2][1]),
+                       "+a"(acc[2][2]), "+a"(acc[2][3]), "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]),
+                       "+a"(acc[3][3]));
+      __builtin_amdgcn_sched_barrier(0);
+      __asm__ volatile("" ::: "memory");
+      if (st + 1 < ntot) wait_stage(st + 1);
+      else METIS_WAIT_VMCNT_LDS(0);
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      __asm__ volatile("" : "+v"(a1f[0]), "+v"(a1f[1]), "+v"(a1f[2]), "+v"(a1f[3]), "+v"(b1f[0]), "+v"(b1f[1]),
+                       "+v"(b1f[2]), "+v"(b1f[3]));
+      if (st + 4 < ntot) issue(st + 4);
+      if ((st + 1) % 4 == 0 && 4 * ((st + 1) / 4 + 1) < nst) issue_scales((st + 1) / 4 + 1);
+      if (st + 1 < ntot) load_frags(st + 1, 0, a0f, b0f, s0a, s0b);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(1, corr, a1f, b1f, s1a, s1b);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int st = 0; st < nst; ++st) step(st, std::false_type{});
+    for (int st = nst; st < ntot; ++st) step(st, std::true_type{});
+    // every LDS read of the tile finished before the last barrier, so the
+    // next tile's first loads may refill the ring while these stores drain
+    store_acc_mx4(acc, m0, n0, M, N, C, ldc);
   }
 }
 
@@ -1214,7 +1181,8 @@ metis_status_t gemm_main(const Side &a, const Side &b, float *C, int64_t ldc, co
     gemm_nv_kernel<<<tiles, kGemmThreads, 0, st>>>(a.R->codes, a.R->scales, a.R->tensor_scale, a.rows, b.R->codes,
                                           b.R->scales, b.R->tensor_scale, b.rows, a.T, l1, l2, rp, C, ldc);
   else if (a.T % 512 == 0 && ((uintptr_t)a.R->codes | (uintptr_t)b.R->codes | (uintptr_t)a.R->scales |
-                              (uintptr_t)b.R->scales) % 16 == 0)
+                              (uintptr_t)b.R->scales) % 16 == 0 &&
+           std::max(a.rows, b.rows) * std::max<int64_t>(a.T / 2, 2 * (int64_t)rp) < ((int64_t)1 << 31))
     gemm_mx_kernel<<<std::min<unsigned>(tiles, kMxMaxGrid), kMxThreads, 0, st>>>(
         a.R->codes, a.R->scales, a.rows, b.R->codes, b.R->scales, b.rows, a.T, l1, l2, rp, C, ldc);
   else
