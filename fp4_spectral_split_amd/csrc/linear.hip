@@ -950,11 +950,16 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     if (ntot > 3) issue(3);
     if (4 < nst) issue_scales(1);
     load_frags(0, 0, a0f, b0f, s0a, s0b);
-    // one pipeline step; the FP4 stages and the bf16 correction stages run
-    // in loops of their own so each MFMA kind keeps the accumulators in place
-    // (scheduling barriers keep the four parts in this order: the compiler
-    // would otherwise gather both MFMA halves behind one wait for all reads)
-    auto step = [&](int st, auto corr) {
+    // One pipeline step; the FP4 stages and the bf16 correction stages run
+    // in loops of their own so each MFMA kind keeps the accumulators in
+    // place. In a steady FP4 step (stages st + 1 .. st + 4 all FP4 stages)
+    // every condition is known at compile time, so the DMA issue and the
+    // fragment reads share one basic block with the MFMAs of half 1 and can
+    // be spread between them; a scale group, when due, follows the MFMAs.
+    // (Scheduling barriers keep the parts in order: the compiler would
+    // otherwise gather both MFMA halves behind one wait for all reads.)
+    auto step = [&](int st, auto corr, auto steady, auto scl) {
+      constexpr bool STEADY = decltype(steady)::value;
       // half 0 (read during the previous MFMA half) is complete before half
       // 1's reads are issued, so the MFMAs below wait for nothing
       __asm__ volatile("" : "+v"(a0f[0]), "+v"(a0f[1]), "+v"(a0f[2]), "+v"(a0f[3]), "+v"(b0f[0]), "+v"(b0f[1]),
@@ -966,8 +971,14 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
         s1a[i] = s0a[i];
         s1b[i] = s0b[i];
       }
-      __builtin_amdgcn_sched_barrier(0);
       mfmas(0, corr, a0f, b0f, s0a, s0b);
+      // half 1's reads go out between the first MFMAs of half 0
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
       // the MFMAs are pure, so the optimizer may move them across the
       // barrier; empty asm statements that take the accumulators here and
       // hand out half 1's fragments after the barrier pin them in place
@@ -977,21 +988,56 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
                        "+a"(acc[3][3]));
       __builtin_amdgcn_sched_barrier(0);
       __asm__ volatile("" ::: "memory");
-      if (st + 1 < ntot) wait_stage(st + 1);
-      else METIS_WAIT_VMCNT_LDS(0);
+      if constexpr (STEADY) {
+        METIS_WAIT_VMCNT_LDS(16);
+      } else {
+        if (st + 1 < ntot) wait_stage(st + 1);
+        else METIS_WAIT_VMCNT_LDS(0);
+      }
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
       __asm__ volatile("" : "+v"(a1f[0]), "+v"(a1f[1]), "+v"(a1f[2]), "+v"(a1f[3]), "+v"(b1f[0]), "+v"(b1f[1]),
                        "+v"(b1f[2]), "+v"(b1f[3]));
-      if (st + 4 < ntot) issue(st + 4);
-      if ((st + 1) % 4 == 0 && 4 * ((st + 1) / 4 + 1) < nst) issue_scales((st + 1) / 4 + 1);
-      if (st + 1 < ntot) load_frags(st + 1, 0, a0f, b0f, s0a, s0b);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (STEADY) {
+        issue(st + 4);
+        load_frags(st + 1, 0, a0f, b0f, s0a, s0b);
+      } else {
+        if (st + 4 < ntot) issue(st + 4);
+        if ((st + 1) % 4 == 0 && 4 * ((st + 1) / 4 + 1) < nst) issue_scales((st + 1) / 4 + 1);
+        if (st + 1 < ntot) load_frags(st + 1, 0, a0f, b0f, s0a, s0b);
+      }
       mfmas(1, corr, a1f, b1f, s1a, s1b);
+      // the DMA of stage st + 4 and the reads of half 0 of stage st + 1 go
+      // out between the MFMAs of half 1
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 1);  // two global loads (to LDS)
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (STEADY && decltype(scl)::value) {
+        if (4 * ((st + 1) / 4 + 1) < nst) issue_scales((st + 1) / 4 + 1);
+      }
     };
-    for (int st = 0; st < nst; ++st) step(st, std::false_type{});
-    for (int st = nst; st < ntot; ++st) step(st, std::true_type{});
+    using F = std::false_type;
+    using Tt = std::true_type;
+    int st = 0;
+    // steady: st + 7 < nst keeps stages st + 1 .. st + 7 FP4 stages, so all
+    // four steps of a group are steady; the scale group is due at st + 3
+    for (; st + 7 < nst; st += 4) {
+      step(st, F{}, Tt{}, F{});
+      step(st + 1, F{}, Tt{}, F{});
+      step(st + 2, F{}, Tt{}, F{});
+      step(st + 3, F{}, Tt{}, Tt{});
+    }
+    for (; st < nst; ++st) step(st, F{}, F{}, F{});
+    for (; st < ntot; ++st) step(st, Tt{}, F{}, F{});
     // every LDS read of the tile finished before the last barrier, so the
     // next tile's first loads may refill the ring while these stores drain
     store_acc_mx4(acc, m0, n0, M, N, C, ldc);
