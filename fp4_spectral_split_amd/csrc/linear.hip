@@ -74,10 +74,14 @@ struct GemmPlan {
   size_t bytes;
 };
 
-int64_t pick_split(int64_t row_tiles, int64_t T, int64_t &chunk) {
-  int64_t want = std::max<int64_t>(1, cdiv(1024, std::max<int64_t>(1, row_tiles)));
-  want = std::min<int64_t>(want, std::max<int64_t>(1, T / 512));
-  chunk = round_up(cdiv(T, want), 128);
+// Split-K of a skinny product over row blocks of 128: at least 256
+// workgroups when the contraction allows, each split at least four stages of
+// 256 elements (chunk a multiple of 256).
+int64_t pick_split(int64_t rows, int64_t T, int64_t &chunk) {
+  const int64_t row_blocks = std::max<int64_t>(1, cdiv(rows, 128));
+  int64_t want = std::max<int64_t>(1, cdiv(256, row_blocks));
+  want = std::min<int64_t>(want, std::max<int64_t>(1, T / 1024));
+  chunk = round_up(cdiv(T, want), 256);
   return cdiv(T, chunk);
 }
 
@@ -85,9 +89,9 @@ GemmPlan make_gemm_plan(int64_t ra, int64_t rb, int64_t T, int ka, int kb, void 
   GemmPlan p;
   p.ra = ra; p.rb = rb; p.T = T; p.ka = ka; p.kb = kb;
   p.rp = (int)round_up(2 * ka + 2 * kb, 64);
-  p.ks_p = kb ? (int)pick_split(cdiv(ra, 32), T, p.tc_p) : 0;
-  p.ks_q = ka ? (int)pick_split(cdiv(rb, 32), T, p.tc_q) : 0;
-  p.ks_c = (ka && kb) ? (int)pick_split(1, T, p.tc_c) : 0;
+  p.ks_p = kb ? (int)pick_split(ra, T, p.tc_p) : 0;
+  p.ks_q = ka ? (int)pick_split(rb, T, p.tc_q) : 0;
+  p.ks_c = (ka && kb) ? (int)pick_split(ka, T, p.tc_c) : 0;
   metis_host::Carver c(ws);
   p.ppart = c.take<float>((size_t)p.ks_p * ra * kb);
   p.qpart = c.take<float>((size_t)p.ks_q * rb * ka);
@@ -802,6 +806,8 @@ __device__ __forceinline__ floatx16 mfma_fp4_ks(const u32x4 a, const u32x4 b, in
 
 // s_waitcnt with the vector-memory count limited and every LDS read done
 #define METIS_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
+// s_waitcnt for every LDS access only
+#define METIS_WAIT_LDS0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14))
 
 __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
     gemm_mx_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t M,
@@ -841,27 +847,31 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     const int rs = 64 * wave + lane;
     const uint32_t offSA = (uint32_t)(min(m0 + rs, M - 1) * nb), offSB = (uint32_t)(min(n0 + rs, N - 1) * nb);
 
-    auto issue = [&](int st) {  // eight loads per wave
+    auto issue_main = [&](int st) {  // eight loads per wave: codes of FP4 stage st
       uint8_t *sbuf = smem + (st % kDmaStages) * DMA_STAGE;
-      if (st < nst) {
-        const uint8_t *as_ = ac + (int64_t)st * 64, *bs_ = bc + (int64_t)st * 64;
+      const uint8_t *as_ = ac + (int64_t)st * 64, *bs_ = bc + (int64_t)st * 64;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dma_load16(as_ + offA[i], sbuf + (4 * wave + i) * 1024);
-          dma_load16(bs_ + offB[i], sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
-        }
-      } else {
-        const uint8_t *l1s = (const uint8_t *)l1 + (int64_t)(st - nst) * 64;
-        const uint8_t *l2s = (const uint8_t *)l2 + (int64_t)(st - nst) * 64;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
-          const uint32_t oa = (uint32_t)(min(m0 + r, M - 1) * rp * 2 + u * 16);
-          const uint32_t ob = (uint32_t)(min(n0 + r, N - 1) * rp * 2 + u * 16);
-          dma_load16(l1s + oa, sbuf + (4 * wave + i) * 1024);
-          dma_load16(l2s + ob, sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
-        }
+      for (int i = 0; i < 4; ++i) {
+        dma_load16(as_ + offA[i], sbuf + (4 * wave + i) * 1024);
+        dma_load16(bs_ + offB[i], sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
       }
+    };
+    auto issue_corr = [&](int st) {  // eight loads per wave: panel columns of correction stage st
+      uint8_t *sbuf = smem + (st % kDmaStages) * DMA_STAGE;
+      const uint8_t *l1s = (const uint8_t *)l1 + (int64_t)(st - nst) * 64;
+      const uint8_t *l2s = (const uint8_t *)l2 + (int64_t)(st - nst) * 64;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
+        const uint32_t oa = (uint32_t)(min(m0 + r, M - 1) * rp * 2 + u * 16);
+        const uint32_t ob = (uint32_t)(min(n0 + r, N - 1) * rp * 2 + u * 16);
+        dma_load16(l1s + oa, sbuf + (4 * wave + i) * 1024);
+        dma_load16(l2s + ob, sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
+      }
+    };
+    auto issue = [&](int st) {
+      if (st < nst) issue_main(st);
+      else issue_corr(st);
     };
     auto issue_scales = [&](int g) {  // two loads per wave: scales of stages 4 g .. 4 g + 3
       uint8_t *sg = smem + DMA_SCALE_BASE + (g % 2) * DMA_SCALE_GROUP;
@@ -883,9 +893,11 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     // (FP4: lane half h takes K 32 h .. of the 64 the MFMA covers) or 2 ks + h
     // (bf16 panels: 8 consecutive columns), and for FP4 half 0 the stage's
     // block-scale word of each row (its bytes 2 h + ks serve half ks)
-    auto load_frags = [&](int st, int ks, u32x4 (&af)[MXW], u32x4 (&bf)[MXW], int (&sa)[MXW], int (&sb)[MXW]) {
+    auto load_frags_k = [&](int st, int ks, auto corr, u32x4 (&af)[MXW], u32x4 (&bf)[MXW], int (&sa)[MXW],
+                            int (&sb)[MXW]) {
+      constexpr bool CORR = decltype(corr)::value;
       const uint8_t *base = smem + (st % kDmaStages) * DMA_STAGE;
-      const int un = st < nst ? 2 * h + ks : 2 * ks + h;
+      const int un = CORR ? 2 * ks + h : 2 * h + ks;
       const uint8_t *pa = base + rA0 * 64 + ((un ^ fA) << 4);
       const uint8_t *pb = base + DMA_CODE_BYTES + rB0 * 64 + ((un ^ fB) << 4);
 #pragma unroll
@@ -893,7 +905,7 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
         af[i] = *(const u32x4 *)(pa + i * 2048);
         bf[i] = *(const u32x4 *)(pb + i * 2048);
       }
-      if (st < nst && ks == 0) {
+      if (!CORR && ks == 0) {
         const uint8_t *sbase = smem + DMA_SCALE_BASE + ((st / 4) % 2) * DMA_SCALE_GROUP + (st % 4) * 4;
 #pragma unroll
         for (int i = 0; i < MXW; ++i) {
@@ -901,6 +913,10 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
           sb[i] = *(const int *)(sbase + BM * 16 + (rB0 + 32 * i) * 16);
         }
       }
+    };
+    auto load_frags = [&](int st, int ks, u32x4 (&af)[MXW], u32x4 (&bf)[MXW], int (&sa)[MXW], int (&sb)[MXW]) {
+      if (st < nst) load_frags_k(st, ks, std::false_type{}, af, bf, sa, sb);
+      else load_frags_k(st, ks, std::true_type{}, af, bf, sa, sb);
     };
 
     floatx16 acc[MXW][MXW];
@@ -952,20 +968,22 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     load_frags(0, 0, a0f, b0f, s0a, s0b);
     // One pipeline step; the FP4 stages and the bf16 correction stages run
     // in loops of their own so each MFMA kind keeps the accumulators in
-    // place. In a steady FP4 step (stages st + 1 .. st + 4 all FP4 stages)
-    // every condition is known at compile time, so the DMA issue and the
-    // fragment reads share one basic block with the MFMAs of half 1 and can
-    // be spread between them; a scale group, when due, follows the MFMAs.
-    // (Scheduling barriers keep the parts in order: the compiler would
-    // otherwise gather both MFMA halves behind one wait for all reads.)
-    auto step = [&](int st, auto corr, auto steady, auto scl) {
+    // place. In a steady step the kinds of stage st (corr), of stage st + 1
+    // (whose half 0 is read, nextc) and of stage st + 4 (whose DMA is issued,
+    // dmac) are known at compile time and stages st + 1 .. st + 4 exist, so
+    // the DMA issue and the fragment reads share one basic block with the
+    // MFMAs of half 1 and can be spread between them; a scale group, when
+    // due, follows the MFMAs. (Scheduling barriers keep the parts in order:
+    // the compiler would otherwise gather both MFMA halves behind one wait
+    // for all reads.)
+    auto step = [&](int st, auto corr, auto steady, auto nextc, auto dmac) {
       constexpr bool STEADY = decltype(steady)::value;
       // half 0 (read during the previous MFMA half) is complete before half
       // 1's reads are issued, so the MFMAs below wait for nothing
       __asm__ volatile("" : "+v"(a0f[0]), "+v"(a0f[1]), "+v"(a0f[2]), "+v"(a0f[3]), "+v"(b0f[0]), "+v"(b0f[1]),
                        "+v"(b0f[2]), "+v"(b0f[3]), "+v"(s0a[0]), "+v"(s0a[1]), "+v"(s0a[2]), "+v"(s0a[3]),
                        "+v"(s0b[0]), "+v"(s0b[1]), "+v"(s0b[2]), "+v"(s0b[3]));
-      load_frags(st, 1, a1f, b1f, s1a, s1b);
+      load_frags_k(st, 1, corr, a1f, b1f, s1a, s1b);
 #pragma unroll
       for (int i = 0; i < MXW; ++i) {
         s1a[i] = s0a[i];
@@ -999,8 +1017,9 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
       __asm__ volatile("" : "+v"(a1f[0]), "+v"(a1f[1]), "+v"(a1f[2]), "+v"(a1f[3]), "+v"(b1f[0]), "+v"(b1f[1]),
                        "+v"(b1f[2]), "+v"(b1f[3]));
       if constexpr (STEADY) {
-        issue(st + 4);
-        load_frags(st + 1, 0, a0f, b0f, s0a, s0b);
+        if constexpr (decltype(dmac)::value) issue_corr(st + 4);
+        else issue_main(st + 4);
+        load_frags_k(st + 1, 0, nextc, a0f, b0f, s0a, s0b);
       } else {
         if (st + 4 < ntot) issue(st + 4);
         if ((st + 1) % 4 == 0 && 4 * ((st + 1) / 4 + 1) < nst) issue_scales((st + 1) / 4 + 1);
@@ -1021,26 +1040,229 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (STEADY && decltype(scl)::value) {
-        if (4 * ((st + 1) / 4 + 1) < nst) issue_scales((st + 1) / 4 + 1);
+      if constexpr (STEADY && !decltype(corr)::value) {
+        if ((st + 1) % 4 == 0 && 4 * ((st + 1) / 4 + 1) < nst) issue_scales((st + 1) / 4 + 1);
       }
     };
     using F = std::false_type;
     using Tt = std::true_type;
     int st = 0;
-    // steady: st + 7 < nst keeps stages st + 1 .. st + 7 FP4 stages, so all
-    // four steps of a group are steady; the scale group is due at st + 3
+    // FP4 stages whose next four stages are FP4 stages too, four per group
     for (; st + 7 < nst; st += 4) {
-      step(st, F{}, Tt{}, F{});
-      step(st + 1, F{}, Tt{}, F{});
-      step(st + 2, F{}, Tt{}, F{});
-      step(st + 3, F{}, Tt{}, Tt{});
+      step(st, F{}, Tt{}, F{}, F{});
+      step(st + 1, F{}, Tt{}, F{}, F{});
+      step(st + 2, F{}, Tt{}, F{}, F{});
+      step(st + 3, F{}, Tt{}, F{}, F{});
     }
-    for (; st < nst; ++st) step(st, F{}, F{}, F{});
-    for (; st < ntot; ++st) step(st, Tt{}, F{}, F{});
+    if (ncs >= 4 && st + 4 == nst) {
+      // the last four FP4 stages issue the first correction stages
+      step(st, F{}, Tt{}, F{}, Tt{});
+      step(st + 1, F{}, Tt{}, F{}, Tt{});
+      step(st + 2, F{}, Tt{}, F{}, Tt{});
+      step(st + 3, F{}, Tt{}, Tt{}, Tt{});
+      st += 4;
+    }
+    for (; st < nst; ++st) step(st, F{}, F{}, F{}, F{});
+    for (; st + 4 < ntot; ++st) step(st, Tt{}, Tt{}, Tt{}, Tt{});
+    for (; st < ntot; ++st) step(st, Tt{}, F{}, F{}, F{});
     // every LDS read of the tile finished before the last barrier, so the
     // next tile's first loads may refill the ring while these stores drain
     store_acc_mx4(acc, m0, n0, M, N, C, ldc);
+  }
+}
+
+// Skinny products on the DMA path (MXFP4, T a multiple of 256): out[s]
+// (rows x cols, cols <= 32 NCT) = NT(A, B) over T-chunk s. A workgroup of
+// four waves takes 128 rows of A (wave w: rows 32 w ..) and all of B; a stage
+// is 256 contraction elements (128 code bytes and 8 scale bytes per row).
+// Codes go to LDS with 16-byte global_load_lds, eight lanes per row, so one
+// load instruction covers eight whole 128-byte row pieces (loading them in
+// the MFMA's own layout, one row per lane, made the address units the
+// bottleneck); slot 8 r + (u ^ (r & 7)) of a stage holds unit u of row r,
+// which keeps the fragment reads free of bank conflicts. Scales follow with
+// 4-byte loads, two per row. A ring of four stages is kept in flight. Rows
+// past the end read the last row: their products reach only rows or columns
+// that are not stored.
+constexpr int kSkRows = 128;
+constexpr int kSkStages = 4;
+template <int NCT>
+struct SkLayout {
+  static constexpr int A_CODES = 0;
+  static constexpr int B_CODES = kSkRows * 128;
+  static constexpr int A_SC = B_CODES + 32 * NCT * 128;
+  static constexpr int B_SC = A_SC + kSkRows * 8;
+  static constexpr int STAGE = B_SC + 32 * NCT * 8;
+  static constexpr int LOADS = 4 + NCT + 2;  // DMA instructions per wave and stage
+};
+
+// LDS reads of one skinny stage. Scales: the two words of the lane's A row
+// and of its B rows 32 j + r (rows 256 bytes apart). Codes: for K-block kk
+// the 16-byte unit 2 kk + h of the lane's A row and B rows, at slot
+// unit ^ (row & 7) (B rows 32 j + r share r & 7, so they are 4096 bytes
+// apart). Each asm block waits for its own loads.
+template <int NCT>
+__device__ __forceinline__ void skinny_read_scales(uint32_t pa, uint32_t pb, uint32_t (&wa)[2], uint32_t (&wb)[NCT][2]) {
+  uint2 a, b0, b1, b2;
+  if constexpr (NCT == 1) {
+    asm volatile("ds_read_b64 %0, %2\n\tds_read_b64 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(a), "=&v"(b0) : "v"(pa), "v"(pb) : "memory");
+  } else if constexpr (NCT == 2) {
+    asm volatile("ds_read_b64 %0, %3\n\tds_read_b64 %1, %4\n\tds_read_b64 %2, %4 offset:256\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(a), "=&v"(b0), "=&v"(b1) : "v"(pa), "v"(pb) : "memory");
+  } else {
+    asm volatile("ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %5 offset:256\n\t"
+                 "ds_read_b64 %3, %5 offset:512\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(a), "=&v"(b0), "=&v"(b1), "=&v"(b2) : "v"(pa), "v"(pb) : "memory");
+  }
+  wa[0] = a.x; wa[1] = a.y;
+  wb[0][0] = b0.x; wb[0][1] = b0.y;
+  if constexpr (NCT > 1) { wb[1][0] = b1.x; wb[1][1] = b1.y; }
+  if constexpr (NCT > 2) { wb[2][0] = b2.x; wb[2][1] = b2.y; }
+}
+
+template <int NCT>
+__device__ __forceinline__ void skinny_read_codes(uint32_t ra, uint32_t rb, int x, int h, u32x4 (&fa)[4],
+                                                  u32x4 (&fb)[4][NCT]) {
+  uint32_t pa[4], pb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const uint32_t off = (uint32_t)(((2 * kk + h) ^ x) << 4);
+    pa[kk] = ra + off;
+    pb[kk] = rb + off;
+  }
+  if constexpr (NCT == 1) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0][0]), "=&v"(fb[1][0]), "=&v"(fb[2][0]),
+          "=&v"(fb[3][0])
+        : "v"(pa[0]), "v"(pa[1]), "v"(pa[2]), "v"(pa[3]), "v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3])
+        : "memory");
+  } else if constexpr (NCT == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %13\n\tds_read_b128 %2, %14\n\tds_read_b128 %3, %15\n\t"
+        "ds_read_b128 %4, %16\n\tds_read_b128 %5, %16 offset:4096\n\t"
+        "ds_read_b128 %6, %17\n\tds_read_b128 %7, %17 offset:4096\n\t"
+        "ds_read_b128 %8, %18\n\tds_read_b128 %9, %18 offset:4096\n\t"
+        "ds_read_b128 %10, %19\n\tds_read_b128 %11, %19 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0][0]), "=&v"(fb[0][1]), "=&v"(fb[1][0]),
+          "=&v"(fb[1][1]), "=&v"(fb[2][0]), "=&v"(fb[2][1]), "=&v"(fb[3][0]), "=&v"(fb[3][1])
+        : "v"(pa[0]), "v"(pa[1]), "v"(pa[2]), "v"(pa[3]), "v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %16\n\tds_read_b128 %1, %17\n\tds_read_b128 %2, %18\n\tds_read_b128 %3, %19\n\t"
+        "ds_read_b128 %4, %20\n\tds_read_b128 %5, %20 offset:4096\n\tds_read_b128 %6, %20 offset:8192\n\t"
+        "ds_read_b128 %7, %21\n\tds_read_b128 %8, %21 offset:4096\n\tds_read_b128 %9, %21 offset:8192\n\t"
+        "ds_read_b128 %10, %22\n\tds_read_b128 %11, %22 offset:4096\n\tds_read_b128 %12, %22 offset:8192\n\t"
+        "ds_read_b128 %13, %23\n\tds_read_b128 %14, %23 offset:4096\n\tds_read_b128 %15, %23 offset:8192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0][0]), "=&v"(fb[0][1]), "=&v"(fb[0][2]),
+          "=&v"(fb[1][0]), "=&v"(fb[1][1]), "=&v"(fb[1][2]), "=&v"(fb[2][0]), "=&v"(fb[2][1]), "=&v"(fb[2][2]),
+          "=&v"(fb[3][0]), "=&v"(fb[3][1]), "=&v"(fb[3][2])
+        : "v"(pa[0]), "v"(pa[1]), "v"(pa[2]), "v"(pa[3]), "v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3])
+        : "memory");
+  }
+}
+
+template <int OP>
+__device__ __forceinline__ floatx16 mfma_fp4_op(const uint4 a, const uint4 b, int sa, int sb, floatx16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4x32(a), fp4x32(b), c, 4, 4, OP, sa, OP, sb);
+}
+
+template <int NCT>
+__global__ void __launch_bounds__(256)
+    skinny_dma_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t rows,
+                      const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int cols, int64_t T,
+                      int64_t chunk, float *__restrict__ out) {
+  using L = SkLayout<NCT>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSkStages * L::STAGE];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r = lane & 31, h = lane >> 5;
+  const int64_t row0 = (int64_t)blockIdx.x * kSkRows;
+  const int64_t t_beg = (int64_t)blockIdx.y * chunk, t_end = std::min<int64_t>(T, t_beg + chunk);
+  const int nst = (int)((t_end - t_beg) / 256);
+  const int64_t nbr = T / 32;  // scale bytes per row
+  // per-thread sources (byte offsets below 2^31 by the host's check)
+  uint32_t offA[4], offB[NCT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = t + 256 * i, rr = p >> 3, u = (p & 7) ^ (rr & 7);
+    offA[i] = (uint32_t)(std::min<int64_t>(row0 + rr, rows - 1) * (T / 2) + u * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NCT; ++i) {
+    const int p = t + 256 * i, rr = p >> 3, u = (p & 7) ^ (rr & 7);
+    offB[i] = (uint32_t)(std::min(rr, cols - 1) * (T / 2) + u * 16);
+  }
+  const uint32_t offSA = (uint32_t)(std::min<int64_t>(row0 + (t >> 1), rows - 1) * nbr + 4 * (t & 1));
+  const int pb = t % (64 * NCT);  // waves past NCT repeat the same loads (same bytes to the same slots)
+  const uint32_t offSB = (uint32_t)(std::min(pb >> 1, cols - 1) * nbr + 4 * (pb & 1));
+  auto issue = [&](int st) {
+    uint8_t *sb = smem + (st % kSkStages) * L::STAGE;
+    const int64_t k0 = t_beg + 256 * (int64_t)st;
+    const uint8_t *a_ = ac + k0 / 2, *b_ = bc + k0 / 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_load16(a_ + offA[i], sb + L::A_CODES + (256 * i + 64 * wave) * 16);
+#pragma unroll
+    for (int i = 0; i < NCT; ++i) dma_load16(b_ + offB[i], sb + L::B_CODES + (256 * i + 64 * wave) * 16);
+    dma_load4(as + k0 / 32 + offSA, sb + L::A_SC + 64 * wave * 4);
+    dma_load4(bs + k0 / 32 + offSB, sb + L::B_SC + (64 * wave % (64 * NCT)) * 4);
+  };
+  floatx16 acc[NCT];
+#pragma unroll
+  for (int j = 0; j < NCT; ++j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[j][q] = 0.0f;
+  const int ra_ = 32 * wave + r;  // this lane's A row in the block
+  for (int st = 0; st < kSkStages && st < nst; ++st) issue(st);
+  for (int st = 0; st < nst; ++st) {
+    // stage st has landed once at most the later stages' loads are pending
+    // (a plain __syncthreads would also wait for every later stage)
+    switch (std::min(kSkStages - 1, nst - 1 - st)) {
+      case 3: METIS_WAIT_VMCNT(3 * L::LOADS); break;
+      case 2: METIS_WAIT_VMCNT(2 * L::LOADS); break;
+      case 1: METIS_WAIT_VMCNT(1 * L::LOADS); break;
+      default: METIS_WAIT_VMCNT(0); break;
+    }
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");  // the reads below stay after the barrier
+    // the stage's reads in asm blocks that wait for their own data (the
+    // compiler would otherwise order them after every DMA still in flight)
+    const uint32_t sb = lds_offset(smem) + (st % kSkStages) * L::STAGE;
+    uint32_t wa[2], wb[NCT][2];
+    skinny_read_scales<NCT>(sb + L::A_SC + ra_ * 8, sb + L::B_SC + r * 8, wa, wb);
+    u32x4 fa[4], fb[4][NCT];
+    skinny_read_codes<NCT>(sb + L::A_CODES + ra_ * 128, sb + L::B_CODES + r * 128, r & 7, h, fa, fb);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      // lane half h holds block 2 kk + h of its row; the scale word of blocks
+      // 4 (kk / 2) .. is shifted by h bytes so opsel = 2 (kk % 2) picks it
+      const int sa = (int)(wa[kk >> 1] >> (8 * h));
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) {
+        const int sbw = (int)(wb[j][kk >> 1] >> (8 * h));
+        const uint4 a4 = {fa[kk].x, fa[kk].y, fa[kk].z, fa[kk].w}, b4 = {fb[kk][j].x, fb[kk][j].y, fb[kk][j].z, fb[kk][j].w};
+        acc[j] = (kk & 1) ? mfma_fp4_op<2>(a4, b4, sa, sbw, acc[j]) : mfma_fp4_op<0>(a4, b4, sa, sbw, acc[j]);
+      }
+    }
+    // every wave is done with the buffer of stage st before it is refilled
+    __asm__ volatile("" ::: "memory");
+    METIS_WAIT_LDS0();
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    if (st + kSkStages < nst) issue(st + kSkStages);
+  }
+  float *o = out + (int64_t)blockIdx.y * rows * cols;
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) {
+    const int col = 32 * j + r;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int64_t orow = row0 + 32 * wave + (q >> 2) * 8 + h * 4 + (q & 3);
+      if (orow < rows && col < cols) o[orow * cols + col] = acc[j][q];
+    }
   }
 }
 
@@ -1142,6 +1364,17 @@ void launch_skinny(const metis_fp4_t *A, int64_t rows, const metis_fp4_t *B, int
     else if (nct == 2) NV_SKINNY(2);
     else NV_SKINNY(3);
 #undef NV_SKINNY
+    return;
+  }
+  if (T % 256 == 0 && chunk % 256 == 0 && (((uintptr_t)A->codes | (uintptr_t)B->codes) & 15) == 0 &&
+      (((uintptr_t)A->scales | (uintptr_t)B->scales) & 3) == 0 && std::max<int64_t>(rows, cols) * (T / 2) < ((int64_t)1 << 31)) {
+    const dim3 g((unsigned)cdiv(rows, kSkRows), ks);
+    if (nct == 1)
+      skinny_dma_kernel<1><<<g, 256, 0, st>>>(A->codes, A->scales, rows, B->codes, B->scales, cols, T, chunk, out);
+    else if (nct == 2)
+      skinny_dma_kernel<2><<<g, 256, 0, st>>>(A->codes, A->scales, rows, B->codes, B->scales, cols, T, chunk, out);
+    else
+      skinny_dma_kernel<3><<<g, 256, 0, st>>>(A->codes, A->scales, rows, B->codes, B->scales, cols, T, chunk, out);
     return;
   }
   if (nct == 1)
