@@ -1925,10 +1925,38 @@ __device__ __forceinline__ void quant_store(const float (&v)[B], float s_t, uint
   *scale = (uint8_t)sb;
 }
 
+// Barrier for LDS traffic only: this wave's LDS accesses are complete, its
+// global loads and stores may still be in flight (the loads of the next tile
+// must stay in flight across the tile's barriers).
+#define METIS_LDS_BARRIER()                                                       \
+  do {                                                                            \
+    __asm__ volatile("" ::: "memory");                                           \
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));                        \
+    __builtin_amdgcn_s_barrier();                                                 \
+    __asm__ volatile("" ::: "memory");                                           \
+  } while (0)
+
+// XCDs of the chip; workgroups go to them round robin by block index.
+constexpr int kXcds = 8;
+
+// Residual + quantization over kRT x kRC tiles, persistent. The tiles are
+// paired vertically (row tiles 2s and 2s + 1, together 256 rows: a whole
+// 128-byte line of an R^T row) and the positions p = s ctiles + c of the
+// pairs are cut into runs of w along the rows. Run q is taken by two
+// workgroups, one per row tile of the pair, both on the same XCD (block
+// 2 X (q % Q) + q / Q + X parity, X = 8, Q runs per XCD), and XCD x takes
+// the runs x Q .. x Q + Q - 1, a contiguous stretch of the matrix: the partial
+// lines the tiles write (16 or 32 bytes of a row per tile) meet in one L2.
+// Per tile: L by MFMA (U of the tile's rows in registers, reloaded when the
+// row tile changes; the W panel of the tile's columns staged in LDS), R = A - L
+// kept in the LDS tile, row blocks quantized along n, then column blocks along
+// m. The W panel and A blocks of the next tile load during the current one.
+// Global loads take clamped, always valid addresses (m and n are multiples of
+// 32), so no branch separates a load from its use and the waits stay counted.
 // MEAN: the mean-residual split, L[r][c] = mu[c] (fp32, passed as `mu`)
 // instead of the MFMA product, so R = A - mu is one fp32 subtraction.
 template <typename T, bool NV, bool AMAX_ONLY, bool MEAN = false>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 registers
     residual_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda, const unsigned short *__restrict__ uhl,
                     const unsigned short *__restrict__ whl, int kp, uint8_t *__restrict__ rcodes,
                     uint8_t *__restrict__ rscales, float *__restrict__ rts, uint8_t *__restrict__ tcodes,
@@ -1939,155 +1967,195 @@ __global__ void __launch_bounds__(kThreads)
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  const int64_t col0 = (int64_t)blockIdx.x * kRC, row0 = (int64_t)blockIdx.y * kRT;
-  // ---- this thread's row blocks of A are loaded first, in flight while L is
-  // formed: block b = t + 256 j is row b / RPB, columns (b % RPB) * B ..
+  // ---- this workgroup's run of tile positions
+  const int ctiles = (int)cdiv(n, kRC), rtiles = (int)cdiv(m, kRT);
+  const int npos = (rtiles + 1) / 2 * ctiles;
+  const int nq = (int)gridDim.x / 2, qx = nq / kXcds;  // runs, runs per XCD (the grid is 2 X qx)
+  const int bx = (int)blockIdx.x;
+  const int parity = (bx / kXcds) & 1, q = (bx % kXcds) * qx + bx / (2 * kXcds);
+  const int w = (npos + nq - 1) / nq;
+  const int p0 = q * w;
+  int p1 = min(npos, p0 + w);
+  if (parity && (rtiles & 1)) p1 = min(p1, (rtiles / 2) * ctiles);  // no row tile 2s + 1 in the last pair
+  if (p0 >= p1) return;
+  // A row block b = t + 256 j of a tile is row b / RPB, columns (b % RPB) * B ..
   constexpr int RPB = kRC / B;                 // blocks per tile row
   constexpr int NJ = kRT * RPB / kThreads;     // row blocks per thread
   constexpr int VEC = B * (int)sizeof(T) / 16;  // 16-byte pieces per block
   static_assert(NJ * kThreads == kRT * RPB, "row blocks must divide over the threads");
-  uint4 apre[NJ][VEC];
-#pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) {
-    const int b = t + kThreads * jb, rr = b / RPB, cb = b % RPB;
-    const int64_t row = row0 + rr, col = col0 + cb * B;
-    const bool ok = row < m && col < n;
-    const uint4 *src = (const uint4 *)(A + row * lda + col);
-#pragma unroll
-    for (int q = 0; q < VEC; ++q) apre[jb][q] = ok ? src[q] : uint4{0u, 0u, 0u, 0u};
-  }
-  if constexpr (MEAN) {
-    // each thread fills a quarter of a column of the tile with mu
-    constexpr int RF = kRT * kRC / kThreads;
-    const int c = t % kRC, r0 = (t / kRC) * RF;
-    const float v = col0 + c < n ? mu[col0 + c] : 0.0f;
-#pragma unroll 8
-    for (int r = 0; r < RF; ++r) lt[r0 + r][c] = v;
-  } else
-  // ---- L tile via MFMA: wave owns rows wave*32 .. +32, all kRC columns.
-  // This wave's U operands (hi, lo) are loaded into registers up front; the W
-  // panel (hi, lo) of the tile's 128 columns is shared by the four waves and
-  // staged once in LDS, in the space the R tile takes later (row stride
-  // kp + 8 bf16 keeps the fragment reads conflict free).
-  {
-    constexpr int KPM = 96;  // largest kp (k <= 96)
-    unsigned short *wst = (unsigned short *)&lt[0][0];  // [2][kRC][kp + 8]
-    static_assert(2 * kRC * (96 + 8) * 2 <= kRT * (kRC + 4) * 4, "the W panel fits the tile's LDS");
-    const int wstride = kp + 8;
-    const int64_t um = m * kp, wn = n * kp;
-    ushortx8 uh[KPM / 32][2], ul[KPM / 32][2];
-#pragma unroll
-    for (int ks = 0; ks < KPM / 32; ++ks)
-#pragma unroll
-      for (int rs = 0; rs < 2; ++rs) {
-        const int64_t row = row0 + wave * 32 + rs * 16 + r16;
-        const bool ok = row < m && ks * 32 < kp;
-        const unsigned short *pu = uhl + row * kp + ks * 32 + g * 8;
-        uh[ks][rs] = ok ? *(const ushortx8 *)pu : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
-        ul[ks][rs] = ok ? *(const ushortx8 *)(pu + um) : ushortx8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    {
-      // the panel's 16-byte pieces, all of a thread's loads in flight together
-      constexpr int PW = 2 * kRC * (KPM / 8) / kThreads;
+  constexpr int KPM = 96;  // largest kp (k <= 96)
+  // 16-byte pieces of the W panel (hi, lo) per thread; none in the mean split
+  constexpr int PW = MEAN ? 0 : 2 * kRC * (KPM / 8) / kThreads;
+  // what a tile needs from HBM apart from U: its A blocks and its W panel
+  struct Pre {
+    uint4 a[NJ][VEC];
+    uint4 w[PW > 0 ? PW : 1];
+  };
+  auto tile_rt = [&](int p) { return 2 * (p / ctiles) + parity; };
+  // Loads of the tile at position p into pre: the panel first, then A.
+  // Panel pieces past kp and columns past n are loaded clamped, never read.
+  auto load_pre = [&](int p, Pre &pre) {
+    const int64_t row0 = (int64_t)tile_rt(p) * kRT, col0 = (int64_t)(p % ctiles) * kRC;
+    if constexpr (!MEAN) {
       const int nw = 2 * kRC * (kp / 8);
-      uint4 v[PW];
+      const int64_t wn = n * kp;
 #pragma unroll
       for (int u = 0; u < PW; ++u) {
-        const int idx = t + u * kThreads;
+        const int idx = min(t + u * kThreads, nw - 1);
         const int h = idx / (kRC * (kp / 8)), rem = idx % (kRC * (kp / 8));
-        const int c = rem / (kp / 8), q = rem % (kp / 8);
-        const int64_t col = col0 + c;
-        v[u] = (idx < nw && col < n) ? *(const uint4 *)(whl + h * wn + col * kp + q * 8) : uint4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < PW; ++u) {
-        const int idx = t + u * kThreads;
-        const int h = idx / (kRC * (kp / 8)), rem = idx % (kRC * (kp / 8));
-        const int c = rem / (kp / 8), q = rem % (kp / 8);
-        if (idx < nw) *(uint4 *)(wst + (h * kRC + c) * wstride + q * 8) = v[u];
+        const int c = rem / (kp / 8), qq = rem % (kp / 8);
+        pre.w[u] = *(const uint4 *)(whl + h * wn + min(col0 + c, n - 1) * kp + qq * 8);
       }
     }
-    __syncthreads();
-    constexpr int NCS = kRC / 16;
-    floatx4 acc[2][NCS];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int jb = 0; jb < NJ; ++jb) {
+      const int b = t + kThreads * jb, rr = b / RPB, cb = b % RPB;
+      const int64_t row = min(row0 + rr, m - 1), col = min(col0 + cb * B, n - B);
+      const uint4 *src = (const uint4 *)(A + row * lda + col);
 #pragma unroll
-      for (int b = 0; b < NCS; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KPM / 32; ++ks) {
-      if (ks * 32 >= kp) break;
-#pragma unroll
-      for (int cs = 0; cs < NCS; ++cs) {
-        const int c = cs * 16 + r16;
-        const ushortx8 wh = *(const ushortx8 *)(wst + c * wstride + ks * 32 + g * 8);
-        const ushortx8 wl = *(const ushortx8 *)(wst + (kRC + c) * wstride + ks * 32 + g * 8);
-#pragma unroll
-        for (int rs = 0; rs < 2; ++rs) {
-          acc[rs][cs] = mfma16_bf16(uh[ks][rs], wh, acc[rs][cs]);
-          acc[rs][cs] = mfma16_bf16(uh[ks][rs], wl, acc[rs][cs]);
-          acc[rs][cs] = mfma16_bf16(ul[ks][rs], wh, acc[rs][cs]);
-        }
-      }
+      for (int qq = 0; qq < VEC; ++qq) pre.a[jb][qq] = src[qq];
     }
-    __syncthreads();  // the W panel is no longer read
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-      for (int cs = 0; cs < NCS; ++cs)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) lt[wave * 32 + rs * 16 + g * 4 + q][cs * 16 + r16] = acc[rs][cs][q];
-  }
-  __syncthreads();
+  };
   float s_t = 1.0f;
   if (NV && !AMAX_ONLY) s_t = nv_tensor_scale(__uint_as_float(*amax));
-  if (NV && !AMAX_ONLY && blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
+  if (NV && !AMAX_ONLY && bx == 0 && t == 0) {
     if (rts) *rts = s_t;
     if (tts) *tts = s_t;
   }
-  // ---- row blocks (along n): R = A - L, kept in LDS for the column pass
+  ushortx8 uh[KPM / 32][2], ul[KPM / 32][2];
+  int cur_rt = -1;
   float mx = 0.0f;
+  // One tile: `cur` holds its loads (issued one tile earlier), `nxt`
+  // receives the next tile's (the last tile of the run loads itself again,
+  // from cache), so the waits of a tile are for loads a tile old.
+  auto tile = [&](int p, Pre &cur, Pre &nxt) {
+    const int rt = tile_rt(p);
+    const int64_t row0 = (int64_t)rt * kRT, col0 = (int64_t)(p % ctiles) * kRC;
+    const int p_n = min(p + 1, p1 - 1);
+    if constexpr (MEAN) {
+      // each thread fills a quarter of a column of the tile with mu
+      constexpr int RF = kRT * kRC / kThreads;
+      const int c = t % kRC, r0 = (t / kRC) * RF;
+      const float v = mu[min(col0 + c, n - 1)];
+      load_pre(p_n, nxt);
+#pragma unroll 8
+      for (int r = 0; r < RF; ++r) lt[r0 + r][c] = v;
+    } else {
+      // ---- L tile via MFMA: wave owns rows wave*32 .. +32, all kRC columns.
+      // The W panel (hi, lo) of the tile's columns is shared by the four
+      // waves and staged in LDS, in the space the R tile takes later (row
+      // stride kp + 8 bf16 keeps the fragment reads conflict free).
+      unsigned short *wst = (unsigned short *)&lt[0][0];  // [2][kRC][kp + 8]
+      static_assert(2 * kRC * (96 + 8) * 2 <= kRT * (kRC + 4) * 4, "the W panel fits the tile's LDS");
+      const int wstride = kp + 8;
+      const int64_t um = m * kp;
+      if (rt != cur_rt) {
+        cur_rt = rt;
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) {
-    const int b = t + kThreads * jb, rr = b / RPB, cb = b % RPB;
-    const int64_t row = row0 + rr, col = col0 + cb * B;
-    float v[B];
-    const bool ok = row < m && col < n;
-    const T *pa = (const T *)&apre[jb][0];
+        for (int ks = 0; ks < KPM / 32; ++ks)
 #pragma unroll
-    for (int i = 0; i < B; ++i) v[i] = ok ? load_f32(pa + i) - lt[rr][cb * B + i] : 0.0f;
+          for (int rs = 0; rs < 2; ++rs) {
+            // rows past m and k past kp are loaded clamped: their products
+            // land in rows of L that are never read or are skipped
+            const int64_t row = min(row0 + wave * 32 + rs * 16 + r16, m - 1);
+            const unsigned short *pu = uhl + row * kp + min(ks * 32, kp - 32) + g * 8;
+            uh[ks][rs] = *(const ushortx8 *)pu;
+            ul[ks][rs] = *(const ushortx8 *)(pu + um);
+          }
+      }
+      load_pre(p_n, nxt);
+      // piece idx of the panel goes to LDS row idx / P, slot idx % P
+      // (P = kp / 8); the pieces past the panel (kp < 96) land in unused rows
+      // below it, byte offset 16 (idx + idx / P) < 16 * 5 / 4 * PW * 256,
+      // inside the tile, so the stores need no branch (a branch would pull
+      // each load into it)
+      static_assert(16 * (PW * kThreads + PW * kThreads / 4) <= (int)sizeof(lt), "spare panel stores stay in the tile");
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
-      lt[rr][cb * B + i] = v[i];
-      mx = fmaxf(mx, fabsf(v[i]));
+      for (int u = 0; u < PW; ++u) {
+        const int idx = t + u * kThreads;
+        *(uint4 *)(wst + (idx / (kp / 8)) * wstride + (idx % (kp / 8)) * 8) = cur.w[u];
+      }
+      METIS_LDS_BARRIER();
+      constexpr int NCS = kRC / 16;
+      floatx4 acc[2][NCS];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < NCS; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KPM / 32; ++ks) {
+        if (ks * 32 >= kp) break;
+#pragma unroll
+        for (int cs = 0; cs < NCS; ++cs) {
+          const int c = cs * 16 + r16;
+          const ushortx8 wh = *(const ushortx8 *)(wst + c * wstride + ks * 32 + g * 8);
+          const ushortx8 wl = *(const ushortx8 *)(wst + (kRC + c) * wstride + ks * 32 + g * 8);
+#pragma unroll
+          for (int rs = 0; rs < 2; ++rs) {
+            acc[rs][cs] = mfma16_bf16(uh[ks][rs], wh, acc[rs][cs]);
+            acc[rs][cs] = mfma16_bf16(uh[ks][rs], wl, acc[rs][cs]);
+            acc[rs][cs] = mfma16_bf16(ul[ks][rs], wh, acc[rs][cs]);
+          }
+        }
+      }
+      METIS_LDS_BARRIER();  // the W panel is no longer read
+#pragma unroll
+      for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+        for (int cs = 0; cs < NCS; ++cs)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) lt[wave * 32 + rs * 16 + g * 4 + qq][cs * 16 + r16] = acc[rs][cs][qq];
     }
-    if (!AMAX_ONLY && ok && rcodes)
-      quant_store<B, NV>(v, s_t, rcodes + row * (n / 2) + col / 2, rscales + row * (n / B) + col / B);
+    METIS_LDS_BARRIER();
+    // ---- row blocks (along n): R = A - L, kept in LDS for the column pass
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb) {
+      const int b = t + kThreads * jb, rr = b / RPB, cb = b % RPB;
+      const int64_t row = row0 + rr, col = col0 + cb * B;
+      float v[B];
+      const bool ok = row < m && col < n;
+      const T *pa = (const T *)&cur.a[jb][0];
+#pragma unroll
+      for (int i = 0; i < B; ++i) v[i] = ok ? load_f32(pa + i) - lt[rr][cb * B + i] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        lt[rr][cb * B + i] = v[i];
+        mx = fmaxf(mx, fabsf(v[i]));
+      }
+      if (!AMAX_ONLY && ok && rcodes)
+        quant_store<B, NV>(v, s_t, rcodes + row * (n / 2) + col / 2, rscales + row * (n / B) + col / B);
+    }
+    if (!AMAX_ONLY && tcodes) {
+      METIS_LDS_BARRIER();
+      // ---- column blocks (along m) into R^T (n x m): thread t takes
+      // consecutive row blocks of column t % kRC, so its code stores are
+      // adjacent in R^T's row
+      constexpr int PER = kRC * (kRT / B) / kThreads;  // row blocks per thread
+      const int cc = t % kRC, rb0 = (t / kRC) * PER;
+      const int64_t col = col0 + cc;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int rb = rb0 + u;
+        const int64_t row = row0 + rb * B;
+        if (col >= n || row >= m) continue;
+        float v[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) v[i] = lt[rb * B + i][cc];
+        quant_store<B, NV>(v, s_t, tcodes + col * (m / 2) + row / 2, tscales + col * (m / B) + row / B);
+      }
+    }
+    METIS_LDS_BARRIER();  // the tile's LDS is free for the next one
+  };
+  Pre pre0, pre1;
+  load_pre(p0, pre0);
+  for (int p = p0; p < p1; p += 2) {
+    tile(p, pre0, pre1);
+    if (p + 1 >= p1) break;
+    tile(p + 1, pre1, pre0);
   }
   if (AMAX_ONLY) {
     mx = wave_max(mx);
     if (lane == 0) atomicMax(amax, __float_as_uint(mx));
-    return;
-  }
-  if (!tcodes) return;
-  __syncthreads();
-  // ---- column blocks (along m) into R^T (n x m): thread t takes
-  // consecutive row blocks of column t % kRC, so its code stores are
-  // adjacent in R^T's row
-  {
-    constexpr int PER = kRC * (kRT / B) / kThreads;  // row blocks per thread
-    const int cc = t % kRC, rb0 = (t / kRC) * PER;
-    const int64_t col = col0 + cc;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int rb = rb0 + u;
-      const int64_t row = row0 + rb * B;
-      if (col >= n || row >= m) continue;
-      float v[B];
-#pragma unroll
-      for (int i = 0; i < B; ++i) v[i] = lt[rb * B + i][cc];
-      quant_store<B, NV>(v, s_t, tcodes + col * (m / 2) + row / 2, tscales + col * (m / B) + row / B);
-    }
   }
 }
 
@@ -2220,7 +2288,10 @@ metis_status_t run_factors_and_residual(const SplitPlan &p, const T *A, int64_t 
         out->Vt_q.scales, nullptr, p.amax, p.uhl, p.whl);
   }
   // ---- pass 3: residual + quantization (NVFP4: a max pass first)
-  const dim3 rgrid((unsigned)cdiv(n, kRC), (unsigned)cdiv(m, kRT));
+  // persistent residual: two workgroups per run, up to 32 runs per XCD (two
+  // resident workgroups per CU; registers bound it)
+  const int64_t npos = (cdiv(m, kRT) + 1) / 2 * cdiv(n, kRC);
+  const unsigned rgrid = (unsigned)(2 * kXcds * std::min<int64_t>(32, cdiv(npos, kXcds)));
   if (nv) {
     residual_kernel<T, true, true, MEAN><<<rgrid, kThreads, 0, st>>>(
         A, m, n, lda, p.uhl, p.whl, kp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p.amax + 2, mu);
