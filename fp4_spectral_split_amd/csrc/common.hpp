@@ -73,6 +73,27 @@ __device__ __forceinline__ void e2m1_pack(const float (&q)[B], uint32_t (&packed
   for (int w = 0; w < B / 8; ++w) packed[w] = e2m1_pack8(&q[8 * w]);
 }
 
+// The fp32 value 2^e for e in [-127, 127] (2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float pow2_f32(int e) {
+  return e > -127 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Codes of one block of B values divided by the power of two `scale`: the
+// gfx950 FP4 conversion divides its inputs by its scale operand before
+// rounding, which for a power of two is exact (subnormal scales included), so
+// these are the codes of e2m1_rne(v / scale) without a separate scaling step.
+template <int B>
+__device__ __forceinline__ void e2m1_pack_scaled(const float (&v)[B], float scale, uint32_t (&packed)[B / 8]) {
+#pragma unroll
+  for (int w = 0; w < B / 8; ++w) {
+    const float *x = &v[8 * w];
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0], x[1], scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[2], x[3], scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[4], x[5], scale, 2);
+    packed[w] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, x[6], x[7], scale, 3);
+  }
+}
+
 // Magnitude of an E2M1 code times 2 (integers 0,1,2,3,4,6,8,12): value = x2 / 2.
 __device__ __forceinline__ float e2m1_value(uint32_t code) {
   const uint32_t m = code & 7u;

@@ -21,21 +21,20 @@ __device__ __forceinline__ uint32_t quant_block(const float (&v)[B], float s_t, 
 #pragma unroll
   for (int i = 0; i < B; ++i) amax = fmaxf(amax, fabsf(v[i]));
   uint32_t scale_byte;
-  float q[B];
   if (!NV) {
     const int se = mx_shared_exponent(amax);
     scale_byte = (uint32_t)(se + 127);
-#pragma unroll
-    for (int i = 0; i < B; ++i) q[i] = ldexpf(v[i], -se);
+    e2m1_pack_scaled<B>(v, pow2_f32(se), packed);
   } else {
     const float d = 6.0f * s_t;
     scale_byte = e4m3_rne_sat(__fdiv_rn(amax, d));
     const float den = e4m3_value(scale_byte) * s_t;
     // a zero scale leaves only the signs (v * 0 keeps the sign of v)
+    float q[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) q[i] = scale_byte ? __fdiv_rn(v[i], den) : v[i] * 0.0f;
+    e2m1_pack<B>(q, packed);
   }
-  e2m1_pack<B>(q, packed);
   return scale_byte;
 }
 

@@ -1872,18 +1872,18 @@ __global__ void __launch_bounds__(kThreads)
   float amx = 0.0f;
   for (int i = 0; i < B; ++i) amx = fmaxf(amx, fabsf(v[i]));
   uint32_t sb;
-  float q[B];
+  uint32_t pk[B / 8];
   if (!NV) {
     const int se = mx_shared_exponent(amx);
     sb = (uint32_t)(se + 127);
-    for (int i = 0; i < B; ++i) q[i] = ldexpf(v[i], -se);
+    e2m1_pack_scaled<B>(v, pow2_f32(se), pk);
   } else {
     sb = e4m3_rne_sat(__fdiv_rn(amx, 6.0f * s_t));
     const float den = e4m3_value(sb) * s_t;
+    float q[B];
     for (int i = 0; i < B; ++i) q[i] = sb ? __fdiv_rn(v[i], den) : v[i] * 0.0f;  // zero scale: signs only
+    e2m1_pack<B>(q, pk);
   }
-  uint32_t pk[B / 8];
-  e2m1_pack<B>(q, pk);
   uint32_t *dst = (uint32_t *)(codes + (int64_t)c * (rows / 2) + blk * (B / 2));
   for (int w = 0; w < B / 8; ++w) dst[w] = pk[w];
   scales[(int64_t)c * (rows / B) + blk] = (uint8_t)sb;
@@ -1903,20 +1903,19 @@ __device__ __forceinline__ void quant_store(const float (&v)[B], float s_t, uint
 #pragma unroll
   for (int i = 0; i < B; ++i) amx = fmaxf(amx, fabsf(v[i]));
   uint32_t sb;
-  float q[B];
+  uint32_t pk[B / 8];
   if (!NV) {
     const int se = mx_shared_exponent(amx);
     sb = (uint32_t)(se + 127);
-#pragma unroll
-    for (int i = 0; i < B; ++i) q[i] = ldexpf(v[i], -se);
+    e2m1_pack_scaled<B>(v, pow2_f32(se), pk);
   } else {
     sb = e4m3_rne_sat(__fdiv_rn(amx, 6.0f * s_t));
     const float den = e4m3_value(sb) * s_t;
+    float q[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) q[i] = sb ? __fdiv_rn(v[i], den) : v[i] * 0.0f;  // zero scale: signs only
+    e2m1_pack<B>(q, pk);
   }
-  uint32_t pk[B / 8];
-  e2m1_pack<B>(q, pk);
   if constexpr (B == 32) {
     *(uint4 *)codes = uint4{pk[0], pk[1], pk[2], pk[3]};
   } else {
