@@ -127,6 +127,24 @@ def power_split_leg(torch, M, A, Om, recs, tensors, reps=5):
     return {"tensor": "X_up 8192x4096 bf16, k 64, l 80", **out}
 
 
+def profile_splits(torch, M, A, Om, recs, tensors, reps):
+    """For kernel profiles of the split and quantize kernels alone (their HBM
+    rate is read from the profiler, not printed): each of the six spectral
+    splits reps times back to back on one stream, then the standalone MXFP4
+    quantizer on X_up in both orientations reps times. Replaces the steps."""
+    for n, t in tensors.items():
+        for _ in range(reps):
+            M.metis_split(A[n], t.l, t.k, "mxfp4", omega=Om[n], out=recs[n])
+        torch.cuda.synchronize()
+        log("profiled split %s x %d" % (n, reps))
+    x = A["X_up"]
+    for _ in range(reps):
+        M.fp4_block_quant(x, "mxfp4")
+        M.fp4_block_quant(x, "mxfp4", transpose=True)
+    torch.cuda.synchronize()
+    log("profiled fp4_block_quant X_up (both orientations) x %d" % reps)
+
+
 def cpu_baseline(tensors, gemm_total_flops):
     """The fp64 oracle on a bounded sample of the same workload: the split of
     X_up (8192 x 4096) and the forward GEMM Y_up on 256 sampled rows; the
@@ -170,6 +188,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain copy of MIB MiB ahead of the steps (counter calibration)")
+    ap.add_argument("--profile-splits", type=int, default=0, metavar="REPS",
+                    help="instead of the steps, run each split and the quantizer REPS times alone (for profiles)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
@@ -201,6 +221,9 @@ def main():
     Om = {n: torch.from_numpy(t.omega.view(np.int16)).view(torch.bfloat16).to(dev).contiguous()
           for n, t in tensors.items()}
     recs = {n: M.empty_split(t.shape[0], t.shape[1], t.k, "mxfp4", ("n", "t"), dev) for n, t in tensors.items()}
+    if args.profile_splits:
+        profile_splits(torch, M, A, Om, recs, tensors, args.profile_splits)
+        return
     outs, gobj = {}, {}
     for out, a, ao, b, bo in gemms:
         g = M.GemmNT(recs[a], ao == "t", recs[b], bo == "t")
