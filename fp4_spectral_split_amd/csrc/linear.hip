@@ -335,31 +335,45 @@ __device__ __forceinline__ void panel_sum_slabs(const float *__restrict__ src, i
 }
 
 // Decoded values of a k x rows factor matrix at rows [r0, r0 + nr), columns
-// c < k: store(c, r, e2m1 * block scale), codes and scales loaded together.
-template <bool NV, typename Store>
-__device__ __forceinline__ void panel_factor_values(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                                                    int64_t rows, int k, int64_t r0, int nr, Store store) {
-  const int t = threadIdx.x;
-  constexpr int B = NV ? 16 : 32;
+// c < k, in two parts so other loads can be in flight between them:
+// load() issues every code and scale load of the thread at once (from a
+// valid index, element (0, r0) when out of range, none behind a branch);
+// decode() then calls store(c, r, e2m1 * block scale). k = 0 (an unsplit
+// side, possibly without buffers) loads and stores nothing.
+template <bool NV>
+struct PanelFactor {
   uint32_t cb[kPanelPer], sb[kPanelPer];
+  __device__ __forceinline__ void load(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                       int64_t rows, int k, int64_t r0, int nr) {
+    constexpr int B = NV ? 16 : 32;
+    if (k <= 0) return;
 #pragma unroll
-  for (int v = 0; v < kPanelPer; ++v) {
-    const int e = t + v * kPanelThreads, c = e / kPanelRows, r = e - c * kPanelRows;
-    const bool ok = c < k && r < nr;
-    const int64_t i = r0 + r;
-    cb[v] = ok ? codes[(int64_t)c * (rows / 2) + i / 2] : 0u;
-    sb[v] = ok ? scales[(int64_t)c * (rows / B) + i / B] : 0u;
-  }
-#pragma unroll
-  for (int v = 0; v < kPanelPer; ++v) {
-    const int e = t + v * kPanelThreads, c = e / kPanelRows, r = e - c * kPanelRows;
-    if (c < k && r < nr) {
-      const uint32_t code = ((r0 + r) & 1) ? (cb[v] >> 4) : (cb[v] & 15u);
-      const float val = NV ? e2m1_value(code) * e4m3_value(sb[v]) : ldexpf(e2m1_value(code), (int)sb[v] - 127);
-      store(c, r, val);
+    for (int v = 0; v < kPanelPer; ++v) {
+      const int e = threadIdx.x + v * kPanelThreads, c = e / kPanelRows, r = e - c * kPanelRows;
+      const bool ok = c < k && r < nr;
+      const int64_t cc = ok ? c : 0, i = r0 + (ok ? r : 0);
+      cb[v] = codes[cc * (rows / 2) + i / 2];
+      sb[v] = scales[cc * (rows / B) + i / B];
     }
   }
-}
+  template <typename Store>
+  __device__ __forceinline__ void decode(int k, int64_t r0, int nr, Store store) {
+    if (k <= 0) return;
+    // the decode stays here (the compiler would otherwise hoist it, and the
+    // wait for these loads, above the loads issued in between)
+#pragma unroll
+    for (int v = 0; v < kPanelPer; ++v) __asm__ volatile("" : "+v"(cb[v]), "+v"(sb[v]));
+#pragma unroll
+    for (int v = 0; v < kPanelPer; ++v) {
+      const int e = threadIdx.x + v * kPanelThreads, c = e / kPanelRows, r = e - c * kPanelRows;
+      if (c < k && r < nr) {
+        const uint32_t code = ((r0 + r) & 1) ? (cb[v] >> 4) : (cb[v] & 15u);
+        const float val = NV ? e2m1_value(code) * e4m3_value(sb[v]) : ldexpf(e2m1_value(code), (int)sb[v] - 127);
+        store(c, r, val);
+      }
+    }
+  }
+};
 
 // Rows [0, nr) of a panel (row stride rp, a multiple of 8) from value(r, c),
 // eight columns per 16-byte store.
@@ -400,8 +414,10 @@ __global__ void __launch_bounds__(kPanelThreads)
   if ((int64_t)blockIdx.x < l1_blocks) {
     const int64_t i0 = (int64_t)blockIdx.x * R;
     const int nr = (int)min<int64_t>(R, ra - i0);
+    PanelFactor<NV> fa;
+    fa.load(ga_c, ga_s, ra, ka, i0, nr);  // in flight during the slab sums
     panel_sum_slabs(ppart + i0 * kb, ra * kb, ks_p, nr * kb, [&](int i, float v) { fv[i / kb][i % kb] = v; });
-    panel_factor_values<NV>(ga_c, ga_s, ra, ka, i0, nr, [&](int c, int r, float v) { gv[r][c] = v; });
+    fa.decode(ka, i0, nr, [&](int c, int r, float v) { gv[r][c] = v; });
     __syncthreads();
     const float fold_b = ts_s[1];
     panel_write_rows(l1 + i0 * rp, nr, rp, [&](int r, int c) -> unsigned short {
@@ -420,8 +436,10 @@ __global__ void __launch_bounds__(kPanelThreads)
     if (ka && kb)
       stage_batched<16>(&cross[0][0], cross_g, ka * kb, [](int i) { return i; },
                         [=](int i) { return (i / kb) * 97 + i % kb; });
-    panel_factor_values<NV>(gb_c, gb_s, rb, kb, j0, nr, [&](int d, int r, float v) { fv[r][d] = v; });
+    PanelFactor<NV> fb;
+    fb.load(gb_c, gb_s, rb, kb, j0, nr);  // in flight during the slab sums
     panel_sum_slabs(qpart + j0 * ka, rb * ka, ks_q, nr * ka, [&](int i, float v) { qv[i / ka][i % ka] = v; });
+    fb.decode(kb, j0, nr, [&](int d, int r, float v) { fv[r][d] = v; });
     __syncthreads();
     const float fold_a = ts_s[0], tsb = NV ? ts_s[1] : 1.0f;
     for (int e = t; e < nr * kb; e += kPanelThreads) {
