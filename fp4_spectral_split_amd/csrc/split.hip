@@ -1939,21 +1939,23 @@ __device__ __forceinline__ void quant_store(const float (&v)[B], float s_t, uint
 constexpr int kXcds = 8;
 
 // Residual + quantization over kRT x kRC tiles, persistent. The tiles are
-// paired vertically (row tiles 2s and 2s + 1, together 256 rows: a whole
-// 128-byte line of an R^T row) and the positions p = s ctiles + c of the
-// pairs are cut into runs of w along the rows. Run q is taken by two
-// workgroups, one per row tile of the pair, both on the same XCD (block
-// 2 X (q % Q) + q / Q + X parity, X = 8, Q runs per XCD), and XCD x takes
-// the runs x Q .. x Q + Q - 1, a contiguous stretch of the matrix: the partial
-// lines the tiles write (16 or 32 bytes of a row per tile) meet in one L2.
-// Per tile: L by MFMA (U of the tile's rows in registers, reloaded when the
-// row tile changes; the W panel of the tile's columns staged in LDS), R = A - L
-// kept in the LDS tile, row blocks quantized along n, then column blocks along
-// m. The W panel and A blocks of the next tile load during the current one.
+// taken in blocks of 2 x 4 (256 rows x 256 columns: whole 128-byte lines of
+// the rows of R (32 code bytes per tile row) and of R^T (64 per tile
+// column)), each block by a group of eight workgroups on one XCD, one tile
+// each (member j: row tile 2 s + j / 4, column tile 4 c + j % 4 of block
+// (s, c)), so the pieces of a line are written together and meet in one L2
+// before it writes the line back. A group walks a run of w blocks along the
+// rows; XCD x takes the groups of a contiguous stretch of runs (block index
+// b goes to XCD b % 8). Tiles past the matrix edge store nothing. Per tile: L by
+// MFMA (U of the tile's rows in registers, reloaded when the row tile
+// changes; the W panel of the tile's columns staged in LDS), R = A - L kept
+// in the LDS tile, row blocks quantized along n, then column blocks along m.
+// The W panel and A blocks of the next tile load during the current one.
 // Global loads take clamped, always valid addresses (m and n are multiples of
 // 32), so no branch separates a load from its use and the waits stay counted.
 // MEAN: the mean-residual split, L[r][c] = mu[c] (fp32, passed as `mu`)
 // instead of the MFMA product, so R = A - mu is one fp32 subtraction.
+constexpr int kResGroup = 8;  // workgroups per block of 2 x 4 tiles
 template <typename T, bool NV, bool AMAX_ONLY, bool MEAN = false>
 __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 registers
     residual_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda, const unsigned short *__restrict__ uhl,
@@ -1966,16 +1968,15 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int r16 = lane & 15, g = lane >> 4;
-  // ---- this workgroup's run of tile positions
+  // ---- this workgroup's run of blocks (the grid is 8 x 8 x groups per XCD)
   const int ctiles = (int)cdiv(n, kRC), rtiles = (int)cdiv(m, kRT);
-  const int npos = (rtiles + 1) / 2 * ctiles;
-  const int nq = (int)gridDim.x / 2, qx = nq / kXcds;  // runs, runs per XCD (the grid is 2 X qx)
-  const int bx = (int)blockIdx.x;
-  const int parity = (bx / kXcds) & 1, q = (bx % kXcds) * qx + bx / (2 * kXcds);
-  const int w = (npos + nq - 1) / nq;
-  const int p0 = q * w;
-  int p1 = min(npos, p0 + w);
-  if (parity && (rtiles & 1)) p1 = min(p1, (rtiles / 2) * ctiles);  // no row tile 2s + 1 in the last pair
+  const int cblocks = (ctiles + 3) / 4, nblk = (rtiles + 1) / 2 * cblocks;
+  const int ngrp = (int)gridDim.x / kResGroup, gpx = ngrp / kXcds;
+  const int bx = (int)blockIdx.x, kx = bx / kXcds;
+  const int grp = (bx % kXcds) * gpx + kx / kResGroup, member = kx % kResGroup;
+  const int parity = member / 4, cofs = member % 4;
+  const int w = (nblk + ngrp - 1) / ngrp;
+  const int p0 = grp * w, p1 = min(nblk, p0 + w);
   if (p0 >= p1) return;
   // A row block b = t + 256 j of a tile is row b / RPB, columns (b % RPB) * B ..
   constexpr int RPB = kRC / B;                 // blocks per tile row
@@ -1990,11 +1991,13 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
     uint4 a[NJ][VEC];
     uint4 w[PW > 0 ? PW : 1];
   };
-  auto tile_rt = [&](int p) { return 2 * (p / ctiles) + parity; };
-  // Loads of the tile at position p into pre: the panel first, then A.
-  // Panel pieces past kp and columns past n are loaded clamped, never read.
+  auto tile_rt = [&](int p) { return 2 * (p / cblocks) + parity; };
+  auto tile_ct = [&](int p) { return 4 * (p % cblocks) + cofs; };
+  // Loads of this workgroup's tile of block p into pre: the panel first, then
+  // A. Panel pieces past kp and rows or columns past the matrix (a skipped
+  // tile's too) are loaded clamped, never read.
   auto load_pre = [&](int p, Pre &pre) {
-    const int64_t row0 = (int64_t)tile_rt(p) * kRT, col0 = (int64_t)(p % ctiles) * kRC;
+    const int64_t row0 = (int64_t)tile_rt(p) * kRT, col0 = (int64_t)tile_ct(p) * kRC;
     if constexpr (!MEAN) {
       const int nw = 2 * kRC * (kp / 8);
       const int64_t wn = n * kp;
@@ -2028,8 +2031,11 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
   // receives the next tile's (the last tile of the run loads itself again,
   // from cache), so the waits of a tile are for loads a tile old.
   auto tile = [&](int p, Pre &cur, Pre &nxt) {
-    const int rt = tile_rt(p);
-    const int64_t row0 = (int64_t)rt * kRT, col0 = (int64_t)(p % ctiles) * kRC;
+    const int rt = tile_rt(p), ct = tile_ct(p);
+    const int64_t row0 = (int64_t)rt * kRT, col0 = (int64_t)ct * kRC;
+    // a tile past the matrix edge runs like the others on clamped loads; the
+    // row and column checks below keep all of its stores out (a branch
+    // around it would cost the loop its counted waits)
     const int p_n = min(p + 1, p1 - 1);
     if constexpr (MEAN) {
       // each thread fills a quarter of a column of the tile with mu
@@ -2287,10 +2293,10 @@ metis_status_t run_factors_and_residual(const SplitPlan &p, const T *A, int64_t 
         out->Vt_q.scales, nullptr, p.amax, p.uhl, p.whl);
   }
   // ---- pass 3: residual + quantization (NVFP4: a max pass first)
-  // persistent residual: two workgroups per run, up to 32 runs per XCD (two
-  // resident workgroups per CU; registers bound it)
-  const int64_t npos = (cdiv(m, kRT) + 1) / 2 * cdiv(n, kRC);
-  const unsigned rgrid = (unsigned)(2 * kXcds * std::min<int64_t>(32, cdiv(npos, kXcds)));
+  // persistent residual: groups of eight workgroups, up to eight groups per
+  // XCD (two resident workgroups per CU; registers bound it)
+  const int64_t nblk = (cdiv(m, kRT) + 1) / 2 * cdiv(cdiv(n, kRC), 4);
+  const unsigned rgrid = (unsigned)(kResGroup * kXcds * std::min<int64_t>(8, cdiv(nblk, kXcds)));
   if (nv) {
     residual_kernel<T, true, true, MEAN><<<rgrid, kThreads, 0, st>>>(
         A, m, n, lda, p.uhl, p.whl, kp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p.amax + 2, mu);
