@@ -11,7 +11,7 @@ using namespace metis;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTransBlocks = 4;  // row blocks per thread in the transposed kernel
+constexpr int kTransBytes = 128;  // code bytes of an output row per thread in the transposed kernel
 
 // Quantize one block held in registers. Returns the scale byte; codes are
 // packed into `packed` (B/2 bytes, element 2j in the low nibble of byte j).
@@ -87,36 +87,53 @@ __global__ void __launch_bounds__(kThreads) quant_rows_kernel(const T *__restric
 }
 
 // out = x^T (cols x rows), blocks along rows. Thread (c, g) quantizes the
-// kTransBlocks consecutive row blocks g*kTransBlocks.. of column c.
+// 256 / B consecutive row blocks g (256 / B).. of column c: 128 bytes of codes
+// of output row c, a whole cache line. They are staged in the thread's own
+// row of LDS and written together at the end, so the line's pieces reach the
+// L2 back to back (stored as each block was done, the L2 wrote many lines
+// back in pieces).
 template <typename T, bool NV>
 __global__ void __launch_bounds__(kThreads) quant_cols_kernel(const T *__restrict__ x, int64_t rows, int64_t cols,
                                                               int64_t ldx, uint8_t *__restrict__ codes,
                                                               uint8_t *__restrict__ scales, const uint32_t *amax_bits,
                                                               float *tensor_scale) {
   constexpr int B = NV ? 16 : 32;
-  const int64_t c = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+  constexpr int TB = kTransBytes * 2 / B;  // row blocks per thread
+  constexpr int W = B / 8;                  // code words per block
+  __shared__ uint32_t cst[kThreads][TB * W + 1];  // odd row stride: no bank conflicts
+  __shared__ uint8_t sst[kThreads][TB];
+  const int t = threadIdx.x;
+  const int64_t c = blockIdx.x * (int64_t)kThreads + t;
   const int64_t g = blockIdx.y;
   float s_t = 1.0f;
   if (NV) {
     s_t = nv_tensor_scale(__uint_as_float(*amax_bits));
     if (c == 0 && g == 0) *tensor_scale = s_t;
   }
-  if (c >= cols) return;
-  const int64_t nblk = rows / B;
+  if (c >= cols) return;  // each thread touches only its own LDS rows: no barrier follows
+  const int64_t nblk = rows / B, blk0 = g * TB;
+  const int nb = (int)min<int64_t>(TB, nblk - blk0);
 #pragma unroll 1
-  for (int j = 0; j < kTransBlocks; ++j) {
-    const int64_t blk = g * kTransBlocks + j;
-    if (blk >= nblk) break;
+  for (int j = 0; j < nb; ++j) {
+    const int64_t blk = blk0 + j;
     float v[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) v[i] = load_f32(x + (blk * B + i) * ldx + c);
-    uint32_t packed[B / 8];
+    uint32_t packed[W];
     const uint32_t sb = quant_block<B, NV>(v, s_t, packed);
-    uint32_t *dst = (uint32_t *)(codes + c * (rows / 2) + blk * (B / 2));
 #pragma unroll
-    for (int w = 0; w < B / 8; ++w) dst[w] = packed[w];
-    scales[c * nblk + blk] = (uint8_t)sb;
+    for (int w = 0; w < W; ++w) cst[t][j * W + w] = packed[w];
+    sst[t][j] = (uint8_t)sb;
   }
+  uint32_t *dst = (uint32_t *)(codes + c * (rows / 2) + blk0 * (B / 2));  // 16-byte aligned (rows % 32 == 0)
+  if (nb == TB) {
+#pragma unroll
+    for (int q = 0; q < TB * W / 4; ++q)
+      ((uint4 *)dst)[q] = uint4{cst[t][4 * q], cst[t][4 * q + 1], cst[t][4 * q + 2], cst[t][4 * q + 3]};
+  } else {
+    for (int w = 0; w < nb * W; ++w) dst[w] = cst[t][w];
+  }
+  for (int j = 0; j < nb; ++j) scales[c * nblk + blk0 + j] = sst[t][j];
 }
 
 template <bool NV>
@@ -168,7 +185,7 @@ metis_status_t launch_quant(const T *x, int64_t rows, int64_t cols, int64_t ldx,
     quant_rows_kernel<T, NV><<<(unsigned)cdiv(nblocks, kThreads), kThreads, 0, stream>>>(
         x, rows, cols, ldx, out->codes, out->scales, amax_ws, out->tensor_scale);
   } else {
-    dim3 grid((unsigned)cdiv(cols, kThreads), (unsigned)cdiv(rows / B, kTransBlocks));
+    dim3 grid((unsigned)cdiv(cols, kThreads), (unsigned)cdiv(rows / B, kTransBytes * 2 / B));
     quant_cols_kernel<T, NV><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, out->codes, out->scales, amax_ws,
                                                             out->tensor_scale);
   }
