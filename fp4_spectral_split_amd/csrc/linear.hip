@@ -260,18 +260,6 @@ __global__ void __launch_bounds__(64)
 }
 
 // =================================================================== panels
-// Decoded value of element i of row c of a k x rows factor matrix. For
-// NVFP4, `ts` (the tensor scale) is applied only when with_ts is set.
-template <bool NV>
-__device__ __forceinline__ float factor_value(const uint8_t *codes, const uint8_t *scales, const float *ts,
-                                              int64_t rows, int c, int64_t i, bool with_ts) {
-  const uint32_t byte = codes[(int64_t)c * (rows / 2) + i / 2];
-  const uint32_t code = (i & 1) ? (byte >> 4) : (byte & 15u);
-  if (!NV) return ldexpf(e2m1_value(code), (int)scales[(int64_t)c * (rows / 32) + i / 32] - 127);
-  const float v = e2m1_value(code) * e4m3_value(scales[(int64_t)c * (rows / 16) + i / 16]);
-  return with_ts ? v * ts[0] : v;
-}
-
 // cross = sum of the ks split-K slabs of Fa^T Fb (fixed order).
 __global__ void cross_reduce_kernel(const float *__restrict__ cpart, int ks, int count, float *__restrict__ cross) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -785,7 +773,8 @@ __device__ __forceinline__ void store_acc_mx4(const floatx16 (&acc)[MXW][MXW], i
 // per row, the same swizzle), consumed by bf16 32x32x16 MFMAs, so its loads
 // overlap the end of the main product instead of following it.
 constexpr int kDmaStages = 4;
-constexpr unsigned kMxMaxGrid = 1u << 30;  // workgroups of the persistent MXFP4 kernel (a multiple of 8)
+constexpr unsigned kMxMaxGrid = 1u << 30;  // cap on the MXFP4 kernel's workgroups: above any tile count, so each
+                                           // takes one tile (persistent grids of 224-256 measured slower)
 constexpr int DMA_CODE_BYTES = BM * 64;            // one operand's codes per stage
 constexpr int DMA_STAGE = 2 * DMA_CODE_BYTES;      // A then B
 constexpr int DMA_SCALE_GROUP = 2 * BM * 16;       // A then B scales of four stages
