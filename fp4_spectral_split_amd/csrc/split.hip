@@ -27,6 +27,7 @@
 // Every reduction runs in a fixed order (no atomics except the order-free
 // integer max of NVFP4 tensor scales), so results are bitwise reproducible.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -1956,10 +1957,12 @@ constexpr int kXcds = 8;
 // MEAN: the mean-residual split, L[r][c] = mu[c] (fp32, passed as `mu`)
 // instead of the MFMA product, so R = A - mu is one fp32 subtraction.
 constexpr int kResGroup = 8;  // workgroups per block of 2 x 4 tiles
-template <typename T, bool NV, bool AMAX_ONLY, bool MEAN = false>
+// KP: the factor rank padded to 32 (32, 64 or 96), fixed at compile time so
+// every panel load and MFMA step is used and the loop bounds are static.
+template <typename T, bool NV, bool AMAX_ONLY, bool MEAN, int KP>
 __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 registers
     residual_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda, const unsigned short *__restrict__ uhl,
-                    const unsigned short *__restrict__ whl, int kp, uint8_t *__restrict__ rcodes,
+                    const unsigned short *__restrict__ whl, uint8_t *__restrict__ rcodes,
                     uint8_t *__restrict__ rscales, float *__restrict__ rts, uint8_t *__restrict__ tcodes,
                     uint8_t *__restrict__ tscales, float *__restrict__ tts, uint32_t *__restrict__ amax,
                     const float *__restrict__ mu = nullptr) {
@@ -1983,9 +1986,11 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
   constexpr int NJ = kRT * RPB / kThreads;     // row blocks per thread
   constexpr int VEC = B * (int)sizeof(T) / 16;  // 16-byte pieces per block
   static_assert(NJ * kThreads == kRT * RPB, "row blocks must divide over the threads");
-  constexpr int KPM = 96;  // largest kp (k <= 96)
+  static_assert(KP == 32 || KP == 64 || KP == 96, "factor rank padded to 32, at most 96");
+  constexpr int kp = KP;
   // 16-byte pieces of the W panel (hi, lo) per thread; none in the mean split
-  constexpr int PW = MEAN ? 0 : 2 * kRC * (KPM / 8) / kThreads;
+  constexpr int PW = MEAN ? 0 : 2 * kRC * (kp / 8) / kThreads;
+  static_assert(MEAN || PW * kThreads == 2 * kRC * (kp / 8), "the W panel divides over the threads");
   // what a tile needs from HBM apart from U: its A blocks and its W panel
   struct Pre {
     uint4 a[NJ][VEC];
@@ -1994,20 +1999,22 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
   auto tile_rt = [&](int p) { return 2 * (p / cblocks) + parity; };
   auto tile_ct = [&](int p) { return 4 * (p % cblocks) + cofs; };
   // Loads of this workgroup's tile of block p into pre: the panel first, then
-  // A. Panel pieces past kp and rows or columns past the matrix (a skipped
-  // tile's too) are loaded clamped, never read.
+  // A. Rows or columns past the matrix (a skipped tile's too) are loaded
+  // clamped, never stored.
   auto load_pre = [&](int p, Pre &pre) {
     const int64_t row0 = (int64_t)tile_rt(p) * kRT, col0 = (int64_t)tile_ct(p) * kRC;
     if constexpr (!MEAN) {
-      const int nw = 2 * kRC * (kp / 8);
       const int64_t wn = n * kp;
 #pragma unroll
       for (int u = 0; u < PW; ++u) {
-        const int idx = min(t + u * kThreads, nw - 1);
+        const int idx = t + u * kThreads;
         const int h = idx / (kRC * (kp / 8)), rem = idx % (kRC * (kp / 8));
         const int c = rem / (kp / 8), qq = rem % (kp / 8);
         pre.w[u] = *(const uint4 *)(whl + h * wn + min(col0 + c, n - 1) * kp + qq * 8);
       }
+      // panel, then A, everywhere (the first tile's loads too): the waits at
+      // the loop head assume one order
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) {
@@ -2024,7 +2031,7 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
     if (rts) *rts = s_t;
     if (tts) *tts = s_t;
   }
-  ushortx8 uh[KPM / 32][2], ul[KPM / 32][2];
+  ushortx8 uh[kp / 32][2], ul[kp / 32][2];
   int cur_rt = -1;
   float mx = 0.0f;
   // One tile: `cur` holds its loads (issued one tile earlier), `nxt`
@@ -2051,30 +2058,33 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
       // waves and staged in LDS, in the space the R tile takes later (row
       // stride kp + 8 bf16 keeps the fragment reads conflict free).
       unsigned short *wst = (unsigned short *)&lt[0][0];  // [2][kRC][kp + 8]
-      static_assert(2 * kRC * (96 + 8) * 2 <= kRT * (kRC + 4) * 4, "the W panel fits the tile's LDS");
+      static_assert(2 * kRC * (kp + 8) * 2 <= kRT * (kRC + 4) * 4, "the W panel fits the tile's LDS");
       const int wstride = kp + 8;
       const int64_t um = m * kp;
       if (rt != cur_rt) {
         cur_rt = rt;
 #pragma unroll
-        for (int ks = 0; ks < KPM / 32; ++ks)
+        for (int ks = 0; ks < kp / 32; ++ks)
 #pragma unroll
           for (int rs = 0; rs < 2; ++rs) {
-            // rows past m and k past kp are loaded clamped: their products
-            // land in rows of L that are never read or are skipped
+            // rows past m are loaded clamped: their products land in rows of
+            // L that are never stored
             const int64_t row = min(row0 + wave * 32 + rs * 16 + r16, m - 1);
-            const unsigned short *pu = uhl + row * kp + min(ks * 32, kp - 32) + g * 8;
+            const unsigned short *pu = uhl + row * kp + ks * 32 + g * 8;
             uh[ks][rs] = *(const ushortx8 *)pu;
             ul[ks][rs] = *(const ushortx8 *)(pu + um);
           }
+        // wait for U here, in the (rare) reload: the loads were issued after
+        // the previous tile's stores, so waiting for them later would make
+        // every tile wait for those stores
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
       }
       load_pre(p_n, nxt);
+      // every load of the next tile is issued before this tile's data is
+      // waited for, so those waits never reach back to the previous stores
+      __builtin_amdgcn_sched_barrier(0);
       // piece idx of the panel goes to LDS row idx / P, slot idx % P
-      // (P = kp / 8); the pieces past the panel (kp < 96) land in unused rows
-      // below it, byte offset 16 (idx + idx / P) < 16 * 5 / 4 * PW * 256,
-      // inside the tile, so the stores need no branch (a branch would pull
-      // each load into it)
-      static_assert(16 * (PW * kThreads + PW * kThreads / 4) <= (int)sizeof(lt), "spare panel stores stay in the tile");
+      // (P = kp / 8)
 #pragma unroll
       for (int u = 0; u < PW; ++u) {
         const int idx = t + u * kThreads;
@@ -2088,8 +2098,7 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
 #pragma unroll
         for (int b = 0; b < NCS; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KPM / 32; ++ks) {
-        if (ks * 32 >= kp) break;
+      for (int ks = 0; ks < kp / 32; ++ks) {
 #pragma unroll
         for (int cs = 0; cs < NCS; ++cs) {
           const int c = cs * 16 + r16;
@@ -2112,6 +2121,15 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
           for (int qq = 0; qq < 4; ++qq) lt[wave * 32 + rs * 16 + g * 4 + qq][cs * 16 + r16] = acc[rs][cs][qq];
     }
     METIS_LDS_BARRIER();
+    // the A registers pass through an empty asm here, so their conversion
+    // to fp32 is not hoisted into the tile that issued the loads (where it
+    // would wait for them)
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb)
+#pragma unroll
+      for (int qq = 0; qq < VEC; ++qq)
+        __asm__ volatile("" : "+v"(cur.a[jb][qq].x), "+v"(cur.a[jb][qq].y), "+v"(cur.a[jb][qq].z),
+                         "+v"(cur.a[jb][qq].w));
     // ---- row blocks (along n): R = A - L, kept in LDS for the column pass
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) {
@@ -2120,12 +2138,16 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
       float v[B];
       const bool ok = row < m && col < n;
       const T *pa = (const T *)&cur.a[jb][0];
+      // computed for every block (a block past the edge holds clamped A and
+      // never reaches an in-range block of either orientation, as m and n are
+      // multiples of B); `ok` only masks the tensor max and the stores, so no
+      // branch holds a use of the loaded registers and their waits stay counted
 #pragma unroll
-      for (int i = 0; i < B; ++i) v[i] = ok ? load_f32(pa + i) - lt[rr][cb * B + i] : 0.0f;
+      for (int i = 0; i < B; ++i) v[i] = load_f32(pa + i) - lt[rr][cb * B + i];
 #pragma unroll
       for (int i = 0; i < B; ++i) {
         lt[rr][cb * B + i] = v[i];
-        mx = fmaxf(mx, fabsf(v[i]));
+        mx = fmaxf(mx, ok ? fabsf(v[i]) : 0.0f);
       }
       if (!AMAX_ONLY && ok && rcodes)
         quant_store<B, NV>(v, s_t, rcodes + row * (n / 2) + col / 2, rscales + row * (n / B) + col / B);
@@ -2153,11 +2175,14 @@ __global__ void __launch_bounds__(kThreads, 2)  // two waves per SIMD: 256 regis
   };
   Pre pre0, pre1;
   load_pre(p0, pre0);
-  for (int p = p0; p < p1; p += 2) {
+  // pairs of tiles, then an odd one: no exit between the two tiles of a
+  // pair, which would leave the waits at the loop head uncounted
+  int p = p0;
+  for (; p + 1 < p1; p += 2) {
     tile(p, pre0, pre1);
-    if (p + 1 >= p1) break;
     tile(p + 1, pre1, pre0);
   }
+  if (p < p1) tile(p, pre0, pre1);
   if (AMAX_ONLY) {
     mx = wave_max(mx);
     if (lane == 0) atomicMax(amax, __float_as_uint(mx));
@@ -2297,17 +2322,25 @@ metis_status_t run_factors_and_residual(const SplitPlan &p, const T *A, int64_t 
   // XCD (two resident workgroups per CU; registers bound it)
   const int64_t nblk = (cdiv(m, kRT) + 1) / 2 * cdiv(cdiv(n, kRC), 4);
   const unsigned rgrid = (unsigned)(kResGroup * kXcds * std::min<int64_t>(8, cdiv(nblk, kXcds)));
-  if (nv) {
-    residual_kernel<T, true, true, MEAN><<<rgrid, kThreads, 0, st>>>(
-        A, m, n, lda, p.uhl, p.whl, kp, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p.amax + 2, mu);
-    residual_kernel<T, true, false, MEAN><<<rgrid, kThreads, 0, st>>>(
-        A, m, n, lda, p.uhl, p.whl, kp, out->R_q.codes, out->R_q.scales, out->R_q.tensor_scale, out->Rt_q.codes,
-        out->Rt_q.scales, out->Rt_q.tensor_scale, p.amax + 2, mu);
-  } else {
-    residual_kernel<T, false, false, MEAN><<<rgrid, kThreads, 0, st>>>(
-        A, m, n, lda, p.uhl, p.whl, kp, out->R_q.codes, out->R_q.scales, nullptr, out->Rt_q.codes, out->Rt_q.scales,
-        nullptr, nullptr, mu);
-  }
+  auto launch = [&](auto kpc) {
+    constexpr int KP = decltype(kpc)::value;
+    if (nv) {
+      residual_kernel<T, true, true, MEAN, KP><<<rgrid, kThreads, 0, st>>>(
+          A, m, n, lda, p.uhl, p.whl, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p.amax + 2, mu);
+      residual_kernel<T, true, false, MEAN, KP><<<rgrid, kThreads, 0, st>>>(
+          A, m, n, lda, p.uhl, p.whl, out->R_q.codes, out->R_q.scales, out->R_q.tensor_scale, out->Rt_q.codes,
+          out->Rt_q.scales, out->Rt_q.tensor_scale, p.amax + 2, mu);
+    } else {
+      residual_kernel<T, false, false, MEAN, KP><<<rgrid, kThreads, 0, st>>>(
+          A, m, n, lda, p.uhl, p.whl, out->R_q.codes, out->R_q.scales, nullptr, out->Rt_q.codes, out->Rt_q.scales,
+          nullptr, nullptr, mu);
+    }
+  };
+  // the mean split reads no factor panels: one instance serves it
+  if (MEAN || kp == 32) launch(std::integral_constant<int, 32>{});
+  else if (kp == 64) launch(std::integral_constant<int, 64>{});
+  else if (kp == 96) launch(std::integral_constant<int, 96>{});
+  else return METIS_ERR_INVALID;
   METIS_LAUNCH_CHECK();
   return METIS_OK;
 }
