@@ -215,31 +215,43 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
 #pragma unroll
     for (int b = 0; b < kLpMax / 16; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 pa[RS][AV], ca[RS][AV], po[NH][OPR];
+  // Every load takes a clamped, valid address and none sits in a branch, so
+  // the waits for a step's data stay counted while the next step's loads
+  // are in flight: rows past m only feed rows of ysk that are not stored;
+  // A's columns past the chunk are zeroed when the step is taken (n and the
+  // chunk ends are multiples of 32, so a lane's 32 columns are all in or all
+  // out), which also cancels the clamped Omega columns they meet; Omega^T
+  // rows past lt go to LDS rows that no MFMA reads.
+  static_assert(OPR * kThreads == kLpMax * (KS / 8), "Omega^T pieces fill the LDS rows exactly");
+  // one step's loads, returned by value (vector values stay in registers)
+  struct Step {
+    intx4 a[RS][AV];
+    intx4 o[NH][OPR];
+  };
   auto load = [&](int64_t c0) {
+    Step st;
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
-      const int64_t row = row0 + rs * 16 + r16;
-      const int64_t cc = c0 + g * 32;
-      const bool ok = row < m && cc < c_end;
-      const uint4 *src = (const uint4 *)(A + row * lda + cc);
+      const int64_t row = min(row0 + rs * 16 + r16, m - 1);
+      const int64_t cc = min(c0 + g * 32, n - 32);
+      const intx4 *src = (const intx4 *)(A + row * lda + cc);
 #pragma unroll
-      for (int j = 0; j < AV; ++j) pa[rs][j] = ok ? src[j] : uint4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < AV; ++j) st.a[rs][j] = src[j];
     }
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int p = 0; p < OPR; ++p) {
         const int idx = t + kThreads * p;
-        const int rr = idx / (KS / 8), q = idx % (KS / 8);
-        const int64_t cc = c0 + q * 8;
-        po[h][p] = (idx < lt * (KS / 8) && cc < c_end)
-                       ? *(const uint4 *)(omt + ((int64_t)h * lp + l0 + rr) * n + cc)
-                       : uint4{0u, 0u, 0u, 0u};
+        const int rr = min(idx / (KS / 8), lt - 1), q = idx % (KS / 8);
+        const int64_t cc = min(c0 + q * 8, n - 8);
+        st.o[h][p] = *(const intx4 *)(omt + ((int64_t)h * lp + l0 + rr) * n + cc);
       }
+    return st;
   };
 
-  if (c_beg < c_end) load(c_beg);
+  intx4 ca[RS][AV];
+  Step nx = load(c_beg < c_end ? c_beg : 0);
   for (int64_t c0 = c_beg; c0 < c_end; c0 += KS) {
     __syncthreads();
 #pragma unroll
@@ -247,13 +259,16 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
 #pragma unroll
       for (int p = 0; p < OPR; ++p) {
         const int idx = t + kThreads * p;
-        if (idx < lt * (KS / 8)) *(uint4 *)&lds[h][idx / (KS / 8)][(idx % (KS / 8)) * 8] = po[h][p];
+        *(intx4 *)&lds[h][idx / (KS / 8)][(idx % (KS / 8)) * 8] = nx.o[h][p];
       }
+    const int a_in = c0 + g * 32 < c_end ? -1 : 0;  // word mask
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
-      for (int j = 0; j < AV; ++j) ca[rs][j] = pa[rs][j];
-    if (c0 + KS < c_end) load(c0 + KS);  // in flight while this step is multiplied
+      for (int j = 0; j < AV; ++j) ca[rs][j] = nx.a[rs][j] & a_in;
+    // the next step's loads (the last step reloads itself, from cache) are
+    // in flight while this step is multiplied
+    nx = load(c0 + KS < c_end ? c0 + KS : c0);
     __syncthreads();
     ushortx8 a[RS][4][NT];
 #pragma unroll
