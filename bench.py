@@ -188,6 +188,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain copy of MIB MiB ahead of the steps (counter calibration)")
+    ap.add_argument("--two-call-splits", action="store_true",
+                    help="enqueue the splits as metis_split_begin / _finish, the down-projection first phases after "
+                         "the up-projection ones (measured slower than one call per split)")
     ap.add_argument("--profile-splits", type=int, default=0, metavar="REPS",
                     help="instead of the steps, run each split and the quantizer REPS times alone (for profiles)")
     args = ap.parse_args()
@@ -246,7 +249,57 @@ def main():
     split_ev = [{n: (ev(), ev()) for n in names} for _ in range(args.steps)]
     main_ev = [{o: (ev(), ev()) for o in outs} for _ in range(args.steps)]
 
+    # two-call splits (opt-in): the full-GPU first phase of the down-projection
+    # splits runs while the up-projection splits are in their one-workgroup
+    # small SVD; the down-projection first phases wait for the up ones
+    two = {n: M.SplitInTwo(A[n], t[n].l, t[n].k, "mxfp4", omega=Om[n], out=recs[n])
+           for n in names} if args.two_call_splits else {}
+    lane_of = {n: li for li, kind, n in order if kind == "split"}
+    up = [n for n in names if n.endswith("_up")]
+    begun = {n: torch.cuda.Event() for n in names}
+
+    def step_two(i):
+        rec = i is not None
+        for s in lanes:
+            for e in lane_end:
+                s.wait_event(e)
+        seq = [("begin", n) for n in up] + [("begin", n) for n in names if n not in up]
+        seq += [("finish", n) for n in up] + [("gemm", g) for _, k, g in order if k == "gemm" and g.endswith("_up")]
+        seq += [("finish", n) for n in names if n not in up]
+        seq += [("gemm", g) for _, k, g in order if k == "gemm" and not g.endswith("_up")]
+        for kind, n in seq:
+            li = lane_of[n] if kind != "gemm" else next(l for l, k, g in order if k == "gemm" and g == n)
+            s = lanes[li]
+            with torch.cuda.stream(s):
+                if kind == "begin":
+                    if n not in up:
+                        for u in up:
+                            s.wait_event(begun[u])
+                    if rec:
+                        split_ev[i][n][0].record(s)
+                    two[n].begin()
+                    begun[n].record(s)
+                elif kind == "finish":
+                    two[n].finish()
+                    if rec:
+                        split_ev[i][n][1].record(s)
+                    done[n].record(s)
+                else:
+                    _, a, ao, b, bo = gemm_of[n]
+                    s.wait_event(done[a])
+                    s.wait_event(done[b])
+                    gobj[n].prepare()
+                    if rec:
+                        main_ev[i][n][0].record(s)
+                    gobj[n].main(outs[n])
+                    if rec:
+                        main_ev[i][n][1].record(s)
+        for s, e in zip(lanes, lane_end):
+            e.record(s)
+
     def step(i):
+        if args.two_call_splits:
+            return step_two(i)
         rec = i is not None
         for s in lanes:  # the previous step's GEMMs are done with every record
             for e in lane_end:

@@ -2211,11 +2211,14 @@ metis_status_t run_factors_and_residual(const SplitPlan &p, const T *A, int64_t 
 
 template <typename T>
 metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void *omega, metis_split_t *out,
-                         int32_t *info, hipStream_t st) {
+                         int32_t *info, hipStream_t st, int phase = 3) {
   const int64_t m = p.m, n = p.n;
   const int l = p.l, lp = p.lp, k = p.k, kp = p.kp;
   const bool nv = p.fmt == METIS_NVFP4;
   const unsigned lz = (unsigned)cdiv(lp, kLpMax);  // sketch-column tiles
+  // phase 1: sketch, orthonormal basis, projection and the Gram of B (full
+  // GPU); phase 2: the small SVD (one workgroup), the factors and the residual
+  if (phase & 1) {
   // ---- pass 1: sketch
   const float *ysrc;
   int yparts;
@@ -2270,12 +2273,6 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     sum_parts4_kernel<<<(unsigned)cdiv(n * l, 1024), 256, 0, st>>>(p.btp, p.pk, n * l, n * l, p.bt);
     gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.bt, 1, 0, n, l, lp, nullptr, nullptr, nullptr, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
-    // ---- small SVD and factors
-    tridiag_eig_kernel<<<1, kEigThreads, 0, st>>>(p.gram, l, lp, k, p.evec, p.sig_inv, out->S);
-    assemble_u_kernel<<<p.am_parts, kThreads, 0, st>>>(p.q, m, l, lp, k, p.evec, p.am_rows, out->U, p.am_val,
-                                                       p.am_idx);
-    assemble_v_kernel<<<(unsigned)cdiv(n, asm_chunk_rows(k)), kThreads, 0, st>>>(p.bt, n, l, lp, k, p.evec,
-                                                                                 p.sig_inv, out->V);
   } else {
     // ---- the same steps with the l x l matrices in global scratch
     const float *y = ysrc;
@@ -2301,6 +2298,21 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     }
     gram_tile_kernel<<<dim3(p.gb_parts, nt, nt), kThreads, 0, st>>>(bt, n, l, lp, p.gb_rows, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
+  }
+  }
+  if (!(phase & 2)) {
+    METIS_LAUNCH_CHECK();
+    return METIS_OK;
+  }
+  // ---- small SVD of B (from its Gram, in p.gram) and the factors
+  if (!p.wide) {
+    tridiag_eig_kernel<<<1, kEigThreads, 0, st>>>(p.gram, l, lp, k, p.evec, p.sig_inv, out->S);
+    assemble_u_kernel<<<p.am_parts, kThreads, 0, st>>>(p.q, m, l, lp, k, p.evec, p.am_rows, out->U, p.am_val,
+                                                       p.am_idx);
+    assemble_v_kernel<<<(unsigned)cdiv(n, asm_chunk_rows(k)), kThreads, 0, st>>>(p.bt, n, l, lp, k, p.evec,
+                                                                                 p.sig_inv, out->V);
+  } else {
+    const float *bt = p.pk > 1 ? p.bt : p.btp;
     jacobi_kernel<true><<<1, kJacThreads, 0, st>>>(p.gram, l, lp, k, 40, p.evec, p.sig_inv, out->S, p.wg, p.wv);
     assemble_wide_kernel<<<(unsigned)cdiv(m * k, 256), 256, 0, st>>>(p.q, m, l, lp, k, p.evec, nullptr, out->U);
     argmax_kernel<<<p.am_parts, 128, 0, st>>>(out->U, m, k, p.am_rows, p.am_val, p.am_idx);
@@ -2470,10 +2482,12 @@ extern "C" size_t metis_split_workspace_bytes(int64_t m, int64_t n, int32_t l, i
   return metis_split_power_workspace_bytes(m, n, l, k, kind, 0, fmt);
 }
 
-extern "C" metis_status_t metis_split_power(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
-                                            const void *omega, metis_omega_t kind, int32_t l, int32_t k, int32_t q,
-                                            metis_fmt_t fmt, metis_split_t *out, int32_t *info, void *ws,
-                                            size_t ws_bytes, hipStream_t stream) {
+namespace {
+// Argument checks and the plan shared by the one-call split and its two
+// phases; phase 1 and 2 as in run_split, 3 for both.
+metis_status_t split_entry(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda, const void *omega,
+                           metis_omega_t kind, int32_t l, int32_t k, int32_t q, metis_fmt_t fmt, metis_split_t *out,
+                           int32_t *info, void *ws, size_t ws_bytes, hipStream_t stream, int phase) {
   if (q < 0) return METIS_ERR_INVALID;
   if (q > kMaxPowerIterations || (q > 0 && l > kLpMax)) return METIS_ERR_UNSUPPORTED;
   if (!A || !omega || !out) return METIS_ERR_INVALID;
@@ -2503,8 +2517,30 @@ extern "C" metis_status_t metis_split_power(const void *A, metis_dtype_t dt, int
   out->Vt_q.rows = k; out->Vt_q.cols = n;
   out->R_q.rows = m; out->R_q.cols = n;
   out->Rt_q.rows = n; out->Rt_q.cols = m;
-  if (dt == METIS_F32) return run_split<float>(p, (const float *)A, lda, omega, out, info, stream);
-  return run_split<unsigned short>(p, (const unsigned short *)A, lda, omega, out, info, stream);
+  if (dt == METIS_F32) return run_split<float>(p, (const float *)A, lda, omega, out, info, stream, phase);
+  return run_split<unsigned short>(p, (const unsigned short *)A, lda, omega, out, info, stream, phase);
+}
+}  // namespace
+
+extern "C" metis_status_t metis_split_power(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                            const void *omega, metis_omega_t kind, int32_t l, int32_t k, int32_t q,
+                                            metis_fmt_t fmt, metis_split_t *out, int32_t *info, void *ws,
+                                            size_t ws_bytes, hipStream_t stream) {
+  return split_entry(A, dt, m, n, lda, omega, kind, l, k, q, fmt, out, info, ws, ws_bytes, stream, 3);
+}
+
+extern "C" metis_status_t metis_split_begin(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                            const void *omega, metis_omega_t kind, int32_t l, int32_t k,
+                                            metis_fmt_t fmt, metis_split_t *out, int32_t *info, void *ws,
+                                            size_t ws_bytes, hipStream_t stream) {
+  return split_entry(A, dt, m, n, lda, omega, kind, l, k, 0, fmt, out, info, ws, ws_bytes, stream, 1);
+}
+
+extern "C" metis_status_t metis_split_finish(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                             const void *omega, metis_omega_t kind, int32_t l, int32_t k,
+                                             metis_fmt_t fmt, metis_split_t *out, int32_t *info, void *ws,
+                                             size_t ws_bytes, hipStream_t stream) {
+  return split_entry(A, dt, m, n, lda, omega, kind, l, k, 0, fmt, out, info, ws, ws_bytes, stream, 2);
 }
 
 extern "C" metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,

@@ -182,6 +182,26 @@ metis_status_t metis_split_power(const void *A, metis_dtype_t dt, int64_t m, int
                                  metis_fmt_t fmt, metis_split_t *out, int32_t *info, void *ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* metis_split in two calls, for callers that interleave several splits on
+ * separate streams (the same randomized range finder and small SVD as
+ * metis_split, Halko-Martinsson-Tropp 2011, Alg. 4.1 and 5.1):
+ *  metis_split_begin: the sketch, its orthonormal basis Q, B^T = A^T Q and
+ *    the Gram of B: every kernel spans the whole GPU;
+ *  metis_split_finish: the small SVD of B (one workgroup), U, S, V, their
+ *    quantization and the residual pass.
+ * Call both with identical arguments, the same workspace (its contents carry
+ * Q, B^T and the Gram from the first call to the second) and in stream order
+ * (finish after begin, on the same stream or one that waits for it); no
+ * other use of the workspace in between. finish reads A again; begin writes
+ * info and nothing of out. The result equals metis_split's bit for bit.
+ * Errors as for metis_split; ws: metis_split_workspace_bytes() bytes. */
+metis_status_t metis_split_begin(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                 const void *omega, metis_omega_t kind, int32_t l, int32_t k, metis_fmt_t fmt,
+                                 metis_split_t *out, int32_t *info, void *ws, size_t ws_bytes, hipStream_t stream);
+metis_status_t metis_split_finish(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
+                                  const void *omega, metis_omega_t kind, int32_t l, int32_t k, metis_fmt_t fmt,
+                                  metis_split_t *out, int32_t *info, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Mean-residual split (Averis, "Averaging-Induced Residual Splitting", as
  * retold on the zhu318.com page, method paragraphs): the mean over all rows,
