@@ -114,6 +114,27 @@ def e8m0_decode(byte):
     return np.ldexp(1.0, np.asarray(byte, dtype=np.int64) - 127)
 
 
+def mx_shared_exponent(amax):
+    """Shared exponent of MXFP4 blocks with maximum magnitude amax (>= 0):
+    floor(log2 amax) minus the largest E2M1 exponent (2), clamped to
+    [-127, 127]; an all-zero block gets -127 (scale byte 0)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    shared = np.full(amax.shape, -127, dtype=np.int64)
+    nz = amax > 0
+    shared[nz] = np.clip(floor_log2(amax[nz]) - 2, -127, 127)
+    return shared
+
+
+def mx_encode_at(x, shared):
+    """E2M1 codes (unpacked, (rows, cols)) of a 2-D array whose blocks of 32
+    along the last axis carry the given shared exponents (rows, cols/32)."""
+    x = _as_f64(x)
+    rows, cols = x.shape
+    xb = x.reshape(rows, cols // MX_BLOCK, MX_BLOCK)
+    scaled = np.ldexp(xb, -np.asarray(shared, dtype=np.int64)[..., None])  # exact: power-of-two scaling
+    return e2m1_encode(scaled).reshape(rows, cols)
+
+
 def mx_quantize(x):
     """MXFP4: blocks of 32 along the last axis of a 2-D array.
 
@@ -123,16 +144,9 @@ def mx_quantize(x):
     rows, cols = x.shape
     if cols % MX_BLOCK:
         raise ValueError("MXFP4 needs the blocked axis to be a multiple of 32")
-    xb = x.reshape(rows, cols // MX_BLOCK, MX_BLOCK)
-    amax = np.max(np.abs(xb), axis=-1)
-    shared = np.zeros(amax.shape, dtype=np.int64)
-    nz = amax > 0
-    # shared exponent: floor(log2 amax) minus the largest E2M1 exponent (2)
-    shared[nz] = np.clip(floor_log2(amax[nz]) - 2, -127, 127)
-    shared[~nz] = -127  # all-zero block: scale byte 0, every code +-0
-    scaled = np.ldexp(xb, -shared[..., None])  # exact: power-of-two scaling
-    codes = e2m1_encode(scaled).reshape(rows, cols)
-    return pack_nibbles(codes), (shared + 127).astype(np.uint8)
+    amax = np.max(np.abs(x.reshape(rows, cols // MX_BLOCK, MX_BLOCK)), axis=-1)
+    shared = mx_shared_exponent(amax)
+    return pack_nibbles(mx_encode_at(x, shared)), (shared + 127).astype(np.uint8)
 
 
 def mx_dequantize(codes, scales):
@@ -177,16 +191,44 @@ def e4m3_decode(byte):
 
 
 # -------------------------------------------------------------------- NVFP4
-def nv_tensor_scale(x):
-    """Per-tensor fp32 scale s_t = max(f32(amax / 2688), 2^-126); 1 for a zero tensor."""
-    x = _as_f64(x)
-    a_t = float(np.max(np.abs(x))) if x.size else 0.0
+def nv_tensor_scale_of_max(a_t):
+    """Per-tensor fp32 scale from the tensor's max magnitude a_t:
+    max(f32(a_t / 2688), 2^-126), and 1 for a zero tensor."""
+    a_t = float(a_t)
     if a_t == 0.0:
         return 1.0
     return float(max(f32(a_t / NV_TENSOR_DIVISOR), FP32_MIN_NORMAL))
 
 
-def nv_quantize(x):
+def nv_tensor_scale(x):
+    """Per-tensor fp32 scale s_t of an array (see nv_tensor_scale_of_max)."""
+    x = _as_f64(x)
+    return nv_tensor_scale_of_max(float(np.max(np.abs(x))) if x.size else 0.0)
+
+
+def nv_block_scale(amax, s_t):
+    """E4M3 scale bytes of NVFP4 blocks with maximum magnitude amax, given
+    the tensor scale s_t: d = f32(6 s_t), b = f32(amax / d), e4m3(b)."""
+    d = f32(6.0 * s_t)
+    return e4m3_encode(f32(np.asarray(amax, dtype=np.float64) / d))
+
+
+def nv_encode_at(x, sb, s_t):
+    """E2M1 codes (unpacked, (rows, cols)) of a 2-D fp32-valued array whose
+    blocks of 16 along the last axis carry the E4M3 scale bytes sb (rows,
+    cols/16), with tensor scale s_t: den = f32(value(sb) s_t), then
+    e2m1(f32(x / den)); a block whose scale is 0 gets +-0 codes."""
+    x = _as_f64(x)
+    rows, cols = x.shape
+    xb = x.reshape(rows, cols // NV_BLOCK, NV_BLOCK)
+    sbv = e4m3_decode(sb)
+    den = f32(sbv * s_t)
+    live = sbv > 0
+    q = np.where(live[..., None], f32(xb / np.where(live, den, 1.0)[..., None]), 0.0 * xb)
+    return e2m1_encode(q).reshape(rows, cols)
+
+
+def nv_quantize(x, tensor_scale=None):
     """NVFP4: blocks of 16 along the last axis of a 2-D fp32-valued array.
 
     Returns (codes, scales, s_t): packed codes (rows, cols/2), one E4M3 byte per
@@ -194,25 +236,18 @@ def nv_quantize(x):
     correctly rounded fp32 operation, in this order:
       d = f32(6 * s_t); b = f32(amax_block / d); sb = e4m3(b);
       den = f32(value(sb) * s_t); code_i = e2m1(f32(x_i / den)).
-    A block whose scale rounds to 0 gets +-0 codes."""
+    A block whose scale rounds to 0 gets +-0 codes. tensor_scale, if given,
+    replaces s_t = nv_tensor_scale(x) (a scale taken from elsewhere)."""
     x = _as_f64(x)
     if np.any(x != f32(x)):
         raise ValueError("NVFP4 oracle takes fp32-representable inputs")
     rows, cols = x.shape
     if cols % NV_BLOCK:
         raise ValueError("NVFP4 needs the blocked axis to be a multiple of 16")
-    s_t = nv_tensor_scale(x)
-    xb = x.reshape(rows, cols // NV_BLOCK, NV_BLOCK)
-    amax = np.max(np.abs(xb), axis=-1)
-    d = f32(6.0 * s_t)
-    b = f32(amax / d)
-    sb = e4m3_encode(b)
-    sbv = e4m3_decode(sb)
-    den = f32(sbv * s_t)
-    live = sbv > 0
-    q = np.where(live[..., None], f32(xb / np.where(live, den, 1.0)[..., None]), 0.0 * xb)
-    codes = e2m1_encode(q).reshape(rows, cols)
-    return pack_nibbles(codes), sb, np.float32(s_t)
+    s_t = nv_tensor_scale(x) if tensor_scale is None else float(tensor_scale)
+    amax = np.max(np.abs(x.reshape(rows, cols // NV_BLOCK, NV_BLOCK)), axis=-1)
+    sb = nv_block_scale(amax, s_t)
+    return pack_nibbles(nv_encode_at(x, sb, s_t)), sb, np.float32(s_t)
 
 
 def nv_dequantize(codes, scales, s_t):

@@ -173,11 +173,14 @@ def test_e4m3_boundaries_by_hand():
     assert F.e4m3_encode(np.array([448.0]))[0] == 0x7E  # exponent 15, mantissa 6
 
 
-def _nv_by_numpy_float32(x32):
-    """The NVFP4 chain written with numpy float32 scalars (IEEE single ops)."""
+def _nv_by_numpy_float32(x32, s_t=None):
+    """The NVFP4 chain written with numpy float32 scalars (IEEE single ops);
+    s_t given: that tensor scale instead of the array's own."""
     x32 = np.asarray(x32, dtype=np.float32)
     a_t = np.max(np.abs(x32))
-    if a_t == 0:
+    if s_t is not None:
+        s_t = np.float32(s_t)
+    elif a_t == 0:
         s_t = np.float32(1.0)
     else:
         s_t = max(np.float32(a_t) / np.float32(2688.0), np.float32(2.0 ** -126))
@@ -209,6 +212,21 @@ def test_nv_matches_float32_arithmetic(dist):
     codes, sb, s_t = F.nv_quantize(x32.astype(np.float64))
     ref_codes, ref_sb, ref_st = _nv_by_numpy_float32(x32)
     assert np.float32(s_t) == ref_st
+    assert np.array_equal(sb, ref_sb)
+    assert np.array_equal(F.unpack_nibbles(codes), ref_codes)
+
+
+@pytest.mark.parametrize("factor", [0.75, 1.0 + 2.0 ** -20, 3.0])
+def test_nv_with_a_given_tensor_scale_matches_float32_arithmetic(factor):
+    """A tensor scale passed in (not the array's own max / 2688) enters the
+    same fp32 chain; blocks past 6 * 448 times it saturate at scale 448."""
+    g = np.random.Generator(np.random.PCG64(6))
+    x32 = (g.standard_normal((8, 64)) * np.exp(3 * g.standard_normal((8, 64)))).astype(np.float32)
+    own = F.nv_tensor_scale(x32.astype(np.float64))
+    s_t = float(np.float32(own * factor))
+    codes, sb, st = F.nv_quantize(x32.astype(np.float64), tensor_scale=s_t)
+    ref_codes, ref_sb, ref_st = _nv_by_numpy_float32(x32, s_t)
+    assert np.float32(st) == ref_st
     assert np.array_equal(sb, ref_sb)
     assert np.array_equal(F.unpack_nibbles(codes), ref_codes)
 
