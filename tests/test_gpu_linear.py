@@ -43,7 +43,7 @@ SHAPES = {"ragged-k": (288, 320, 416), "fwd-k512": (288, 512, 416), "k512": (512
 
 @pytest.mark.parametrize("shape", list(SHAPES))
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
-@pytest.mark.parametrize("kx,kw,kdy", [(8, 8, 8), (0, 8, 0), (8, 0, 8), (0, 0, 0), (16, 8, 4)])
+@pytest.mark.parametrize("kx,kw,kdy", [(8, 8, 8), (0, 8, 0), (8, 0, 8), (0, 0, 0), (16, 8, 4), (80, 72, 80)])
 def test_linear_fwd_bwd_small(kx, kw, kdy, fmt, shape):
     Mt, K, N = SHAPES[shape]
     X = _small(201, Mt, K, kx, kx + 8, fmt=fmt)
@@ -120,6 +120,13 @@ def _bwd_dw(dY, X):
     """dW through the public bwd entry point (dX skipped)."""
     fake_w = M.SplitRecord(dY.n, X.n, 0, X.fmt)
     return M.spectral_fp4_linear_bwd(dY, X, fake_w, need_dx=False, need_dw=True)[1]
+
+
+def test_linear_full_size_cfg2():
+    """1.1B-class layer: X 4096 x 2048 unsplit with eight x20 outlier
+    channels, W^T 5632 x 2048 split at k = 32 (K = 2048: the asynchronous-load
+    MXFP4 kernel with a one-sided correction)."""
+    _full(2, synth.GEMMS[2])
 
 
 def test_linear_full_size_cfg3():
