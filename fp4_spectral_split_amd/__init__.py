@@ -11,6 +11,7 @@ Calls (same names as the C ABI in include/metis_fp4.h):
   fp4_block_dequant(q)                         -> fp32 tensor
   metis_split(A, l, k, fmt, omega=, columns=)  -> SplitRecord
   spectral_fp4_linear_fwd(X, W)                -> Y = X W^T
+  spectral_fp4_linear_fwd_noalloc(X, W, out)   -> the same, static scratch
   spectral_fp4_linear_bwd(dY, X, W)            -> (dX = dY W, dW = dY^T X)
 """
 import ctypes
@@ -88,6 +89,8 @@ def load():
     L.metis_linear_workspace_bytes.argtypes = [ctypes.POINTER(_Split)] * 3
     L.spectral_fp4_linear_fwd.restype = i32
     L.spectral_fp4_linear_fwd.argtypes = [ctypes.POINTER(_Split), ctypes.POINTER(_Split), vp, i64, vp, sz, vp]
+    L.spectral_fp4_linear_fwd_noalloc.restype = i32
+    L.spectral_fp4_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_Split), ctypes.POINTER(_Split), vp, i64, vp]
     L.spectral_fp4_linear_bwd.restype = i32
     L.spectral_fp4_linear_bwd.argtypes = [ctypes.POINTER(_Split)] * 3 + [vp, i64, vp, i64, vp, sz, vp]
     sp = ctypes.POINTER(_Split)
@@ -105,7 +108,7 @@ EXPORTS = ["metis_status_str", "metis_abi_version", "fp4_block_quant_workspace_b
            "fp4_block_dequant", "metis_split_workspace_bytes", "metis_split", "metis_split_power_workspace_bytes",
            "metis_split_power", "metis_split_begin", "metis_split_finish", "metis_mean_split_workspace_bytes",
            "metis_mean_split", "metis_linear_workspace_bytes",
-           "spectral_fp4_linear_fwd", "spectral_fp4_linear_bwd", "metis_gemm_nt_workspace_bytes",
+           "spectral_fp4_linear_fwd", "spectral_fp4_linear_fwd_noalloc", "spectral_fp4_linear_bwd", "metis_gemm_nt_workspace_bytes",
            "metis_gemm_nt_prepare", "metis_gemm_nt_main"]
 
 
@@ -364,6 +367,19 @@ def spectral_fp4_linear_fwd(X, W, out=None):
     cx, cw = X.c(), W.c()
     _check(L.spectral_fp4_linear_fwd(ctypes.byref(cx), ctypes.byref(cw), _ptr(out), out.stride(0), _ptr(ws), n,
                                      _stream(dev)))
+    return out
+
+
+def spectral_fp4_linear_fwd_noalloc(X, W, out):
+    """Y = X_hat W_hat^T into the caller's fp32 tensor out (M x N), with the
+    workspace taken from the library's static per-GPU scratch: the C call
+    allocates nothing (the binding allocates nothing either). Calls that
+    overlap on one GPU race on that scratch."""
+    L = load()
+    assert out.dtype == torch.float32 and out.is_cuda and out.stride(1) == 1
+    cx, cw = X.c(), W.c()
+    _check(L.spectral_fp4_linear_fwd_noalloc(ctypes.byref(cx), ctypes.byref(cw), _ptr(out), out.stride(0),
+                                             _stream(out.device)))
     return out
 
 

@@ -26,7 +26,8 @@
 //                  E8M0 scales per 32 elements), tensor scales in the epilogue.
 //   skinny_nv_kernel, panel_kernel<true>: the NVFP4 forms of the first two.
 #include <algorithm>
-
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1530,6 +1531,56 @@ extern "C" metis_status_t spectral_fp4_linear_fwd(const metis_split_t *X, const 
   Side a, b;
   if (!make_side(X, false, a) || !make_side(W, false, b)) return METIS_ERR_INVALID;
   return gemm_nt(a, b, Y, ldy, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------- forward without allocation
+// Scratch of spectral_fp4_linear_fwd_noalloc: a device array in the library's
+// code object, so every GPU the library runs on holds its own copy from the
+// code object's load until the process ends. Host code never passes its name
+// to a kernel (on the host it is only a stand-in): the device address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kStaticScratchBytes = METIS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up on the
+// device's first call, then cached).
+metis_status_t scratch_on_current_device(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return METIS_ERR_HIP;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return METIS_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return METIS_OK;
+}
+}  // namespace
+
+extern "C" metis_status_t spectral_fp4_linear_fwd_noalloc(const metis_split_t *X, const metis_split_t *W, float *Y,
+                                                          int64_t ldy, hipStream_t stream) {
+  if (!X || !W || X->n != W->n || X->k < 0 || W->k < 0) return METIS_ERR_INVALID;
+  Side a, b;
+  if (!make_side(X, false, a) || !make_side(W, false, b)) return METIS_ERR_INVALID;
+  const metis_status_t s = check_pair(a, b);
+  if (s != METIS_OK) return s;
+  const size_t need = gemm_bytes(X, false, W, false);
+  if (need > kStaticScratchBytes) return METIS_ERR_TOO_LARGE;
+  void *ws = nullptr;
+  if (a.rows && b.rows && a.T && (a.k || b.k)) {
+    const metis_status_t g = scratch_on_current_device(&ws);
+    if (g != METIS_OK) return g;
+  }
+  return gemm_nt(a, b, Y, ldy, ws, kStaticScratchBytes, stream);
 }
 
 extern "C" metis_status_t spectral_fp4_linear_bwd(const metis_split_t *dY, const metis_split_t *X,

@@ -256,6 +256,7 @@ extern "C" const char *metis_status_str(metis_status_t s) {
     case METIS_ERR_UNSUPPORTED: return "METIS_ERR_UNSUPPORTED";
     case METIS_ERR_WORKSPACE: return "METIS_ERR_WORKSPACE";
     case METIS_ERR_HIP: return "METIS_ERR_HIP";
+    case METIS_ERR_TOO_LARGE: return "METIS_ERR_TOO_LARGE";
   }
   return "METIS_ERR_UNKNOWN";
 }

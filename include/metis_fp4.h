@@ -13,7 +13,9 @@
  * Conventions for every call
  *  - Array pointers are DEVICE pointers owned by the caller. The library never
  *    allocates or frees memory, never synchronizes the device and keeps no
- *    global state: calls are re-entrant and may run on any stream.
+ *    global state: calls are re-entrant and may run on any stream. (The one
+ *    exception, spectral_fp4_linear_fwd_noalloc, uses a static per-GPU
+ *    scratch array instead of a workspace argument.)
  *  - All work is enqueued on `stream` (asynchronous). Outputs are valid once
  *    the stream reaches that point.
  *  - Arguments are validated on the host before any HIP call; a failed check
@@ -41,7 +43,8 @@ typedef enum {
   METIS_ERR_INVALID = 1,     /* bad pointer, shape, leading dimension or missing operand */
   METIS_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement */
   METIS_ERR_WORKSPACE = 3,   /* ws == NULL or ws_bytes below the matching *_workspace_bytes() */
-  METIS_ERR_HIP = 4          /* a HIP launch failed */
+  METIS_ERR_HIP = 4,         /* a HIP launch failed */
+  METIS_ERR_TOO_LARGE = 5    /* the request needs more than a fixed-size static scratch */
 } metis_status_t;
 
 /* FP4 block formats (the pages name MXFP4 and NVFP4: SII post, project
@@ -235,6 +238,28 @@ metis_status_t metis_mean_split(const void *A, metis_dtype_t dt, int64_t m, int6
 size_t metis_linear_workspace_bytes(const metis_split_t *X, const metis_split_t *W, const metis_split_t *dY);
 metis_status_t spectral_fp4_linear_fwd(const metis_split_t *X, const metis_split_t *W, float *Y, int64_t ldy,
                                        void *ws, size_t ws_bytes, hipStream_t stream);
+/* The forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * spectral_fp4_linear_fwd with its workspace taken from a static device array
+ * of METIS_NOALLOC_SCRATCH_BYTES in the library instead of a ws argument. The
+ * call itself allocates nothing; each GPU the library runs on holds its own
+ * copy of the array from the library's load until the process ends. Inputs
+ * and Y are the caller's, as for spectral_fp4_linear_fwd, and the result is
+ * the same bit for bit.
+ *  - Work is enqueued on `stream`, which must belong to the current device.
+ *  - A forward whose metis_linear_workspace_bytes(X, W, NULL) exceeds
+ *    METIS_NOALLOC_SCRATCH_BYTES returns METIS_ERR_TOO_LARGE and enqueues
+ *    nothing (64 MiB covers 8192 tokens x 4096 x 14336 at k = 64).
+ *  - Every call on one GPU shares that GPU's array, and the array keeps the
+ *    last call's contents (nothing in it needs to start at zero). Calls that
+ *    overlap on one GPU (concurrent streams, or host threads without
+ *    ordering) race on it: serialize them.
+ * Other errors as for spectral_fp4_linear_fwd; METIS_ERR_HIP also when the
+ * array's device address cannot be looked up. */
+#define METIS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+metis_status_t spectral_fp4_linear_fwd_noalloc(const metis_split_t *X, const metis_split_t *W, float *Y,
+                                               int64_t ldy, hipStream_t stream);
+
 /* dX or dW may be NULL to skip that product. */
 metis_status_t spectral_fp4_linear_bwd(const metis_split_t *dY, const metis_split_t *X, const metis_split_t *W,
                                        float *dX, int64_t lddx, float *dW, int64_t lddw, void *ws,
