@@ -73,9 +73,6 @@ def load():
     L.metis_split_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
     L.metis_split.restype = i32
     L.metis_split.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, i32, ctypes.POINTER(_Split), vp, vp, sz, vp]
-    for f in (L.metis_split_begin, L.metis_split_finish):
-        f.restype = i32
-        f.argtypes = L.metis_split.argtypes
     L.metis_split_power_workspace_bytes.restype = sz
     L.metis_split_power_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32]
     L.metis_split_power.restype = i32
@@ -106,7 +103,7 @@ def load():
 
 EXPORTS = ["metis_status_str", "metis_abi_version", "fp4_block_quant_workspace_bytes", "fp4_block_quant",
            "fp4_block_dequant", "metis_split_workspace_bytes", "metis_split", "metis_split_power_workspace_bytes",
-           "metis_split_power", "metis_split_begin", "metis_split_finish", "metis_mean_split_workspace_bytes",
+           "metis_split_power", "metis_mean_split_workspace_bytes",
            "metis_mean_split", "metis_linear_workspace_bytes",
            "spectral_fp4_linear_fwd", "spectral_fp4_linear_fwd_noalloc", "spectral_fp4_linear_bwd", "metis_gemm_nt_workspace_bytes",
            "metis_gemm_nt_prepare", "metis_gemm_nt_main"]
@@ -281,44 +278,6 @@ def metis_split(A, l, k, fmt="mxfp4", omega=None, columns=None, orientations=("n
         _check(L.metis_split_power(_ptr(A), _dtype_code(A), m, n, A.stride(0), _ptr(om), kind, l, k, q, fmt,
                                    ctypes.byref(c), _ptr(rec.info), _ptr(ws), nws, _stream(A.device)))
     return rec
-
-
-class SplitInTwo:
-    """metis_split as two calls (metis_split_begin / metis_split_finish): the
-    object holds the arguments and the workspace that carries the state from
-    the first call to the second. begin() and finish() are enqueued on the
-    current stream; finish must run after begin in stream order."""
-
-    def __init__(self, A, l, k, fmt="mxfp4", omega=None, columns=None, orientations=("n", "t"), out=None):
-        L = load()
-        assert A.dim() == 2 and A.is_cuda and A.stride(1) == 1
-        m, n = A.shape
-        if (omega is None) == (columns is None):
-            raise MetisError("give exactly one of omega or columns")
-        if omega is not None:
-            assert omega.dtype == torch.bfloat16 and omega.is_contiguous() and tuple(omega.shape) == (n, l)
-            self.kind, self.om = OMEGA_GAUSSIAN, omega
-        else:
-            assert columns.dtype == torch.int32 and columns.is_contiguous() and columns.numel() == l
-            self.kind, self.om = OMEGA_COLUMNS, columns
-        self.A, self.l, self.k, self.fmt = A, l, k, _FMT[fmt]
-        self.rec = out if out is not None else empty_split(m, n, k, self.fmt, orientations, A.device)
-        self.nws = L.metis_split_workspace_bytes(m, n, l, k, self.kind, self.fmt)
-        # a buffer of its own (not the per-stream cache): it carries state
-        # from begin to finish, which another call on the stream must not touch
-        self.ws = torch.empty(max(int(self.nws), 256), dtype=torch.uint8, device=A.device)
-
-    def _call(self, f):
-        A, c = self.A, self.rec.c()
-        _check(f(_ptr(A), _dtype_code(A), A.shape[0], A.shape[1], A.stride(0), _ptr(self.om), self.kind, self.l,
-                 self.k, self.fmt, ctypes.byref(c), _ptr(self.rec.info), _ptr(self.ws), self.nws, _stream(A.device)))
-
-    def begin(self):
-        self._call(load().metis_split_begin)
-
-    def finish(self):
-        self._call(load().metis_split_finish)
-        return self.rec
 
 
 def metis_mean_split(A, fmt="mxfp4", orientations=("n", "t"), out=None):

@@ -261,4 +261,4 @@ extern "C" const char *metis_status_str(metis_status_t s) {
   return "METIS_ERR_UNKNOWN";
 }
 
-extern "C" int32_t metis_abi_version(void) { return 1; }
+extern "C" int32_t metis_abi_version(void) { return 2; }

@@ -2211,14 +2211,11 @@ metis_status_t run_factors_and_residual(const SplitPlan &p, const T *A, int64_t 
 
 template <typename T>
 metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void *omega, metis_split_t *out,
-                         int32_t *info, hipStream_t st, int phase = 3) {
+                         int32_t *info, hipStream_t st) {
   const int64_t m = p.m, n = p.n;
   const int l = p.l, lp = p.lp, k = p.k, kp = p.kp;
   const bool nv = p.fmt == METIS_NVFP4;
   const unsigned lz = (unsigned)cdiv(lp, kLpMax);  // sketch-column tiles
-  // phase 1: sketch, orthonormal basis, projection and the Gram of B (full
-  // GPU); phase 2: the small SVD (one workgroup), the factors and the residual
-  if (phase & 1) {
   // ---- pass 1: sketch
   const float *ysrc;
   int yparts;
@@ -2298,11 +2295,6 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     }
     gram_tile_kernel<<<dim3(p.gb_parts, nt, nt), kThreads, 0, st>>>(bt, n, l, lp, p.gb_rows, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
-  }
-  }
-  if (!(phase & 2)) {
-    METIS_LAUNCH_CHECK();
-    return METIS_OK;
   }
   // ---- small SVD of B (from its Gram, in p.gram) and the factors
   if (!p.wide) {
@@ -2483,11 +2475,10 @@ extern "C" size_t metis_split_workspace_bytes(int64_t m, int64_t n, int32_t l, i
 }
 
 namespace {
-// Argument checks and the plan shared by the one-call split and its two
-// phases; phase 1 and 2 as in run_split, 3 for both.
+// Argument checks and the plan of a split (q power iterations).
 metis_status_t split_entry(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda, const void *omega,
                            metis_omega_t kind, int32_t l, int32_t k, int32_t q, metis_fmt_t fmt, metis_split_t *out,
-                           int32_t *info, void *ws, size_t ws_bytes, hipStream_t stream, int phase) {
+                           int32_t *info, void *ws, size_t ws_bytes, hipStream_t stream) {
   if (q < 0) return METIS_ERR_INVALID;
   if (q > kMaxPowerIterations || (q > 0 && l > kLpMax)) return METIS_ERR_UNSUPPORTED;
   if (!A || !omega || !out) return METIS_ERR_INVALID;
@@ -2517,8 +2508,8 @@ metis_status_t split_entry(const void *A, metis_dtype_t dt, int64_t m, int64_t n
   out->Vt_q.rows = k; out->Vt_q.cols = n;
   out->R_q.rows = m; out->R_q.cols = n;
   out->Rt_q.rows = n; out->Rt_q.cols = m;
-  if (dt == METIS_F32) return run_split<float>(p, (const float *)A, lda, omega, out, info, stream, phase);
-  return run_split<unsigned short>(p, (const unsigned short *)A, lda, omega, out, info, stream, phase);
+  if (dt == METIS_F32) return run_split<float>(p, (const float *)A, lda, omega, out, info, stream);
+  return run_split<unsigned short>(p, (const unsigned short *)A, lda, omega, out, info, stream);
 }
 }  // namespace
 
@@ -2526,21 +2517,7 @@ extern "C" metis_status_t metis_split_power(const void *A, metis_dtype_t dt, int
                                             const void *omega, metis_omega_t kind, int32_t l, int32_t k, int32_t q,
                                             metis_fmt_t fmt, metis_split_t *out, int32_t *info, void *ws,
                                             size_t ws_bytes, hipStream_t stream) {
-  return split_entry(A, dt, m, n, lda, omega, kind, l, k, q, fmt, out, info, ws, ws_bytes, stream, 3);
-}
-
-extern "C" metis_status_t metis_split_begin(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
-                                            const void *omega, metis_omega_t kind, int32_t l, int32_t k,
-                                            metis_fmt_t fmt, metis_split_t *out, int32_t *info, void *ws,
-                                            size_t ws_bytes, hipStream_t stream) {
-  return split_entry(A, dt, m, n, lda, omega, kind, l, k, 0, fmt, out, info, ws, ws_bytes, stream, 1);
-}
-
-extern "C" metis_status_t metis_split_finish(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,
-                                             const void *omega, metis_omega_t kind, int32_t l, int32_t k,
-                                             metis_fmt_t fmt, metis_split_t *out, int32_t *info, void *ws,
-                                             size_t ws_bytes, hipStream_t stream) {
-  return split_entry(A, dt, m, n, lda, omega, kind, l, k, 0, fmt, out, info, ws, ws_bytes, stream, 2);
+  return split_entry(A, dt, m, n, lda, omega, kind, l, k, q, fmt, out, info, ws, ws_bytes, stream);
 }
 
 extern "C" metis_status_t metis_split(const void *A, metis_dtype_t dt, int64_t m, int64_t n, int64_t lda,

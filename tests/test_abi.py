@@ -37,7 +37,7 @@ def test_status_strings_and_version():
     L = M.load()
     assert L.metis_status_str(0) == b"METIS_OK"
     assert L.metis_status_str(3) == b"METIS_ERR_WORKSPACE"
-    assert L.metis_abi_version() == 1
+    assert L.metis_abi_version() == 2
 
 
 def _fp4(fmt=0, codes=None, scales=None):

@@ -214,33 +214,3 @@ def test_split_power_iterations_parity_small(name, q):
 def test_split_power_iterations_full_size():
     """8192 x 4096 bf16 (LLaMA-3-8B FFN input), k = 64, l = 80, q = 1."""
     _full_size(synth.make_tensor(4, "X_up"), q=1)
-
-
-@pytest.mark.parametrize("name", ["ragged-powerlaw-bf16", "planted-f32", "sampled-columns", "nvfp4", "wide-columns-l160"])
-def test_split_in_two_calls_equals_one_call(name):
-    """metis_split_begin + metis_split_finish (each on its own stream, the
-    second waiting for the first) give metis_split's record bit for bit."""
-    t = CASES[name]()
-    print("case", name, t.shape, flush=True)
-    A = G.to_gpu(t)
-    kw = {"omega": G.omega_gpu(t)} if t.sketch == "gaussian" else {"columns": G.columns_gpu(t)}
-    ref = M.metis_split(A, t.l, t.k, t.fmt, orientations=("n", "t"), **kw)
-    two = M.SplitInTwo(A, t.l, t.k, t.fmt, orientations=("n", "t"), **kw)
-    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
-    s1.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s1):
-        two.begin()
-    e = torch.cuda.Event()
-    e.record(s1)
-    s2.wait_event(e)
-    with torch.cuda.stream(s2):
-        rec = two.finish()
-    torch.cuda.synchronize()
-    a, b = G.record_to_dict(rec), G.record_to_dict(ref)
-    assert np.array_equal(a["S"], b["S"])
-    for key in ("Ut_q", "Vt_q", "R_q", "Rt_q"):
-        assert np.array_equal(a[key]["codes"], b[key]["codes"]), key
-        assert np.array_equal(a[key]["scales"], b[key]["scales"]), key
-        assert a[key]["tensor_scale"] == b[key]["tensor_scale"], key
-    assert torch.equal(rec.U, ref.U) and torch.equal(rec.V, ref.V)
-    assert int(rec.info.item()) == int(ref.info.item())
