@@ -16,7 +16,7 @@
 //                  small SVD     eigen-decomposition of B B^T (fp64, l x l) in one
 //                                 workgroup: Householder tridiagonalization,
 //                                 multisection, twisted-factorization vectors
-//                                 (l > 96: parallel cyclic Jacobi)
+//                                 (l > 96: the multi-workgroup forms of wide.hip)
 //                  assemble      U = Q E_k, S = sqrt(lambda_k), V = B^T E_k / S
 //                  signs         largest-|entry| of each U column made positive
 //                  factors       U^T, V^T block-quantized along their length
@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "wide.hpp"
 
 using namespace metis;
 
@@ -90,6 +91,7 @@ struct SplitPlan {
   unsigned short *uhl;   // 2 x m x kp bf16 (U hi, lo)
   unsigned short *whl;   // 2 x n x kp bf16 ((V S) hi, lo)
   double *wa, *winv, *wg, *wv;  // lp x lp scratch of the global-memory (wide) forms
+  double *waux;                 // small vectors of the wide forms
   uint32_t *amax;        // 8 words: NVFP4 tensor maxima (U^T, V^T, R)
   float *z1;             // n x l (power iterations: A^T Q after one R^-1)
   unsigned short *zt;    // 2 x lp x n bf16 (power iterations: orth(A^T Q)^T hi, lo)
@@ -155,6 +157,7 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
   p.winv = c.take<double>((size_t)p.lp * p.lp);
   p.wg = c.take<double>((size_t)p.lp * p.lp);
   p.wv = c.take<double>((size_t)p.lp * p.lp);
+  p.waux = c.take<double>(p.wide ? metis_wide::aux_doubles(p.lp) : 0);
   p.amax = c.take<uint32_t>(8);
   p.info_ws = c.take<int>(1);
   p.z1 = c.take<float>(q > 0 ? (size_t)n * l : 0);
@@ -583,78 +586,6 @@ __global__ void __launch_bounds__(256)
 }
 
 // ========================================================= Cholesky + inverse
-// One workgroup: G = R^T R (upper R, right-looking, fp64 in LDS), then
-// R^-1 by back substitution, one column per thread. A pivot at or below
-// l * 2^-52 * max(diag G) marks that direction as absent: its row of R and
-// its row and column of R^-1 are zero (the orthonormalized column comes out
-// zero) and *info records the first such pivot (1-based).
-template <bool WIDE>
-__global__ void __launch_bounds__(kThreads)
-    chol_inv_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ rinv, int *info,
-                    double *__restrict__ wa, double *__restrict__ winv) {
-  // LDS copies for l <= kLpMax; global scratch (wa, winv: lp x lp) beyond
-  constexpr int SD = WIDE ? 1 : kLpMax;
-  __shared__ double a_s[SD * (kLpMax + 1)];
-  __shared__ double inv_s[SD * (kLpMax + 1)];
-  __shared__ int dead[512];
-  __shared__ double tol_s;
-  __shared__ int first_dead;
-  double *a = WIDE ? wa : a_s;
-  double *inv = WIDE ? winv : inv_s;
-  const int sa = WIDE ? lp : kLpMax + 1;
-  const int t = threadIdx.x;
-  for (int i = t; i < lp * lp; i += kThreads) a[(i / lp) * sa + i % lp] = g[i];
-  if (t == 0) {
-    double md = 0.0;
-    for (int i = 0; i < l; ++i) md = fmax(md, g[i * lp + i]);
-    tol_s = (double)l * 2.220446049250313e-16 * md;
-    first_dead = 0;
-  }
-  __syncthreads();
-  for (int j = 0; j < l; ++j) {
-    if (t == 0) {
-      const double piv = a[j * sa + j];
-      if (piv > tol_s) {
-        a[j * sa + j] = sqrt(piv);
-        dead[j] = 0;
-      } else {
-        a[j * sa + j] = 0.0;
-        dead[j] = 1;
-        if (first_dead == 0) first_dead = j + 1;
-      }
-    }
-    __syncthreads();
-    const double d = a[j * sa + j];
-    const bool dj = dead[j];
-    for (int c = j + 1 + t; c < l; c += kThreads) a[j * sa + c] = dj ? 0.0 : a[j * sa + c] / d;
-    __syncthreads();
-    if (!dj) {
-      const int w = l - j - 1;
-      for (int idx = t; idx < w * w; idx += kThreads) {
-        const int p = j + 1 + idx / w, q = j + 1 + idx % w;
-        if (q >= p) a[p * sa + q] -= a[j * sa + p] * a[j * sa + q];
-      }
-    }
-    __syncthreads();
-  }
-  // column c of R^-1: solve R x = e_c from the bottom up
-  for (int c = t; c < lp; c += kThreads) {
-    for (int i = 0; i < lp; ++i) inv[i * sa + c] = 0.0;
-    if (c < l && !dead[c]) {
-      inv[c * sa + c] = 1.0 / a[c * sa + c];
-      for (int i = c - 1; i >= 0; --i) {
-        if (dead[i]) continue;
-        double s = 0.0;
-        for (int q = i + 1; q <= c; ++q) s += a[i * sa + q] * inv[q * sa + c];
-        inv[i * sa + c] = -s / a[i * sa + i];
-      }
-    }
-  }
-  __syncthreads();
-  for (int i = t; i < lp * lp; i += kThreads) rinv[i] = inv[(i / lp) * sa + i % lp];
-  if (t == 0 && info) *info = first_dead;
-}
-
 // The same factorization for l <= kLpMax as one elimination on [G | I]:
 // step j subtracts m_p = G'[j][p] / d_j times row j from every later row p,
 // on the upper part of the trailing matrix G' and on the lower-triangular
@@ -1111,142 +1042,6 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
     }
 }
 
-// ================================================================== Jacobi
-// Eigen-decomposition of the symmetric lp x lp matrix G (fp64) by cyclic
-// two-sided Jacobi rotations, all lp/2 disjoint pairs of a round at once
-// (round-robin pairing). Rows/columns >= l are zero padding and never rotate.
-// Output: eigenvectors (columns, lp x lp) in descending eigenvalue order,
-// S[c] = sqrt(lambda_c) for c < k (0 below 2^-24 sigma_max) and sig_inv.
-constexpr int kJacThreads = 1024;
-
-__device__ __forceinline__ int rr_player(int pos, int round, int N) {
-  return pos == 0 ? 0 : 1 + (pos - 1 + round) % (N - 1);
-}
-
-template <bool WIDE>
-__global__ void __launch_bounds__(kJacThreads)
-    jacobi_kernel(const double *__restrict__ gin, int l, int lp, int k, int max_sweeps, double *__restrict__ evec,
-                  double *__restrict__ sig_inv, float *__restrict__ S, double *__restrict__ wg,
-                  double *__restrict__ wv) {
-  // G and V live in LDS for lp <= kLpMax and in global scratch (wg, wv) beyond
-  constexpr int SD = WIDE ? 1 : kLpMax;
-  __shared__ double G_s[SD * (kLpMax + 1)];
-  __shared__ double V_s[SD * (kLpMax + 1)];
-  __shared__ double cs_c[256], cs_s[256];
-  __shared__ int pp[256], qq[256];
-  __shared__ int rotated;
-  __shared__ double floor_s;
-  __shared__ int rank[512];
-  double *Gp = WIDE ? wg : G_s;
-  double *Vp = WIDE ? wv : V_s;
-  const int gstr = WIDE ? lp : kLpMax + 1;
-#define G(i, j) Gp[(i) * gstr + (j)]
-#define V(i, j) Vp[(i) * gstr + (j)]
-  const int t = threadIdx.x;
-  const int N = lp, H = lp / 2;
-  for (int i = t; i < N * N; i += kJacThreads) {
-    G(i / N, i % N) = gin[i];
-    V(i / N, i % N) = (i / N == i % N) ? 1.0 : 0.0;
-  }
-  if (t == 0) {
-    double md = 0.0;
-    for (int i = 0; i < l; ++i) md = fmax(md, gin[i * N + i]);
-    floor_s = 4.0 * 2.220446049250313e-16 * md;
-  }
-  __syncthreads();
-  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
-    if (t == 0) rotated = 0;
-    __syncthreads();
-    for (int round = 0; round < N - 1; ++round) {
-      if (t < H) {
-        int p = rr_player(t, round, N), q = rr_player(N - 1 - t, round, N);
-        if (p > q) {
-          const int x = p;
-          p = q;
-          q = x;
-        }
-        const double app = G(p, p), aqq = G(q, q), apq = G(p, q);
-        double c = 1.0, s = 0.0;
-        if (apq != 0.0 && fabs(apq) > 1e-14 * sqrt(fabs(app * aqq)) && fabs(apq) > floor_s) {
-          const double zeta = (aqq - app) / (2.0 * apq);
-          const double tt = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
-          c = 1.0 / sqrt(1.0 + tt * tt);
-          s = c * tt;
-          rotated = 1;
-        }
-        cs_c[t] = c;
-        cs_s[t] = s;
-        pp[t] = p;
-        qq[t] = q;
-      }
-      __syncthreads();
-      // G <- J^T G J on 2x2 blocks (each block owned by one thread)
-      for (int idx = t; idx < H * H; idx += kJacThreads) {
-        const int P = idx / H, Q = idx % H;
-        const double c1 = cs_c[P], s1 = cs_s[P], c2 = cs_c[Q], s2 = cs_s[Q];
-        if (s1 == 0.0 && s2 == 0.0) continue;
-        const int p1 = pp[P], q1 = qq[P], p2 = pp[Q], q2 = qq[Q];
-        const double b00 = G(p1, p2), b01 = G(p1, q2), b10 = G(q1, p2), b11 = G(q1, q2);
-        const double h00 = c2 * b00 - s2 * b01, h01 = s2 * b00 + c2 * b01;
-        const double h10 = c2 * b10 - s2 * b11, h11 = s2 * b10 + c2 * b11;
-        double n00 = c1 * h00 - s1 * h10, n01 = c1 * h01 - s1 * h11;
-        double n10 = s1 * h00 + c1 * h10, n11 = s1 * h01 + c1 * h11;
-        if (P == Q) {
-          n01 = 0.0;
-          n10 = 0.0;
-        }
-        G(p1, p2) = n00;
-        G(p1, q2) = n01;
-        G(q1, p2) = n10;
-        G(q1, q2) = n11;
-      }
-      // V <- V J
-      for (int idx = t; idx < N * H; idx += kJacThreads) {
-        const int i = idx / H, P = idx % H;
-        const double c = cs_c[P], s = cs_s[P];
-        if (s == 0.0) continue;
-        const int p = pp[P], q = qq[P];
-        const double vp = V(i, p), vq = V(i, q);
-        V(i, p) = c * vp - s * vq;
-        V(i, q) = s * vp + c * vq;
-      }
-      __syncthreads();
-    }
-    if (!rotated) break;
-    __syncthreads();
-  }
-  // rank of each eigenvalue (descending, ties by index); padding ranks last
-  if (t < N) {
-    int r = 0;
-    if (t < l) {
-      const double d = G(t, t);
-      for (int j = 0; j < l; ++j) {
-        const double e = G(j, j);
-        r += (e > d) || (e == d && j < t);
-      }
-    } else {
-      r = t;
-    }
-    rank[t] = r;
-  }
-  __syncthreads();
-  for (int idx = t; idx < N * N; idx += kJacThreads) {
-    const int row = idx / N, col = idx % N;
-    evec[row * N + rank[col]] = V(row, col);
-  }
-  if (t < N) {
-    double smax = sqrt(fmax(G(0, 0), 0.0));
-    for (int j = 1; j < l; ++j) smax = fmax(smax, sqrt(fmax(G(j, j), 0.0)));
-    double sg = t < l ? sqrt(fmax(G(t, t), 0.0)) : 0.0;
-    if (!(sg > smax * 5.9604644775390625e-08)) sg = 0.0;
-    const int r = rank[t];
-    sig_inv[r] = sg > 0.0 ? 1.0 / sg : 0.0;
-    if (r < k) S[r] = (float)sg;
-  }
-#undef G
-#undef V
-}
-
 // ================================================ tridiagonal eigensolver
 // All wanted eigenpairs of the symmetric l x l matrix G (upper triangle read,
 // fp64) in one workgroup, in four stages:
@@ -1266,7 +1061,7 @@ __global__ void __launch_bounds__(kJacThreads)
 //   4. Back-transformation x = H z, sixteen lanes per vector, no barriers.
 // Off-diagonals at or below 2^-52 ||T|| split T into blocks that are solved
 // separately; an eigenvalue's slot index is its place in its block.
-// Output as the Jacobi kernel: evec[row * lp + rank] (descending eigenvalue,
+// Output: evec[row * lp + rank] (descending eigenvalue,
 // unit columns, zero beyond l rows and k columns), sig_inv[rank] = 1 / sigma
 // with sigma = sqrt(lambda) (0 for sigma <= 2^-24 sigma_max and for ranks
 // whose eigenvalue was not computed), S[rank < k].
@@ -2280,11 +2075,14 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     const unsigned nt = (unsigned)(lp / 64);
     gram_tile_kernel<<<dim3(p.gy_parts, nt, nt), kThreads, 0, st>>>(y, m, l, lp, p.gy_rows, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
-    chol_inv_kernel<true><<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, info ? info : p.info_ws, p.wa, p.winv);
+    metis_status_t ws = metis_wide::wide_chol_inv(p.gram, l, lp, p.rinv, info ? info : p.info_ws, p.wa, p.winv,
+                                                  p.waux, st);
+    if (ws != METIS_OK) return ws;
     apply_rinv_kernel<<<dim3((unsigned)cdiv(m, 64), nt), kThreads, 0, st>>>(y, m, l, lp, p.rinv, p.q1, nullptr);
     gram_tile_kernel<<<dim3(p.gy_parts, nt, nt), kThreads, 0, st>>>(p.q1, m, l, lp, p.gy_rows, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gy_parts, lp * lp, p.gram);
-    chol_inv_kernel<true><<<1, kThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws, p.wa, p.winv);
+    ws = metis_wide::wide_chol_inv(p.gram, l, lp, p.rinv, p.info_ws, p.wa, p.winv, p.waux, st);
+    if (ws != METIS_OK) return ws;
     apply_rinv_kernel<<<dim3((unsigned)cdiv(m, 64), nt), kThreads, 0, st>>>(p.q1, m, l, lp, p.rinv, p.q, p.qt);
     project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
                                                                                  p.pk_rows, p.btp);
@@ -2305,7 +2103,9 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
                                                                                  p.sig_inv, out->V);
   } else {
     const float *bt = p.pk > 1 ? p.bt : p.btp;
-    jacobi_kernel<true><<<1, kJacThreads, 0, st>>>(p.gram, l, lp, k, 40, p.evec, p.sig_inv, out->S, p.wg, p.wv);
+    const metis_status_t es =
+        metis_wide::wide_eigh(p.gram, l, lp, k, p.evec, p.sig_inv, out->S, p.wg, p.wv, p.wa, p.waux, st);
+    if (es != METIS_OK) return es;
     assemble_wide_kernel<<<(unsigned)cdiv(m * k, 256), 256, 0, st>>>(p.q, m, l, lp, k, p.evec, nullptr, out->U);
     argmax_kernel<<<p.am_parts, 128, 0, st>>>(out->U, m, k, p.am_rows, p.am_val, p.am_idx);
     assemble_wide_kernel<<<(unsigned)cdiv(n * k, 256), 256, 0, st>>>(bt, n, l, lp, k, p.evec, p.sig_inv, out->V);

@@ -1,0 +1,29 @@
+// Host entry points of the wide-sketch (96 < l <= 512) small-matrix stages
+// (wide.hip). All matrices are lp x lp fp64, row-major; lp <= kWideMax.
+#pragma once
+#include <stddef.h>
+
+#include "metis_fp4.h"
+
+namespace metis_wide {
+
+constexpr int kWideMax = 512;
+
+// Doubles of the small-vector scratch both calls take (aux).
+size_t aux_doubles(int lp);
+
+// rinv = R^-1 for G = R^T R (upper triangle of g read); a pivot at or below
+// l 2^-52 max diag G is absent (zero row and column of R^-1, info = its
+// 1-based index; info may be NULL). C, F: lp x lp scratch.
+metis_status_t wide_chol_inv(const double *g, int l, int lp, double *rinv, int *info, double *C, double *F,
+                             double *aux, hipStream_t st);
+
+// The k largest eigenpairs of the symmetric g (upper triangle read):
+// evec[row * lp + rank] (unit columns, descending eigenvalue, rows beyond l
+// zero), sig_inv[rank] = 1 / sqrt(lambda) (0 for sqrt(lambda) at or below
+// 2^-24 of the largest and for ranks >= k), S[rank < k] = sqrt(lambda).
+// W, V, Dm: lp x lp scratch.
+metis_status_t wide_eigh(const double *g, int l, int lp, int k, double *evec, double *sig_inv, float *S, double *W,
+                         double *V, double *Dm, double *aux, hipStream_t st);
+
+}  // namespace metis_wide
