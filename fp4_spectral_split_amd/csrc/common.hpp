@@ -188,6 +188,37 @@ __device__ __forceinline__ double wave_max(double v) {
   return v;
 }
 
+
+// ------------------------------------------------------------ fp64 lanes
+// A DPP move of an fp64 value (both halves with the same control).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __double2loint(v), hi = __double2hiint(v);
+  return __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false),
+                          __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false));
+}
+
+// Sum over an aligned group of 8 lanes; every lane gets the bitwise same sum.
+__device__ __forceinline__ double group8_sum(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror: lane i with lane 7 - i
+  return v;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
+                          __builtin_amdgcn_readlane(__double2loint(v), lane));
+}
+
+// Sum over the whole wave (every lane active), the same bits in every lane:
+// DPP within rows of 16 lanes, then the four row sums read as scalars.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = group8_sum(v);
+  v += dpp_f64<0x140>(v);  // row_mirror: lane i with lane 15 - i
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
 }  // namespace metis
 
 // ------------------------------------------------------------------ host

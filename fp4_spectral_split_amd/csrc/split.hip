@@ -131,7 +131,7 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
   p.pk = (int)cdiv(m, p.pk_rows);
   p.gb_rows = p.wide ? pick_rows_per_part(n, 16, 32) : kGramRows;
   p.gb_parts = (int)cdiv(n, p.gb_rows);
-  p.am_rows = p.wide ? 256 : asm_chunk_rows(k);  // assemble_u's chunk (16 rows per thread)
+  p.am_rows = p.wide ? 64 : asm_chunk_rows(k);  // rows per argmax partial of the assemble kernels
   p.am_parts = (int)cdiv(m, p.am_rows);
 
   metis_host::Carver c(ws);
@@ -360,21 +360,6 @@ __device__ __forceinline__ float sum_parts(const float *p, int parts, int64_t st
 }
 
 // ==================================================================== gram
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const int lo = __double2loint(v), hi = __double2hiint(v);
-  return __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false),
-                          __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false));
-}
-
-// Sum over an aligned group of 8 lanes; every lane gets the bitwise same sum.
-__device__ __forceinline__ double group8_sum(double v) {
-  v += dpp_f64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += dpp_f64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v += dpp_f64<0x141>(v);  // row_half_mirror: lane i with lane 7 - i
-  return v;
-}
-
 typedef double doublex4 __attribute__((ext_vector_type(4)));
 
 // fp64 MFMA 16x16x4: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16];
@@ -881,39 +866,6 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// out[r][c] = sum_t x[r][t] E[t][c] * colscale[c]  (fp64), r < rows, c < k
-__global__ void assemble_wide_kernel(const float *__restrict__ x, int64_t rows, int l, int lp, int k,
-                                     const double *__restrict__ evec, const double *__restrict__ colscale,
-                                     float *__restrict__ out) {
-  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (idx >= rows * k) return;
-  const int64_t r = idx / k;
-  const int c = (int)(idx - r * k);
-  double s = 0.0;
-  for (int q = 0; q < l; ++q) s += (double)x[r * l + q] * evec[(int64_t)q * lp + c];
-  out[idx] = (float)(colscale ? s * colscale[c] : s);
-}
-
-// Per chunk of rows: argmax |U[:, c]| (lowest row on ties) and its value.
-__global__ void argmax_kernel(const float *__restrict__ U, int64_t m, int k, int64_t chunk_rows,
-                              float *__restrict__ am_val, int *__restrict__ am_idx) {
-  const int c = threadIdx.x;
-  if (c >= k) return;
-  const int64_t r_beg = blockIdx.x * chunk_rows, r_end = std::min<int64_t>(m, r_beg + chunk_rows);
-  float ba = -1.0f, bv = 0.0f;
-  int bi = 0x7FFFFFFF;
-  for (int64_t r = r_beg; r < r_end; ++r) {
-    const float u = U[r * k + c];
-    if (fabsf(u) > ba) {
-      ba = fabsf(u);
-      bv = u;
-      bi = (int)r;
-    }
-  }
-  am_val[blockIdx.x * k + c] = bv;
-  am_idx[blockIdx.x * k + c] = bi;
-}
-
 // ============================================================== projection
 // btp[s] = (A[rows of chunk s, :])^T Q[rows of chunk s, :]   (n x l, fp32)
 // with Q given transposed as bf16 hi + lo (2 x lp x m). WG: 128 columns of A,
@@ -1068,19 +1020,6 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
 constexpr int kEigThreads = 1024;
 constexpr int kEigCols = kLpMax / 8;  // register columns of a row segment
 constexpr int kEigIters = 16;         // each keeps 1/9 of the bracket: 9^-16 < 2^-50
-
-__device__ __forceinline__ double readlane_f64(double v, int lane) {
-  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
-                          __builtin_amdgcn_readlane(__double2loint(v), lane));
-}
-
-// Sum over the whole wave (every lane active), the same bits in every lane:
-// DPP within rows of 16 lanes, then the four row sums read as scalars.
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  v = group8_sum(v);
-  v += dpp_f64<0x140>(v);  // row_mirror: lane i with lane 15 - i
-  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
-}
 
 // Sum over an aligned group of 16 lanes (row_ror:8 pairs the two halves).
 __device__ __forceinline__ double group16_sum(double v) {
@@ -2106,9 +2045,10 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     const metis_status_t es =
         metis_wide::wide_eigh(p.gram, l, lp, k, p.evec, p.sig_inv, out->S, p.wg, p.wv, p.wa, p.waux, st);
     if (es != METIS_OK) return es;
-    assemble_wide_kernel<<<(unsigned)cdiv(m * k, 256), 256, 0, st>>>(p.q, m, l, lp, k, p.evec, nullptr, out->U);
-    argmax_kernel<<<p.am_parts, 128, 0, st>>>(out->U, m, k, p.am_rows, p.am_val, p.am_idx);
-    assemble_wide_kernel<<<(unsigned)cdiv(n * k, 256), 256, 0, st>>>(bt, n, l, lp, k, p.evec, p.sig_inv, out->V);
+    metis_status_t as = metis_wide::wide_assemble(p.q, m, l, lp, k, p.evec, nullptr, out->U, p.am_val, p.am_idx, st);
+    if (as == METIS_OK)
+      as = metis_wide::wide_assemble(bt, n, l, lp, k, p.evec, p.sig_inv, out->V, nullptr, nullptr, st);
+    if (as != METIS_OK) return as;
   }
   sign_kernel<<<1, 1024, 0, st>>>(p.am_val, p.am_idx, p.am_parts, k, p.sign);
   return run_factors_and_residual<T, false>(p, A, lda, out, nullptr, st);

@@ -35,11 +35,10 @@ constexpr int kWMax = metis_wide::kWideMax;
 constexpr int kWC = kWMax / 64;        // columns per lane of a row
 constexpr int kPiv = 16;               // pivots per Cholesky launch
 
-// Sum over the workgroup (kWT threads), the same bits in every thread:
-// lane 0's butterfly sum of each wave, then the waves in order.
+// Sum over the workgroup (kWT threads), the same bits in every thread: each
+// wave's DPP sum (wave_sum_f64), then the waves in order.
 __device__ __forceinline__ double block_sum(double v, double *red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sum_f64(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -61,12 +60,8 @@ __device__ __forceinline__ double block_max(double v, double *red) {
   return s;
 }
 
-// Sum over one wave, lane 0's value in every lane.
-__device__ __forceinline__ double wave_sum0(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return __shfl(v, 0, 64);
-}
+// Sum over one wave, the same bits in every lane.
+__device__ __forceinline__ double wave_sum0(double v) { return wave_sum_f64(v); }
 
 // ============================================================ Cholesky
 // C (lp x lp) starts as the upper triangle of G (zero below the diagonal and
@@ -95,58 +90,81 @@ __global__ void __launch_bounds__(kWT) wchol_init_kernel(const double *__restric
 // reached, so they go to F (read by the finish kernel, never in place: other
 // workgroups are still reading C's copy); rows below them are updated in C,
 // one row per wave.
+// NC = lp / 64 columns per lane, fixed at compile time: every load takes an
+// always-valid address and every per-element condition is a select, so no
+// branch separates a load from its use.
+template <int NC>
 __global__ void __launch_bounds__(kWT) wchol_step_kernel(double *__restrict__ C, double *__restrict__ F, int l,
-                                                         int lp, int j0, const double *__restrict__ aux) {
-  __shared__ double P[kPiv][kWMax];
+                                                         int j0, const double *__restrict__ aux) {
+  constexpr int lp = NC * 64;
+  __shared__ double P[kPiv][lp];
   __shared__ double ip[kPiv];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j1 = min(j0 + kPiv, l), b = j1 - j0;
   const double tol = aux[0];
-  for (int e = t; e < b * lp; e += kWT) P[e / lp][e % lp] = C[(int64_t)(j0 + e / lp) * lp + e % lp];
+  // own row below the pivots (one per wave), loaded with the pivot rows
+  const int p = j1 + blockIdx.x * (kWT / 64) + wave;
+  const bool own = p < l;
+  double *row = C + (int64_t)(own ? p : 0) * lp;
+  double r[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) r[u] = row[lane + 64 * u];
+  // pivot rows (rows past the block repeat its last row: same values)
+  double pr[4][NC];
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) {
+    const int i = min(wave + 4 * k4, b - 1);
+#pragma unroll
+    for (int u = 0; u < NC; ++u) pr[k4][u] = C[(int64_t)(j0 + i) * lp + lane + 64 * u];
+  }
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) {
+    const int i = min(wave + 4 * k4, b - 1);
+#pragma unroll
+    for (int u = 0; u < NC; ++u) P[i][lane + 64 * u] = pr[k4][u];
+  }
   __syncthreads();
-  // the pivot rows among themselves
+  // the pivot rows among themselves, a row per wave
   for (int i = 0; i < b; ++i) {
     const int j = j0 + i;
     const double d = P[i][j];
     const double inv = d > tol ? 1.0 / d : 0.0;
     if (t == 0) ip[i] = inv;
-    for (int e = t; e < (b - i - 1) * lp; e += kWT) {
-      const int i2 = i + 1 + e / lp, x = e % lp, p = j0 + i2;
-      const double m = P[i][p] * inv;
-      if (x >= p || x < j) P[i2][x] = fma(-m, P[i][x], P[i2][x]);
-      else if (x == j) P[i2][x] -= m;
+    for (int i2 = i + 1 + wave; i2 < b; i2 += kWT / 64) {
+      const int q = j0 + i2;
+      const double m = P[i][q] * inv;
+      double pi[NC], p2[NC];
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        pi[u] = P[i][lane + 64 * u];
+        p2[u] = P[i2][lane + 64 * u];
+      }
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        const int x = lane + 64 * u;
+        const double mm = (x >= q || x < j) ? m : 0.0;
+        P[i2][x] = fma(-mm, pi[u], p2[u]) - (x == j ? m : 0.0);
+      }
     }
     __syncthreads();
   }
   if (blockIdx.x == 0)
-    for (int e = t; e < b * lp; e += kWT) F[(int64_t)(j0 + e / lp) * lp + e % lp] = P[e / lp][e % lp];
-  // own rows below the pivots
-  const int p = j1 + blockIdx.x * (kWT / 64) + wave;
-  if (p >= l) return;
-  double r[kWC];
-  double *row = C + (int64_t)p * lp;
+    for (int i = wave; i < b; i += kWT / 64)
 #pragma unroll
-  for (int u = 0; u < kWC; ++u) {
-    const int x = lane + 64 * u;
-    r[u] = x < lp ? row[x] : 0.0;
-  }
+      for (int u = 0; u < NC; ++u) F[(int64_t)(j0 + i) * lp + lane + 64 * u] = P[i][lane + 64 * u];
+  if (!own) return;
   for (int i = 0; i < b; ++i) {
     const int j = j0 + i;
     const double m = P[i][p] * ip[i];
 #pragma unroll
-    for (int u = 0; u < kWC; ++u) {
+    for (int u = 0; u < NC; ++u) {
       const int x = lane + 64 * u;
-      if (x < lp) {
-        if (x >= p || x < j) r[u] = fma(-m, P[i][x], r[u]);
-        else if (x == j) r[u] -= m;
-      }
+      const double mm = (x >= p || x < j) ? m : 0.0;
+      r[u] = fma(-mm, P[i][x], r[u]) - (x == j ? m : 0.0);
     }
   }
 #pragma unroll
-  for (int u = 0; u < kWC; ++u) {
-    const int x = lane + 64 * u;
-    if (x < lp) row[x] = r[u];
-  }
+  for (int u = 0; u < NC; ++u) row[lane + 64 * u] = r[u];
 }
 
 // R^-1[i][c] = L^-1[c][i] d_c^-1/2 for i <= c < l (zero column for an absent
@@ -165,11 +183,21 @@ __global__ void __launch_bounds__(kWT) wchol_finish_kernel(const double *__restr
     }
     rinv[e] = r;
   }
-  if (info && blockIdx.x == 0 && threadIdx.x == 0) {
-    int first = 0;
-    for (int c = 0; c < l && !first; ++c)
-      if (!(F[(int64_t)c * lp + c] > tol)) first = c + 1;
-    *info = first;
+  if (info && blockIdx.x == 0) {
+    // first absent pivot: the least absent index over the workgroup
+    __shared__ int firsts[kWT / 64];
+    int first = 0x7FFFFFFF;
+    for (int c = threadIdx.x; c < l; c += kWT)
+      if (!(F[(int64_t)c * lp + c] > tol)) first = min(first, c);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o, 64));
+    if ((threadIdx.x & 63) == 0) firsts[threadIdx.x >> 6] = first;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int f = firsts[0];
+      for (int w = 1; w < kWT / 64; ++w) f = min(f, firsts[w]);
+      *info = f == 0x7FFFFFFF ? 0 : f + 1;
+    }
   }
 }
 
@@ -196,38 +224,65 @@ __global__ void __launch_bounds__(kWT) wtri_init_kernel(const double *__restrict
 //    p_r = beta_jn (W v_jn)_r into pbuf[jn & 1].
 // Workgroup 0 records V[jn], beta[jn], d[jn] and e[jn]. Row jn itself is not
 // written (nothing reads it again), so every workgroup reads the same copy.
-__global__ void __launch_bounds__(kWT) wtri_step_kernel(double *__restrict__ W, int l, int lp, int j,
-                                                        double *__restrict__ V, double *__restrict__ beta,
-                                                        double *__restrict__ dg, double *__restrict__ eo,
-                                                        double *__restrict__ pbuf) {
-  __shared__ double sv[kWMax], sw[kWMax], sx[kWMax];
+template <int NC>
+__global__ void __launch_bounds__(kWT) wtri_step_kernel(double *__restrict__ W, int l, int j, double *__restrict__ V,
+                                                        double *__restrict__ beta, double *__restrict__ dg,
+                                                        double *__restrict__ eo, double *__restrict__ pbuf) {
+  constexpr int lp = NC * 64;
+  __shared__ double sv[lp], sw[lp], sx[lp];
   __shared__ double red[kWT / 64];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int jn = j + 1;
   const bool apply = j >= 0;
-  // ---- w of reflector j
-  {
-    double part = 0.0;
-    for (int c = t; c < kWMax; c += kWT) {
-      const bool in = apply && c > j && c < l;
-      const double v = in ? V[(int64_t)j * lp + c] : 0.0;
-      const double p = in ? pbuf[(int64_t)(j & 1) * lp + c] : 0.0;
-      sv[c] = v;
-      sw[c] = p;
-      part = fma(p, v, part);
-    }
-    const double K = apply ? 0.5 * beta[j] * block_sum(part, red) : 0.0;
-    for (int c = t; c < kWMax; c += kWT) sw[c] = fma(-K, sv[c], sw[c]);
-    __syncthreads();
+  // every global load of the launch is issued here, before any is used:
+  // reflector j and p_j, row jn (clamped addresses, masked values), the
+  // wave's own row
+  constexpr int PC = (lp + kWT - 1) / kWT;
+  const int js = max(j, 0);
+  double lv[PC], lq[PC], lx[PC];
+#pragma unroll
+  for (int u = 0; u < PC; ++u) {
+    const int c = min(t + kWT * u, lp - 1);
+    lv[u] = V[(int64_t)js * lp + c];
+    lq[u] = pbuf[(int64_t)(js & 1) * lp + c];
+    lx[u] = W[(int64_t)jn * lp + c];
   }
+  const double bj = beta[js];
+  const int r = jn + 1 + blockIdx.x * (kWT / 64) + wave;
+  const bool own = r < l;
+  double *row = W + (int64_t)(own ? r : jn) * lp;
+  double a[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) a[u] = row[lane + 64 * u];
+  // ---- w of reflector j: w = p - (beta_j / 2) (p . v) v
+  double part = 0.0;
+#pragma unroll
+  for (int u = 0; u < PC; ++u) {
+    const int c = t + kWT * u;
+    const bool in = apply && c > j && c < l;
+    lv[u] = in ? lv[u] : 0.0;
+    lq[u] = in ? lq[u] : 0.0;
+    if (c < lp) sv[c] = lv[u];
+    part = fma(lq[u], lv[u], part);
+  }
+  const double K = apply ? 0.5 * bj * block_sum(part, red) : 0.0;
+#pragma unroll
+  for (int u = 0; u < PC; ++u) {
+    const int c = t + kWT * u;
+    if (c < lp) sw[c] = fma(-K, lv[u], lq[u]);
+  }
+  __syncthreads();
   // ---- row jn after the update, and reflector jn from it
   const double vr_n = sv[jn], wr_n = sw[jn];
   double s2 = 0.0;
-  for (int c = t; c < kWMax; c += kWT) {
-    double x = 0.0;
-    if (c >= jn && c < l) x = fma(-vr_n, sw[c], fma(-wr_n, sv[c], W[(int64_t)jn * lp + c]));
-    sx[c] = x;
-    if (c > jn) s2 = fma(x, x, s2);
+#pragma unroll
+  for (int u = 0; u < PC; ++u) {
+    const int c = t + kWT * u;
+    if (c < lp) {
+      const double x = (c >= jn && c < l) ? fma(-vr_n, sw[c], fma(-wr_n, sv[c], lx[u])) : 0.0;
+      sx[c] = x;
+      s2 = fma(c > jn ? x : 0.0, x, s2);
+    }
   }
   const double a2 = block_sum(s2, red);  // also orders the sx writes
   const bool refl = jn <= l - 3;
@@ -249,20 +304,24 @@ __global__ void __launch_bounds__(kWT) wtri_step_kernel(double *__restrict__ W, 
   if (refl && blockIdx.x == 0)
     for (int c = t; c < lp; c += kWT) V[(int64_t)jn * lp + c] = c > jn ? sx[c] : 0.0;
   // ---- the rows below jn: update, write back, next product
-  const int r = jn + 1 + blockIdx.x * (kWT / 64) + wave;
-  if (r >= l) return;
-  double *row = W + (int64_t)r * lp;
+  if (!own) return;
   const double vr = sv[r], wr = sw[r];
   double acc = 0.0;
 #pragma unroll
-  for (int u = 0; u < kWC; ++u) {
+  for (int u = 0; u < NC; ++u) {
     const int c = lane + 64 * u;
-    if (c > jn && c < l) {
-      const double a = fma(-vr, sw[c], fma(-wr, sv[c], row[c]));
-      row[c] = a;
-      if (refl) acc = fma(a, sx[c], acc);
-      if (c == r && jn == l - 2) dg[r] = a;  // the last diagonal (r = l - 1)
-    }
+    const bool in = c > jn && c < l;
+    const double x = in ? fma(-vr, sw[c], fma(-wr, sv[c], a[u])) : a[u];
+    a[u] = x;
+    acc = fma(in ? x : 0.0, sx[c], acc);
+  }
+#pragma unroll
+  for (int u = 0; u < NC; ++u) row[lane + 64 * u] = a[u];
+  if (jn == l - 2) {
+    // the last diagonal (r = l - 1)
+#pragma unroll
+    for (int u = 0; u < NC; ++u)
+      if (lane + 64 * u == r) dg[r] = a[u];
   }
   if (refl) {
     const double s = wave_sum0(acc);
@@ -271,10 +330,21 @@ __global__ void __launch_bounds__(kWT) wtri_step_kernel(double *__restrict__ W, 
 }
 
 // ============================================================ eigenvalues
+// 1 / q from the hardware estimate (about 2^-25 relative) and two Newton
+// steps: correct to about 2^-52.
+__device__ __forceinline__ double recip(double q) {
+  double r = __builtin_amdgcn_rcp(q);
+  r = fma(r, fma(-q, r, 1.0), r);
+  return fma(r, fma(-q, r, 1.0), r);
+}
+
 // One step of the LDL^T pivot recurrence q' = (d - x) - e^2 / q; a pivot
-// smaller than pivmin is replaced by -pivmin.
+// smaller than pivmin is replaced by -pivmin. The counts take one Newton
+// step on the reciprocal estimate (about 2^-50).
 __device__ __forceinline__ double ldl_next(double dmx, double e2, double q, double pivmin) {
-  q = dmx - e2 / q;
+  double rq = __builtin_amdgcn_rcp(q);
+  rq = fma(rq, fma(-q, rq, 1.0), rq);
+  q = fma(-e2, rq, dmx);
   return fabs(q) < pivmin ? -pivmin : q;
 }
 __device__ __forceinline__ double ldl_start(double dmx, double pivmin) { return fabs(dmx) < pivmin ? -pivmin : dmx; }
@@ -370,40 +440,69 @@ __global__ void __launch_bounds__(kWT) weig_vectors_kernel(const double *__restr
   if (t < k) {
     const int c = t;
     const double lm = lam[c];
+    double *zc = Z + c, *mc = Dm + c;
     double dp = ldl_start(s.d[0] - lm, pivmin);
-    Z[c] = dp;
+    zc[0] = dp;
     for (int q = 0; q + 1 < l; ++q) {
       dp = ldl_next(s.d[q + 1] - lm, s.e2[q], dp, pivmin);
-      Z[(int64_t)(q + 1) * lp + c] = dp;
+      zc[(int64_t)(q + 1) * lp] = dp;
     }
+    // bottom-up pivots and the twist; D+ read back eight rows at a time
     double dm = ldl_start(s.d[l - 1] - lm, pivmin);
-    Dm[(int64_t)(l - 1) * lp + c] = dm;
-    double gmin = fabs(Z[(int64_t)(l - 1) * lp + c] + dm - (s.d[l - 1] - lm));
+    mc[(int64_t)(l - 1) * lp] = dm;
+    double gmin = fabs(dp + dm - (s.d[l - 1] - lm));
     int r = l - 1;
-    for (int q = l - 2; q >= 0; --q) {
-      dm = ldl_next(s.d[q] - lm, s.e2[q], dm, pivmin);
-      Dm[(int64_t)q * lp + c] = dm;
-      const double g = fabs(Z[(int64_t)q * lp + c] + dm - (s.d[q] - lm));
-      if (g < gmin) {
-        gmin = g;
-        r = q;
+    for (int q0 = l - 2; q0 >= 0; q0 -= 8) {
+      double pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = q0 - u >= 0 ? zc[(int64_t)(q0 - u) * lp] : 1.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 - u;
+        if (q >= 0) {
+          dm = ldl_next(s.d[q] - lm, s.e2[q], dm, pivmin);
+          mc[(int64_t)q * lp] = dm;
+          const double g = fabs(pv[u] + dm - (s.d[q] - lm));
+          if (g < gmin) {
+            gmin = g;
+            r = q;
+          }
+        }
       }
     }
     double z = 1.0, nrm2 = 1.0;
-    for (int q = r - 1; q >= 0; --q) {
-      z = -(s.e[q] / Z[(int64_t)q * lp + c]) * z;
-      Z[(int64_t)q * lp + c] = z;
-      nrm2 = fma(z, z, nrm2);
+    for (int q0 = r - 1; q0 >= 0; q0 -= 8) {
+      double pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = q0 - u >= 0 ? zc[(int64_t)(q0 - u) * lp] : 1.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 - u;
+        if (q >= 0) {
+          z = -(s.e[q] * recip(pv[u])) * z;
+          zc[(int64_t)q * lp] = z;
+          nrm2 = fma(z, z, nrm2);
+        }
+      }
     }
-    Z[(int64_t)r * lp + c] = 1.0;
+    zc[(int64_t)r * lp] = 1.0;
     z = 1.0;
-    for (int q = r + 1; q < l; ++q) {
-      z = -(s.e[q - 1] / Dm[(int64_t)q * lp + c]) * z;
-      Z[(int64_t)q * lp + c] = z;
-      nrm2 = fma(z, z, nrm2);
+    for (int q0 = r + 1; q0 < l; q0 += 8) {
+      double mv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mv[u] = q0 + u < l ? mc[(int64_t)(q0 + u) * lp] : 1.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + u;
+        if (q < l) {
+          z = -(s.e[q - 1] * recip(mv[u])) * z;
+          zc[(int64_t)q * lp] = z;
+          nrm2 = fma(z, z, nrm2);
+        }
+      }
     }
     const double inv = 1.0 / sqrt(nrm2);
-    for (int q = 0; q < l; ++q) Z[(int64_t)q * lp + c] *= inv;
+    for (int q = 0; q < l; ++q) zc[(int64_t)q * lp] *= inv;
   }
   if (t == 0) {
     int any = 0;
@@ -458,35 +557,36 @@ __global__ void __launch_bounds__(kWT) weig_back_kernel(double *__restrict__ Z, 
                                                         const double *__restrict__ beta) {
   const int lane = threadIdx.x & 63, c = blockIdx.x * (kWT / 64) + (threadIdx.x >> 6);
   if (c >= k) return;
-  double z[kWC], v[kWC], vn[kWC];
+  constexpr int D = 4;  // reflectors loaded ahead of the one being applied
+  double z[kWC], v[D][kWC];
 #pragma unroll
   for (int u = 0; u < kWC; ++u) {
     const int q = lane + 64 * u;
     z[u] = q < l ? Z[(int64_t)q * lp + c] : 0.0;
   }
-  int j = l - 3;
-  if (j >= 0) {
+  auto load = [&](int j, double (&dst)[kWC]) {
 #pragma unroll
     for (int u = 0; u < kWC; ++u) {
       const int q = lane + 64 * u;
-      v[u] = q < lp ? V[(int64_t)j * lp + q] : 0.0;
+      dst[u] = (j >= 0 && q < lp) ? V[(int64_t)j * lp + q] : 0.0;
     }
-  }
-  for (; j >= 0; --j) {
-    const double bj = beta[j];
+  };
+  const int j_top = l - 3;
 #pragma unroll
-    for (int u = 0; u < kWC; ++u) {
-      const int q = lane + 64 * u;
-      vn[u] = (j > 0 && q < lp) ? V[(int64_t)(j - 1) * lp + q] : 0.0;
-    }
-    double part = 0.0;
+  for (int d = 0; d < D; ++d) load(j_top - d, v[d]);
+  for (int j0 = j_top; j0 >= 0; j0 -= D) {
 #pragma unroll
-    for (int u = 0; u < kWC; ++u) part = fma(v[u], z[u], part);
-    const double sc = bj * wave_sum0(part);
+    for (int d = 0; d < D; ++d) {
+      const int j = j0 - d;
+      if (j >= 0) {
+        double part = 0.0;
 #pragma unroll
-    for (int u = 0; u < kWC; ++u) {
-      z[u] = fma(-sc, v[u], z[u]);
-      v[u] = vn[u];
+        for (int u = 0; u < kWC; ++u) part = fma(v[d][u], z[u], part);
+        const double sc = beta[j] * wave_sum0(part);
+#pragma unroll
+        for (int u = 0; u < kWC; ++u) z[u] = fma(-sc, v[d][u], z[u]);
+      }
+      load(j - D, v[d]);
     }
   }
 #pragma unroll
@@ -496,6 +596,141 @@ __global__ void __launch_bounds__(kWT) weig_back_kernel(double *__restrict__ Z, 
   }
 }
 
+// out[r][c] = (sum_q x[r][q] E[q][c]) * colscale[c] for r < rows, c < k,
+// fp64 sums over q in order, rounded once to fp32: 64 x 64 tiles of out, x
+// and E staged through LDS 32 q at a time, 4 x 4 outputs per thread. With
+// am_val, the tile's argmax of |out[:, c]| (lowest row on ties) goes to
+// am_val / am_idx[tile row * k + c].
+__global__ void __launch_bounds__(kWT) wassemble_kernel(const float *__restrict__ x, int64_t rows, int l, int lp,
+                                                        int k, const double *__restrict__ E,
+                                                        const double *__restrict__ colscale, float *__restrict__ out,
+                                                        float *__restrict__ am_val, int *__restrict__ am_idx) {
+  __shared__ double xs[64][33];
+  __shared__ double es[32][65];
+  __shared__ float bvs[16][64], bsg[16][64];
+  __shared__ int bis[16][64];
+  const int t = threadIdx.x, ti = t >> 4, tj = t & 15;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int q0 = 0; q0 < l; q0 += 32) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = t + kWT * u, rr = e >> 5, qq = e & 31;
+      const int64_t row = r0 + rr;
+      xs[rr][qq] = (row < rows && q0 + qq < l) ? (double)x[row * l + q0 + qq] : 0.0;
+      const int qe = e >> 6, cc = e & 63;
+      es[qe][cc] = (q0 + qe < l && c0 + cc < k) ? E[(int64_t)(q0 + qe) * lp + c0 + cc] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int q = 0; q < 32; ++q) {
+      double xv[4], ev[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        xv[a] = xs[ti * 4 + a][q];
+        ev[a] = es[q][tj * 4 + a];
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fma(xv[a], ev[b], acc[a][b]);
+    }
+  }
+  float best[4], bsig[4];
+  int bidx[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    best[b] = -1.0f;
+    bsig[b] = 0.0f;
+    bidx[b] = 0x7FFFFFFF;
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int64_t row = r0 + ti * 4 + a;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c = c0 + tj * 4 + b;
+      if (row < rows && c < k) {
+        const float v = (float)(colscale ? acc[a][b] * colscale[c] : acc[a][b]);
+        out[row * k + c] = v;
+        if (fabsf(v) > best[b]) {
+          best[b] = fabsf(v);
+          bsig[b] = v;
+          bidx[b] = (int)row;
+        }
+      }
+    }
+  }
+  if (!am_val) return;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    bvs[ti][tj * 4 + b] = best[b];
+    bsg[ti][tj * 4 + b] = bsig[b];
+    bis[ti][tj * 4 + b] = bidx[b];
+  }
+  __syncthreads();
+  if (t < 64 && c0 + t < k) {
+    float ba = -1.0f, val = 0.0f;
+    int bi = 0x7FFFFFFF;
+    for (int g = 0; g < 16; ++g)
+      if (bvs[g][t] > ba) {
+        ba = bvs[g][t];
+        val = bsg[g][t];
+        bi = bis[g][t];
+      }
+    am_val[blockIdx.x * k + c0 + t] = val;
+    am_idx[blockIdx.x * k + c0 + t] = bi;
+  }
+}
+
+
+template <int NC>
+void chol_steps(double *C, double *F, int l, const double *aux, hipStream_t st) {
+  for (int j0 = 0; j0 < l; j0 += kPiv) {
+    const int below = l - std::min(j0 + kPiv, l);
+    const unsigned grid = (unsigned)std::max<int64_t>(1, cdiv(below, kWT / 64));
+    wchol_step_kernel<NC><<<grid, kWT, 0, st>>>(C, F, l, j0, aux);
+  }
+}
+
+template <int NC>
+void tri_steps(double *W, int l, double *V, double *beta, double *dg, double *eo, double *pbuf, hipStream_t st) {
+  for (int j = -1; j <= l - 3 || j == -1; ++j) {
+    const int below = l - (j + 2);
+    const unsigned grid = (unsigned)std::max<int64_t>(1, cdiv(std::max(below, 0), kWT / 64));
+    wtri_step_kernel<NC><<<grid, kWT, 0, st>>>(W, l, j, V, beta, dg, eo, pbuf);
+  }
+}
+
+// The column count lp / 64 as a compile-time constant (lp a multiple of 64).
+template <template <int> class Fn, typename... Args>
+bool by_columns(int lp, Args... args) {
+  switch (lp / 64) {
+    case 2: Fn<2>::run(args...); return true;
+    case 3: Fn<3>::run(args...); return true;
+    case 4: Fn<4>::run(args...); return true;
+    case 5: Fn<5>::run(args...); return true;
+    case 6: Fn<6>::run(args...); return true;
+    case 7: Fn<7>::run(args...); return true;
+    case 8: Fn<8>::run(args...); return true;
+  }
+  return false;
+}
+template <int NC> struct CholSteps {
+  static void run(double *C, double *F, int l, const double *aux, hipStream_t st) { chol_steps<NC>(C, F, l, aux, st); }
+};
+template <int NC> struct TriSteps {
+  static void run(double *W, int l, double *V, double *beta, double *dg, double *eo, double *pbuf, hipStream_t st) {
+    tri_steps<NC>(W, l, V, beta, dg, eo, pbuf, st);
+  }
+};
+
 }  // namespace
 
 namespace metis_wide {
@@ -504,30 +739,31 @@ size_t aux_doubles(int lp) { return (size_t)8 * lp + 64; }
 
 metis_status_t wide_chol_inv(const double *g, int l, int lp, double *rinv, int *info, double *C, double *F,
                              double *aux, hipStream_t st) {
-  if (l < 1 || l > kWideMax || lp < l || lp > kWideMax) return METIS_ERR_UNSUPPORTED;
+  if (l < 1 || l > kWideMax || lp < l || lp > kWideMax || lp % 64 || lp < 128) return METIS_ERR_UNSUPPORTED;
   const unsigned fill = (unsigned)cdiv((int64_t)lp * lp, kWT);
   wchol_init_kernel<<<fill, kWT, 0, st>>>(g, l, lp, C, aux);
-  for (int j0 = 0; j0 < l; j0 += kPiv) {
-    const int below = l - std::min(j0 + kPiv, l);
-    const unsigned grid = (unsigned)std::max<int64_t>(1, cdiv(below, kWT / 64));
-    wchol_step_kernel<<<grid, kWT, 0, st>>>(C, F, l, lp, j0, aux);
-  }
+  by_columns<CholSteps>(lp, C, F, l, (const double *)aux, st);
   wchol_finish_kernel<<<fill, kWT, 0, st>>>(F, l, lp, aux, rinv, info);
+  return hipGetLastError() == hipSuccess ? METIS_OK : METIS_ERR_HIP;
+}
+
+metis_status_t wide_assemble(const float *x, int64_t rows, int l, int lp, int k, const double *evec,
+                             const double *colscale, float *out, float *am_val, int *am_idx, hipStream_t st) {
+  if (rows <= 0) return METIS_OK;
+  wassemble_kernel<<<dim3((unsigned)cdiv(rows, 64), (unsigned)cdiv(k, 64)), kWT, 0, st>>>(x, rows, l, lp, k, evec,
+                                                                                        colscale, out, am_val, am_idx);
   return hipGetLastError() == hipSuccess ? METIS_OK : METIS_ERR_HIP;
 }
 
 metis_status_t wide_eigh(const double *g, int l, int lp, int k, double *evec, double *sig_inv, float *S, double *W,
                          double *V, double *Dm, double *aux, hipStream_t st) {
-  if (l < 1 || l > kWideMax || lp < l || lp > kWideMax || k < 1 || k > l || k > kWT) return METIS_ERR_UNSUPPORTED;
+  if (l < 1 || l > kWideMax || lp < l || lp > kWideMax || lp % 64 || lp < 128 || k < 1 || k > l || k > kWT)
+    return METIS_ERR_UNSUPPORTED;
   double *dg = aux, *eo = aux + lp, *beta = aux + 2 * lp, *pbuf = aux + 3 * lp, *lam = aux + 5 * lp,
          *tn = aux + 6 * lp;
   const unsigned fill = (unsigned)cdiv((int64_t)lp * lp, kWT);
   wtri_init_kernel<<<fill, kWT, 0, st>>>(g, l, lp, W);
-  for (int j = -1; j <= l - 3 || j == -1; ++j) {
-    const int below = l - (j + 2);
-    const unsigned grid = (unsigned)std::max<int64_t>(1, cdiv(std::max(below, 0), kWT / 64));
-    wtri_step_kernel<<<grid, kWT, 0, st>>>(W, l, lp, j, V, beta, dg, eo, pbuf);
-  }
+  by_columns<TriSteps>(lp, W, l, V, beta, dg, eo, pbuf, st);
   weig_values_kernel<<<(unsigned)cdiv(k, kWT / 64), kWT, 0, st>>>(dg, eo, l, k, lam, tn);
   weig_vectors_kernel<<<1, kWT, 0, st>>>(dg, eo, l, lp, k, lam, evec, Dm, sig_inv, S);
   weig_back_kernel<<<(unsigned)cdiv(k, kWT / 64), kWT, 0, st>>>(evec, l, lp, k, V, beta);

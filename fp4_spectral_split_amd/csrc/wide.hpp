@@ -26,4 +26,10 @@ metis_status_t wide_chol_inv(const double *g, int l, int lp, double *rinv, int *
 metis_status_t wide_eigh(const double *g, int l, int lp, int k, double *evec, double *sig_inv, float *S, double *W,
                          double *V, double *Dm, double *aux, hipStream_t st);
 
+// out (rows x k, fp32) = x (rows x l fp32) E[:, :k] diag(colscale) (colscale
+// may be NULL), fp64 sums; with am_val / am_idx (may be NULL), per tile of 64
+// rows the argmax of |out[:, c]| (lowest row on ties) at [tile * k + c].
+metis_status_t wide_assemble(const float *x, int64_t rows, int l, int lp, int k, const double *evec,
+                             const double *colscale, float *out, float *am_val, int *am_idx, hipStream_t st);
+
 }  // namespace metis_wide
