@@ -508,8 +508,11 @@ def main():
     torch.cuda.synchronize()
     log("warmup done (%d steps)" % args.warmup)
     t0 = time.perf_counter()
+    host_s = 0.0
     for i in range(args.steps):
+        h0 = time.perf_counter()
         step(i)
+        host_s += time.perf_counter() - h0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -529,6 +532,7 @@ def main():
                    round(total_flops / 1e9, 2)},
         "split_ms": {n: round(v, 4) for n, v in split_ms.items()},
         "gemm_main_ms": {o: round(v, 4) for o, v in main_ms.items()},
+        "host_enqueue_ms_per_step": round(host_s * 1e3 / args.steps, 4),
     }
     torch.cuda.synchronize()
     if not args.no_legs:
