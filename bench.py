@@ -35,6 +35,8 @@ stream the kernels run on):
                  (fwd), the 8B attention projection (fwd + dX), and the NVFP4
                  + 512-column-sampling down projection (fwd + bwd);
   mean_split, power_split   the two extra split variants on the FFN tensors;
+  optim          the dual-range regularizer on W_up and the adaptive spectral
+                 learning rate on the step's dW_up;
   cpu_baseline   the fp64 oracle on a bounded sample (one full split and one
                  full GEMM of the step), extrapolated to the step.
 
@@ -345,6 +347,34 @@ def power_split_leg(torch, ops, reps=5):
     return {"tensor": "X_up 8192x4096 bf16, k 64, l 80", **out}
 
 
+def optim_leg(torch, ops, reps=10):
+    """The optimizer-side kernels timed alone: the dual-range regularizer
+    (loss and gradient) on W_up, and the adaptive spectral learning rate on
+    the fp32 dW_up of the step (its split at k = 64, l = 80 first, untimed).
+    HBM rate against algorithmic bytes (regularizer: W read, gradient
+    written; rescale: G read and written)."""
+    M = ops.M
+    out = {}
+    W = ops.A["W_up"]
+    e = W.numel()
+    loss, grad = M.metis_dual_range_reg(W, 0.002, 0.05, 10.0, 100.0)
+    torch.cuda.synchronize()
+    ms = statistics.median(timed_ms(torch, lambda: M.metis_dual_range_reg(W, 0.002, 0.05, 10.0, 100.0, grad=grad),
+                                    reps))
+    nb = 2 * e + 4 * e
+    out["dual_range_W_up"] = {"ms": round(ms, 4), "GB/s": round(nb / (ms / 1e3) / 1e9, 1), "algorithmic_bytes": nb}
+    G = ops.outs["dW_up"]
+    t = ops.tensors["W_up"]
+    om = ops.sk["W_up"]["omega"]
+    rec = M.metis_split(G, t.l, t.k, "mxfp4", omega=om, orientations=("n",))
+    torch.cuda.synchronize()
+    ms = statistics.median(timed_ms(torch, lambda: M.metis_spectral_lr_rescale(G, rec, 8, 8.0), reps))
+    nb = 8 * G.numel()
+    out["spectral_lr_dW_up"] = {"ms": round(ms, 4), "GB/s": round(nb / (ms / 1e3) / 1e9, 1),
+                                "algorithmic_bytes": nb, "k": t.k, "r_ref": 8, "gamma_max": 8.0}
+    return out
+
+
 def profile_splits(torch, ops, reps):
     """For kernel profiles of the split and quantize kernels alone (their HBM
     rate is read from the profiler, not printed): each of the six spectral
@@ -542,6 +572,7 @@ def main():
         log("split HBM leg done")
         line["mean_split"] = mean_split_leg(torch, M, ops.A, tensors)
         line["power_split"] = power_split_leg(torch, ops)
+        line["optim"] = optim_leg(torch, ops)
         cfgs = [int(c) for c in args.configs.split(",") if c.strip()]
         if cfgs:
             line["configs"] = {}

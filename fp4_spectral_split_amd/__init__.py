@@ -13,6 +13,8 @@ Calls (same names as the C ABI in include/metis_fp4.h):
   spectral_fp4_linear_fwd(X, W)                -> Y = X W^T
   spectral_fp4_linear_fwd_noalloc(X, W, out)   -> the same, static scratch
   spectral_fp4_linear_bwd(dY, X, W)            -> (dX = dY W, dW = dY^T X)
+  metis_spectral_lr_rescale(G, rec, r, gmax)   -> G rescaled in place
+  metis_dual_range_reg(W, ...)                 -> (loss, grad)
 """
 import ctypes
 import os
@@ -90,6 +92,13 @@ def load():
     L.spectral_fp4_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_Split), ctypes.POINTER(_Split), vp, i64, vp]
     L.spectral_fp4_linear_bwd.restype = i32
     L.spectral_fp4_linear_bwd.argtypes = [ctypes.POINTER(_Split)] * 3 + [vp, i64, vp, i64, vp, sz, vp]
+    L.metis_spectral_lr_rescale.restype = i32
+    L.metis_spectral_lr_rescale.argtypes = [vp, i64, i64, i64, vp, vp, vp, i32, i32, ctypes.c_float, vp]
+    L.metis_dual_range_workspace_bytes.restype = sz
+    L.metis_dual_range_workspace_bytes.argtypes = []
+    L.metis_dual_range_reg.restype = i32
+    L.metis_dual_range_reg.argtypes = [vp, i32, i64, i64, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_float, vp, i64, i32, vp, vp, sz, vp]
     sp = ctypes.POINTER(_Split)
     L.metis_gemm_nt_workspace_bytes.restype = sz
     L.metis_gemm_nt_workspace_bytes.argtypes = [sp, i32, sp, i32]
@@ -106,7 +115,8 @@ EXPORTS = ["metis_status_str", "metis_abi_version", "fp4_block_quant_workspace_b
            "metis_split_power", "metis_mean_split_workspace_bytes",
            "metis_mean_split", "metis_linear_workspace_bytes",
            "spectral_fp4_linear_fwd", "spectral_fp4_linear_fwd_noalloc", "spectral_fp4_linear_bwd", "metis_gemm_nt_workspace_bytes",
-           "metis_gemm_nt_prepare", "metis_gemm_nt_main"]
+           "metis_gemm_nt_prepare", "metis_gemm_nt_main", "metis_spectral_lr_rescale",
+           "metis_dual_range_workspace_bytes", "metis_dual_range_reg"]
 
 
 def _check(status):
@@ -397,3 +407,33 @@ class GemmNT:
         self.prepare()
         return self.main(out)
 
+
+def metis_spectral_lr_rescale(G, rec, r_ref, gamma_max):
+    """Adaptive spectral learning rate: G (fp32, m x n) rescaled in place along
+    the split rec of G (its fp32 U, S, V): G += U diag(S (gamma - 1)) V^T."""
+    L = load()
+    assert G.dtype == torch.float32 and G.is_cuda and G.stride(1) == 1 and rec.k > 0
+    m, n = G.shape
+    _check(L.metis_spectral_lr_rescale(_ptr(G), m, n, G.stride(0), _ptr(rec.U), _ptr(rec.S), _ptr(rec.V), rec.k,
+                                       int(r_ref), float(gamma_max), _stream(G.device)))
+    return G
+
+
+def metis_dual_range_reg(W, tau_lo, tau_hi, lam_lo, lam_hi, grad=None, accumulate=False, want_grad=True):
+    """Dual-range regularizer of a 2-D fp32/bf16 CUDA tensor W: returns
+    (loss as a 1-element fp64 tensor, grad as fp32 or None). With grad given
+    and accumulate=True the gradient is added to it."""
+    L = load()
+    assert W.dim() == 2 and W.is_cuda and W.stride(1) == 1
+    rows, cols = W.shape
+    if want_grad and grad is None:
+        grad = torch.empty(rows, cols, dtype=torch.float32, device=W.device)
+        accumulate = False
+    loss = torch.empty(1, dtype=torch.float64, device=W.device)
+    nws = L.metis_dual_range_workspace_bytes()
+    ws = workspace(nws, W.device)
+    _check(L.metis_dual_range_reg(_ptr(W), _dtype_code(W), rows, cols, W.stride(0), float(tau_lo), float(tau_hi),
+                                  float(lam_lo), float(lam_hi), _ptr(grad) if want_grad else None,
+                                  grad.stride(0) if want_grad else 0, int(bool(accumulate)), _ptr(loss), _ptr(ws), nws,
+                                  _stream(W.device)))
+    return loss, grad

@@ -264,6 +264,47 @@ metis_status_t metis_gemm_nt_prepare(const metis_split_t *a, int32_t a_trans, co
 metis_status_t metis_gemm_nt_main(const metis_split_t *a, int32_t a_trans, const metis_split_t *b, int32_t b_trans,
                                   float *C, int64_t ldc, const void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Adaptive spectral learning rate (SII post on Metis, §2.4 item 2; the
+ * earlier version's abstract, chatpaper.ai page, item (ii)): the gradient
+ * along a split's mid and low singular directions is scaled up by the
+ * inverse of its normalized singular value, the dominant directions and the
+ * unresolved tail R left as they are. With the split G = U diag(S) V^T + R of
+ * the gradient (metis_split of G):
+ *   gamma_i = min(gamma_max, max(1, S[r_ref] / S_i))  (1 where S_i = 0),
+ *   G <- G + U diag(S (gamma - 1)) V^T,   in place.
+ *  G:  m x n fp32, leading dimension ldg >= n (device).
+ *  U (m x k), S (k, descending), V (n x k): fp32 row-major, as in a split
+ *      record of G (device).
+ *  1 <= k <= 96, 0 <= r_ref < k, gamma_max >= 1 (else METIS_ERR_INVALID;
+ *  k > 96: METIS_ERR_UNSUPPORTED).
+ * The rank-k term is summed in fp32 in ascending i and added to G once. */
+metis_status_t metis_spectral_lr_rescale(float *G, int64_t m, int64_t n, int64_t ldg, const float *U,
+                                         const float *S, const float *V, int32_t k, int32_t r_ref, float gamma_max,
+                                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Dual-range regularizer (SII post on Metis, §2.4 item 3; chatpaper.ai
+ * abstract, item (iii)): a penalty that restrains oversized values and
+ * suppresses near-zero ones, compressing a parameter tensor's range. Two-sided
+ * hinge on each element w of W:
+ *   loss = lam_hi sum relu(|w| - tau_hi)^2 + lam_lo sum_{w != 0} relu(tau_lo - |w|)^2,
+ *   dloss/dw = 2 lam_hi relu(|w| - tau_hi) sign(w) - 2 lam_lo relu(tau_lo - |w|) sign(w).
+ *  W:     rows x cols of type dt (leading dimension ldw >= cols; cols % 8 == 0;
+ *         16-byte aligned rows).
+ *  grad:  optional fp32 rows x cols (ldg >= cols, 16-byte aligned rows): the
+ *         gradient, stored (accumulate == 0) or added to what is there
+ *         (accumulate != 0). Each gradient value is formed in fp64 and rounded
+ *         once to fp32 (after the addition when accumulating).
+ *  loss:  optional device fp64 scalar; needs ws of
+ *         metis_dual_range_workspace_bytes() bytes (8-byte aligned), and is
+ *         summed in a fixed order (bitwise reproducible).
+ *  0 <= tau_lo <= tau_hi, lam_lo, lam_hi >= 0 (else METIS_ERR_INVALID). */
+size_t metis_dual_range_workspace_bytes(void);
+metis_status_t metis_dual_range_reg(const void *W, metis_dtype_t dt, int64_t rows, int64_t cols, int64_t ldw,
+                                    float tau_lo, float tau_hi, float lam_lo, float lam_hi, float *grad, int64_t ldg,
+                                    int32_t accumulate, double *loss, void *ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

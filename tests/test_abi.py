@@ -147,3 +147,24 @@ def test_split_power_rejects_bad_arguments_on_host():
     assert ok(q=17) == 2                                   # more iterations than this build takes
     assert ok(q=1, l=128, m=1024, n=1024, ws_bytes=1 << 40) == 2  # wide sketches take no iterations
     assert ok(q=1, ws_bytes=n0) == 3                       # the q = 0 workspace is too small
+
+
+def test_optim_calls_reject_bad_arguments_on_host():
+    L = M.load()
+    f = ctypes.c_void_p(256)
+    # spectral rescale: k out of range, r_ref out of range, gamma_max < 1, k > 96
+    assert L.metis_spectral_lr_rescale(f, 8, 8, 8, f, f, f, 0, 0, 2.0, None) == 1
+    assert L.metis_spectral_lr_rescale(f, 8, 8, 8, f, f, f, 4, 4, 2.0, None) == 1
+    assert L.metis_spectral_lr_rescale(f, 8, 8, 8, f, f, f, 4, 1, 0.5, None) == 1
+    assert L.metis_spectral_lr_rescale(f, 8, 8, 8, f, f, f, 97, 1, 2.0, None) == 2
+    assert L.metis_spectral_lr_rescale(f, 8, 8, 4, f, f, f, 4, 1, 2.0, None) == 1  # ldg < n
+    assert L.metis_spectral_lr_rescale(None, 0, 8, 8, None, None, None, 4, 1, 2.0, None) == 0  # empty
+    # dual-range: cols % 8, tau order, negative lambda, missing workspace for the loss
+    ws = L.metis_dual_range_workspace_bytes()
+    assert ws > 0
+    assert L.metis_dual_range_reg(f, 1, 4, 12, 12, 0.1, 1.0, 1.0, 1.0, f, 12, 0, None, None, 0, None) == 1
+    assert L.metis_dual_range_reg(f, 1, 4, 16, 16, 1.0, 0.1, 1.0, 1.0, f, 16, 0, None, None, 0, None) == 1
+    assert L.metis_dual_range_reg(f, 1, 4, 16, 16, 0.1, 1.0, -1.0, 1.0, f, 16, 0, None, None, 0, None) == 1
+    assert L.metis_dual_range_reg(f, 1, 4, 16, 16, 0.1, 1.0, 1.0, 1.0, f, 16, 0, f, None, 0, None) == 3
+    assert L.metis_dual_range_reg(f, 7, 4, 16, 16, 0.1, 1.0, 1.0, 1.0, f, 16, 0, None, None, 0, None) == 1
+
