@@ -376,10 +376,11 @@ def optim_leg(torch, ops, reps=10):
 
 
 def profile_splits(torch, ops, reps):
-    """For kernel profiles of the split and quantize kernels alone (their HBM
-    rate is read from the profiler, not printed): each of the six spectral
-    splits reps times back to back on one stream, then the standalone MXFP4
-    quantizer on X_up in both orientations reps times. Replaces the steps."""
+    """For kernel profiles of the step's kernels alone (their durations and
+    HBM rates are read from the profiler, not printed): each of the six
+    spectral splits reps times back to back on one stream, the standalone
+    MXFP4 quantizer on X_up in both orientations reps times, then each of the
+    six GEMMs (prepare + main) reps times. Replaces the steps."""
     for n in ops.tensors:
         for _ in range(reps):
             ops.split(n)
@@ -391,6 +392,11 @@ def profile_splits(torch, ops, reps):
         ops.M.fp4_block_quant(x, "mxfp4", transpose=True)
     torch.cuda.synchronize()
     log("profiled fp4_block_quant X_up (both orientations) x %d" % reps)
+    for out in ops.gobj:
+        for _ in range(reps):
+            ops.gemm(out)
+        torch.cuda.synchronize()
+        log("profiled GEMM %s (prepare + main) x %d" % (out, reps))
 
 
 def cpu_model():
@@ -452,7 +458,8 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain copy of MIB MiB ahead of the steps (counter calibration)")
     ap.add_argument("--profile-splits", type=int, default=0, metavar="REPS",
-                    help="instead of the steps, run each split and the quantizer REPS times alone (for profiles)")
+                    help="instead of the steps, run each split, the quantizer and each GEMM REPS times alone "
+                         "(for profiles)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "

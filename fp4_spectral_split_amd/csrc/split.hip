@@ -173,12 +173,22 @@ __global__ void fill_u32(uint32_t *p, uint32_t v, int count) {
 }
 
 // Omega (n x l bf16, row-major) -> Omega^T (lp x n), rows l..lp-1 zero.
-__global__ void omega_transpose_kernel(const unsigned short *__restrict__ om, int64_t n, int l, int lp,
-                                       unsigned short *__restrict__ omt) {
-  const int64_t j = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int c = blockIdx.y;
-  if (j >= n) return;
-  omt[(int64_t)c * n + j] = c < l ? om[j * l + c] : (unsigned short)0;
+// 64 rows of Omega per workgroup through an LDS tile: the rows are read as
+// one contiguous block and the columns written contiguously.
+constexpr int kOtRows = 64;
+__global__ void __launch_bounds__(256) omega_transpose_kernel(const unsigned short *__restrict__ om, int64_t n, int l,
+                                                              int lp, unsigned short *__restrict__ omt) {
+  __shared__ unsigned short tile[metis_wide::kWideMax][kOtRows + 2];  // l <= 512 columns
+  const int t = threadIdx.x;
+  const int64_t j0 = (int64_t)blockIdx.x * kOtRows;
+  const int rows = (int)std::min<int64_t>(kOtRows, n - j0);
+  const unsigned short *src = om + j0 * l;
+  for (int e = t; e < rows * l; e += 256) tile[e % l][e / l] = src[e];
+  __syncthreads();
+  for (int e = t; e < lp * kOtRows; e += 256) {
+    const int c = e / kOtRows, jj = e % kOtRows;
+    if (jj < rows) omt[(int64_t)c * n + j0 + jj] = c < l ? tile[c][jj] : (unsigned short)0;
+  }
 }
 
 // ================================================================== sketch
@@ -1954,8 +1964,8 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
   const float *ysrc;
   int yparts;
   if (p.kind == METIS_OMEGA_GAUSSIAN) {
-    omega_transpose_kernel<<<dim3((unsigned)cdiv(n, 256), lp), 256, 0, st>>>((const unsigned short *)omega, n, l, lp,
-                                                                          p.omt);
+    omega_transpose_kernel<<<(unsigned)cdiv(n, kOtRows), 256, 0, st>>>((const unsigned short *)omega, n, l, lp,
+                                                                       p.omt);
     sketch_kernel<T><<<dim3((unsigned)cdiv(m, 64 * kSketchRS), p.sk, lz), kThreads, 0, st>>>(A, m, n, lda, p.omt, l, lp,
                                                                                 p.sk_chunk, p.ysk);
     ysrc = p.ysk;
