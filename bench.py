@@ -62,7 +62,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP4_PEAK_TFLOPS = 10100.0   # MI355X dense MXFP4 / NVFP4-class MFMA
-BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (the NVFP4 GEMM runs on it)
+F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA (the NVFP4 GEMM runs on it)
 HBM_PEAK_GBS = 8000.0
 CFG = 4
 HW_QUEUES = 8
@@ -308,7 +308,7 @@ def config_leg(torch, np, M, synth, cfg, dev, steps, warmup):
            "main_gemm_TFLOP/s": round(main_tf, 2),
            "main_gemm_frac_fp4_peak": round(main_tf / FP4_PEAK_TFLOPS, 4)}
     if fmt == "nvfp4":
-        out["main_gemm_frac_bf16_peak"] = round(main_tf / BF16_PEAK_TFLOPS, 4)
+        out["main_gemm_frac_f16_peak"] = round(main_tf / F16_PEAK_TFLOPS, 4)
     log("config %d: %.3f ms/step, main GEMMs %.0f TFLOP/s" % (cfg, step_ms, main_tf))
     del ops
     torch.cuda.synchronize()

@@ -20,6 +20,8 @@ typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short ushortx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float(((uint32_t)b) << 16); }

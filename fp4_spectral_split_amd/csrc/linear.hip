@@ -21,9 +21,11 @@
 //                  ring, then one fp32 store (K a multiple of 512).
 //   gemm_mx8_kernel the same product for any K (register-staged loads,
 //                  correction panels staged in the epilogue).
-//   gemm_nv_kernel the NVFP4 form: E2M1 x E4M3 decoded exactly to bf16 in the
-//                  LDS staging, bf16 MFMA (gfx950's scaled MFMA takes only
-//                  E8M0 scales per 32 elements), tensor scales in the epilogue.
+//   gemm_nv_kernel the NVFP4 form: E2M1 x E4M3 decoded exactly to fp16 in the
+//                  LDS staging (hardware FP4 conversion, one packed fp16
+//                  multiply by the block scale), fp16 MFMA (gfx950's scaled
+//                  MFMA takes only E8M0 scales per 32 elements), tensor
+//                  scales in the epilogue.
 //   skinny_nv_kernel, panel_kernel<true>: the NVFP4 forms of the first two.
 #include <algorithm>
 #include <atomic>
@@ -1274,11 +1276,22 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// NVFP4: codes and E4M3 block scales are decoded exactly to bf16 while being
+// NVFP4: codes and E4M3 block scales are decoded exactly to fp16 while being
 // staged into LDS (64 contraction elements per stage), multiplied on the
-// bf16 32x32x16 MFMA with fp32 accumulation; the product of the two tensor
+// fp16 32x32x16 MFMA with fp32 accumulation; the product of the two tensor
 // scales multiplies the accumulators once before the correction. Thread t
 // stages half (t & 1) of row t >> 1 of each operand: 32 codes, two blocks.
+// Eight E2M1 codes (element 2p in the low nibble of byte p, 2p + 1 in the
+// high one) times one block scale, as fp16. The byte selector of the FP4
+// conversion is an immediate, hence the four spelled-out calls.
+__device__ __forceinline__ halfx8 fp4x8_to_f16(uint32_t word, halfx2 scale) {
+  const halfx2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * scale;
+  const halfx2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * scale;
+  const halfx2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * scale;
+  const halfx2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * scale;
+  return halfx8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+}
+
 __global__ void __launch_bounds__(kGemmThreads, 1)
     gemm_nv_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, const float *__restrict__ ats,
                    int64_t M, const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs,
@@ -1319,17 +1332,16 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     const uint32_t wb[4] = {gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      // word w holds elements 8w .. 8w+7 of this half; blocks of 16
-      const float sa = e4m3_value((gsa >> (8 * (w >> 1))) & 0xFFu);
-      const float sb = e4m3_value((gsb >> (8 * (w >> 1))) & 0xFFu);
-      ushortx8 da, db;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        da[e] = (unsigned short)(__float_as_uint(e2m1_value((wa[w] >> (4 * e)) & 15u) * sa) >> 16);
-        db[e] = (unsigned short)(__float_as_uint(e2m1_value((wb[w] >> (4 * e)) & 15u) * sb) >> 16);
-      }
-      *(ushortx8 *)(A_ + rr * NV_ROWB + (half * 32 + w * 8) * 2) = da;
-      *(ushortx8 *)(B_ + rr * NV_ROWB + (half * 32 + w * 8) * 2) = db;
+      // word w holds elements 8w .. 8w+7 of this half (block w / 2); byte p
+      // of it elements 2p (low nibble) and 2p + 1. The FP4 conversion at
+      // scale 1 gives the E2M1 values in fp16; the product with the E4M3
+      // block scale has at most five significant bits and lies in
+      // [2^-10, 2688], so the fp16 multiply is exact.
+      const _Float16 fa = (_Float16)e4m3_value((gsa >> (8 * (w >> 1))) & 0xFFu);
+      const _Float16 fb = (_Float16)e4m3_value((gsb >> (8 * (w >> 1))) & 0xFFu);
+      const halfx2 sa2 = {fa, fa}, sb2 = {fb, fb};
+      *(halfx8 *)(A_ + rr * NV_ROWB + (half * 32 + w * 8) * 2) = fp4x8_to_f16(wa[w], sa2);
+      *(halfx8 *)(B_ + rr * NV_ROWB + (half * 32 + w * 8) * 2) = fp4x8_to_f16(wb[w], sb2);
     }
   };
   load_stage(0);
@@ -1341,17 +1353,17 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     const uint8_t *A_ = smem + cur * NV_STAGE_BYTES, *B_ = A_ + BM * NV_ROWB;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      ushortx8 a8[WM], b8[WN];
+      halfx8 a8[WM], b8[WN];
 #pragma unroll
       for (int i = 0; i < WM; ++i)
-        a8[i] = *(const ushortx8 *)(A_ + (wm * 128 + i * 32 + r32) * NV_ROWB + ks * 32 + h * 16);
+        a8[i] = *(const halfx8 *)(A_ + (wm * 128 + i * 32 + r32) * NV_ROWB + ks * 32 + h * 16);
 #pragma unroll
       for (int j = 0; j < WN; ++j)
-        b8[j] = *(const ushortx8 *)(B_ + (wn * 64 + j * 32 + r32) * NV_ROWB + ks * 32 + h * 16);
+        b8[j] = *(const halfx8 *)(B_ + (wn * 64 + j * 32 + r32) * NV_ROWB + ks * 32 + h * 16);
 #pragma unroll
       for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int j = 0; j < WN; ++j) acc[i][j] = mfma32_bf16(a8[i], b8[j], acc[i][j]);
+        for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8[i], b8[j], acc[i][j], 0, 0, 0);
     }
     if (st + 1 < nst) store_stage(cur ^ 1);
     __syncthreads();
