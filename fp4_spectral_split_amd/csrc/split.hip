@@ -40,8 +40,8 @@ constexpr int kLpMax = 96;
 constexpr int kSketchRS = 2;  // 16-row groups per wave in the sketch (a workgroup: 64 kSketchRS rows)
 constexpr int kMaxPowerIterations = 16;  // Gaussian / sampled sketch width handled in LDS
 constexpr int kThreads = 256;
-constexpr int kGramRows = 128;     // rows per Gram chunk (narrow path)
-constexpr int kGramThreads = 512;  // 8 waves, 16 rows each
+constexpr int kGramRows = 64;      // rows per Gram chunk (narrow path)
+constexpr int kGramThreads = 512;  // 8 waves: two per 16-row block
 // assemble kernels: 16 rows per thread, at most 8 row groups (128 rows) per workgroup
 constexpr int kAsmRows = 16;
 constexpr int kAsmGroups = 8;
@@ -157,7 +157,7 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
   p.winv = c.take<double>((size_t)p.lp * p.lp);
   p.wg = c.take<double>((size_t)p.lp * p.lp);
   p.wv = c.take<double>((size_t)p.lp * p.lp);
-  p.waux = c.take<double>(p.wide ? metis_wide::aux_doubles(p.lp) : 0);
+  p.waux = c.take<double>(metis_wide::aux_doubles(p.lp));
   p.amax = c.take<uint32_t>(8);
   p.info_ws = c.take<int>(1);
   p.z1 = c.take<float>(q > 0 ? (size_t)n * l : 0);
@@ -378,16 +378,19 @@ __device__ __forceinline__ doublex4 mfma16_f64(double a, double b, doublex4 c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
-// One 128-row chunk of a tall matrix X (rows x l, fp32, lp = l rounded up to 16):
+// One 64-row chunk of a tall matrix X (rows x l, fp32, lp = l rounded up to 16):
 //   rinv == nullptr: X = sum of `parts` slabs of xin (fixed order);
 //   rinv != nullptr: X = xin R^-1 with fp64 products and sums (fp64 MFMA),
 //                    rounded to fp32 (R^-1 upper triangular, lp x lp).
 // X goes to xout (if given), to xt as bf16 hi/lo transposed (2 x lp x rows,
 // if given), and the fp64 Gram X^T X of the chunk (upper 16 x 16 tiles) to
-// gpart[chunk] (lp x lp, if given). Eight waves; the chunk sits in LDS. Wave
-// w applies R^-1 to rows 16 w .. 16 w + 15 in place, column tile by column
-// tile from the last (tile J reads only columns below 16 (J + 1)); then each
-// wave accumulates Gram tiles over the chunk's rows, 4 rows per MFMA.
+// gpart[chunk] (lp x lp, if given). Eight waves; the chunk sits in LDS. The
+// two waves of a 16-row block share its column tiles of xin R^-1 (tile J
+// reads columns below 16 (J + 1), so the costs differ; the tiles are dealt
+// from the last in the order 0 1 1 0 0 1 1 0 ..., which evens them out) and
+// write them to a second LDS copy; then each wave accumulates Gram tiles over
+// the chunk's rows, 4 rows per MFMA. The fp64 matrix cores bound the kernel,
+// so a chunk is kept short to spread a Gram over many workgroups.
 
 __host__ __device__ constexpr int gram_ys_stride(int lp) { return lp + 4; }                  // (lp + 4) / 4 odd
 __host__ __device__ constexpr int gram_rl_stride(int lp) { return lp % 32 == 16 ? lp : lp + 16; }  // 16 mod 32
@@ -471,7 +474,9 @@ __global__ void __launch_bounds__(kGramThreads)
                 const double *__restrict__ rinv, float *__restrict__ xout, unsigned short *__restrict__ xt,
                 double *__restrict__ gpart) {
   __shared__ __attribute__((aligned(16))) float Ys[kGramRows * (kLpMax + 4)];
+  __shared__ __attribute__((aligned(16))) float Xs[kGramRows * (kLpMax + 4)];
   __shared__ double Rl[kLpMax * (kLpMax + 16)];
+  static_assert(kGramRows == 64 && kGramThreads == 512, "four 16-row blocks, two waves each");
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, lr = lane & 15, lk = lane >> 4;
   const int S = gram_ys_stride(lp), RS = gram_rl_stride(lp), T = lp >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * kGramRows;
@@ -498,9 +503,12 @@ __global__ void __launch_bounds__(kGramThreads)
     }
   }
   __syncthreads();
+  const float *X = Ys;
   if (rinv) {
-    const int rb = 16 * wave;
+    const int rb = 16 * (wave & 3), half = wave >> 2;
     for (int J = T - 1; J >= 0; --J) {
+      const int d = (T - 1 - J) & 3;
+      if ((d == 1 || d == 2) != (half == 1)) continue;
       doublex4 acc = {0.0, 0.0, 0.0, 0.0};
       for (int s4 = 0; s4 < 4 * (J + 1); ++s4) {
         const double a = (double)Ys[(rb + lr) * S + 4 * s4 + lk];
@@ -508,14 +516,15 @@ __global__ void __launch_bounds__(kGramThreads)
         acc = mfma16_f64(a, b, acc);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Ys[(rb + lk + 4 * i) * S + 16 * J + lr] = (float)acc[i];
+      for (int i = 0; i < 4; ++i) Xs[(rb + lk + 4 * i) * S + 16 * J + lr] = (float)acc[i];
     }
     __syncthreads();
+    X = Xs;
   }
   if (xout)
     for (int idx = t; idx < kGramRows * l; idx += kGramThreads) {
       const int r = idx / l, c = idx - (idx / l) * l;
-      if (row0 + r < rows) xout[(row0 + r) * l + c] = Ys[r * S + c];
+      if (row0 + r < rows) xout[(row0 + r) * l + c] = X[r * S + c];
     }
   if (xt) {
     // 8 consecutive rows of one column per thread (16-byte stores)
@@ -526,7 +535,7 @@ __global__ void __launch_bounds__(kGramThreads)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         unsigned short h, w;
-        split_bf16(Ys[(q * 8 + e) * S + c], h, w);
+        split_bf16(X[(q * 8 + e) * S + c], h, w);
         hi[e] = h;
         lo[e] = w;
       }
@@ -547,8 +556,8 @@ __global__ void __launch_bounds__(kGramThreads)
       doublex4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
       for (int r = 0; r < kGramRows; r += 4) {
-        const double a = (double)Ys[(r + lk) * S + 16 * I + lr];
-        const double b = (double)Ys[(r + lk) * S + 16 * J + lr];
+        const double a = (double)X[(r + lk) * S + 16 * I + lr];
+        const double b = (double)X[(r + lk) * S + 16 * J + lr];
         acc = mfma16_f64(a, b, acc);
       }
 #pragma unroll
@@ -1004,414 +1013,192 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
     }
 }
 
-// ================================================ tridiagonal eigensolver
-// All wanted eigenpairs of the symmetric l x l matrix G (upper triangle read,
-// fp64) in one workgroup, in four stages:
-//   1. Householder reduction G = H T H^T to tridiagonal T (H = H_0 ... H_{l-3}).
-//      Thread (r, j) holds row r of the active block at columns j, j + 8, ...
-//      in registers; the column being reduced and p = beta A v pass through
-//      LDS, so a reflector costs two barriers. Waves whose rows are all
-//      eliminated (or beyond l) only keep the barriers.
-//   2. Eigenvalues of T by multisection on Sturm counts of the LDL^T form:
-//      eight lanes test eight points of an eigenvalue's bracket at once and
-//      keep the ninth part that holds it; no barriers. When T does not split,
-//      only the k largest are computed.
-//   3. Eigenvectors of T from twisted factorizations T - lambda I = N_r D N_r^T,
-//      the twist r where |gamma_r| is least (one thread per vector; the
-//      factorization's pivots are staged in the vector's own LDS column),
-//      Gram-Schmidt inside chains of eigenvalues closer than 1e-7 ||T||.
-//   4. Back-transformation x = H z, sixteen lanes per vector, no barriers.
-// Off-diagonals at or below 2^-52 ||T|| split T into blocks that are solved
-// separately; an eigenvalue's slot index is its place in its block.
-// Output: evec[row * lp + rank] (descending eigenvalue,
-// unit columns, zero beyond l rows and k columns), sig_inv[rank] = 1 / sigma
-// with sigma = sqrt(lambda) (0 for sigma <= 2^-24 sigma_max and for ranks
-// whose eigenvalue was not computed), S[rank < k].
-constexpr int kEigThreads = 1024;
-constexpr int kEigCols = kLpMax / 8;  // register columns of a row segment
-constexpr int kEigIters = 16;         // each keeps 1/9 of the bracket: 9^-16 < 2^-50
+// ================================================ tridiagonal reduction
+// Householder reduction of the symmetric l x l matrix G (upper triangle read,
+// fp64) to tridiagonal T = H^T G H, H = H_0 ... H_{l-3}, in one workgroup of
+// four waves with one barrier per reflector. Lane c holds columns c and
+// c + 64 of the rows r = wave + 4 i (both triangles) in registers. Step j,
+// with x = row j right of its diagonal (the reflector maps it to
+// alpha e_{j+1}: v = x - alpha e_{j+1}, beta = 2 / v.v):
+//  - by symmetry each wave's rows give a partial of A x over all columns
+//    (sum_r A[r][c] x_r, the x_r of its rows through a wave-private LDS
+//    list); the partials meet in LDS across the barrier, with a copy of row
+//    j + 1 left by its owner. Since A v = A x - alpha A[j + 1], |x|, alpha
+//    and beta (square root, reciprocal) are formed by every wave alongside
+//    the products instead of ahead of them;
+//  - after the barrier every wave sums the partials in one order, so all
+//    hold the same p = beta A v, K = beta p.v / 2 and w = p - K v; it
+//    forms row j + 1 after the update (T's diagonal entry and the next x)
+//    and applies A -= v w^T + w v^T to its rows. Rows at or above j are left
+//    as they are (v and p vanish there), and row j + 1 is never read again,
+//    so every row takes the update with v_r = x_r, branch free.
+// Columns at or left of j keep their values (p and v vanish there).
+// T (diagonal, off-diagonal), the beta_j and the reflectors go to global
+// memory for the eigenpair kernels.
+constexpr int kTriThreads = 256;
 
-// Sum over an aligned group of 16 lanes (row_ror:8 pairs the two halves).
-__device__ __forceinline__ double group16_sum(double v) {
-  v = group8_sum(v);
-  return v + dpp_f64<0x128>(v);
+// x at position idx (uniform) of a lane-distributed vector (column c in lane
+// c % 64, slot c / 64)
+template <int NS>
+__device__ __forceinline__ double lane_value(const double (&x)[NS], int idx) {
+  if (NS == 1 || idx < 64) return readlane_f64(x[0], idx & 63);
+  return readlane_f64(x[NS - 1], idx & 63);
 }
 
-// One step of the LDL^T pivot recurrence q' = (d - x) - e^2 / q, a pivot
-// smaller than pivmin replaced by -pivmin. The reciprocal estimate (about
-// 2^-25 relative) gets one Newton step, which leaves about 2^-50.
-__device__ __forceinline__ double ldl_step(double dmx, double e2, double q, double pivmin) {
-  double rq = __builtin_amdgcn_rcp(q);
-  rq = fma(rq, fma(-q, rq, 1.0), rq);
-  q = fma(-e2, rq, dmx);
-  return fabs(q) < pivmin ? -pivmin : q;
-}
-
-__device__ __forceinline__ double ldl_first(double dmx, double pivmin) { return fabs(dmx) < pivmin ? -pivmin : dmx; }
-
-// Highest set position <= p (p < 128) of the 128-bit mask (m1:m0); -1 if none.
-__device__ __forceinline__ int last_set_upto(unsigned long long m0, unsigned long long m1, int p) {
-  if (p >= 64) {
-    const unsigned long long b1 = m1 & ((2ull << (p - 64)) - 1ull);
-    if (b1) return 127 - __builtin_clzll(b1);
-    return m0 ? 63 - __builtin_clzll(m0) : -1;
-  }
-  const unsigned long long b0 = m0 & ((2ull << p) - 1ull);
-  return b0 ? 63 - __builtin_clzll(b0) : -1;
-}
-
-// Lowest set position >= p (p < 128) of (m1:m0); -1 if none.
-__device__ __forceinline__ int first_set_from(unsigned long long m0, unsigned long long m1, int p) {
-  if (p < 64) {
-    const unsigned long long c0 = m0 & ~((1ull << p) - 1ull);
-    if (c0) return __builtin_ctzll(c0);
-    return m1 ? 64 + __builtin_ctzll(m1) : -1;
-  }
-  const unsigned long long c1 = m1 & ~((1ull << (p - 64)) - 1ull);
-  return c1 ? 64 + __builtin_ctzll(c1) : -1;
-}
-
-__global__ void __launch_bounds__(kEigThreads)
-    tridiag_eig_kernel(const double *__restrict__ g, int l, int lp, int k, double *__restrict__ evec,
-                       double *__restrict__ sig_inv, float *__restrict__ S) {
-  __shared__ double V[kLpMax][kLpMax];      // V[j][r]: reflector j at rows j + 1 .. l - 1, zero elsewhere
-  __shared__ double Z[kLpMax][kLpMax + 1];  // Z[row][rank]: eigenvectors of T
-  __shared__ double xb[2][kLpMax], yb[2][kLpMax];  // columns j and j + 1 of the active block
-  __shared__ double nx2[2];                         // squared norm of xb
-  __shared__ double pv[kLpMax], dg[kLpMax], eo[kLpMax], ee[kLpMax], e2[kLpMax], bet[kLpMax], lam[kLpMax];
-  __shared__ double2 de[kLpMax];            // (d_q, e_{q-1}^2) for the Sturm counts
-  __shared__ double dots[kLpMax];
-  __shared__ int blo[kLpMax], bhi[kLpMax], slot_of[kLpMax], chain[kLpMax];
-  __shared__ double nrm_s;
-  __shared__ int any_chain;
-  const int n = l, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int r = t >> 3, cj = t & 7;
-
-  // ---- stage 1: Householder tridiagonalization. By symmetry the column
-  // being reduced at step j is row j of the active block and the column that
-  // corrects A v for the shift of v's first entry is row j + 1. Those rows'
-  // threads publish them from registers at the end of step j - 1 (x: the
-  // entries right of the diagonal, zero elsewhere, with its squared norm;
-  // y: the whole row).
-  // With x, v (in V[j]) and p zero outside rows j + 1 .. l - 1 no element
-  // needs a mask: products over eliminated columns add zero and leave their
-  // registers as they are.
-  double a[kEigCols];
+template <int NS>
+__global__ void __launch_bounds__(kTriThreads)
+    tridiag_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ dg_out,
+                   double *__restrict__ eo_out, double *__restrict__ beta_out, double *__restrict__ v_out) {
+  static_assert(kLpMax <= 128 && kLpMax % 16 == 0, "two column slots, rows below 128");
+  constexpr int RPW = NS == 1 ? 16 : kLpMax / 4;  // rows per wave: r = wave + 4 i
+  __shared__ double qp[2][4][64 * NS];
+  __shared__ double yb[2][64 * NS];
+  // per wave: x and p at its own rows (entry i: row wave + 4 i; entries
+  // RPW + lane take the writes of lanes holding other rows), written and
+  // read by that wave alone
+  __shared__ __attribute__((aligned(16))) double xl[4][RPW + 64], pl[4][RPW + 64];
+  __shared__ double td[kLpMax + 64], te[kLpMax + 64], tb[kLpMax + 64];  // T and beta (+ discard slots)
+  const int n = l, t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  double a[RPW][NS];
 #pragma unroll
-  for (int u = 0; u < kEigCols; ++u) {
-    const int c = cj + 8 * u;
-    const int lo = r < c ? r : c, hi = r < c ? c : r;
-    a[u] = (r < n && c < n) ? g[lo * lp + hi] : 0.0;
-  }
-  for (int e = t; e < kLpMax * kLpMax; e += kEigThreads) (&V[0][0])[e] = 0.0;
-  if (t < kLpMax) pv[t] = 0.0;
-  // row i's threads (r == i): x = row i right of the diagonal into xb[i & 1],
-  // its squared norm into nx2[i & 1] and the diagonal into dg
-  auto publish_row = [&](int i) {
-    double s2 = 0.0;
+  for (int i = 0; i < RPW; ++i) {
+    const int r = w + 4 * i;
 #pragma unroll
-    for (int u = 0; u < kEigCols; ++u) {
-      const int c = cj + 8 * u;
-      const double xv = c > i ? a[u] : 0.0;
-      xb[i & 1][c] = xv;
-      s2 = fma(xv, xv, s2);
-      if (c == i) dg[i] = a[u];
+    for (int s = 0; s < NS; ++s) {
+      const int c = lane + 64 * s;
+      const int lo = r < c ? r : c, hi = r < c ? c : r;
+      a[i][s] = (r < n && c < n) ? g[lo * lp + hi] : 0.0;
     }
-    const double a2 = group8_sum(s2);
-    if (cj == 0) nx2[i & 1] = a2;
+  }
+  for (int i = t; i < kLpMax; i += kTriThreads) {
+    td[i] = 0.0;
+    te[i] = 0.0;
+    tb[i] = 0.0;
+  }
+  for (int e = t; e < lp * lp; e += kTriThreads)
+    if (e >= (n > 2 ? n - 2 : 0) * lp) v_out[e] = 0.0;
+  // the wave's entries of a lane-distributed vector, by its own rows (every
+  // lane writes: those of other rows into the discard slot)
+  auto own_rows = [&](const double (&x)[NS], double *lst) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c = lane + 64 * s;
+      lst[((c & 3) == w && (c >> 2) < RPW) ? (c >> 2) : RPW + lane] = x[s];
+    }
+    __builtin_amdgcn_wave_barrier();
   };
-  __syncthreads();
-  if (r == 0) publish_row(0);
-  if (r == 1 && r < n) {
+  auto read_rows = [&](const double *lst, double (&out)[RPW]) {
 #pragma unroll
-    for (int u = 0; u < kEigCols; ++u) yb[0][cj + 8 * u] = a[u];
+    for (int i = 0; i < RPW; i += 2) {
+      const double2 d2 = *(const double2 *)&lst[i];
+      out[i] = d2.x;
+      out[i + 1] = d2.y;
+    }
+  };
+  double xv[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int c = lane + 64 * s;
+    xv[s] = (c > 0 && c < n) ? g[c] : 0.0;
   }
   __syncthreads();
+  if (t == 0) td[0] = n > 0 ? g[0] : 0.0;
+
   for (int j = 0; j + 2 < n; ++j) {
-    const double *x = xb[j & 1], *y = yb[j & 1];
-    const bool wact = 8 * wave + 7 > j && 8 * wave < n;  // the wave holds a row of the active block
-    double alpha = 0.0, beta = 0.0;
-    if (wact) {
-      // the reflector: x -> alpha e_{j+1}, v = x - alpha e_{j+1}, beta = 2 / v.v
-      const double a2 = nx2[j & 1], x0 = x[j + 1], nrm = sqrt(a2);
-      alpha = x0 >= 0.0 ? -nrm : nrm;
-      beta = a2 > 0.0 ? recip_f64(nrm * (nrm + fabs(x0))) : 0.0;
-      // (A v)_r: the alpha term is y_r = A[r][j + 1]
-      double sx = 0.0;
+    const int buf = j & 1;
+    // ---- this wave's partial of A x, and (alongside) |x|, alpha, beta
+    double xr[RPW];
+    own_rows(xv, xl[w]);
+    read_rows(xl[w], xr);
+    double q4[4][NS], x2 = 0.0;
 #pragma unroll
-      for (int u = 0; u < kEigCols; ++u) sx = fma(a[u], x[cj + 8 * u], sx);
-      const double sp = beta * fma(-alpha, y[r], group8_sum(sx));
-      if (r > j && r < n) {
-        if (cj == 0) pv[r] = sp;
-        if (cj == 1) V[j][r] = r == j + 1 ? x[r] - alpha : x[r];
-        if (cj == 2 && r == j + 1) {
-          eo[j] = alpha;
-          bet[j] = beta;
-        }
-      }
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) q4[u][s] = 0.0;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) q4[i & 3][s] = fma(a[i][s], xr[i], q4[i & 3][s]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qp[buf][w][lane + 64 * s] = (q4[0][s] + q4[1][s]) + (q4[2][s] + q4[3][s]);
+      x2 = fma(xv[s], xv[s], x2);
     }
-    if (t == 0) pv[j] = 0.0;
-    __syncthreads();
-    // A <- A - v w^T - w v^T with w = p - (beta p.v / 2) v; then rows j + 1
-    // and j + 2 publish the next step's x (with alpha, beta) and y
-    if (wact) {
-      const double p1 = pv[lane], p2 = lane + 64 < kLpMax ? pv[lane + 64] : 0.0;
-      const double v1 = V[j][lane], v2 = lane + 64 < kLpMax ? V[j][lane + 64] : 0.0;
-      const double kk = 0.5 * beta * wave_sum_f64(fma(p1, v1, p2 * v2));
-      const double vr = V[j][r], wr = fma(-kk, vr, pv[r]);
+    const double nrm2 = wave_sum_f64(x2), x0 = lane_value(xv, j + 1), nrm = sqrt(nrm2);
+    const double alpha = x0 >= 0.0 ? -nrm : nrm;
+    const double beta = nrm2 > 0.0 ? recip_f64(nrm * (nrm + fabs(x0))) : 0.0;
+    if (w == ((j + 1) & 3)) {
 #pragma unroll
-      for (int u = 0; u < kEigCols; ++u) {
-        const double vc = V[j][cj + 8 * u], wc = fma(-kk, vc, pv[cj + 8 * u]);
-        a[u] = fma(-vr, wc, fma(-wr, vc, a[u]));
-      }
-      if (r == j + 1) publish_row(j + 1);
-      if (r == j + 2 && r < n) {
+      for (int i = 0; i < RPW; ++i)
+        if (w + 4 * i == j + 1) {
 #pragma unroll
-        for (int u = 0; u < kEigCols; ++u) yb[(j + 1) & 1][cj + 8 * u] = a[u];
-      }
+          for (int s = 0; s < NS; ++s) yb[buf][lane + 64 * s] = a[i][s];
+        }
     }
     __syncthreads();
-  }
-  if (n >= 2 && t == 0) eo[n - 2] = xb[(n - 2) & 1][n - 1];  // the last off-diagonal: no reflector
-  if (r == n - 1) {
+    // ---- v, p = beta (A x - alpha A[j + 1]), K, w
+    double v[NS], pv[NS], wv[NS], pvs = 0.0;
 #pragma unroll
-    for (int u = 0; u < kEigCols; ++u)
-      if (cj + 8 * u == n - 1) dg[n - 1] = a[u];
+    for (int s = 0; s < NS; ++s) {
+      const int c = lane + 64 * s;
+      v[s] = c == j + 1 ? xv[s] - alpha : xv[s];
+      const double sum = ((qp[buf][0][c] + qp[buf][1][c]) + qp[buf][2][c]) + qp[buf][3][c];
+      pv[s] = (c > j && c < n) ? beta * fma(-alpha, yb[buf][c], sum) : 0.0;
+      pvs = fma(pv[s], v[s], pvs);
+    }
+    double pr[RPW];
+    own_rows(pv, pl[w]);
+    read_rows(pl[w], pr);
+    const double K = 0.5 * beta * wave_sum_f64(pvs);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) wv[s] = fma(-K, v[s], pv[s]);
+    // ---- row j + 1 after the update: T's diagonal entry and the next x
+    const double v1 = lane_value(v, j + 1), w1 = lane_value(wv, j + 1);
+    double dnext = 0.0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c = lane + 64 * s;
+      const double xn = fma(-v1, wv[s], fma(-w1, v[s], yb[buf][c]));
+      dnext = c == j + 1 ? xn : dnext;
+      xv[s] = (c > j + 1 && c < n) ? xn : 0.0;
+    }
+    // ---- A -= v w^T + w v^T on every row
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const double wr = fma(-K, xr[i], pr[i]);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) a[i][s] = fma(-xr[i], wv[s], fma(-wr, v[s], a[i][s]));
+    }
+    // ---- outputs of the step: T's entries (LDS, written out at the end)
+    // and the reflector
+    if (w == 0) {
+      td[lane == ((j + 1) & 63) ? j + 1 : kLpMax + lane] = dnext;
+      te[lane == 0 ? j : kLpMax + lane] = alpha;
+      tb[lane == 0 ? j : kLpMax + lane] = beta;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        if (lane + 64 * s < lp) v_out[(int64_t)j * lp + lane + 64 * s] = v[s];
+    }
+  }
+  // the last off-diagonal (no reflector) and the last diagonal entry
+  if (n >= 2) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (w == 0 && lane + 64 * s == n - 1) te[n - 2] = xv[s];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      if (w + 4 * i == n - 1) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          if (lane + 64 * s == n - 1) td[n - 1] = a[i][s];
+      }
   }
   __syncthreads();
-
-  // ---- stage 2: Gershgorin bracket, splitting, multisection
-  double glo = 1.0e308, ghi = -1.0e308, tn = 0.0, e2m = 0.0;
-  for (int i = lane; i < n; i += 64) {
-    const double rad = (i > 0 ? fabs(eo[i - 1]) : 0.0) + (i < n - 1 ? fabs(eo[i]) : 0.0);
-    glo = fmin(glo, dg[i] - rad);
-    ghi = fmax(ghi, dg[i] + rad);
-    tn = fmax(tn, fabs(dg[i]) + rad);
-    if (i < n - 1) e2m = fmax(e2m, eo[i] * eo[i]);
-  }
-  glo = -wave_max(-glo);
-  ghi = wave_max(ghi);
-  tn = wave_max(tn);
-  e2m = wave_max(e2m);
-  const double tol_split = 2.220446049250313e-16 * tn;
-  const double pivmin = 2.2250738585072014e-308 * fmax(1.0, e2m);
-  if (t < n) {
-    const double e = t < n - 1 ? (fabs(eo[t]) <= tol_split ? 0.0 : eo[t]) : 0.0;
-    ee[t] = e;
-    e2[t] = e * e;
-    const double ep = t > 0 ? (fabs(eo[t - 1]) <= tol_split ? 0.0 : eo[t - 1]) : 0.0;
-    de[t] = make_double2(dg[t], ep * ep);
-  }
-  if (wave == 0) {
-    // blocks: a split after position s where e_s was zeroed
-    const unsigned long long m0 = __ballot(lane < n - 1 && fabs(eo[lane]) <= tol_split);
-    const unsigned long long m1 = __ballot(lane + 64 < n - 1 && fabs(eo[lane + 64 < kLpMax ? lane + 64 : 0]) <= tol_split);
-    for (int h = 0; h < 2; ++h) {
-      const int i = lane + 64 * h;
-      if (i < n) {
-        const int s = i > 0 ? last_set_upto(m0, m1, i - 1) : -1;
-        const int e = first_set_from(m0, m1, i);
-        blo[i] = s + 1;
-        bhi[i] = e < 0 ? n - 1 : e;
-      }
-    }
-  }
-  __syncthreads();
-  const bool one_block = bhi[0] == n - 1;
-  const int nslot = one_block ? k : n, slot0 = one_block ? n - k : 0;
-  {
-    const int gi = t >> 3, js = t & 7;
-    if (gi < nslot) {
-      const int i = slot0 + gi, b0 = blo[i], b1 = bhi[i], il = i - b0;
-      const double pad = 8.881784197001252e-16 * fmax(fabs(glo), fabs(ghi)) + pivmin;
-      double lo = glo - pad, hi = ghi + pad;
-      const double fj = (double)(js + 1) * (1.0 / 9.0);
-      for (int it = 0; it < kEigIters; ++it) {
-        const double w = hi - lo, xs = fma(w, fj, lo);
-        double q = ldl_first(de[b0].x - xs, pivmin);
-        int cnt = q < 0.0;
-#pragma unroll 4
-        for (int kq = b0 + 1; kq <= b1; ++kq) {
-          const double2 v = de[kq];
-          q = ldl_step(v.x - xs, v.y, q, pivmin);
-          cnt += q < 0.0;
-        }
-        const unsigned long long bal = __ballot(cnt > il);
-        const unsigned m8 = (unsigned)(bal >> (lane & ~7)) & 0xFFu;
-        const int qf = m8 ? __builtin_ctz(m8) : 8;
-        const double nlo = qf > 0 ? fma(w, (double)qf * (1.0 / 9.0), lo) : lo;
-        const double nhi = qf < 8 ? fma(w, (double)(qf + 1) * (1.0 / 9.0), lo) : hi;
-        lo = nlo;
-        hi = nhi;
-      }
-      if (js == 0) lam[i] = 0.5 * (lo + hi);
-    }
-  }
-  __syncthreads();
-  if (t < nslot) {
-    const int i = slot0 + t;
-    int rk;
-    if (one_block) {
-      rk = n - 1 - i;  // slots of one block ascend
-    } else {
-      const double d = lam[i];
-      rk = 0;
-      for (int q = 0; q < n; ++q) {
-        const double e = lam[q];
-        rk += (e > d) || (e == d && q < i);
-      }
-    }
-    slot_of[rk] = i;
-  }
-  __syncthreads();
-  if (t < lp) {
-    double sg = 0.0;
-    if (t < nslot) {
-      const double smax = sqrt(fmax(lam[slot_of[0]], 0.0));
-      sg = sqrt(fmax(lam[slot_of[t]], 0.0));
-      if (!(sg > smax * 5.9604644775390625e-08)) sg = 0.0;
-    }
-    sig_inv[t] = sg > 0.0 ? 1.0 / sg : 0.0;
-    if (t < k) S[t] = (float)sg;
-  }
-  if (wave == kEigThreads / 64 - 1) {
-    // chains of consecutive ranks whose eigenvalues are closer than 1e-7 ||T||
-    bool brk[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = lane + 64 * h;
-      brk[h] = c == 0 || c >= k || !(lam[slot_of[c - 1]] - lam[slot_of[c]] < 1.0e-7 * tn);
-    }
-    const unsigned long long m0 = __ballot(brk[0]), m1 = __ballot(brk[1]);
-    for (int h = 0; h < 2; ++h) {
-      const int c = lane + 64 * h;
-      if (c < k) chain[c] = last_set_upto(m0, m1, c);
-    }
-    if (lane == 0) any_chain = (~m0 | ~m1) != 0ull;
-  }
-
-  // ---- stage 3: eigenvectors of T, one thread per wanted rank
-  if (t < k) {
-    const int c = t, i = slot_of[c], b0 = blo[i], b1 = bhi[i];
-    const double lm = lam[i];
-    for (int q = 0; q < n; ++q)
-      if (q < b0 || q > b1) Z[q][c] = 0.0;
-    // forward pivots D+ into the column
-    double dp = ldl_first(dg[b0] - lm, pivmin);
-    Z[b0][c] = dp;
-    for (int q = b0; q < b1; ++q) {
-      const double2 v = de[q + 1];
-      dp = ldl_step(v.x - lm, v.y, dp, pivmin);
-      Z[q + 1][c] = dp;
-    }
-    // backward pivots D-, twist where |gamma| = |D+ + D- - (d - lambda)| is least
-    double dm = ldl_first(dg[b1] - lm, pivmin);
-    double best = fabs(Z[b1][c] + dm - (dg[b1] - lm));
-    int tw = b1;
-    for (int q = b1 - 1; q >= b0; --q) {
-      dm = ldl_step(dg[q] - lm, e2[q], dm, pivmin);
-      const double gm = fabs(Z[q][c] + dm - (dg[q] - lm));
-      if (gm <= best) {
-        best = gm;
-        tw = q;
-      }
-    }
-    // z_q = -(e_q / D+_q) z_{q+1} above the twist
-    double z = 1.0, nz = 1.0;
-    for (int q = tw - 1; q >= b0; --q) {
-      z = -(ee[q] * recip_f64(Z[q][c])) * z;
-      Z[q][c] = z;
-      nz = fma(z, z, nz);
-    }
-    // D- again below the twist (same operations, same values), then
-    // z_{q+1} = -(e_q / D-_{q+1}) z_q
-    if (b1 > tw) {
-      dm = ldl_first(dg[b1] - lm, pivmin);
-      Z[b1][c] = dm;
-      for (int q = b1 - 1; q > tw; --q) {
-        dm = ldl_step(dg[q] - lm, e2[q], dm, pivmin);
-        Z[q][c] = dm;
-      }
-    }
-    Z[tw][c] = 1.0;
-    z = 1.0;
-    for (int q = tw; q < b1; ++q) {
-      z = -(ee[q] * recip_f64(Z[q + 1][c])) * z;
-      Z[q + 1][c] = z;
-      nz = fma(z, z, nz);
-    }
-    const double sc = 1.0 / sqrt(nz);
-    for (int q = b0; q <= b1; ++q) Z[q][c] *= sc;
-  }
-  __syncthreads();
-  // Gram-Schmidt (twice) of a chained vector against its chain predecessors
-  // of the same block
-  if (any_chain) {
-    for (int c = 1; c < k; ++c) {
-      const int c0 = chain[c];
-      if (c0 == c) continue;
-      const int bc = blo[slot_of[c]];
-      for (int pass = 0; pass < 2; ++pass) {
-        for (int b = c0 + wave; b < c; b += kEigThreads / 64) {
-          double s = 0.0;
-          for (int q = lane; q < n; q += 64) s = fma(Z[q][b], Z[q][c], s);
-          s = wave_sum_f64(s);
-          if (lane == 0) dots[b] = blo[slot_of[b]] == bc ? s : 0.0;
-        }
-        __syncthreads();
-        if (t < n) {
-          double zc = Z[t][c];
-          for (int b = c0; b < c; ++b) zc = fma(-dots[b], Z[t][b], zc);
-          Z[t][c] = zc;
-        }
-        __syncthreads();
-      }
-      if (wave == 0) {
-        double s = 0.0;
-        for (int q = lane; q < n; q += 64) s = fma(Z[q][c], Z[q][c], s);
-        s = wave_sum_f64(s);
-        if (lane == 0) nrm_s = s;
-      }
-      __syncthreads();
-      if (t < n && nrm_s > 0.0) Z[t][c] *= 1.0 / sqrt(nrm_s);
-      __syncthreads();
-    }
-  }
-
-  // ---- stage 4: x = H_0 H_1 ... H_{l-3} z, lanes (vector, rows i16 + 16 u)
-  constexpr int ZR = kLpMax / 16;
-  const int i16 = t & 15;
-  for (int c = t >> 4; c < ((k + 63) & ~63); c += kEigThreads / 16) {
-    const bool act = c < k;
-    double z[ZR];
-#pragma unroll
-    for (int u = 0; u < ZR; ++u) {
-      const int row = i16 + 16 * u;
-      z[u] = (act && row < n) ? Z[row][c] : 0.0;
-    }
-    for (int j = n - 3; j >= 0; --j) {
-      double vj[ZR], s = 0.0;
-#pragma unroll
-      for (int u = 0; u < ZR; ++u) {
-        vj[u] = V[j][i16 + 16 * u];
-        s = fma(vj[u], z[u], s);
-      }
-      const double f = bet[j] * group16_sum(s);
-#pragma unroll
-      for (int u = 0; u < ZR; ++u) z[u] = fma(-f, vj[u], z[u]);
-    }
-    if (act) {
-#pragma unroll
-      for (int u = 0; u < ZR; ++u) {
-        const int row = i16 + 16 * u;
-        if (row < n) evec[row * lp + c] = z[u];
-      }
-    }
-  }
-  // zeros beyond l rows and k columns
-  for (int e = t; e < lp * lp; e += kEigThreads) {
-    const int row = e / lp, col = e - (e / lp) * lp;
-    if (row >= n || col >= k) evec[e] = 0.0;
+  for (int i = t; i < lp; i += kTriThreads) {
+    dg_out[i] = i < n ? td[i] : 0.0;
+    eo_out[i] = i + 1 < n ? te[i] : 0.0;
+    beta_out[i] = i + 2 < n ? tb[i] : 0.0;
   }
 }
 
@@ -2045,7 +1832,12 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
   }
   // ---- small SVD of B (from its Gram, in p.gram) and the factors
   if (!p.wide) {
-    tridiag_eig_kernel<<<1, kEigThreads, 0, st>>>(p.gram, l, lp, k, p.evec, p.sig_inv, out->S);
+    if (lp > 64)
+      tridiag_kernel<2><<<1, kTriThreads, 0, st>>>(p.gram, l, lp, p.waux, p.waux + lp, p.waux + 2 * lp, p.wv);
+    else
+      tridiag_kernel<1><<<1, kTriThreads, 0, st>>>(p.gram, l, lp, p.waux, p.waux + lp, p.waux + 2 * lp, p.wv);
+    const metis_status_t es = metis_wide::eigh_tridiag(l, lp, k, p.wv, p.evec, p.sig_inv, out->S, p.wa, p.waux, st);
+    if (es != METIS_OK) return es;
     assemble_u_kernel<<<p.am_parts, kThreads, 0, st>>>(p.q, m, l, lp, k, p.evec, p.am_rows, out->U, p.am_val,
                                                        p.am_idx);
     assemble_v_kernel<<<(unsigned)cdiv(n, asm_chunk_rows(k)), kThreads, 0, st>>>(p.bt, n, l, lp, k, p.evec,

@@ -32,7 +32,6 @@ namespace {
 
 constexpr int kWT = 256;               // threads per workgroup
 constexpr int kWMax = metis_wide::kWideMax;
-constexpr int kWC = kWMax / 64;        // columns per lane of a row
 constexpr int kPiv = 16;               // pivots per Cholesky launch
 
 // Sum over the workgroup (kWT threads), the same bits in every thread: each
@@ -388,27 +387,77 @@ __device__ void load_tri(const double *__restrict__ dg, const double *__restrict
 }
 
 // The k largest eigenvalues of T, one wave per eigenvalue: 64 points cut
-// its bracket into 65 parts per step, nine steps (65^9 > 2^54).
+// its bracket into 65 parts per step, nine steps (65^9 > 2^54). The count at
+// a point x is the number of eigenvalues below x: the sign changes along the
+// leading minors p_i = det(T_i - x I) of each block of T (Sturm), with
+// p_i = (d_i - x) p_{i-1} - e_{i-1}^2 p_{i-2} from p = 1 at the block's start,
+// summed over the blocks (T splits where an off-diagonal was set to zero).
+// T is scaled by a power of two at or above ||T|| (exact), and the last two
+// minors are rescaled by a power of two every eight steps. A minor that is
+// exactly zero counts as positive: inside a block the next minor,
+// -e^2 p_{i-2}, gives the same total as any other sign convention, and at a
+// block's end it leaves an eigenvalue equal to x uncounted. The dependence
+// chain holds one fused multiply-add per step.
 __global__ void __launch_bounds__(kWT) weig_values_kernel(const double *__restrict__ dg, const double *__restrict__ eo,
                                                           int l, int k, double *__restrict__ lam,
                                                           double *__restrict__ tn_out) {
   __shared__ TriShared s;
+  __shared__ double2 sde[kWMax];  // (d_i, e_{i-1}^2) scaled
+  __shared__ int bstart[kWMax + 1], nblk;
   load_tri(dg, eo, l, s);
-  const int lane = threadIdx.x & 63, rk = blockIdx.x * (kWT / 64) + (threadIdx.x >> 6);
+  const int ex = s.tn > 0.0 ? __builtin_amdgcn_frexp_exp(s.tn) : 0;  // ||T|| < 2^ex
+  for (int i = threadIdx.x; i < l; i += kWT)
+    sde[i] = make_double2(ldexp(s.d[i], -ex), i > 0 ? ldexp(s.e2[i - 1], -2 * ex) : 0.0);
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    // block starts in order: position 0 and every i with e_{i-1} = 0
+    int base = 0;
+    for (int i0 = 0; i0 < l; i0 += 64) {
+      const int i = i0 + lane;
+      const bool st = i < l && (i == 0 || s.e2[i - 1] == 0.0);
+      const unsigned long long m = __ballot(st);
+      if (st) bstart[base + __popcll(m & ((1ull << lane) - 1ull))] = i;
+      base += __popcll(m);
+    }
+    if (lane == 0) {
+      nblk = base;
+      bstart[base] = l;
+    }
+  }
+  __syncthreads();
+  const int rk = blockIdx.x * (kWT / 64) + (threadIdx.x >> 6);
   if (blockIdx.x == 0 && threadIdx.x == 0) *tn_out = s.tn;
   if (rk >= k) return;
   const int a = l - 1 - rk;  // ascending index
+  const int nb = nblk;
   const double pivmin = s.pivmin;
   const double pad = 8.881784197001252e-16 * fmax(fabs(s.glo), fabs(s.ghi)) + pivmin;
   double lo = s.glo - pad, hi = s.ghi + pad;
   const double fj = (double)(lane + 1) * (1.0 / 65.0);
   for (int it = 0; it < 9; ++it) {
-    const double w = hi - lo, xs = fma(w, fj, lo);
-    double q = ldl_start(s.d[0] - xs, pivmin);
-    int cnt = q < 0.0;
-    for (int i = 1; i < l; ++i) {
-      q = ldl_next(s.d[i] - xs, s.e2[i - 1], q, pivmin);
-      cnt += q < 0.0;
+    const double w = hi - lo, xs = ldexp(fma(w, fj, lo), -ex);
+    int cnt = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int i1 = bstart[b + 1];
+      int i = bstart[b];
+      double pm = 0.0, pc = 1.0;
+      auto step = [&](double2 de) {
+        const double pn = fma(de.x - xs, pc, -(de.y * pm));
+        cnt += (pn < 0.0) != (pc < 0.0);
+        pm = pc;
+        pc = pn;
+      };
+      for (; i + 8 <= i1; i += 8) {
+        double2 de[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) de[u] = sde[i + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) step(de[u]);
+        const int e = max(__builtin_amdgcn_frexp_exp(pc), __builtin_amdgcn_frexp_exp(pm));
+        pc = ldexp(pc, -e);
+        pm = ldexp(pm, -e);
+      }
+      for (; i < i1; ++i) step(sde[i]);
     }
     const unsigned long long bal = __ballot(cnt > a);
     const int qf = bal ? __builtin_ctzll(bal) : 64;
@@ -549,31 +598,175 @@ __global__ void __launch_bounds__(kWT) weig_vectors_kernel(const double *__restr
   }
 }
 
-// x = H_0 H_1 ... H_{l-3} z for each wanted rank, one wave per vector, the
-// reflectors read in reverse order (the next one loaded during the current
-// one's sum). Rows of Z beyond l come out zero.
+// The same eigenvectors for l <= kNarrow, with the pivots in registers: for
+// rank c, thread c (waves 0 and 1) runs the top-down pivots D+ and thread
+// 128 + c (waves 2 and 3) the bottom-up pivots D-, both at once. D+ goes
+// through LDS to the bottom-up thread, which finds the twist r (least
+// |D+_q + D-_q - (d_q - lambda)|, lowest q on ties); then the top-down
+// thread forms z above r (z_q = -(e_q / D+_q) z_{q+1}) and the bottom-up
+// thread z from r down (z_r = 1, z_q = -(e_{q-1} / D-_q) z_{q-1}), in LDS.
+// Normalization, chains and the outputs as in weig_vectors_kernel.
+constexpr int kNarrow = 96;
+__global__ void __launch_bounds__(kWT) neig_vectors_kernel(const double *__restrict__ dg, const double *__restrict__ eo,
+                                                           int l, int lp, int k, const double *__restrict__ lam,
+                                                           double *__restrict__ Z, double *__restrict__ sig_inv,
+                                                           float *__restrict__ S) {
+  __shared__ TriShared s;
+  __shared__ double Zs[kNarrow][kNarrow + 1];
+  __shared__ double nz_part[2][kNarrow];
+  __shared__ int twist[kNarrow];
+  __shared__ int chain_any;
+  static_assert(kWT == 256 && kNarrow <= 128, "two roles of 128 threads");
+  load_tri(dg, eo, l, s);
+  const int t = threadIdx.x;
+  const bool down = t >= 128;
+  const int c = down ? t - 128 : t;
+  const bool act = c < k;
+  const double pivmin = s.pivmin;
+  const double lm = act ? lam[c] : 0.0;
+  double P[kNarrow];  // D+ (top-down thread) or D- (bottom-up thread), then z
+  if (!down) {
+    double dp = 0.0;
+#pragma unroll
+    for (int q = 0; q < kNarrow; ++q)
+      if (q < l) {
+        const double dmx = s.d[q] - lm;
+        dp = q == 0 ? ldl_start(dmx, pivmin) : ldl_next(dmx, s.e2[q - 1], dp, pivmin);
+        P[q] = dp;
+        if (act) Zs[q][c] = dp;
+      }
+  } else {
+    double dm = 0.0;
+#pragma unroll
+    for (int q = kNarrow - 1; q >= 0; --q)
+      if (q < l) {
+        const double dmx = s.d[q] - lm;
+        dm = q == l - 1 ? ldl_start(dmx, pivmin) : ldl_next(dmx, s.e2[q], dm, pivmin);
+        P[q] = dm;
+      }
+  }
+  __syncthreads();
+  if (down && act) {
+    double gbest = 1.0e308;
+    int r = 0;
+#pragma unroll
+    for (int q = kNarrow - 1; q >= 0; --q)
+      if (q < l) {
+        const double g = fabs(Zs[q][c] + P[q] - (s.d[q] - lm));
+        if (g <= gbest) {
+          gbest = g;
+          r = q;
+        }
+      }
+    twist[c] = r;
+  }
+  __syncthreads();
+  if (act) {
+    const int r = twist[c];
+    double z = 1.0, nz = 0.0;
+    if (!down) {
+      // rows above the twist, from r - 1 up to 0
+#pragma unroll
+      for (int q = kNarrow - 2; q >= 0; --q)
+        if (q + 1 < l) {
+          const double f = -(s.e[q] * recip(P[q]));
+          if (q < r) {
+            z = f * z;
+            Zs[q][c] = z;
+            nz = fma(z, z, nz);
+          }
+        }
+    } else {
+      Zs[r][c] = 1.0;
+      nz = 1.0;
+#pragma unroll
+      for (int q = 1; q < kNarrow; ++q)
+        if (q < l) {
+          const double f = -(s.e[q - 1] * recip(P[q]));
+          if (q > r) {
+            z = f * z;
+            Zs[q][c] = z;
+            nz = fma(z, z, nz);
+          }
+        }
+    }
+    nz_part[down][c] = nz;
+  }
+  __syncthreads();
+  for (int e = t; e < l * k; e += kWT) {
+    const int q = e / k, cc = e - (e / k) * k;
+    Zs[q][cc] *= 1.0 / sqrt(nz_part[1][cc] + nz_part[0][cc]);
+  }
+  if (t == 0) {
+    int any = 0;
+    for (int cc = 1; cc < k; ++cc) any |= lam[cc - 1] - lam[cc] < 1.0e-7 * s.tn;
+    chain_any = any;
+  }
+  __syncthreads();
+  if (chain_any) {
+    __shared__ double red2[kWT / 64];
+    int start = 0;
+    for (int cc = 1; cc < k; ++cc) {
+      if (!(lam[cc - 1] - lam[cc] < 1.0e-7 * s.tn)) {
+        start = cc;
+        continue;
+      }
+      for (int pass = 0; pass < 2; ++pass) {
+        for (int b = start; b < cc; ++b) {
+          const double dot = block_sum(t < l ? Zs[t][b] * Zs[t][cc] : 0.0, red2);
+          if (t < l) Zs[t][cc] = fma(-dot, Zs[t][b], Zs[t][cc]);
+          __syncthreads();
+        }
+        const double inv = 1.0 / sqrt(block_sum(t < l ? Zs[t][cc] * Zs[t][cc] : 0.0, red2));
+        if (t < l) Zs[t][cc] *= inv;
+        __syncthreads();
+      }
+    }
+  }
+  for (int e = t; e < lp * k; e += kWT) {
+    const int q = e / k, cc = e - (e / k) * k;
+    Z[(int64_t)q * lp + cc] = q < l ? Zs[q][cc] : 0.0;
+  }
+  for (int cc = t; cc < lp; cc += kWT) {
+    double sg = 0.0;
+    if (cc < k) {
+      const double smax = sqrt(fmax(lam[0], 0.0));
+      sg = sqrt(fmax(lam[cc], 0.0));
+      if (!(sg > smax * 5.9604644775390625e-08)) sg = 0.0;
+    }
+    sig_inv[cc] = sg > 0.0 ? 1.0 / sg : 0.0;
+    if (cc < k) S[cc] = (float)sg;
+  }
+}
+
+// x = H_0 H_1 ... H_{l-3} z for each wanted rank, one wave per vector
+// (NC = lp / 64 rounded up rows per lane), the reflectors read in reverse
+// order, D of them loaded ahead of the one being applied. Rows of Z beyond l
+// come out zero.
+template <int NC>
 __global__ void __launch_bounds__(kWT) weig_back_kernel(double *__restrict__ Z, int l, int lp, int k,
                                                         const double *__restrict__ V,
                                                         const double *__restrict__ beta) {
   const int lane = threadIdx.x & 63, c = blockIdx.x * (kWT / 64) + (threadIdx.x >> 6);
   if (c >= k) return;
-  constexpr int D = 4;  // reflectors loaded ahead of the one being applied
-  double z[kWC], v[D][kWC];
+  constexpr int D = NC <= 2 ? 16 : 4;
+  double z[NC], v[D][NC], bt[D];
 #pragma unroll
-  for (int u = 0; u < kWC; ++u) {
+  for (int u = 0; u < NC; ++u) {
     const int q = lane + 64 * u;
     z[u] = q < l ? Z[(int64_t)q * lp + c] : 0.0;
   }
-  auto load = [&](int j, double (&dst)[kWC]) {
+  auto load = [&](int j, double (&dst)[NC], double &b) {
 #pragma unroll
-    for (int u = 0; u < kWC; ++u) {
+    for (int u = 0; u < NC; ++u) {
       const int q = lane + 64 * u;
       dst[u] = (j >= 0 && q < lp) ? V[(int64_t)j * lp + q] : 0.0;
     }
+    b = j >= 0 ? beta[j] : 0.0;
   };
   const int j_top = l - 3;
 #pragma unroll
-  for (int d = 0; d < D; ++d) load(j_top - d, v[d]);
+  for (int d = 0; d < D; ++d) load(j_top - d, v[d], bt[d]);
   for (int j0 = j_top; j0 >= 0; j0 -= D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -581,19 +774,24 @@ __global__ void __launch_bounds__(kWT) weig_back_kernel(double *__restrict__ Z, 
       if (j >= 0) {
         double part = 0.0;
 #pragma unroll
-        for (int u = 0; u < kWC; ++u) part = fma(v[d][u], z[u], part);
-        const double sc = beta[j] * wave_sum0(part);
+        for (int u = 0; u < NC; ++u) part = fma(v[d][u], z[u], part);
+        const double sc = bt[d] * wave_sum0(part);
 #pragma unroll
-        for (int u = 0; u < kWC; ++u) z[u] = fma(-sc, v[d][u], z[u]);
+        for (int u = 0; u < NC; ++u) z[u] = fma(-sc, v[d][u], z[u]);
       }
-      load(j - D, v[d]);
+      load(j - D, v[d], bt[d]);
     }
   }
 #pragma unroll
-  for (int u = 0; u < kWC; ++u) {
+  for (int u = 0; u < NC; ++u) {
     const int q = lane + 64 * u;
     if (q < lp) Z[(int64_t)q * lp + c] = q < l ? z[u] : 0.0;
   }
+}
+
+template <int NC>
+void launch_back(double *Z, int l, int lp, int k, const double *V, const double *beta, hipStream_t st) {
+  weig_back_kernel<NC><<<(unsigned)cdiv(k, kWT / 64), kWT, 0, st>>>(Z, l, lp, k, V, beta);
 }
 
 // out[r][c] = (sum_q x[r][q] E[q][c]) * colscale[c] for r < rows, c < k,
@@ -755,19 +953,37 @@ metis_status_t wide_assemble(const float *x, int64_t rows, int l, int lp, int k,
   return hipGetLastError() == hipSuccess ? METIS_OK : METIS_ERR_HIP;
 }
 
+metis_status_t eigh_tridiag(int l, int lp, int k, const double *V, double *evec, double *sig_inv, float *S,
+                            double *Dm, double *aux, hipStream_t st) {
+  if (l < 1 || l > kWideMax || lp < l || lp > kWideMax || k < 1 || k > l || k > kWT) return METIS_ERR_UNSUPPORTED;
+  double *dg = aux, *eo = aux + lp, *beta = aux + 2 * lp, *lam = aux + 5 * lp, *tn = aux + 6 * lp;
+  weig_values_kernel<<<(unsigned)cdiv(k, kWT / 64), kWT, 0, st>>>(dg, eo, l, k, lam, tn);
+  if (l <= kNarrow)
+    neig_vectors_kernel<<<1, kWT, 0, st>>>(dg, eo, l, lp, k, lam, evec, sig_inv, S);
+  else
+    weig_vectors_kernel<<<1, kWT, 0, st>>>(dg, eo, l, lp, k, lam, evec, Dm, sig_inv, S);
+  switch ((lp + 63) / 64) {
+    case 1: launch_back<1>(evec, l, lp, k, V, beta, st); break;
+    case 2: launch_back<2>(evec, l, lp, k, V, beta, st); break;
+    case 3: launch_back<3>(evec, l, lp, k, V, beta, st); break;
+    case 4: launch_back<4>(evec, l, lp, k, V, beta, st); break;
+    case 5: launch_back<5>(evec, l, lp, k, V, beta, st); break;
+    case 6: launch_back<6>(evec, l, lp, k, V, beta, st); break;
+    case 7: launch_back<7>(evec, l, lp, k, V, beta, st); break;
+    default: launch_back<8>(evec, l, lp, k, V, beta, st); break;
+  }
+  return hipGetLastError() == hipSuccess ? METIS_OK : METIS_ERR_HIP;
+}
+
 metis_status_t wide_eigh(const double *g, int l, int lp, int k, double *evec, double *sig_inv, float *S, double *W,
                          double *V, double *Dm, double *aux, hipStream_t st) {
   if (l < 1 || l > kWideMax || lp < l || lp > kWideMax || lp % 64 || lp < 128 || k < 1 || k > l || k > kWT)
     return METIS_ERR_UNSUPPORTED;
-  double *dg = aux, *eo = aux + lp, *beta = aux + 2 * lp, *pbuf = aux + 3 * lp, *lam = aux + 5 * lp,
-         *tn = aux + 6 * lp;
+  double *dg = aux, *eo = aux + lp, *beta = aux + 2 * lp, *pbuf = aux + 3 * lp;
   const unsigned fill = (unsigned)cdiv((int64_t)lp * lp, kWT);
   wtri_init_kernel<<<fill, kWT, 0, st>>>(g, l, lp, W);
   by_columns<TriSteps>(lp, W, l, V, beta, dg, eo, pbuf, st);
-  weig_values_kernel<<<(unsigned)cdiv(k, kWT / 64), kWT, 0, st>>>(dg, eo, l, k, lam, tn);
-  weig_vectors_kernel<<<1, kWT, 0, st>>>(dg, eo, l, lp, k, lam, evec, Dm, sig_inv, S);
-  weig_back_kernel<<<(unsigned)cdiv(k, kWT / 64), kWT, 0, st>>>(evec, l, lp, k, V, beta);
-  return hipGetLastError() == hipSuccess ? METIS_OK : METIS_ERR_HIP;
+  return eigh_tridiag(l, lp, k, V, evec, sig_inv, S, Dm, aux, st);
 }
 
 }  // namespace metis_wide

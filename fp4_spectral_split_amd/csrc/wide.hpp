@@ -26,6 +26,13 @@ metis_status_t wide_chol_inv(const double *g, int l, int lp, double *rinv, int *
 metis_status_t wide_eigh(const double *g, int l, int lp, int k, double *evec, double *sig_inv, float *S, double *W,
                          double *V, double *Dm, double *aux, hipStream_t st);
 
+// The same eigenpairs from a tridiagonal reduction already made: T's
+// diagonal in aux[0 .. l), its off-diagonal in aux[lp ..), the reflector
+// scales beta_j in aux[2 lp ..), reflector j in V[j * lp + row] (G = H T H^T,
+// H = H_0 ... H_{l-3}, H_j = I - beta_j v_j v_j^T). Dm: lp x lp scratch.
+metis_status_t eigh_tridiag(int l, int lp, int k, const double *V, double *evec, double *sig_inv, float *S,
+                            double *Dm, double *aux, hipStream_t st);
+
 // out (rows x k, fp32) = x (rows x l fp32) E[:, :k] diag(colscale) (colscale
 // may be NULL), fp64 sums; with am_val / am_idx (may be NULL), per tile of 64
 // rows the argmax of |out[:, c]| (lowest row on ties) at [tile * k + c].
