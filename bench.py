@@ -457,13 +457,16 @@ def main():
     ap.add_argument("--no-legs", action="store_true", help="the headline step only")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain copy of MIB MiB ahead of the steps (counter calibration)")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="only the --configs workloads, each as its step (for per-workload profiles); prints "
+                         "their JSON")
     ap.add_argument("--profile-splits", type=int, default=0, metavar="REPS",
                     help="instead of the steps, run each split, the quantizer and each GEMM REPS times alone "
                          "(for profiles)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
-              "would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     # one hardware queue per lane (read by the HIP runtime when it starts)
@@ -477,6 +480,12 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         calibrate_copy(torch, dev, args.calibrate_copy)
+    if args.configs_only:
+        out = {}
+        for c in [int(c) for c in args.configs.split(",") if c.strip()]:
+            out[CONFIG_LABEL[c]] = config_leg(torch, np, M, synth, c, dev, args.steps, args.warmup)
+        print(json.dumps({"configs": out}), flush=True)
+        return
     names = synth.TENSOR_NAMES[CFG]
     gemms = synth.GEMMS[CFG]
     t0 = time.perf_counter()

@@ -19,7 +19,7 @@ format descriptions:
 * NVFP4 (NVIDIA's public NVFP4 description): 16-element blocks with an E4M3
   scale, plus one fp32 scale per tensor.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 round-to-nearest-even with ties to the even code, saturation at +-6 (E2M1)
 and +-448 (E4M3), the sign of zero kept, all-zero block -> scale byte 0,
 NVFP4 scale arithmetic as a chain of correctly rounded fp32 operations with a

@@ -6,7 +6,7 @@ Two mechanisms the pages name next to the spectral split (SII open-source-week
 post on Metis, §2 "architecture" strategies 2 and 3 and §2.4 items 2 and 3;
 the earlier version's abstract on the chatpaper.ai page, items (ii) and (iii)).
 The pages give neither formula; the readings below are the plainest ones the
-text supports, and the design doc lists them.
+text supports.
 
 Adaptive spectral learning rate (§2.4 item 2): large singular directions
 learn strongly by themselves while small ones are neglected, so the gradient
