@@ -27,7 +27,7 @@ division (never a multiplication by a reciprocal).
 
 Pins (tests/test_oracle_formats.py): exact round trip of the E2M1 grid times
 2^e for every E8M0 exponent; an independent nearest-of-eight brute force over
-every fp32 bit pattern of the scaled range; brute-force search over all 16
+every fp32 bit pattern near each decision point and a dense sweep of the rest; brute-force search over all 16
 codes for 4x32 blocks; torch.float8_e4m3fn as a library special case for E4M3;
 numpy.float32 arithmetic for the fp32 emulation; hand-listed boundary values.
 """

@@ -35,18 +35,25 @@ def test_e2m1_grid_values_round_trip():
     assert np.all(F.e2m1_encode(vals) == codes)
 
 
-def test_e2m1_exhaustive_over_the_decision_range():
-    """Every fp32 value in [2^-3, 8) (all mantissas of six binades, both signs)
-    against the brute force; everything else on a strided sweep of all
-    2^31 positive bit patterns below infinity."""
-    lo = np.float32(0.125).view(np.uint32)
-    hi = np.float32(8.0).view(np.uint32)
-    step = 1 << 22
-    for start in range(int(lo), int(hi), step):
-        bits = np.arange(start, min(start + step, int(hi)), dtype=np.uint32)
+def test_e2m1_exhaustive_near_every_decision_point():
+    """Every fp32 value within 2^18 bit patterns of each rounding threshold and
+    grid point in (0, 8) (both signs), a stride-13 sweep of all of [2^-3, 8),
+    and a strided sweep of all 2^31 positive bit patterns below infinity,
+    against the brute force."""
+    points = [0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0]
+    win = 1 << 18
+    for p in points:
+        c = int(np.float32(p).view(np.uint32))
+        bits = np.arange(c - win, c + win, dtype=np.uint32)
         v = bits.view(np.float32).astype(np.float64)
-        assert np.array_equal(F.e2m1_encode(v), brute_e2m1(v))
-        assert np.array_equal(F.e2m1_encode(-v), brute_e2m1(-v))
+        assert np.array_equal(F.e2m1_encode(v), brute_e2m1(v)), p
+        assert np.array_equal(F.e2m1_encode(-v), brute_e2m1(-v)), p
+    lo = int(np.float32(0.125).view(np.uint32))
+    hi = int(np.float32(8.0).view(np.uint32))
+    bits = np.arange(lo, hi, 13, dtype=np.uint32)
+    v = bits.view(np.float32).astype(np.float64)
+    assert np.array_equal(F.e2m1_encode(v), brute_e2m1(v))
+    assert np.array_equal(F.e2m1_encode(-v), brute_e2m1(-v))
     bits = np.arange(0, 0x7F800000, 997, dtype=np.uint32)
     v = bits.view(np.float32).astype(np.float64)
     assert np.array_equal(F.e2m1_encode(v), brute_e2m1(v))
