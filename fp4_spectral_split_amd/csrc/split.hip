@@ -590,21 +590,26 @@ __global__ void __launch_bounds__(256)
 }
 
 // ========================================================= Cholesky + inverse
-// The same factorization for l <= kLpMax as one elimination on [G | I]:
-// step j subtracts m_p = G'[j][p] / d_j times row j from every later row p,
-// on the upper part of the trailing matrix G' and on the lower-triangular
-// block that starts as I. After the last step the pivots d_j are those of
-// G = L D L^T and the block holds L^-1, so R = D^1/2 L^T and
-// R^-1 = L^-T D^-1/2. Each thread keeps its matrix elements in registers;
-// a row is written to LDS once it is final (after the step before it is
-// used), so one barrier per step suffices. Absent pivots (d_j <= tol) get
-// m_p = 0 and a zero row and column of R^-1, as above.
-// Combined layout of row p: columns x >= p hold G'[p][x], columns x < p hold
-// L^-1[p][x] (its unit diagonal is implicit).
-constexpr int kCholThreads = 1024;
-// a row is shared by floor(threads / l) threads; each owns every tpr-th
-// column of it: at most 10 columns (l = 96)
-constexpr int kCholSlots = 10;
+// The factorization for l <= kLpMax as one elimination on [G | I]: step j
+// subtracts m_p = G'[j][p] / d_j times row j from every later row p, on the
+// upper part of the trailing matrix G' and on the block L^-1 that starts as
+// I. After the last step the pivots d_j are those of G = L D L^T and the
+// block holds L^-1, so R = D^1/2 L^T and R^-1 = L^-T D^-1/2. Absent pivots
+// (d_j <= tol) get m_p = 0 and a zero row and column of R^-1.
+// Each thread keeps its elements of G' and L^-1 in registers; a row is
+// written to LDS (CG, CL) once it is final (after the step before it is
+// used), so one barrier per step suffices. Ownership: the 256 threads form a
+// 16 x 16 grid; thread (tr, tc) holds rows tr + 16 a and columns tc + 16 b
+// (a, b < kCholB), so per step it reads 3 B + 1 values of the published row
+// j for its updates. The updates need no per-element test: a row of L^-1 is
+// zero right of its diagonal, so subtracting row j leaves every column
+// beyond j unchanged, and the lower part of G', rows at or above j and the
+// rows a thread already published take garbage that is never read again
+// (each published row is read only in its own step and by the output), so
+// every step is the same straight-line code. Each thread forms 1 / d_j
+// itself.
+constexpr int kCholThreads = 256;
+constexpr int kCholB = kLpMax / 16;
 
 __device__ __forceinline__ double recip_f64(double d) {
   double r = __builtin_amdgcn_rcp(d);  // hardware estimate, refined by Newton steps
@@ -614,26 +619,29 @@ __device__ __forceinline__ double recip_f64(double d) {
 
 __global__ void __launch_bounds__(kCholThreads)
     chol_small_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ out, int *info) {
-  __shared__ double C[kLpMax][kLpMax + 1];
-  __shared__ double ipiv[kLpMax];  // 1 / d_j, 0 for an absent pivot
-  __shared__ double rs[kLpMax];    // d_j^-1/2, 0 for an absent pivot
+  __shared__ double CG[kLpMax][kLpMax + 1];  // published rows of G' (upper part meaningful)
+  __shared__ double CL[kLpMax][kLpMax + 1];  // published rows of L^-1
+  __shared__ double rs[kLpMax];               // d_j^-1/2, 0 for an absent pivot
   __shared__ int dead[kLpMax];
   __shared__ double tol_s;
   const int t = threadIdx.x;
   {
-    // upper triangle of G (the lower part of C starts as zeros), all of a
-    // thread's loads in flight together
+    // upper triangle of G (zeros elsewhere, also beyond l), all of a
+    // thread's loads in flight together; CL = I
     constexpr int PER = (kLpMax * kLpMax + kCholThreads - 1) / kCholThreads;
     double v[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int e = t + u * kCholThreads, p = e / l, x = e - (e / l) * l;
-      v[u] = (e < l * l && x >= p) ? g[p * lp + x] : 0.0;
+      const int e = t + u * kCholThreads, p = e / kLpMax, x = e - p * kLpMax;
+      v[u] = (e < kLpMax * kLpMax && p < l && x < l && x >= p) ? g[p * lp + x] : 0.0;
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int e = t + u * kCholThreads, p = e / l, x = e - (e / l) * l;
-      if (e < l * l) C[p][x] = v[u];
+      const int e = t + u * kCholThreads, p = e / kLpMax, x = e - p * kLpMax;
+      if (e < kLpMax * kLpMax) {
+        CG[p][x] = v[u];
+        CL[p][x] = p == x ? 1.0 : 0.0;
+      }
     }
     {
       // the second CholeskyQR pass sees G = I + E with E tiny: then
@@ -644,8 +652,8 @@ __global__ void __launch_bounds__(kCholThreads)
       double em = 0.0;
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
-        const int e = t + u * kCholThreads, p = e / l, x = e - (e / l) * l;
-        if (e < l * l && x >= p) em = fmax(em, fabs(v[u] - (x == p ? 1.0 : 0.0)));
+        const int e = t + u * kCholThreads, p = e / kLpMax, x = e - p * kLpMax;
+        if (e < kLpMax * kLpMax && p < l && x < l && x >= p) em = fmax(em, fabs(v[u] - (x == p ? 1.0 : 0.0)));
       }
       em = wave_max(em);
       if ((t & 63) == 0) emax_w[t >> 6] = em;
@@ -657,7 +665,7 @@ __global__ void __launch_bounds__(kCholThreads)
         for (int e = t; e < lp * lp; e += kCholThreads) {
           const int i = e / lp, c = e - (e / lp) * lp;
           double r = 0.0;
-          if (c < l && i <= c) r = i == c ? 1.0 - 0.5 * (C[i][i] - 1.0) : -C[i][c];
+          if (c < l && i <= c) r = i == c ? 1.0 - 0.5 * (CG[i][i] - 1.0) : -CG[i][c];
           out[e] = r;
         }
         if (t == 0 && info) *info = 0;
@@ -665,62 +673,61 @@ __global__ void __launch_bounds__(kCholThreads)
       }
     }
   }
-  __syncthreads();
   if (t < 64) {
     double md = 0.0;
-    for (int i = t; i < l; i += 64) md = fmax(md, C[i][i]);
+    for (int i = t; i < l; i += 64) md = fmax(md, CG[i][i]);
     md = wave_max(md);
-    if (t == 0) {
-      const double tol = (double)l * 2.220446049250313e-16 * md;
-      tol_s = tol;
-    }
+    if (t == 0) tol_s = (double)l * 2.220446049250313e-16 * md;
   }
-  __syncthreads();
-  if (t == 0) {
-    const double d = C[0][0];
-    ipiv[0] = d > tol_s ? recip_f64(d) : 0.0;
-  }
-  // owned elements: row p = t / tpr, columns x = q + tpr s (q = t % tpr), so
-  // the multiplier G'[j][p] / d_j is one load per step and the row-j values
-  // C[j][x] read by a wave are a handful of broadcast addresses
-  const int tpr = kCholThreads / l;
-  const int p = t / tpr, q = t - (t / tpr) * tpr;
-  double v[kCholSlots];
+  const int tr = t >> 4, tc = t & 15;
+  double vg[kCholB][kCholB], vl[kCholB][kCholB];
   __syncthreads();
   const double tol = tol_s;
 #pragma unroll
-  for (int s = 0; s < kCholSlots; ++s) {
-    const int x = q + tpr * s;
-    v[s] = (p < l && x < l) ? C[p][x] : 0.0;
-  }
-  for (int j = 0; j + 1 < l; ++j) {
-    const double ij = ipiv[j];
-    if (p > j && p < l) {
-      const double m = C[j][p] * ij;
+  for (int a = 0; a < kCholB; ++a)
 #pragma unroll
-      for (int s = 0; s < kCholSlots; ++s) {
-        const int x = q + tpr * s;
-        if (x < l && (x <= j || x >= p)) {
-          const double w = x == j ? 1.0 : C[j][x];
-          v[s] = fma(-m, w, v[s]);
-        }
+    for (int b = 0; b < kCholB; ++b) {
+      vg[a][b] = CG[tr + 16 * a][tc + 16 * b];
+      vl[a][b] = CL[tr + 16 * a][tc + 16 * b];
+    }
+  for (int j = 0; j + 1 < l; ++j) {
+    const double d = CG[j][j];
+    double cm[kCholB], gx[kCholB], lx[kCholB];
+#pragma unroll
+    for (int a = 0; a < kCholB; ++a) cm[a] = CG[j][tr + 16 * a];
+#pragma unroll
+    for (int b = 0; b < kCholB; ++b) {
+      gx[b] = CG[j][tc + 16 * b];
+      lx[b] = CL[j][tc + 16 * b];
+    }
+    const double ij = d > tol ? recip_f64(d) : 0.0;
+#pragma unroll
+    for (int a = 0; a < kCholB; ++a) {
+      const double m = cm[a] * ij;
+#pragma unroll
+      for (int b = 0; b < kCholB; ++b) {
+        vg[a][b] = fma(-m, gx[b], vg[a][b]);
+        vl[a][b] = fma(-m, lx[b], vl[a][b]);
       }
     }
-    if (p == j + 1) {
+    // row j + 1 is final now: its owners publish it
+    if (tr == ((j + 1) & 15)) {
+      const int a1 = (j + 1) >> 4;
 #pragma unroll
-      for (int s = 0; s < kCholSlots; ++s) {
-        const int x = q + tpr * s;
-        if (x < l) {
-          C[j + 1][x] = v[s];
-          if (x == j + 1) ipiv[j + 1] = v[s] > tol ? recip_f64(v[s]) : 0.0;
+      for (int a = 0; a < kCholB; ++a)
+        if (a == a1) {
+#pragma unroll
+          for (int b = 0; b < kCholB; ++b) {
+            CG[j + 1][tc + 16 * b] = vg[a][b];
+            CL[j + 1][tc + 16 * b] = vl[a][b];
+          }
         }
-      }
     }
     __syncthreads();
   }
   // pivots d_j sit on the diagonal of the published rows
   for (int j = t; j < l; j += kCholThreads) {
-    const double d = C[j][j];
+    const double d = CG[j][j];
     const bool alive = d > tol;
     rs[j] = alive ? 1.0 / sqrt(d) : 0.0;
     dead[j] = !alive;
@@ -730,7 +737,7 @@ __global__ void __launch_bounds__(kCholThreads)
   for (int e = t; e < lp * lp; e += kCholThreads) {
     const int i = e / lp, c = e - (e / lp) * lp;
     double r = 0.0;
-    if (c < l && i <= c) r = (i == c ? 1.0 : C[c][i]) * rs[c];
+    if (c < l && i <= c) r = CL[c][i] * rs[c];
     out[e] = r;
   }
   if (t == 0 && info) {
