@@ -201,7 +201,7 @@ __global__ void __launch_bounds__(256) omega_transpose_kernel(const unsigned sho
 // HL: the right-hand factor is an fp32 matrix carried as bf16 hi + lo
 // (omt holds its hi rows 0 .. lp - 1, then its lo rows), both multiplied, so
 // the product is fp32-accurate (the power iterations' Y = A Z).
-template <typename T, bool HL = false, int RS = kSketchRS>
+template <typename T, bool HL = false, int RS = kSketchRS, int NC = 0>
 __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda,
                                                           const unsigned short *__restrict__ omt, int l, int lp,
                                                           int64_t chunk, float *__restrict__ ysk) {
@@ -221,12 +221,15 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
   const int s = blockIdx.y;
   const int64_t c_beg = (int64_t)s * chunk;
   const int64_t c_end = std::min<int64_t>(n, c_beg + chunk);
-  const int nct = lt >> 4;
-  floatx4 acc[RS][kLpMax / 16];
+  // NC > 0: the launch has exactly NC 16-column tiles (no runtime test, so
+  // the accumulators never leave the MFMA registers)
+  constexpr int NCM = NC ? NC : kLpMax / 16;
+  const int nct = NC ? NC : lt >> 4;
+  floatx4 acc[RS][NCM];
 #pragma unroll
   for (int a = 0; a < RS; ++a)
 #pragma unroll
-    for (int b = 0; b < kLpMax / 16; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NCM; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // Every load takes a clamped, valid address and none sits in a branch, so
   // the waits for a step's data stay counted while the next step's loads
@@ -310,8 +313,8 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < kLpMax / 16; ++ct) {
-      if (ct < nct) {
+    for (int ct = 0; ct < NCM; ++ct) {
+      if (NC || ct < nct) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -329,8 +332,8 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
-    for (int ct = 0; ct < kLpMax / 16; ++ct) {
-      if (ct < nct) {
+    for (int ct = 0; ct < NCM; ++ct) {
+      if (NC || ct < nct) {
         const int col = l0 + ct * 16 + r16;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -898,7 +901,7 @@ __global__ void __launch_bounds__(kThreads)
 // 4 waves x 32 columns. Per step, 64 rows of A (bf16 or fp32) and the
 // matching 64 columns of Q^T (hi, lo) pass through LDS; the next step's
 // pieces are loaded into registers while the current step is multiplied.
-template <typename T>
+template <typename T, int NC = 0>
 __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__ A, int64_t m, int64_t n, int64_t lda,
                                                            const unsigned short *__restrict__ qt, int l, int lp,
                                                            int64_t chunk_rows, float *__restrict__ btp) {
@@ -920,12 +923,14 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
   const int s = blockIdx.y;
   const int64_t r_beg = (int64_t)s * chunk_rows;
   const int64_t r_end = std::min<int64_t>(m, r_beg + chunk_rows);
-  const int nit = lt >> 4;
-  floatx4 acc[2][kLpMax / 16];
+  // NC > 0: exactly NC 16-column tiles of Q (as in the sketch)
+  constexpr int NCM = NC ? NC : kLpMax / 16;
+  const int nit = NC ? NC : lt >> 4;
+  floatx4 acc[2][NCM];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < kLpMax / 16; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NCM; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   uint4 ra[APR], rq[QPR];
   auto load = [&](int64_t r0) {
@@ -971,35 +976,39 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
     __syncthreads();
 #pragma unroll
     for (int kq = 0; kq < KS / 32; ++kq) {
+      // both column sets' A fragments first, so each Q^T fragment read from
+      // LDS feeds the MFMAs of both
+      ushortx8 af[2][NT];
 #pragma unroll
       for (int cs = 0; cs < 2; ++cs) {
         const int cl = wave * 32 + cs * 16 + r16;  // A column inside the tile
-        ushortx8 af[NT];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           if constexpr (sizeof(T) == 2) {
-            af[0][e] = at[kq * 32 + g * 8 + e][cl];
+            af[cs][0][e] = at[kq * 32 + g * 8 + e][cl];
           } else {
             const float x = at[kq * 32 + g * 8 + e][cl];
             const unsigned short hi = f32_to_bf16(x);
             const float r1 = x - bf16_to_f32(hi);
             const unsigned short mid = f32_to_bf16(r1);
-            af[0][e] = hi;
-            af[NT > 1 ? 1 : 0][e] = mid;
-            af[NT > 2 ? 2 : 0][e] = f32_to_bf16(r1 - bf16_to_f32(mid));
+            af[cs][0][e] = hi;
+            af[cs][NT > 1 ? 1 : 0][e] = mid;
+            af[cs][NT > 2 ? 2 : 0][e] = f32_to_bf16(r1 - bf16_to_f32(mid));
           }
         }
+      }
 #pragma unroll
-        for (int it = 0; it < kLpMax / 16; ++it) {
-          if (it < nit) {
-            const ushortx8 qh = *(const ushortx8 *)&qs[0][it * 16 + r16][kq * 32 + g * 8];
-            const ushortx8 ql = *(const ushortx8 *)&qs[1][it * 16 + r16][kq * 32 + g * 8];
+      for (int it = 0; it < NCM; ++it) {
+        if (NC || it < nit) {
+          const ushortx8 qh = *(const ushortx8 *)&qs[0][it * 16 + r16][kq * 32 + g * 8];
+          const ushortx8 ql = *(const ushortx8 *)&qs[1][it * 16 + r16][kq * 32 + g * 8];
+#pragma unroll
+          for (int cs = 0; cs < 2; ++cs)
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-              acc[cs][it] = mfma16_bf16(af[tt], qh, acc[cs][it]);
-              acc[cs][it] = mfma16_bf16(af[tt], ql, acc[cs][it]);
+              acc[cs][it] = mfma16_bf16(af[cs][tt], qh, acc[cs][it]);
+              acc[cs][it] = mfma16_bf16(af[cs][tt], ql, acc[cs][it]);
             }
-          }
         }
       }
     }
@@ -1008,8 +1017,8 @@ __global__ void __launch_bounds__(kThreads) project_kernel(const T *__restrict__
 #pragma unroll
   for (int cs = 0; cs < 2; ++cs)
 #pragma unroll
-    for (int it = 0; it < kLpMax / 16; ++it) {
-      if (it < nit) {
+    for (int it = 0; it < NCM; ++it) {
+      if (NC || it < nit) {
         const int i = l0 + it * 16 + r16;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1052,12 +1061,13 @@ __device__ __forceinline__ double lane_value(const double (&x)[NS], int idx) {
   return readlane_f64(x[NS - 1], idx & 63);
 }
 
-template <int NS>
+// RPW: rows per wave (r = wave + 4 i), 4 RPW >= l; lp = 80 takes 20.
+template <int NS, int RPW = NS == 1 ? 16 : kLpMax / 4>
 __global__ void __launch_bounds__(kTriThreads)
     tridiag_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ dg_out,
                    double *__restrict__ eo_out, double *__restrict__ beta_out, double *__restrict__ v_out) {
   static_assert(kLpMax <= 128 && kLpMax % 16 == 0, "two column slots, rows below 128");
-  constexpr int RPW = NS == 1 ? 16 : kLpMax / 4;  // rows per wave: r = wave + 4 i
+  static_assert(RPW % 2 == 0 && 4 * RPW <= 64 * NS, "rows read in pairs, within the column slots");
   __shared__ double qp[2][4][64 * NS];
   __shared__ double yb[2][64 * NS];
   // per wave: x and p at its own rows (entry i: row wave + 4 i; entries
@@ -1747,6 +1757,31 @@ template <typename T, bool MEAN>
 metis_status_t run_factors_and_residual(const SplitPlan &p, const T *A, int64_t lda, metis_split_t *out,
                                         const float *mu, hipStream_t st);
 
+// The sketch and the projection with the exact count of 16-column tiles
+// compiled in for the common sketch widths (lp = 80, 96: one tile of kLpMax
+// columns), else the form that tests the count at run time.
+template <typename T, bool HL>
+void launch_sketch(dim3 grid, hipStream_t st, const T *A, int64_t m, int64_t n, int64_t lda,
+                   const unsigned short *omt, int l, int lp, int64_t chunk, float *ysk) {
+  if (lp == 80)
+    sketch_kernel<T, HL, kSketchRS, 5><<<grid, kThreads, 0, st>>>(A, m, n, lda, omt, l, lp, chunk, ysk);
+  else if (lp == 96)
+    sketch_kernel<T, HL, kSketchRS, 6><<<grid, kThreads, 0, st>>>(A, m, n, lda, omt, l, lp, chunk, ysk);
+  else
+    sketch_kernel<T, HL><<<grid, kThreads, 0, st>>>(A, m, n, lda, omt, l, lp, chunk, ysk);
+}
+
+template <typename T>
+void launch_project(dim3 grid, hipStream_t st, const T *A, int64_t m, int64_t n, int64_t lda,
+                    const unsigned short *qt, int l, int lp, int64_t chunk_rows, float *btp) {
+  if (lp == 80)
+    project_kernel<T, 5><<<grid, kThreads, 0, st>>>(A, m, n, lda, qt, l, lp, chunk_rows, btp);
+  else if (lp == 96)
+    project_kernel<T, 6><<<grid, kThreads, 0, st>>>(A, m, n, lda, qt, l, lp, chunk_rows, btp);
+  else
+    project_kernel<T><<<grid, kThreads, 0, st>>>(A, m, n, lda, qt, l, lp, chunk_rows, btp);
+}
+
 template <typename T>
 metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void *omega, metis_split_t *out,
                          int32_t *info, hipStream_t st) {
@@ -1760,8 +1795,8 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
   if (p.kind == METIS_OMEGA_GAUSSIAN) {
     omega_transpose_kernel<<<(unsigned)cdiv(n, kOtRows), 256, 0, st>>>((const unsigned short *)omega, n, l, lp,
                                                                        p.omt);
-    sketch_kernel<T><<<dim3((unsigned)cdiv(m, 64 * kSketchRS), p.sk, lz), kThreads, 0, st>>>(A, m, n, lda, p.omt, l, lp,
-                                                                                p.sk_chunk, p.ysk);
+    launch_sketch<T, false>(dim3((unsigned)cdiv(m, 64 * kSketchRS), p.sk, lz), st, A, m, n, lda, p.omt, l, lp,
+                            p.sk_chunk, p.ysk);
     ysrc = p.ysk;
     yparts = p.sk;
   } else {
@@ -1788,8 +1823,7 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     // ---- power iterations: Z = orth(A^T Q) by CholeskyQR2 over the n rows,
     // then Y = A Z (Z as bf16 hi + lo) and Q = orth(Y) again
     for (int it = 0; it < p.power; ++it) {
-      project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
-                                                                                   p.pk_rows, p.btp);
+      launch_project<T>(dim3((unsigned)cdiv(n, 128), p.pk, lz), st, A, m, n, lda, p.qt, l, lp, p.pk_rows, p.btp);
       sum_parts4_kernel<<<(unsigned)cdiv(n * l, 1024), 256, 0, st>>>(p.btp, p.pk, n * l, n * l, p.bt);
       gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.bt, 1, 0, n, l, lp, nullptr, nullptr, nullptr, p.gpart);
       gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
@@ -1798,13 +1832,12 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
       gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
       chol_small_kernel<<<1, kCholThreads, 0, st>>>(p.gram, l, lp, p.rinv, p.info_ws);
       gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.z1, 1, 0, n, l, lp, p.rinv, nullptr, p.zt, nullptr);
-      sketch_kernel<T, true><<<dim3((unsigned)cdiv(m, 64 * kSketchRS), p.sk, lz), kThreads, 0, st>>>(A, m, n, lda, p.zt, l, lp,
-                                                                                        p.sk_chunk, p.ysk);
+      launch_sketch<T, true>(dim3((unsigned)cdiv(m, 64 * kSketchRS), p.sk, lz), st, A, m, n, lda, p.zt, l, lp,
+                             p.sk_chunk, p.ysk);
       cholqr2_y(p.ysk, p.sk);
     }
     // ---- pass 2: projection B^T = A^T Q, then the Gram B B^T
-    project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
-                                                                                 p.pk_rows, p.btp);
+    launch_project<T>(dim3((unsigned)cdiv(n, 128), p.pk, lz), st, A, m, n, lda, p.qt, l, lp, p.pk_rows, p.btp);
     sum_parts4_kernel<<<(unsigned)cdiv(n * l, 1024), 256, 0, st>>>(p.btp, p.pk, n * l, n * l, p.bt);
     gram_kernel<<<p.gb_parts, kGramThreads, 0, st>>>(p.bt, 1, 0, n, l, lp, nullptr, nullptr, nullptr, p.gpart);
     gram_reduce_kernel<<<rgrid_red, 256, 0, st>>>(p.gpart, p.gb_parts, lp * lp, p.gram);
@@ -1827,8 +1860,7 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
     ws = metis_wide::wide_chol_inv(p.gram, l, lp, p.rinv, p.info_ws, p.wa, p.winv, p.waux, st);
     if (ws != METIS_OK) return ws;
     apply_rinv_kernel<<<dim3((unsigned)cdiv(m, 64), nt), kThreads, 0, st>>>(p.q1, m, l, lp, p.rinv, p.q, p.qt);
-    project_kernel<T><<<dim3((unsigned)cdiv(n, 128), p.pk, lz), kThreads, 0, st>>>(A, m, n, lda, p.qt, l, lp,
-                                                                                 p.pk_rows, p.btp);
+    launch_project<T>(dim3((unsigned)cdiv(n, 128), p.pk, lz), st, A, m, n, lda, p.qt, l, lp, p.pk_rows, p.btp);
     const float *bt = p.btp;
     if (p.pk > 1) {
       sum_parts_kernel<<<(unsigned)cdiv(n * l, 256), 256, 0, st>>>(p.btp, p.pk, n * l, n * l, p.bt);
@@ -1839,7 +1871,9 @@ metis_status_t run_split(const SplitPlan &p, const T *A, int64_t lda, const void
   }
   // ---- small SVD of B (from its Gram, in p.gram) and the factors
   if (!p.wide) {
-    if (lp > 64)
+    if (lp == 80)
+      tridiag_kernel<2, 20><<<1, kTriThreads, 0, st>>>(p.gram, l, lp, p.waux, p.waux + lp, p.waux + 2 * lp, p.wv);
+    else if (lp > 64)
       tridiag_kernel<2><<<1, kTriThreads, 0, st>>>(p.gram, l, lp, p.waux, p.waux + lp, p.waux + 2 * lp, p.wv);
     else
       tridiag_kernel<1><<<1, kTriThreads, 0, st>>>(p.gram, l, lp, p.waux, p.waux + lp, p.waux + 2 * lp, p.wv);
