@@ -1121,14 +1121,30 @@ __global__ void __launch_bounds__(kTriThreads)
   }
   __syncthreads();
   if (t == 0) td[0] = n > 0 ? g[0] : 0.0;
+  // |x|, alpha and beta of the reflector for x (row j right of its
+  // diagonal). Each step forms the next step's values as soon as the next x
+  // is known, so their reduction, square root and reciprocal run between
+  // the update's multiply-adds instead of ahead of the next matrix-vector
+  // product.
+  double nrm2, alpha, beta;
+  auto reflector = [&](int j) {
+    double x2 = 0.0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) x2 = fma(xv[s], xv[s], x2);
+    nrm2 = wave_sum_f64(x2);
+    const double x0 = lane_value(xv, j + 1), nrm = sqrt(nrm2);
+    alpha = x0 >= 0.0 ? -nrm : nrm;
+    beta = nrm2 > 0.0 ? recip_f64(nrm * (nrm + fabs(x0))) : 0.0;
+  };
+  reflector(0);
 
   for (int j = 0; j + 2 < n; ++j) {
     const int buf = j & 1;
-    // ---- this wave's partial of A x, and (alongside) |x|, alpha, beta
+    // ---- this wave's partial of A x
     double xr[RPW];
     own_rows(xv, xl[w]);
     read_rows(xl[w], xr);
-    double q4[4][NS], x2 = 0.0;
+    double q4[4][NS];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -1138,13 +1154,7 @@ __global__ void __launch_bounds__(kTriThreads)
 #pragma unroll
       for (int s = 0; s < NS; ++s) q4[i & 3][s] = fma(a[i][s], xr[i], q4[i & 3][s]);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qp[buf][w][lane + 64 * s] = (q4[0][s] + q4[1][s]) + (q4[2][s] + q4[3][s]);
-      x2 = fma(xv[s], xv[s], x2);
-    }
-    const double nrm2 = wave_sum_f64(x2), x0 = lane_value(xv, j + 1), nrm = sqrt(nrm2);
-    const double alpha = x0 >= 0.0 ? -nrm : nrm;
-    const double beta = nrm2 > 0.0 ? recip_f64(nrm * (nrm + fabs(x0))) : 0.0;
+    for (int s = 0; s < NS; ++s) qp[buf][w][lane + 64 * s] = (q4[0][s] + q4[1][s]) + (q4[2][s] + q4[3][s]);
     if (w == ((j + 1) & 3)) {
 #pragma unroll
       for (int i = 0; i < RPW; ++i)
@@ -1180,6 +1190,8 @@ __global__ void __launch_bounds__(kTriThreads)
       dnext = c == j + 1 ? xn : dnext;
       xv[s] = (c > j + 1 && c < n) ? xn : 0.0;
     }
+    const double alpha_j = alpha, beta_j = beta;
+    reflector(j + 1);
     // ---- A -= v w^T + w v^T on every row
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -1191,8 +1203,8 @@ __global__ void __launch_bounds__(kTriThreads)
     // and the reflector
     if (w == 0) {
       td[lane == ((j + 1) & 63) ? j + 1 : kLpMax + lane] = dnext;
-      te[lane == 0 ? j : kLpMax + lane] = alpha;
-      tb[lane == 0 ? j : kLpMax + lane] = beta;
+      te[lane == 0 ? j : kLpMax + lane] = alpha_j;
+      tb[lane == 0 ? j : kLpMax + lane] = beta_j;
 #pragma unroll
       for (int s = 0; s < NS; ++s)
         if (lane + 64 * s < lp) v_out[(int64_t)j * lp + lane + 64 * s] = v[s];
