@@ -776,8 +776,8 @@ __device__ __forceinline__ void store_acc_mx4(const floatx16 (&acc)[MXW][MXW], i
 // per row, the same swizzle), consumed by bf16 32x32x16 MFMAs, so its loads
 // overlap the end of the main product instead of following it.
 constexpr int kDmaStages = 4;
-constexpr unsigned kMxMaxGrid = 1u << 30;  // cap on the MXFP4 kernel's workgroups: above any tile count, so each
-                                           // takes one tile (persistent grids of 224-256 measured slower)
+constexpr unsigned kMxMaxGrid = 256;  // persistent grid: one workgroup per CU (the LDS ring allows one), each
+                                      // taking every 256th tile (1-3 % faster than one workgroup per tile)
 constexpr int DMA_CODE_BYTES = BM * 64;            // one operand's codes per stage
 constexpr int DMA_STAGE = 2 * DMA_CODE_BYTES;      // A then B
 constexpr int DMA_SCALE_GROUP = 2 * BM * 16;       // A then B scales of four stages
