@@ -49,11 +49,12 @@ __global__ void fill_u32_kernel(uint32_t *p, uint32_t v, int n) {
 // independent of the order of arrival).
 template <typename T>
 __global__ void amax_kernel(const T *__restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint32_t *out) {
+  // workgroup b takes rows b, b + gridDim.x, ...; its threads stride along
+  // the row (coalesced loads, no index division)
   float m = 0.0f;
-  const int64_t total = rows * cols;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / cols, c = i - r * cols;
-    m = fmaxf(m, fabsf(load_f32(x + r * ldx + c)));
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const T *row = x + r * ldx;
+    for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) m = fmaxf(m, fabsf(load_f32(row + c)));
   }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(m));
@@ -175,8 +176,7 @@ metis_status_t launch_quant(const T *x, int64_t rows, int64_t cols, int64_t ldx,
                             uint32_t *amax_ws, hipStream_t stream) {
   if (NV) {
     fill_u32_kernel<int><<<1, 64, 0, stream>>>(amax_ws, 0u, 1);
-    const int64_t total = rows * cols;
-    const int grid = (int)std::min<int64_t>(2048, cdiv(total, kThreads * 8));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(2048, rows));
     amax_kernel<T><<<grid, kThreads, 0, stream>>>(x, rows, cols, ldx, amax_ws);
   }
   constexpr int B = NV ? 16 : 32;
