@@ -203,18 +203,29 @@ __global__ void __launch_bounds__(64)
   }
 }
 
-// NVFP4 variant: both operands decoded exactly to bf16 (E2M1 x E4M3 has at
-// most six significant bits) and multiplied on the bf16 MFMA; the two tensor
-// scales multiply the fp32 result once. One wave: 32 rows x 32*NCT columns;
-// per 32-element step lane (r, h) decodes block h (16 elements) of its row and
-// feeds its first and second 8 values to two 32x32x16 MFMAs.
-__device__ __forceinline__ void nv_decode16(const uint2 codes, uint32_t sbyte, ushortx8 &lo8, ushortx8 &hi8) {
-  const float sv = e4m3_value(sbyte);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    lo8[e] = (unsigned short)(__float_as_uint(e2m1_value((codes.x >> (4 * e)) & 15u) * sv) >> 16);
-    hi8[e] = (unsigned short)(__float_as_uint(e2m1_value((codes.y >> (4 * e)) & 15u) * sv) >> 16);
-  }
+// Eight E2M1 codes (element 2p in the low nibble of byte p, 2p + 1 in the
+// high one) times one block scale, as fp16. The byte selector of the FP4
+// conversion is an immediate, hence the four spelled-out calls.
+__device__ __forceinline__ halfx8 fp4x8_to_f16(uint32_t word, halfx2 scale) {
+  const halfx2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * scale;
+  const halfx2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * scale;
+  const halfx2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * scale;
+  const halfx2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * scale;
+  return halfx8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+}
+
+// NVFP4 variant: both operands decoded exactly to fp16 by the hardware FP4
+// conversion and one packed multiply by the E4M3 block scale (each product
+// has at most five significant bits and lies in [2^-10, 2688]) and multiplied
+// on the fp16 MFMA; the two tensor scales multiply the fp32 result once. One
+// wave: 32 rows x 32*NCT columns; per 32-element step lane (r, h) decodes
+// block h (16 elements) of its row and feeds its first and second 8 values to
+// two 32x32x16 MFMAs.
+__device__ __forceinline__ void nv_decode16(const uint2 codes, uint32_t sbyte, halfx8 &lo8, halfx8 &hi8) {
+  const _Float16 sv = (_Float16)e4m3_value(sbyte);  // exact: every E4M3 value is an fp16 value
+  const halfx2 s2 = {sv, sv};
+  lo8 = fp4x8_to_f16(codes.x, s2);
+  hi8 = fp4x8_to_f16(codes.y, s2);
 }
 
 template <int NCT>
@@ -234,19 +245,19 @@ __global__ void __launch_bounds__(64)
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[j][q] = 0.0f;
   const bool rok = row < rows;
-  const ushortx8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  const halfx8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int64_t t0 = t_beg; t0 < t_end; t0 += 32) {
     const int64_t e0 = t0 + h * 16;
-    ushortx8 a0 = z8, a1 = z8;
+    halfx8 a0 = z8, a1 = z8;
     if (rok && e0 < t_end) nv_decode16(*(const uint2 *)(ac + row * (T / 2) + e0 / 2), as[row * nb + e0 / 16], a0, a1);
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
       const int col = j * 32 + r;
-      ushortx8 b0 = z8, b1 = z8;
+      halfx8 b0 = z8, b1 = z8;
       if (col < cols && e0 < t_end)
         nv_decode16(*(const uint2 *)(bc + (int64_t)col * (T / 2) + e0 / 2), bs[(int64_t)col * nb + e0 / 16], b0, b1);
-      acc[j] = mfma32_bf16(a0, b0, acc[j]);
-      acc[j] = mfma32_bf16(a1, b1, acc[j]);
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc[j], 0, 0, 0);
     }
   }
   const float sc = ats[0] * bts[0];
@@ -1281,16 +1292,6 @@ __global__ void __launch_bounds__(256)
 // fp16 32x32x16 MFMA with fp32 accumulation; the product of the two tensor
 // scales multiplies the accumulators once before the correction. Thread t
 // stages half (t & 1) of row t >> 1 of each operand: 32 codes, two blocks.
-// Eight E2M1 codes (element 2p in the low nibble of byte p, 2p + 1 in the
-// high one) times one block scale, as fp16. The byte selector of the FP4
-// conversion is an immediate, hence the four spelled-out calls.
-__device__ __forceinline__ halfx8 fp4x8_to_f16(uint32_t word, halfx2 scale) {
-  const halfx2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * scale;
-  const halfx2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * scale;
-  const halfx2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * scale;
-  const halfx2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * scale;
-  return halfx8{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
-}
 
 __global__ void __launch_bounds__(kGemmThreads, 1)
     gemm_nv_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, const float *__restrict__ ats,
