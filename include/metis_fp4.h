@@ -149,8 +149,10 @@ metis_status_t fp4_block_dequant(const metis_fp4_t *in, float *y, int64_t ldy, h
  *         values); METIS_OMEGA_COLUMNS: int32[l] distinct ids in [0, n)
  *         (ids out of range give undefined values, never an out-of-bounds read).
  *  1 <= k <= l <= min(m, n); k <= 96 and l <= 512 (beyond: METIS_ERR_UNSUPPORTED).
- *  Sketches with l <= 96 keep the l x l problems in LDS; wider ones use
- *  global-memory forms (correct, much slower). m and n multiples of 32; A
+ *  Sketches with l <= 96 keep the l x l problems in LDS; wider ones keep
+ *  them in global memory (their Cholesky and tridiagonal reduction take one
+ *  launch per 16 pivots or per reflector, so they are launch-bound). m and n
+ *  multiples of 32; A
  *  16-byte aligned and lda * sizeof(element) a multiple of 16.
  *  out:   caller provides U, S, V (fp32) and the codes/scales (/tensor_scale)
  *         buffers of Ut_q, Vt_q, R_q and/or Rt_q (each fp4 member's fmt must
