@@ -84,6 +84,25 @@ def test_linear_deterministic():
     assert torch.equal(a, b)
 
 
+def test_linear_persistent_grid_with_ragged_tiles():
+    """More output tiles than the MXFP4 kernel's persistent grid of 256
+    workgroups (17 x 17 = 289), the last tile row and column ragged: the
+    workgroups that take a second tile take the ragged ones. Rows of the
+    first and of the last two tile rows are checked against the oracle."""
+    Mt, K, N = 4128, 1024, 4160
+    X = _small(211, Mt, K, 8, 16)
+    W = _small(212, N, K, 8, 16, kind="powerlaw")
+    rx, rw = _operand(X, ("n",)), _operand(W, ("n",))
+    Y = M.spectral_fp4_linear_fwd(rx, rw)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(0, 64), np.arange(Mt - 96, Mt)])
+    got = Y[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    want = OL.gemm_nt(G.record_to_dict(rx), "n", G.record_to_dict(rw), "n", rows=rows)
+    err = _rel(got, want)
+    print("persistent ragged rel err %.3e" % err, flush=True)
+    assert err <= 1e-5
+
+
 def _full(cfg, gemms, nrows=512):
     names = set()
     for _, a, _, b, _ in gemms:
