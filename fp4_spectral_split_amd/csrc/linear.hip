@@ -770,7 +770,11 @@ __device__ __forceinline__ void store_acc_mx4(const floatx16 (&acc)[MXW][MXW], i
 // MXFP4 main kernel (K a multiple of 512): C = Ra Rb^T (+ L1 L2^T) on the
 // scaled FP4 MFMA. Four waves, one per SIMD, each a 128 x 128 sub-tile (4 x 4
 // MFMA blocks of 32 x 32; 256 accumulators, kept in AGPRs). Operands go
-// straight from global memory to LDS (global_load_lds, 16 bytes per lane)
+// straight from global memory to LDS (buffer loads with the LDS destination,
+// 16 bytes per lane: the operand base in a buffer resource, a fixed 32-bit
+// offset per lane, the stage's offset in a scalar register, so a load costs
+// no vector address arithmetic; the wave index is made uniform so each LDS
+// destination is a scalar)
 // into a ring of four stages of 128 contraction elements (A and B codes, 256
 // rows x 64 bytes each, 16-byte units XOR-swizzled by row so the fragment
 // reads are conflict free: unit u of row r sits at r * 4 + (u ^ ((r / 4) & 3))),
@@ -804,14 +808,20 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void *)p);
 }
 
-// lane i of the wave writes its bytes at lds_wave_base + i * size
-__device__ __forceinline__ void dma_load16(const void *g, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)g,
-                                   (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+// 16 bytes per lane from a buffer (base in the resource, voffset per lane,
+// soffset uniform) straight into LDS at lds_wave_base + lane * 16
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                          void *lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voff,
+                                           soff, 0, 0);
 }
-__device__ __forceinline__ void dma_load4(const void *g, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)g,
-                                   (__attribute__((address_space(3))) void *)lds_wave_base, 4, 0, 0);
+__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                         void *lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_wave_base, 4, voff,
+                                           soff, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
 // s_waitcnt with only the vector-memory count limited (gfx9 encoding)
@@ -837,10 +847,14 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
                    float *__restrict__ C, int64_t ldc) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[DMA_LDS];
   const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int r32 = lane & 31, h = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
   const int mtiles = (int)cdiv(M, BM), ntiles_n = (int)cdiv(N, BN), ntiles = mtiles * ntiles_n;
+  // buffer resources of the operands (byte ranges below 2^31 by the host's check)
+  const __amdgpu_buffer_rsrc_t rA = raw_rsrc(ac, (uint32_t)(M * (T / 2))), rB = raw_rsrc(bc, (uint32_t)(N * (T / 2)));
+  const __amdgpu_buffer_rsrc_t rSA = raw_rsrc(as, (uint32_t)(M * (T / 32))), rSB = raw_rsrc(bs, (uint32_t)(N * (T / 32)));
+  const __amdgpu_buffer_rsrc_t rL1 = raw_rsrc(l1, (uint32_t)(M * rp * 2)), rL2 = raw_rsrc(l2, (uint32_t)(N * rp * 2));
   const int64_t nb = T / 32;
   const int nst = (int)(T / 128);
   // correction stages: 32 bf16 panel columns (64 bytes per row) of L1 rows
@@ -870,24 +884,25 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
 
     auto issue_main = [&](int st) {  // eight loads per wave: codes of FP4 stage st
       uint8_t *sbuf = smem + (st % kDmaStages) * DMA_STAGE;
-      const uint8_t *as_ = ac + (int64_t)st * 64, *bs_ = bc + (int64_t)st * 64;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dma_load16(as_ + offA[i], sbuf + (4 * wave + i) * 1024);
-        dma_load16(bs_ + offB[i], sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
+        buf_dma16(rA, offA[i], (uint32_t)st * 64, sbuf + (4 * wave + i) * 1024);
+        buf_dma16(rB, offB[i], (uint32_t)st * 64, sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
       }
     };
+    uint32_t offL1[4], offL2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
+      offL1[i] = (uint32_t)(min(m0 + r, M - 1) * rp * 2 + u * 16);
+      offL2[i] = (uint32_t)(min(n0 + r, N - 1) * rp * 2 + u * 16);
+    }
     auto issue_corr = [&](int st) {  // eight loads per wave: panel columns of correction stage st
       uint8_t *sbuf = smem + (st % kDmaStages) * DMA_STAGE;
-      const uint8_t *l1s = (const uint8_t *)l1 + (int64_t)(st - nst) * 64;
-      const uint8_t *l2s = (const uint8_t *)l2 + (int64_t)(st - nst) * 64;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
-        const uint32_t oa = (uint32_t)(min(m0 + r, M - 1) * rp * 2 + u * 16);
-        const uint32_t ob = (uint32_t)(min(n0 + r, N - 1) * rp * 2 + u * 16);
-        dma_load16(l1s + oa, sbuf + (4 * wave + i) * 1024);
-        dma_load16(l2s + ob, sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
+        buf_dma16(rL1, offL1[i], (uint32_t)(st - nst) * 64, sbuf + (4 * wave + i) * 1024);
+        buf_dma16(rL2, offL2[i], (uint32_t)(st - nst) * 64, sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
       }
     };
     auto issue = [&](int st) {
@@ -896,8 +911,8 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     };
     auto issue_scales = [&](int g) {  // two loads per wave: scales of stages 4 g .. 4 g + 3
       uint8_t *sg = smem + DMA_SCALE_BASE + (g % 2) * DMA_SCALE_GROUP;
-      dma_load16(as + (int64_t)g * 16 + offSA, sg + wave * 1024);
-      dma_load16(bs + (int64_t)g * 16 + offSB, sg + BM * 16 + wave * 1024);
+      buf_dma16(rSA, offSA, (uint32_t)g * 16, sg + wave * 1024);
+      buf_dma16(rSB, offSB, (uint32_t)g * 16, sg + BM * 16 + wave * 1024);
     };
     // Wait until the codes of stage s (and the scales of its group, issued
     // before them) have landed: at most the 8 loads of each later stage
@@ -1096,7 +1111,7 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
 // (rows x cols, cols <= 32 NCT) = NT(A, B) over T-chunk s. A workgroup of
 // four waves takes 128 rows of A (wave w: rows 32 w ..) and all of B; a stage
 // is 256 contraction elements (128 code bytes and 8 scale bytes per row).
-// Codes go to LDS with 16-byte global_load_lds, eight lanes per row, so one
+// Codes go to LDS with 16-byte buffer loads (LDS destination), eight lanes per row, so one
 // load instruction covers eight whole 128-byte row pieces (loading them in
 // the MFMA's own layout, one row per lane, made the address units the
 // bottleneck); slot 8 r + (u ^ (r & 7)) of a stage holds unit u of row r,
@@ -1200,7 +1215,7 @@ __global__ void __launch_bounds__(256)
                       int64_t chunk, float *__restrict__ out) {
   using L = SkLayout<NCT>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSkStages * L::STAGE];
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, r = lane & 31, h = lane >> 5;
+  const int t = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63, r = lane & 31, h = lane >> 5;
   const int64_t row0 = (int64_t)blockIdx.x * kSkRows;
   const int64_t t_beg = (int64_t)blockIdx.y * chunk, t_end = std::min<int64_t>(T, t_beg + chunk);
   const int nst = (int)((t_end - t_beg) / 256);
@@ -1220,16 +1235,20 @@ __global__ void __launch_bounds__(256)
   const uint32_t offSA = (uint32_t)(std::min<int64_t>(row0 + (t >> 1), rows - 1) * nbr + 4 * (t & 1));
   const int pb = t % (64 * NCT);  // waves past NCT repeat the same loads (same bytes to the same slots)
   const uint32_t offSB = (uint32_t)(std::min(pb >> 1, cols - 1) * nbr + 4 * (pb & 1));
+  // buffer resources (byte ranges below 2^31 by the host's check): the loads
+  // take a fixed 32-bit offset per lane and the stage's offset as a scalar
+  const __amdgpu_buffer_rsrc_t rA = raw_rsrc(ac, (uint32_t)(rows * (T / 2))), rB = raw_rsrc(bc, (uint32_t)(cols * (T / 2)));
+  const __amdgpu_buffer_rsrc_t rSA = raw_rsrc(as, (uint32_t)(rows * nbr)), rSB = raw_rsrc(bs, (uint32_t)(cols * nbr));
   auto issue = [&](int st) {
     uint8_t *sb = smem + (st % kSkStages) * L::STAGE;
     const int64_t k0 = t_beg + 256 * (int64_t)st;
-    const uint8_t *a_ = ac + k0 / 2, *b_ = bc + k0 / 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_load16(a_ + offA[i], sb + L::A_CODES + (256 * i + 64 * wave) * 16);
+    for (int i = 0; i < 4; ++i) buf_dma16(rA, offA[i], (uint32_t)(k0 / 2), sb + L::A_CODES + (256 * i + 64 * wave) * 16);
 #pragma unroll
-    for (int i = 0; i < NCT; ++i) dma_load16(b_ + offB[i], sb + L::B_CODES + (256 * i + 64 * wave) * 16);
-    dma_load4(as + k0 / 32 + offSA, sb + L::A_SC + 64 * wave * 4);
-    dma_load4(bs + k0 / 32 + offSB, sb + L::B_SC + (64 * wave % (64 * NCT)) * 4);
+    for (int i = 0; i < NCT; ++i)
+      buf_dma16(rB, offB[i], (uint32_t)(k0 / 2), sb + L::B_CODES + (256 * i + 64 * wave) * 16);
+    buf_dma4(rSA, offSA, (uint32_t)(k0 / 32), sb + L::A_SC + 64 * wave * 4);
+    buf_dma4(rSB, offSB, (uint32_t)(k0 / 32), sb + L::B_SC + (64 * wave % (64 * NCT)) * 4);
   };
   floatx16 acc[NCT];
 #pragma unroll
