@@ -40,6 +40,9 @@ constexpr int kLpMax = 96;
 constexpr int kSketchRS = 2;  // 16-row groups per wave in the sketch (a workgroup: 64 kSketchRS rows)
 constexpr int kMaxPowerIterations = 16;  // Gaussian / sampled sketch width handled in LDS
 constexpr int kThreads = 256;
+// workgroups resident at once in the sketch and projection launches: two per
+// CU (two waves per SIMD) on the 256 CUs
+constexpr int64_t kSlots = 512;
 constexpr int kGramRows = 64;      // rows per Gram chunk (narrow path)
 constexpr int kGramThreads = 512;  // 8 waves: two per 16-row block
 // assemble kernels: 16 rows per thread, at most 8 row groups (128 rows) per workgroup
@@ -99,6 +102,22 @@ struct SplitPlan {
   size_t bytes;
 };
 
+// Split-K factor of a launch of `tiles` output tiles whose contraction takes
+// `steps` steps of `step_bytes` per workgroup, each split writing a partial
+// of `part_bytes` that the next kernel reads. The workgroups run in rounds of
+// kSlots and a workgroup's time is its steps plus about two (its first loads
+// and its stores), so the cost in bytes moved is rounds x (steps per
+// workgroup + 2) x kSlots x step_bytes + 2 x factor x part_bytes; the least
+// cost wins, the smallest factor on a tie.
+int64_t pick_split(int64_t tiles, int64_t steps, int64_t step_bytes, int64_t part_bytes) {
+  int64_t best = 1, best_cost = INT64_MAX;
+  for (int64_t f = 1; f <= std::min<int64_t>(steps, 64); ++f) {
+    const int64_t cost = cdiv(tiles * f, kSlots) * (cdiv(steps, f) + 2) * kSlots * step_bytes + 2 * f * part_bytes;
+    if (cost < best_cost) best = f, best_cost = cost;
+  }
+  return best;
+}
+
 int64_t pick_rows_per_part(int64_t rows, int64_t want_parts, int64_t quantum) {
   int64_t per = round_up(cdiv(rows, std::max<int64_t>(1, want_parts)), quantum);
   return std::max<int64_t>(per, quantum);
@@ -110,11 +129,10 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
   p.wide = l > kLpMax;
   p.lp = (int)round_up(l, p.wide ? 64 : 16);
   p.kp = (int)round_up(k, 32);
-  // sketch: 128-row tiles, split-K bounded so partial traffic stays ~10% of A
-  const int64_t m_tiles = cdiv(m, 128);
+  // sketch: 128-row tiles of 128-column steps, split-K as pick_split finds
+  const int64_t l_tiles = cdiv(p.lp, kLpMax);
   if (kind == METIS_OMEGA_GAUSSIAN || q > 0) {
-    int64_t want = std::min<int64_t>(cdiv(768, m_tiles), std::max<int64_t>(1, n * elem / (20 * l)));
-    want = std::max<int64_t>(1, std::min<int64_t>(want, n / 128));
+    const int64_t want = pick_split(cdiv(m, 128) * l_tiles, cdiv(n, 128), 128 * 128 * elem, m * p.lp * 4);
     p.sk_chunk = round_up(cdiv(n, want), 128);
     p.sk = (int)cdiv(n, p.sk_chunk);
   } else {
@@ -124,9 +142,8 @@ SplitPlan make_plan(int64_t m, int64_t n, int l, int k, int kind, int fmt, int e
   // narrow Grams: one partial per 128-row chunk; wide Grams: 16 row ranges
   p.gy_rows = p.wide ? pick_rows_per_part(m, 16, 32) : kGramRows;
   p.gy_parts = (int)cdiv(m, p.gy_rows);
-  const int64_t n_tiles = cdiv(n, 128);
-  int64_t wantp = std::min<int64_t>(cdiv(768, n_tiles), std::max<int64_t>(1, m * elem / (8 * l)));
-  wantp = std::max<int64_t>(1, std::min<int64_t>(wantp, m / 64));
+  // projection: 128-column tiles of 64-row steps, split the same way
+  const int64_t wantp = pick_split(cdiv(n, 128) * l_tiles, cdiv(m, 64), 64 * 128 * elem, n * p.lp * 4);
   p.pk_rows = round_up(cdiv(m, wantp), 64);
   p.pk = (int)cdiv(m, p.pk_rows);
   p.gb_rows = p.wide ? pick_rows_per_part(n, 16, 32) : kGramRows;
@@ -193,11 +210,12 @@ __global__ void __launch_bounds__(256) omega_transpose_kernel(const unsigned sho
 
 // ================================================================== sketch
 // ysk[s] = A[:, chunk s] * Omega[chunk s, :]. 4 waves x 32 rows; the Omega^T
-// chunk (lp x 128) is staged in LDS and shared by the waves. Lane (r, g) loads
-// 32 consecutive elements of its row (contraction slots permuted consistently
-// with the Omega operand), so each row's 256 bytes per step are read whole.
-// The next step's A elements and Omega^T pieces are loaded into registers
-// while the current step is multiplied.
+// chunk (lp x 128) is staged in LDS and shared by the waves. A step is four
+// 32-column MFMA slots; lane (r, g) holds elements 8g .. 8g + 7 of each slot
+// of its row, so one load instruction reads 64 contiguous bytes of each of
+// its 16 rows (a lane reading 64 contiguous bytes of one slot-permuted row
+// took 5-20 % longer). The next step's A elements and Omega^T pieces are
+// loaded into registers while the current step is multiplied.
 // HL: the right-hand factor is an fp32 matrix carried as bf16 hi + lo
 // (omt holds its hi rows 0 .. lp - 1, then its lo rows), both multiplied, so
 // the product is fp32-accurate (the power iterations' Y = A Z).
@@ -235,7 +253,7 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
   // the waits for a step's data stay counted while the next step's loads
   // are in flight: rows past m only feed rows of ysk that are not stored;
   // A's columns past the chunk are zeroed when the step is taken (n and the
-  // chunk ends are multiples of 32, so a lane's 32 columns are all in or all
+  // chunk ends are multiples of 32, so a 32-column slot is all in or all
   // out), which also cancels the clamped Omega columns they meet; Omega^T
   // rows past lt go to LDS rows that no MFMA reads.
   static_assert(OPR * kThreads == kLpMax * (KS / 8), "Omega^T pieces fill the LDS rows exactly");
@@ -249,10 +267,13 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs) {
       const int64_t row = min(row0 + rs * 16 + r16, m - 1);
-      const int64_t cc = min(c0 + g * 32, n - 32);
-      const intx4 *src = (const intx4 *)(A + row * lda + cc);
+      const T *arow = A + row * lda;
 #pragma unroll
-      for (int j = 0; j < AV; ++j) st.a[rs][j] = src[j];
+      for (int j = 0; j < AV; ++j) {
+        const int64_t cc = min(c0 + (j / (AV / 4)) * 32 + g * 8 + (j % (AV / 4)) * (16 / (int)sizeof(T)),
+                               n - 16 / (int)sizeof(T));
+        st.a[rs][j] = *(const intx4 *)(arow + cc);
+      }
     }
 #pragma unroll
     for (int h = 0; h < NH; ++h)
@@ -277,11 +298,10 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
         const int idx = t + kThreads * p;
         *(intx4 *)&lds[h][idx / (KS / 8)][(idx % (KS / 8)) * 8] = nx.o[h][p];
       }
-    const int a_in = c0 + g * 32 < c_end ? -1 : 0;  // word mask
 #pragma unroll
     for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
-      for (int j = 0; j < AV; ++j) ca[rs][j] = nx.a[rs][j] & a_in;
+      for (int j = 0; j < AV; ++j) ca[rs][j] = nx.a[rs][j] & (c0 + (j / (AV / 4)) * 32 < c_end ? -1 : 0);
     // the next step's loads (the last step reloads itself, from cache) are
     // in flight while this step is multiplied
     nx = load(c0 + KS < c_end ? c0 + KS : c0);
@@ -319,7 +339,7 @@ __global__ void __launch_bounds__(kThreads) sketch_kernel(const T *__restrict__ 
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int h = 0; h < NH; ++h) {
-            const ushortx8 b = *(const ushortx8 *)&lds[h][ct * 16 + r16][g * 32 + j * 8];
+            const ushortx8 b = *(const ushortx8 *)&lds[h][ct * 16 + r16][j * 32 + g * 8];
 #pragma unroll
             for (int rs = 0; rs < RS; ++rs)
 #pragma unroll
