@@ -619,20 +619,20 @@ __global__ void __launch_bounds__(256)
 // I. After the last step the pivots d_j are those of G = L D L^T and the
 // block holds L^-1, so R = D^1/2 L^T and R^-1 = L^-T D^-1/2. Absent pivots
 // (d_j <= tol) get m_p = 0 and a zero row and column of R^-1.
-// Each thread keeps its elements of G' and L^-1 in registers; a row is
-// written to LDS (CG, CL) once it is final (after the step before it is
-// used), so one barrier per step suffices. Ownership: the 256 threads form a
-// 16 x 16 grid; thread (tr, tc) holds rows tr + 16 a and columns tc + 16 b
-// (a, b < kCholB), so per step it reads 3 B + 1 values of the published row
-// j for its updates. The updates need no per-element test: a row of L^-1 is
-// zero right of its diagonal, so subtracting row j leaves every column
-// beyond j unchanged, and the lower part of G', rows at or above j and the
-// rows a thread already published take garbage that is never read again
-// (each published row is read only in its own step and by the output), so
-// every step is the same straight-line code. Each thread forms 1 / d_j
-// itself.
+// The steps are taken in panels of 16 pivots (blocked Gauss-Jordan):
+//  - panel phase, wave 0 alone and without barriers: the panel's 16 rows sit
+//    in registers (lane y holds columns y and y + 64 of the row laid out as
+//    [L^-1 columns 0 .. j0 + 15 | G' columns j0 ..]) and are eliminated among
+//    themselves; a step's multipliers are the pivot row's own entries at the
+//    later rows' columns (the trailing matrix is symmetric), read from the
+//    lanes that hold them;
+//  - trailing phase, all four waves: every row p below the panel loses
+//    sum_j m_pj row_j over the panel's final rows, m_pj = row_j[p] / d_j,
+//    which is what the panel's 16 single steps would subtract from it.
+// Each published row is final; the lower part of G' takes values that are
+// never read. Rows and columns in [l, lpad) are zero: absent pivots.
 constexpr int kCholThreads = 256;
-constexpr int kCholB = kLpMax / 16;
+constexpr int kCholPanel = 16;
 
 __device__ __forceinline__ double recip_f64(double d) {
   double r = __builtin_amdgcn_rcp(d);  // hardware estimate, refined by Newton steps
@@ -642,9 +642,13 @@ __device__ __forceinline__ double recip_f64(double d) {
 
 __global__ void __launch_bounds__(kCholThreads)
     chol_small_kernel(const double *__restrict__ g, int l, int lp, double *__restrict__ out, int *info) {
-  __shared__ double CG[kLpMax][kLpMax + 1];  // published rows of G' (upper part meaningful)
-  __shared__ double CL[kLpMax][kLpMax + 1];  // published rows of L^-1
+  // published rows of G' (upper part meaningful) and of L^-1, one array so
+  // a lane can address either by an offset from its start
+  __shared__ double CGL[2][kLpMax][kLpMax + 1];
+  auto &CG = CGL[0];
+  auto &CL = CGL[1];
   __shared__ double rs[kLpMax];               // d_j^-1/2, 0 for an absent pivot
+  __shared__ double dinv[kLpMax];             // 1 / d_j, 0 for an absent pivot
   __shared__ int dead[kLpMax];
   __shared__ double tol_s;
   const int t = threadIdx.x;
@@ -702,49 +706,89 @@ __global__ void __launch_bounds__(kCholThreads)
     md = wave_max(md);
     if (t == 0) tol_s = (double)l * 2.220446049250313e-16 * md;
   }
-  const int tr = t >> 4, tc = t & 15;
-  double vg[kCholB][kCholB], vl[kCholB][kCholB];
+  constexpr int PB = kCholPanel;
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lpad = (l + PB - 1) / PB * PB;
   __syncthreads();
   const double tol = tol_s;
+  // Every LDS access below is unconditional, its address selected per lane
+  // (a lane with no element uses the pad column kLpMax of CG, never read as
+  // data), so no branch separates the accesses and they stay in flight
+  // together.
+  for (int j0 = 0; j0 < lpad; j0 += PB) {
+    if (wave == 0) {
+      // unified column y: L^-1 column y for y < j0 + PB, else G' column y - PB
+      double *ad[2];
+      bool ok[2];
 #pragma unroll
-  for (int a = 0; a < kCholB; ++a)
-#pragma unroll
-    for (int b = 0; b < kCholB; ++b) {
-      vg[a][b] = CG[tr + 16 * a][tc + 16 * b];
-      vl[a][b] = CL[tr + 16 * a][tc + 16 * b];
-    }
-  for (int j = 0; j + 1 < l; ++j) {
-    const double d = CG[j][j];
-    double cm[kCholB], gx[kCholB], lx[kCholB];
-#pragma unroll
-    for (int a = 0; a < kCholB; ++a) cm[a] = CG[j][tr + 16 * a];
-#pragma unroll
-    for (int b = 0; b < kCholB; ++b) {
-      gx[b] = CG[j][tc + 16 * b];
-      lx[b] = CL[j][tc + 16 * b];
-    }
-    const double ij = d > tol ? recip_f64(d) : 0.0;
-#pragma unroll
-    for (int a = 0; a < kCholB; ++a) {
-      const double m = cm[a] * ij;
-#pragma unroll
-      for (int b = 0; b < kCholB; ++b) {
-        vg[a][b] = fma(-m, gx[b], vg[a][b]);
-        vl[a][b] = fma(-m, lx[b], vl[a][b]);
+      for (int s = 0; s < 2; ++s) {
+        const int y = lane + 64 * s;
+        ok[s] = y - PB < kLpMax;
+        ad[s] = y < j0 + PB ? &CL[j0][y] : &CG[j0][ok[s] ? y - PB : kLpMax];
       }
-    }
-    // row j + 1 is final now: its owners publish it
-    if (tr == ((j + 1) & 15)) {
-      const int a1 = (j + 1) >> 4;
+      double pr[PB][2];
 #pragma unroll
-      for (int a = 0; a < kCholB; ++a)
-        if (a == a1) {
+      for (int q = 0; q < PB; ++q)
 #pragma unroll
-          for (int b = 0; b < kCholB; ++b) {
-            CG[j + 1][tc + 16 * b] = vg[a][b];
-            CL[j + 1][tc + 16 * b] = vl[a][b];
-          }
+        for (int s = 0; s < 2; ++s) {
+          const double v = ad[s][q * (kLpMax + 1)];
+          pr[q][s] = ok[s] ? v : 0.0;
         }
+#pragma unroll
+      for (int jj = 0; jj < PB; ++jj) {
+        const int yd = j0 + jj + PB;  // d_j = G'[j][j]
+        const double d = readlane_f64(yd < 64 ? pr[jj][0] : pr[jj][1], yd & 63);
+        const double id = d > tol ? recip_f64(d) : 0.0;
+        dinv[j0 + jj] = id;  // the same value from every lane
+#pragma unroll
+        for (int q = jj + 1; q < PB; ++q) {
+          const int yq = j0 + q + PB;  // G'[j][j0 + q]
+          const double m = readlane_f64(yq < 64 ? pr[jj][0] : pr[jj][1], yq & 63) * id;
+          pr[q][0] = fma(-m, pr[jj][0], pr[q][0]);
+          pr[q][1] = fma(-m, pr[jj][1], pr[q][1]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < PB; ++q)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) ad[s][q * (kLpMax + 1)] = pr[q][s];
+    }
+    __syncthreads();
+    const int p0 = j0 + PB;
+    if (p0 < lpad) {
+      // unified column y: L^-1 column y for y < p0, else G' column y
+      int off[2];
+      bool ok[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int y = lane + 64 * s;
+        ok[s] = y < lpad;
+        off[s] = y < p0 ? kLpMax * (kLpMax + 1) + y : (ok[s] ? y : kLpMax);
+      }
+      double *const base = &CGL[0][0][0];
+      double pv[PB][2], idv[PB];
+#pragma unroll
+      for (int jj = 0; jj < PB; ++jj) {
+        idv[jj] = dinv[j0 + jj];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const double v = base[off[s] + (j0 + jj) * (kLpMax + 1)];
+          pv[jj][s] = ok[s] ? v : 0.0;
+        }
+      }
+      for (int p = p0 + wave; p < lpad; p += kCholThreads / 64) {
+        double acc[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) acc[s] = base[off[s] + p * (kLpMax + 1)];
+#pragma unroll
+        for (int jj = 0; jj < PB; ++jj) {
+          const double m = CG[j0 + jj][p] * idv[jj];
+          acc[0] = fma(-m, pv[jj][0], acc[0]);
+          acc[1] = fma(-m, pv[jj][1], acc[1]);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) base[off[s] + p * (kLpMax + 1)] = acc[s];
+      }
     }
     __syncthreads();
   }
