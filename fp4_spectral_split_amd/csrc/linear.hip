@@ -293,11 +293,13 @@ __global__ void cross_reduce_kernel(const float *__restrict__ cpart, int ks, int
 // phase are in flight together), since the block is bound by load latency.
 constexpr int kPanelRows = 32;
 constexpr int kPanelThreads = 256;
-constexpr int kPanelPer = (kPanelRows * 96 + kPanelThreads - 1) / kPanelThreads;  // elements per thread, k <= 96
+// elements per thread of a kPanelRows x k block, k <= KM (64 or 96)
+template <int KM>
+constexpr int panel_per() { return (kPanelRows * KM + kPanelThreads - 1) / kPanelThreads; }
 
 // dst(i, sum) for i < count, sum = src[i] + src[stride + i] + ... over
 // nslabs slabs in slab order; four slabs' loads in flight at a time.
-template <typename Store>
+template <int kPanelPer, typename Store>
 __device__ __forceinline__ void panel_sum_slabs(const float *__restrict__ src, int64_t stride, int nslabs, int count,
                                                 Store store) {
   const int t = threadIdx.x;
@@ -342,8 +344,9 @@ __device__ __forceinline__ void panel_sum_slabs(const float *__restrict__ src, i
 // valid index, element (0, r0) when out of range, none behind a branch);
 // decode() then calls store(c, r, e2m1 * block scale). k = 0 (an unsplit
 // side, possibly without buffers) loads and stores nothing.
-template <bool NV>
+template <bool NV, int KM>
 struct PanelFactor {
+  static constexpr int kPanelPer = panel_per<KM>();
   uint32_t cb[kPanelPer], sb[kPanelPer];
   __device__ __forceinline__ void load(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                        int64_t rows, int k, int64_t r0, int nr) {
@@ -377,21 +380,38 @@ struct PanelFactor {
   }
 };
 
-// Rows [0, nr) of a panel (row stride rp, a multiple of 8) from value(r, c),
-// eight columns per 16-byte store.
+// n / d for 0 <= n, n * d < 2^32 and d > 0: the high half of n * m with
+// m = floor((2^32 - 1) / d) + 1 (then m d - 2^32 < d, which keeps the
+// quotient exact in that range). d = 1 (m = 2^32 does not fit) returns n;
+// d = 0 is never divided by.
+struct FastDiv {
+  uint32_t d, m;
+  __device__ explicit FastDiv(int dd) : d((uint32_t)dd), m(dd > 1 ? 0xFFFFFFFFu / (uint32_t)dd + 1u : 0u) {}
+  __device__ __forceinline__ int div(int n) const { return d == 1u ? n : (int)__umulhi((uint32_t)n, m); }
+  __device__ __forceinline__ int mod(int n) const { return n - div(n) * (int)d; }
+};
+
+// Rows [0, nr) of a panel (row stride rp, a multiple of 64) from value(r, c),
+// eight columns per 16-byte store. Wave w takes the 64-column groups w,
+// w + 4, ...; its lane (p, rr) writes piece p of the group on rows rr,
+// rr + 8, ... (eight whole 128-byte row pieces per store instruction). A
+// panel's column sections are 64 wide when k = 64, so value() takes one
+// path per wave.
 template <typename Value>
 __device__ __forceinline__ void panel_write_rows(unsigned short *__restrict__ dst, int nr, int rp, Value value) {
-  const int pieces = rp / 8;
-  for (int e = threadIdx.x; e < nr * pieces; e += kPanelThreads) {
-    const int r = e / pieces, c0 = (e - r * pieces) * 8;
-    ushortx8 v;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int g = w; g * 64 < rp; g += kPanelThreads / 64) {
+    const int c0 = 64 * g + 8 * (lane & 7);
+    for (int r = lane >> 3; r < nr; r += 8) {
+      ushortx8 v;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = value(r, c0 + u);
-    *(ushortx8 *)(dst + (int64_t)r * rp + c0) = v;
+      for (int u = 0; u < 8; ++u) v[u] = value(r, c0 + u);
+      *(ushortx8 *)(dst + (int64_t)r * rp + c0) = v;
+    }
   }
 }
 
-template <bool NV>
+template <bool NV, int KM>
 __global__ void __launch_bounds__(kPanelThreads)
     panel_kernel(int64_t ra, int64_t rb, int ka, int kb, int rp, const float *__restrict__ ppart, int ks_p,
                  const float *__restrict__ qpart, int ks_q, const float *__restrict__ cross_g,
@@ -399,12 +419,13 @@ __global__ void __launch_bounds__(kPanelThreads)
                  const uint8_t *__restrict__ ga_s, const float *__restrict__ ga_t, const uint8_t *__restrict__ gb_c,
                  const uint8_t *__restrict__ gb_s, const float *__restrict__ gb_t, unsigned short *__restrict__ l1,
                  unsigned short *__restrict__ l2) {
-  constexpr int R = kPanelRows;
-  __shared__ float cross[96][97];
-  __shared__ float fv[R][97];  // L1: P (summed partials); L2: Gb values
-  __shared__ float gv[R][97];  // L1: Ga values; L2: Gb values * tensor scale * Sb
-  __shared__ float qv[R][97];  // L2: Q
-  __shared__ float sa_s[96], sb_s[96], ts_s[2];
+  constexpr int R = kPanelRows, KP = KM + 1, PER = panel_per<KM>();
+  constexpr int CPER = (KM * KM + kPanelThreads - 1) / kPanelThreads;  // cross elements per thread
+  __shared__ float cross[KM][KP];
+  __shared__ float fv[R][KP];  // L1: P (summed partials); L2: Gb values
+  __shared__ float gv[R][KP];  // L1: Ga values; L2: Gb values * tensor scale * Sb
+  __shared__ float qv[R][KP];  // L2: Q
+  __shared__ float sa_s[KM], sb_s[KM], ts_s[2];
   const int t = threadIdx.x;
   const int64_t l1_blocks = (ra + R - 1) / R;
   if (t < ka) sa_s[t] = Sa[t];
@@ -416,9 +437,13 @@ __global__ void __launch_bounds__(kPanelThreads)
   if ((int64_t)blockIdx.x < l1_blocks) {
     const int64_t i0 = (int64_t)blockIdx.x * R;
     const int nr = (int)min<int64_t>(R, ra - i0);
-    PanelFactor<NV> fa;
+    PanelFactor<NV, KM> fa;
     fa.load(ga_c, ga_s, ra, ka, i0, nr);  // in flight during the slab sums
-    panel_sum_slabs(ppart + i0 * kb, ra * kb, ks_p, nr * kb, [&](int i, float v) { fv[i / kb][i % kb] = v; });
+    const FastDiv dkb(kb);
+    panel_sum_slabs<PER>(ppart + i0 * kb, ra * kb, ks_p, nr * kb, [&](int i, float v) {
+      const int r = dkb.div(i);
+      fv[r][i - r * kb] = v;
+    });
     fa.decode(ka, i0, nr, [&](int c, int r, float v) { gv[r][c] = v; });
     __syncthreads();
     const float fold_b = ts_s[1];
@@ -435,17 +460,39 @@ __global__ void __launch_bounds__(kPanelThreads)
   } else {
     const int64_t j0 = ((int64_t)blockIdx.x - l1_blocks) * R;
     const int nr = (int)min<int64_t>(R, rb - j0);
-    if (ka && kb)
-      stage_batched<16>(&cross[0][0], cross_g, ka * kb, [](int i) { return i; },
-                        [=](int i) { return (i / kb) * 97 + i % kb; });
-    PanelFactor<NV> fb;
-    fb.load(gb_c, gb_s, rb, kb, j0, nr);  // in flight during the slab sums
-    panel_sum_slabs(qpart + j0 * ka, rb * ka, ks_q, nr * ka, [&](int i, float v) { qv[i / ka][i % ka] = v; });
+    // the factor codes, the summed Fa^T Fb and the Q partials of the block's
+    // rows are all requested before the first of them is used
+    PanelFactor<NV, KM> fb;
+    fb.load(gb_c, gb_s, rb, kb, j0, nr);
+    const int ncross = (ka && kb) ? ka * kb : 0;
+    float xc[CPER];
+#pragma unroll
+    for (int u = 0; u < CPER; ++u) {
+      const int i = t + u * kPanelThreads;
+      xc[u] = ncross ? cross_g[i < ncross ? i : 0] : 0.0f;  // (a uniform test: no cross for an unsplit side)
+    }
+    const FastDiv dka(ka), dkb(kb);
+    panel_sum_slabs<PER>(qpart + j0 * ka, rb * ka, ks_q, nr * ka, [&](int i, float v) {
+      const int r = dka.div(i);
+      qv[r][i - r * ka] = v;
+    });
+    // the stores stay here (the compiler would otherwise hoist them, and the
+    // wait for these loads, above the slab loads)
+#pragma unroll
+    for (int u = 0; u < CPER; ++u) __asm__ volatile("" : "+v"(xc[u]));
+#pragma unroll
+    for (int u = 0; u < CPER; ++u) {
+      const int i = t + u * kPanelThreads;
+      if (i < ncross) {
+        const int c = dkb.div(i);
+        cross[c][i - c * kb] = xc[u];
+      }
+    }
     fb.decode(kb, j0, nr, [&](int d, int r, float v) { fv[r][d] = v; });
     __syncthreads();
     const float fold_a = ts_s[0], tsb = NV ? ts_s[1] : 1.0f;
     for (int e = t; e < nr * kb; e += kPanelThreads) {
-      const int r = e / kb, d = e - (e / kb) * kb;
+      const int r = dkb.div(e), d = e - r * kb;
       gv[r][d] = fv[r][d] * tsb * sb_s[d];
     }
     __syncthreads();
@@ -453,7 +500,7 @@ __global__ void __launch_bounds__(kPanelThreads)
     // eight rows, so each cross value feeds eight FMAs (the gv reads are
     // broadcasts within the wave)
     for (int idx = t; idx < ka * (R / 8); idx += kPanelThreads) {
-      const int cc = idx % ka, r0 = (idx / ka) * 8;
+      const int qi = dka.div(idx), cc = idx - qi * ka, r0 = qi * 8;
       float q[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = qv[r0 + i][cc];
@@ -1116,11 +1163,13 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
 // the MFMA's own layout, one row per lane, made the address units the
 // bottleneck); slot 8 r + (u ^ (r & 7)) of a stage holds unit u of row r,
 // which keeps the fragment reads free of bank conflicts. Scales follow with
-// 4-byte loads, two per row. A ring of four stages is kept in flight. Rows
-// past the end read the last row: their products reach only rows or columns
-// that are not stored.
+// 4-byte loads, two per row. A ring of three stages is kept in flight (at
+// most two column tiles: 78 KB, so two workgroups share a CU; a split has
+// only four to six stages, so a workgroup is mostly waiting for its loads).
+// Rows past the end read the last row: their products reach only rows or
+// columns that are not stored.
 constexpr int kSkRows = 128;
-constexpr int kSkStages = 4;
+constexpr int kSkStages = 3;
 template <int NCT>
 struct SkLayout {
   static constexpr int A_CODES = 0;
@@ -1208,16 +1257,18 @@ __device__ __forceinline__ floatx16 mfma_fp4_op(const uint4 a, const uint4 b, in
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4x32(a), fp4x32(b), c, 4, 4, OP, sa, OP, sb);
 }
 
+// The product of row block bx and contraction split by (the body of both
+// skinny kernels below).
 template <int NCT>
-__global__ void __launch_bounds__(256)
-    skinny_dma_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t rows,
-                      const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int cols, int64_t T,
-                      int64_t chunk, float *__restrict__ out) {
+__device__ __forceinline__ void skinny_dma_block(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as,
+                                                 int64_t rows, const uint8_t *__restrict__ bc,
+                                                 const uint8_t *__restrict__ bs, int cols, int64_t T, int64_t chunk,
+                                                 float *__restrict__ out, int bx, int by) {
   using L = SkLayout<NCT>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSkStages * L::STAGE];
   const int t = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63, r = lane & 31, h = lane >> 5;
-  const int64_t row0 = (int64_t)blockIdx.x * kSkRows;
-  const int64_t t_beg = (int64_t)blockIdx.y * chunk, t_end = std::min<int64_t>(T, t_beg + chunk);
+  const int64_t row0 = (int64_t)bx * kSkRows;
+  const int64_t t_beg = (int64_t)by * chunk, t_end = std::min<int64_t>(T, t_beg + chunk);
   const int nst = (int)((t_end - t_beg) / 256);
   const int64_t nbr = T / 32;  // scale bytes per row
   // per-thread sources (byte offsets below 2^31 by the host's check)
@@ -1294,7 +1345,7 @@ __global__ void __launch_bounds__(256)
     __asm__ volatile("" ::: "memory");
     if (st + kSkStages < nst) issue(st + kSkStages);
   }
-  float *o = out + (int64_t)blockIdx.y * rows * cols;
+  float *o = out + (int64_t)by * rows * cols;
 #pragma unroll
   for (int j = 0; j < NCT; ++j) {
     const int col = 32 * j + r;
@@ -1304,6 +1355,41 @@ __global__ void __launch_bounds__(256)
       if (orow < rows && col < cols) o[orow * cols + col] = acc[j][q];
     }
   }
+}
+
+template <int NCT>
+__global__ void __launch_bounds__(256)
+    skinny_dma_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t rows,
+                      const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs, int cols, int64_t T,
+                      int64_t chunk, float *__restrict__ out) {
+  skinny_dma_block<NCT>(ac, as, rows, bc, bs, cols, T, chunk, out, blockIdx.x, blockIdx.y);
+}
+
+// Up to three skinny products of one GEMM preparation (P, Q and Fa^T Fb) in
+// one launch: the grid is the concatenation of their (row block, split)
+// grids, so the small products run beside the large ones instead of after
+// them.
+struct SkinnyJob {
+  const uint8_t *ac, *as, *bc, *bs;
+  float *out;
+  int64_t rows, chunk;
+  int cols, gx, blocks;
+};
+struct SkinnyJobs {
+  SkinnyJob job[3];
+  int64_t T;
+  int count;
+};
+
+template <int NCT>
+__global__ void __launch_bounds__(256) skinny_dma_jobs_kernel(const SkinnyJobs jobs) {
+  int b = blockIdx.x, j = 0;
+  while (j + 1 < jobs.count && b >= jobs.job[j].blocks) {
+    b -= jobs.job[j].blocks;
+    ++j;
+  }
+  const SkinnyJob &q = jobs.job[j];
+  skinny_dma_block<NCT>(q.ac, q.as, q.rows, q.bc, q.bs, q.cols, jobs.T, q.chunk, q.out, b % q.gx, b / q.gx);
 }
 
 // NVFP4: codes and E4M3 block scales are decoded exactly to fp16 while being
@@ -1392,6 +1478,17 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
 }
 
 // ====================================================================== host
+// The asynchronous-load skinny kernel applies: K and the split a multiple of
+// 256, 16-byte aligned codes, 4-byte aligned scales, byte offsets below 2^31.
+bool skinny_dma_ok(const metis_fp4_t *A, int64_t rows, const metis_fp4_t *B, int cols, int64_t T, int64_t chunk) {
+  return A->fmt == METIS_MXFP4 && T % 256 == 0 && chunk % 256 == 0 &&
+         (((uintptr_t)A->codes | (uintptr_t)B->codes) & 15) == 0 &&
+         (((uintptr_t)A->scales | (uintptr_t)B->scales) & 3) == 0 &&
+         std::max<int64_t>(rows, cols) * (T / 2) < ((int64_t)1 << 31);
+}
+
+int skinny_nct(int cols) { return cols <= 32 ? 1 : (cols <= 64 ? 2 : 3); }
+
 void launch_skinny(const metis_fp4_t *A, int64_t rows, const metis_fp4_t *B, int cols, int64_t T, int ks,
                    int64_t chunk, float *out, hipStream_t st) {
   const dim3 grid((unsigned)cdiv(rows, 32), ks);
@@ -1406,8 +1503,7 @@ void launch_skinny(const metis_fp4_t *A, int64_t rows, const metis_fp4_t *B, int
 #undef NV_SKINNY
     return;
   }
-  if (T % 256 == 0 && chunk % 256 == 0 && (((uintptr_t)A->codes | (uintptr_t)B->codes) & 15) == 0 &&
-      (((uintptr_t)A->scales | (uintptr_t)B->scales) & 3) == 0 && std::max<int64_t>(rows, cols) * (T / 2) < ((int64_t)1 << 31)) {
+  if (skinny_dma_ok(A, rows, B, cols, T, chunk)) {
     const dim3 g((unsigned)cdiv(rows, kSkRows), ks);
     if (nct == 1)
       skinny_dma_kernel<1><<<g, 256, 0, st>>>(A->codes, A->scales, rows, B->codes, B->scales, cols, T, chunk, out);
@@ -1455,22 +1551,61 @@ metis_status_t gemm_prepare(const Side &a, const Side &b, void *ws, size_t ws_by
   GemmPlan p = make_gemm_plan(a.rows, b.rows, a.T, a.k, b.k, ws);
   if (!ws || ws_bytes < p.bytes) return METIS_ERR_WORKSPACE;
   if (((uintptr_t)ws) & 255) return METIS_ERR_INVALID;
-  if (b.k) launch_skinny(a.R, a.rows, b.F, b.k, a.T, p.ks_p, p.tc_p, p.ppart, st);
-  if (a.k) launch_skinny(b.R, b.rows, a.F, a.k, a.T, p.ks_q, p.tc_q, p.qpart, st);
-  if (a.k && b.k) launch_skinny(a.F, a.k, b.F, b.k, a.T, p.ks_c, p.tc_c, p.cpart, st);
+  {
+    // the products this GEMM needs: P = Ra Fb, Q = Rb Fa, Fa^T Fb
+    struct Prod {
+      const metis_fp4_t *A, *B;
+      int64_t rows;
+      int cols, ks;
+      int64_t chunk;
+      float *out;
+    } prods[3];
+    int np = 0;
+    if (b.k) prods[np++] = {a.R, b.F, a.rows, b.k, p.ks_p, p.tc_p, p.ppart};
+    if (a.k) prods[np++] = {b.R, a.F, b.rows, a.k, p.ks_q, p.tc_q, p.qpart};
+    if (a.k && b.k) prods[np++] = {a.F, b.F, a.k, b.k, p.ks_c, p.tc_c, p.cpart};
+    bool one = np > 1;
+    for (int i = 0; i < np; ++i)
+      one = one && skinny_dma_ok(prods[i].A, prods[i].rows, prods[i].B, prods[i].cols, a.T, prods[i].chunk) &&
+            skinny_nct(prods[i].cols) == skinny_nct(prods[0].cols);
+    if (one) {
+      SkinnyJobs jobs{};
+      jobs.T = a.T;
+      jobs.count = np;
+      int64_t total = 0;
+      for (int i = 0; i < np; ++i) {
+        const Prod &q = prods[i];
+        const int gx = (int)cdiv(q.rows, kSkRows);
+        jobs.job[i] = {q.A->codes, q.A->scales, q.B->codes, q.B->scales, q.out, q.rows, q.chunk, q.cols, gx, gx * q.ks};
+        total += (int64_t)gx * q.ks;
+      }
+      const int nct = skinny_nct(prods[0].cols);
+      if (nct == 1) skinny_dma_jobs_kernel<1><<<(unsigned)total, 256, 0, st>>>(jobs);
+      else if (nct == 2) skinny_dma_jobs_kernel<2><<<(unsigned)total, 256, 0, st>>>(jobs);
+      else skinny_dma_jobs_kernel<3><<<(unsigned)total, 256, 0, st>>>(jobs);
+    } else {
+      for (int i = 0; i < np; ++i)
+        launch_skinny(prods[i].A, prods[i].rows, prods[i].B, prods[i].cols, a.T, prods[i].ks, prods[i].chunk,
+                      prods[i].out, st);
+    }
+  }
   if (a.k && b.k)
     cross_reduce_kernel<<<(unsigned)cdiv(a.k * b.k, 256), 256, 0, st>>>(p.cpart, p.ks_c, a.k * b.k, p.cross);
   const unsigned pgrid = (unsigned)(cdiv(a.rows, kPanelRows) + cdiv(b.rows, kPanelRows));
-#define PANEL(NV)                                                                                                 \
-  panel_kernel<NV><<<pgrid, 256, 0, st>>>(a.rows, b.rows, a.k, b.k, p.rp, p.ppart, p.ks_p, p.qpart, p.ks_q,        \
+#define PANEL(NV, KM)                                                                                             \
+  panel_kernel<NV, KM><<<pgrid, 256, 0, st>>>(a.rows, b.rows, a.k, b.k, p.rp, p.ppart, p.ks_p, p.qpart, p.ks_q,        \
                                          p.cross, a.S, b.S, a.k ? a.G->codes : nullptr,                            \
                                          a.k ? a.G->scales : nullptr, a.k ? a.G->tensor_scale : nullptr,           \
                                          b.k ? b.G->codes : nullptr, b.k ? b.G->scales : nullptr,                  \
                                          b.k ? b.G->tensor_scale : nullptr, p.l1, p.l2)
-  if (a.R->fmt == METIS_NVFP4)
-    PANEL(true);
-  else
-    PANEL(false);
+  const bool km64 = a.k <= 64 && b.k <= 64;
+  if (a.R->fmt == METIS_NVFP4) {
+    if (km64) PANEL(true, 64);
+    else PANEL(true, 96);
+  } else {
+    if (km64) PANEL(false, 64);
+    else PANEL(false, 96);
+  }
 #undef PANEL
   METIS_LAUNCH_CHECK();
   return METIS_OK;
