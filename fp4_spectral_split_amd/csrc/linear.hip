@@ -1154,6 +1154,222 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
   }
 }
 
+// NVFP4 main kernel on the same ring (K a multiple of 128): C = ts_a ts_b
+// (Ra Rb^T) + L1 L2^T. Four waves, one per SIMD, each a 128 x 128 sub-tile
+// (4 x 4 blocks of 32 x 32, 256 accumulators). A stage of 128 contraction
+// elements holds the codes of A and B (256 rows x 64 bytes each, the swizzled
+// 16-byte units of the MXFP4 kernel) and their E4M3 block scales (8 bytes per
+// row), all loaded straight to LDS three stages ahead. Lane (r, h) of a wave
+// reads the 64 codes of its row's half h (two units) and its half's four
+// scale bytes; step s of the stage's eight fp16 32x32x16 MFMA steps takes the
+// lane's codes 8 s .. 8 s + 7, decoded exactly to fp16 with their block's
+// scale (the hardware FP4 conversion and one packed multiply, as in the
+// skinny NVFP4 products). A and B lanes take the same contraction elements
+// in every step, so the products pair up; the contraction order differs from
+// the natural one only in how the fp32 sums are grouped. After the last FP4
+// stage the accumulators take the product of the two tensor scales; the bf16
+// correction stages follow through the same ring.
+constexpr int NVD_SC_BYTES = BM * 8;  // one operand's E4M3 scales per stage
+constexpr int NVD_STAGE = 2 * DMA_CODE_BYTES + 2 * NVD_SC_BYTES;
+constexpr int NVD_LDS = kDmaStages * NVD_STAGE;
+static_assert(NVD_LDS <= 160 * 1024, "LDS budget of one CU");
+
+__global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+    gemm_nvd_kernel(const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, const float *__restrict__ ats,
+                    int64_t M, const uint8_t *__restrict__ bc, const uint8_t *__restrict__ bs,
+                    const float *__restrict__ bts, int64_t N, int64_t T, const unsigned short *__restrict__ l1,
+                    const unsigned short *__restrict__ l2, int rp, float *__restrict__ C, int64_t ldc) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NVD_LDS];
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int mtiles = (int)cdiv(M, BM), ntiles_n = (int)cdiv(N, BN), ntiles = mtiles * ntiles_n;
+  const int64_t nbs = T / 16;  // scale bytes per row
+  // buffer resources (byte ranges below 2^31 by the host's check)
+  const __amdgpu_buffer_rsrc_t rA = raw_rsrc(ac, (uint32_t)(M * (T / 2))), rB = raw_rsrc(bc, (uint32_t)(N * (T / 2)));
+  const __amdgpu_buffer_rsrc_t rSA = raw_rsrc(as, (uint32_t)(M * nbs)), rSB = raw_rsrc(bs, (uint32_t)(N * nbs));
+  const __amdgpu_buffer_rsrc_t rL1 = raw_rsrc(l1, (uint32_t)(M * rp * 2)), rL2 = raw_rsrc(l2, (uint32_t)(N * rp * 2));
+  const int nst = (int)(T / 128), ncs = rp / 32, ntot = nst + ncs;
+  const float tscale = ats[0] * bts[0] * 65536.0f;
+  const int rA0 = wm * 128 + r32, rB0 = wn * 128 + r32;
+  const int fA = (rA0 >> 2) & 3, fB = (rB0 >> 2) & 3;  // the same for rows + 32 i
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    int tm, tn;
+    tile_coords_of(tm, tn, tile, ntiles, mtiles, ntiles_n);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    // per-lane load offsets (rows past M or N read the last row: their
+    // products reach only rows and columns of C that are not stored)
+    uint32_t offA[4], offB[4], offL1[4], offL2[4], offSA[2], offSB[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
+      const int64_t ra = min(m0 + r, M - 1), rb = min(n0 + r, N - 1);
+      offA[i] = (uint32_t)(ra * (T / 2) + u * 16);
+      offB[i] = (uint32_t)(rb * (T / 2) + u * 16);
+      offL1[i] = (uint32_t)(ra * rp * 2 + u * 16);
+      offL2[i] = (uint32_t)(rb * rp * 2 + u * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // 4-byte piece q of the stage's scales: row q / 2, half q % 2
+      const int q = 128 * wave + 64 * u + lane, r = q >> 1;
+      offSA[u] = (uint32_t)(min(m0 + r, M - 1) * nbs + (q & 1) * 4);
+      offSB[u] = (uint32_t)(min(n0 + r, N - 1) * nbs + (q & 1) * 4);
+    }
+    auto issue_main = [&](int st) {  // twelve loads per wave: codes and scales of FP4 stage st
+      uint8_t *sbuf = smem + (st % kDmaStages) * NVD_STAGE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        buf_dma16(rA, offA[i], (uint32_t)st * 64, sbuf + (4 * wave + i) * 1024);
+        buf_dma16(rB, offB[i], (uint32_t)st * 64, sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        buf_dma4(rSA, offSA[u], (uint32_t)st * 8, sbuf + 2 * DMA_CODE_BYTES + (128 * wave + 64 * u) * 4);
+        buf_dma4(rSB, offSB[u], (uint32_t)st * 8, sbuf + 2 * DMA_CODE_BYTES + NVD_SC_BYTES + (128 * wave + 64 * u) * 4);
+      }
+    };
+    auto issue_corr = [&](int st) {  // eight loads per wave: 32 bf16 panel columns
+      uint8_t *sbuf = smem + (st % kDmaStages) * NVD_STAGE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        buf_dma16(rL1, offL1[i], (uint32_t)(st - nst) * 64, sbuf + (4 * wave + i) * 1024);
+        buf_dma16(rL2, offL2[i], (uint32_t)(st - nst) * 64, sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
+      }
+    };
+    auto issue = [&](int st) {
+      if (st < nst) issue_main(st);
+      else if (st < ntot) issue_corr(st);
+    };
+    // stage s has landed once at most the loads of the later stages issued
+    // so far (s + 1, s + 2) are pending; every LDS read of the wave is done too
+    auto wait_stage = [&](int s) {
+      int n = 0;
+      for (int k = s + 1; k <= min(s + 2, ntot - 1); ++k) n += k < nst ? 12 : 8;
+      switch (n) {
+        case 24: METIS_WAIT_VMCNT_LDS(24); break;
+        case 20: METIS_WAIT_VMCNT_LDS(20); break;
+        case 16: METIS_WAIT_VMCNT_LDS(16); break;
+        case 12: METIS_WAIT_VMCNT_LDS(12); break;
+        case 8: METIS_WAIT_VMCNT_LDS(8); break;
+        default: METIS_WAIT_VMCNT_LDS(0); break;
+      }
+    };
+    floatx16 acc[MXW][MXW];
+    auto pin_acc = [&] {
+      __asm__ volatile("" : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+                       "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]), "+a"(acc[2][0]), "+a"(acc[2][1]),
+                       "+a"(acc[2][2]), "+a"(acc[2][3]), "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]),
+                       "+a"(acc[3][3]));
+    };
+#pragma unroll
+    for (int i = 0; i < MXW; ++i)
+#pragma unroll
+      for (int j = 0; j < MXW; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    issue(0);
+    issue(1);
+    issue(2);
+    // FP4 stages
+    for (int st = 0; st < nst; ++st) {
+      wait_stage(st);
+      __builtin_amdgcn_s_barrier();  // stage st landed for every wave; stage st - 1's buffer is free
+      __asm__ volatile("" ::: "memory");
+      issue(st + 3);
+      const uint8_t *base = smem + (st % kDmaStages) * NVD_STAGE;
+      u32x4 ca[MXW][2], cb[MXW][2];
+      uint32_t sa4[MXW], sb4[MXW];
+#pragma unroll
+      for (int i = 0; i < MXW; ++i) {
+        const uint8_t *pa = base + (rA0 + 32 * i) * 64, *pb = base + DMA_CODE_BYTES + (rB0 + 32 * i) * 64;
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          ca[i][v] = *(const u32x4 *)(pa + (((2 * h + v) ^ fA) << 4));
+          cb[i][v] = *(const u32x4 *)(pb + (((2 * h + v) ^ fB) << 4));
+        }
+        sa4[i] = *(const uint32_t *)(base + 2 * DMA_CODE_BYTES + (rA0 + 32 * i) * 8 + 4 * h);
+        sb4[i] = *(const uint32_t *)(base + 2 * DMA_CODE_BYTES + NVD_SC_BYTES + (rB0 + 32 * i) * 8 + 4 * h);
+      }
+      // A block scale as an fp16 pair: the E4M3 byte's sign, exponent and
+      // mantissa moved into the fp16 fields give its value times 2^-8 exactly
+      // (normal and subnormal E4M3 alike), so each decoded product is an
+      // exact fp16 value (a multiple of 2^-18 below 11); the 2^16 the two
+      // operands lose is given back with the tensor scales.
+      auto scale2 = [](uint32_t word, int b) {
+        const uint32_t e = (word >> (8 * b)) & 255u;
+        const uint32_t f = ((e & 0x80u) << 8) | ((e & 0x7Fu) << 7);
+        return __builtin_bit_cast(halfx2, f | (f << 16));
+      };
+      auto decode = [&](int s8, halfx8 (&af)[MXW], halfx8 (&bf)[MXW]) {
+#pragma unroll
+        for (int i = 0; i < MXW; ++i) {
+          af[i] = fp4x8_to_f16(ca[i][s8 >> 2][s8 & 3], scale2(sa4[i], s8 >> 1));
+          bf[i] = fp4x8_to_f16(cb[i][s8 >> 2][s8 & 3], scale2(sb4[i], s8 >> 1));
+        }
+      };
+      auto mfmas16 = [&](const halfx8 (&af)[MXW], const halfx8 (&bf)[MXW]) {
+#pragma unroll
+        for (int i = 0; i < MXW; ++i)
+#pragma unroll
+          for (int j = 0; j < MXW; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      };
+      halfx8 af0[MXW], bf0[MXW], af1[MXW], bf1[MXW];
+      decode(0, af0, bf0);
+#pragma unroll
+      for (int s8 = 0; s8 < 8; s8 += 2) {
+        decode(s8 + 1, af1, bf1);
+        mfmas16(af0, bf0);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (s8 + 2 < 8) decode(s8 + 2, af0, bf0);
+        mfmas16(af1, bf1);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pin_acc();
+    }
+#pragma unroll
+    for (int i = 0; i < MXW; ++i)
+#pragma unroll
+      for (int j = 0; j < MXW; ++j) acc[i][j] *= tscale;  // includes the 2^16 of the scale decoding
+    pin_acc();
+    // correction stages
+    for (int st = nst; st < ntot; ++st) {
+      wait_stage(st);
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      if (st + 3 < ntot) issue_corr(st + 3);
+      const uint8_t *base = smem + (st % kDmaStages) * NVD_STAGE;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {  // 16 panel columns: unit 2 ks + h of the row
+        u32x4 fa[MXW], fb[MXW];
+#pragma unroll
+        for (int i = 0; i < MXW; ++i) {
+          fa[i] = *(const u32x4 *)(base + (rA0 + 32 * i) * 64 + (((2 * ks + h) ^ fA) << 4));
+          fb[i] = *(const u32x4 *)(base + DMA_CODE_BYTES + (rB0 + 32 * i) * 64 + (((2 * ks + h) ^ fB) << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < MXW; ++i)
+#pragma unroll
+          for (int j = 0; j < MXW; ++j)
+            acc[i][j] = mfma32_bf16(__builtin_bit_cast(ushortx8, fa[i]), __builtin_bit_cast(ushortx8, fb[j]), acc[i][j]);
+      }
+      pin_acc();
+    }
+    store_acc_mx4(acc, m0, n0, M, N, C, ldc);
+  }
+}
+
 // Skinny products on the DMA path (MXFP4, T a multiple of 256): out[s]
 // (rows x cols, cols <= 32 NCT) = NT(A, B) over T-chunk s. A workgroup of
 // four waves takes 128 rows of A (wave w: rows 32 w ..) and all of B; a stage
@@ -1631,7 +1847,13 @@ metis_status_t gemm_main(const Side &a, const Side &b, float *C, int64_t ldc, co
     l2 = p.l2;
   }
   const unsigned tiles = (unsigned)(cdiv(a.rows, BM) * cdiv(b.rows, BN));
-  if (a.R->fmt == METIS_NVFP4)
+  if (a.R->fmt == METIS_NVFP4 && a.T % 128 == 0 &&
+      ((uintptr_t)a.R->codes | (uintptr_t)b.R->codes) % 16 == 0 &&
+      std::max(a.rows, b.rows) * std::max<int64_t>(a.T / 2, 2 * (int64_t)rp) < ((int64_t)1 << 31))
+    gemm_nvd_kernel<<<std::min<unsigned>(tiles, kMxMaxGrid), kMxThreads, 0, st>>>(
+        a.R->codes, a.R->scales, a.R->tensor_scale, a.rows, b.R->codes, b.R->scales, b.R->tensor_scale, b.rows, a.T,
+        l1, l2, rp, C, ldc);
+  else if (a.R->fmt == METIS_NVFP4)
     gemm_nv_kernel<<<tiles, kGemmThreads, 0, st>>>(a.R->codes, a.R->scales, a.R->tensor_scale, a.rows, b.R->codes,
                                           b.R->scales, b.R->tensor_scale, b.rows, a.T, l1, l2, rp, C, ldc);
   else if (a.T % 512 == 0 && ((uintptr_t)a.R->codes | (uintptr_t)b.R->codes | (uintptr_t)a.R->scales |
