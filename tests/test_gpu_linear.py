@@ -63,6 +63,24 @@ def test_linear_fwd_bwd_small(kx, kw, kdy, fmt, shape):
         assert err <= 1e-5, name  # far inside the gate: fp32-accurate everywhere
 
 
+# NVFP4 forwards whose contraction is one to three 128-element stages of the
+# ring kernel (its waits take their short-pipeline forms), with no correction
+# stage, with two, and with ranks that differ; ragged rows and columns.
+@pytest.mark.parametrize("K", [128, 256, 384])
+@pytest.mark.parametrize("kx,kw", [(0, 0), (8, 8), (16, 8)])
+def test_linear_nvfp4_short_contraction(K, kx, kw):
+    X = _small(211, 288, K, kx, kx + 8, fmt="nvfp4")
+    W = _small(212, 416, K, kw, kw + 8, kind="powerlaw", fmt="nvfp4")
+    print("case", K, kx, kw, flush=True)
+    rx, rw = _operand(X, ("n",)), _operand(W, ("n",))
+    Y = M.spectral_fp4_linear_fwd(rx, rw)
+    torch.cuda.synchronize()
+    want = OL.linear_fwd(G.record_to_dict(rx), G.record_to_dict(rw))
+    err = _rel(Y.cpu().numpy().astype(np.float64), want)
+    print("Y rel err %.3e" % err, flush=True)
+    assert err <= 1e-5
+
+
 def test_linear_unsplit_is_a_plain_fp4_gemm_and_handles_empty():
     X = _small(204, 64, 256, 0, 0, kind="normal")
     W = _small(205, 96, 256, 0, 0, kind="normal")
