@@ -1159,7 +1159,8 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
 // (4 x 4 blocks of 32 x 32, 256 accumulators). A stage of 128 contraction
 // elements holds the codes of A and B (256 rows x 64 bytes each, the swizzled
 // 16-byte units of the MXFP4 kernel) and their E4M3 block scales (8 bytes per
-// row), all loaded straight to LDS three stages ahead. Lane (r, h) of a wave
+// row), all loaded straight to LDS; stage st + 4 is requested once every
+// wave has read stage st, half-way through it. Lane (r, h) of a wave
 // reads the 64 codes of its row's half h (two units) and its half's four
 // scale bytes; step s of the stage's eight fp16 32x32x16 MFMA steps takes the
 // lane's codes 8 s .. 8 s + 7, decoded exactly to fp16 with their block's
@@ -1268,102 +1269,165 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
       for (int j = 0; j < MXW; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    // A stage is consumed in two halves of four 32x32x16 steps: half v uses
+    // unit 2 h + v of the lane's row (steps 4 v .. 4 v + 3) and scale bytes
+    // 2 v, 2 v + 1. Half 1 of stage st is read while the MFMAs of half 0 run;
+    // then one barrier (stage st + 1 landed, every read of stage st done)
+    // frees buffer st % 4 for stage st + 4, and half 0 of stage st + 1 is
+    // read while the MFMAs of half 1 run. Each step's MFMAs run while the
+    // next step's operands are decoded.
+    u32x4 c0a[MXW], c0b[MXW], c1a[MXW], c1b[MXW];
+    uint32_t s0a[MXW], s0b[MXW], s1a[MXW], s1b[MXW];
+    halfx8 fa0[MXW], fb0[MXW], fa1[MXW], fb1[MXW];
+    auto read_half = [&](int st, int v, u32x4 (&ca)[MXW], u32x4 (&cb)[MXW]) {
+      const uint8_t *base = smem + (st % kDmaStages) * NVD_STAGE;
+#pragma unroll
+      for (int i = 0; i < MXW; ++i) {
+        ca[i] = *(const u32x4 *)(base + (rA0 + 32 * i) * 64 + (((2 * h + v) ^ fA) << 4));
+        cb[i] = *(const u32x4 *)(base + DMA_CODE_BYTES + (rB0 + 32 * i) * 64 + (((2 * h + v) ^ fB) << 4));
+      }
+    };
+    auto read_scales = [&](int st) {  // the four scale bytes of the lane's row half
+      const uint8_t *base = smem + (st % kDmaStages) * NVD_STAGE + 2 * DMA_CODE_BYTES;
+#pragma unroll
+      for (int i = 0; i < MXW; ++i) {
+        s0a[i] = *(const uint32_t *)(base + (rA0 + 32 * i) * 8 + 4 * h);
+        s0b[i] = *(const uint32_t *)(base + NVD_SC_BYTES + (rB0 + 32 * i) * 8 + 4 * h);
+      }
+    };
+    // A block scale as an fp16 pair: the E4M3 byte's sign, exponent and
+    // mantissa moved into the fp16 fields give its value times 2^-8 exactly
+    // (normal and subnormal E4M3 alike), so each decoded product is an exact
+    // fp16 value (a multiple of 2^-18 below 11); the 2^16 the two operands
+    // lose is given back with the tensor scales.
+    auto scale2 = [](uint32_t word, int b) {
+      const uint32_t e = (word >> (8 * b)) & 255u;
+      const uint32_t f = ((e & 0x80u) << 8) | ((e & 0x7Fu) << 7);
+      return __builtin_bit_cast(halfx2, f | (f << 16));
+    };
+    // step s of a stage: code word s % 4 of the half's unit, scale byte s / 2
+    auto decode = [&](int s, const u32x4 (&ca)[MXW], const u32x4 (&cb)[MXW], const uint32_t (&sa)[MXW],
+                      const uint32_t (&sb)[MXW], halfx8 (&af)[MXW], halfx8 (&bf)[MXW]) {
+#pragma unroll
+      for (int i = 0; i < MXW; ++i) {
+        af[i] = fp4x8_to_f16(ca[i][s & 3], scale2(sa[i], s >> 1));
+        bf[i] = fp4x8_to_f16(cb[i][s & 3], scale2(sb[i], s >> 1));
+      }
+    };
+    auto mfmas16 = [&](const halfx8 (&af)[MXW], const halfx8 (&bf)[MXW]) {
+#pragma unroll
+      for (int i = 0; i < MXW; ++i)
+#pragma unroll
+        for (int j = 0; j < MXW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    };
+    // the MFMAs of a step with the next step's decode spread between them
+    // (and, where given, nr LDS reads or nv global loads placed first)
+    auto sched = [](auto nr, auto nv) {
+      constexpr int R = decltype(nr)::value, V = decltype(nv)::value;
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if constexpr (V > 0) {
+          if (g < V) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load (to LDS)
+        }
+        if constexpr (R > 0) {
+          if (g >= V && g < V + R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    // one FP4 stage; LAST: stage st + 1 is not an FP4 stage (no half 0 to
+    // read and decode ahead)
+    auto fp4_stage = [&](int st, auto last) {
+      constexpr bool LAST = decltype(last)::value;
+      read_half(st, 1, c1a, c1b);
+      decode(1, c0a, c0b, s0a, s0b, fa1, fb1);
+      mfmas16(fa0, fb0);
+      sched(std::integral_constant<int, 8>{}, I0{});
+      decode(2, c0a, c0b, s0a, s0b, fa0, fb0);
+      mfmas16(fa1, fb1);
+      sched(I0{}, I0{});
+      decode(3, c0a, c0b, s0a, s0b, fa1, fb1);
+      mfmas16(fa0, fb0);
+      sched(I0{}, I0{});
+      decode(4, c1a, c1b, s0a, s0b, fa0, fb0);
+      mfmas16(fa1, fb1);
+      sched(I0{}, I0{});
+#pragma unroll
+      for (int i = 0; i < MXW; ++i) {
+        s1a[i] = s0a[i];
+        s1b[i] = s0b[i];
+      }
+      // the MFMAs are pure and could move across the barrier: empty asm
+      // statements pin the accumulators before it and the decoded operands
+      // of step 4 after it
+      pin_acc();
+      __builtin_amdgcn_sched_barrier(0);
+      __asm__ volatile("" ::: "memory");
+      wait_stage(st + 1);
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      __asm__ volatile("" : "+v"(fa0[0]), "+v"(fa0[1]), "+v"(fa0[2]), "+v"(fa0[3]), "+v"(fb0[0]), "+v"(fb0[1]),
+                       "+v"(fb0[2]), "+v"(fb0[3]));
+      issue(st + 4);
+      if constexpr (!LAST) {
+        read_half(st + 1, 0, c0a, c0b);
+        read_scales(st + 1);
+      }
+      decode(5, c1a, c1b, s1a, s1b, fa1, fb1);
+      mfmas16(fa0, fb0);
+      sched(I0{}, std::integral_constant<int, 12>{});
+      decode(6, c1a, c1b, s1a, s1b, fa0, fb0);
+      mfmas16(fa1, fb1);
+      sched(std::integral_constant<int, LAST ? 0 : 16>{}, I0{});
+      decode(7, c1a, c1b, s1a, s1b, fa1, fb1);
+      mfmas16(fa0, fb0);
+      sched(I0{}, I0{});
+      if constexpr (!LAST) decode(0, c0a, c0b, s0a, s0b, fa0, fb0);
+      mfmas16(fa1, fb1);
+      sched(I0{}, I0{});
+      pin_acc();
+    };
     issue(0);
     issue(1);
     issue(2);
-    // FP4 stages
-    for (int st = 0; st < nst; ++st) {
-      wait_stage(st);
-      __builtin_amdgcn_s_barrier();  // stage st landed for every wave; stage st - 1's buffer is free
-      __asm__ volatile("" ::: "memory");
-      issue(st + 3);
-      const uint8_t *base = smem + (st % kDmaStages) * NVD_STAGE;
-      u32x4 ca[MXW][2], cb[MXW][2];
-      uint32_t sa4[MXW], sb4[MXW];
-#pragma unroll
-      for (int i = 0; i < MXW; ++i) {
-        const uint8_t *pa = base + (rA0 + 32 * i) * 64, *pb = base + DMA_CODE_BYTES + (rB0 + 32 * i) * 64;
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          ca[i][v] = *(const u32x4 *)(pa + (((2 * h + v) ^ fA) << 4));
-          cb[i][v] = *(const u32x4 *)(pb + (((2 * h + v) ^ fB) << 4));
-        }
-        sa4[i] = *(const uint32_t *)(base + 2 * DMA_CODE_BYTES + (rA0 + 32 * i) * 8 + 4 * h);
-        sb4[i] = *(const uint32_t *)(base + 2 * DMA_CODE_BYTES + NVD_SC_BYTES + (rB0 + 32 * i) * 8 + 4 * h);
-      }
-      // A block scale as an fp16 pair: the E4M3 byte's sign, exponent and
-      // mantissa moved into the fp16 fields give its value times 2^-8 exactly
-      // (normal and subnormal E4M3 alike), so each decoded product is an
-      // exact fp16 value (a multiple of 2^-18 below 11); the 2^16 the two
-      // operands lose is given back with the tensor scales.
-      auto scale2 = [](uint32_t word, int b) {
-        const uint32_t e = (word >> (8 * b)) & 255u;
-        const uint32_t f = ((e & 0x80u) << 8) | ((e & 0x7Fu) << 7);
-        return __builtin_bit_cast(halfx2, f | (f << 16));
-      };
-      auto decode = [&](int s8, halfx8 (&af)[MXW], halfx8 (&bf)[MXW]) {
-#pragma unroll
-        for (int i = 0; i < MXW; ++i) {
-          af[i] = fp4x8_to_f16(ca[i][s8 >> 2][s8 & 3], scale2(sa4[i], s8 >> 1));
-          bf[i] = fp4x8_to_f16(cb[i][s8 >> 2][s8 & 3], scale2(sb4[i], s8 >> 1));
-        }
-      };
-      auto mfmas16 = [&](const halfx8 (&af)[MXW], const halfx8 (&bf)[MXW]) {
-#pragma unroll
-        for (int i = 0; i < MXW; ++i)
-#pragma unroll
-          for (int j = 0; j < MXW; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      };
-      halfx8 af0[MXW], bf0[MXW], af1[MXW], bf1[MXW];
-      decode(0, af0, bf0);
-#pragma unroll
-      for (int s8 = 0; s8 < 8; s8 += 2) {
-        decode(s8 + 1, af1, bf1);
-        mfmas16(af0, bf0);
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (s8 + 2 < 8) decode(s8 + 2, af0, bf0);
-        mfmas16(af1, bf1);
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      pin_acc();
-    }
+    wait_stage(0);
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    issue(3);
+    read_half(0, 0, c0a, c0b);
+    read_scales(0);
+    decode(0, c0a, c0b, s0a, s0b, fa0, fb0);
+    int st = 0;
+    for (; st + 1 < nst; ++st) fp4_stage(st, std::false_type{});
+    fp4_stage(st, std::true_type{});
 #pragma unroll
     for (int i = 0; i < MXW; ++i)
 #pragma unroll
       for (int j = 0; j < MXW; ++j) acc[i][j] *= tscale;  // includes the 2^16 of the scale decoding
     pin_acc();
-    // correction stages
-    for (int st = nst; st < ntot; ++st) {
-      wait_stage(st);
+    // correction stages (stage st landed and the barrier after it passed):
+    // read, wait for stage st + 1 and every read, barrier, refill, MFMAs
+    for (st = nst; st < ntot; ++st) {
+      read_half(st, 0, c0a, c0b);  // units 2 h and 2 h + 1: panel columns 16 h .. 16 h + 15
+      read_half(st, 1, c1a, c1b);
+      wait_stage(st + 1);
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
-      if (st + 3 < ntot) issue_corr(st + 3);
-      const uint8_t *base = smem + (st % kDmaStages) * NVD_STAGE;
+      issue(st + 4);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {  // 16 panel columns: unit 2 ks + h of the row
-        u32x4 fa[MXW], fb[MXW];
+      for (int i = 0; i < MXW; ++i)
 #pragma unroll
-        for (int i = 0; i < MXW; ++i) {
-          fa[i] = *(const u32x4 *)(base + (rA0 + 32 * i) * 64 + (((2 * ks + h) ^ fA) << 4));
-          fb[i] = *(const u32x4 *)(base + DMA_CODE_BYTES + (rB0 + 32 * i) * 64 + (((2 * ks + h) ^ fB) << 4));
-        }
+        for (int j = 0; j < MXW; ++j)
+          acc[i][j] = mfma32_bf16(__builtin_bit_cast(ushortx8, c0a[i]), __builtin_bit_cast(ushortx8, c0b[j]), acc[i][j]);
 #pragma unroll
-        for (int i = 0; i < MXW; ++i)
+      for (int i = 0; i < MXW; ++i)
 #pragma unroll
-          for (int j = 0; j < MXW; ++j)
-            acc[i][j] = mfma32_bf16(__builtin_bit_cast(ushortx8, fa[i]), __builtin_bit_cast(ushortx8, fb[j]), acc[i][j]);
-      }
+        for (int j = 0; j < MXW; ++j)
+          acc[i][j] = mfma32_bf16(__builtin_bit_cast(ushortx8, c1a[i]), __builtin_bit_cast(ushortx8, c1b[j]), acc[i][j]);
       pin_acc();
     }
     store_acc_mx4(acc, m0, n0, M, N, C, ldc);
