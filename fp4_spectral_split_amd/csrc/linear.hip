@@ -909,11 +909,26 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
   const int ncs = rp / 32, ntot = nst + ncs;
   const int rA0 = wm * 128 + r32, rB0 = wn * 128 + r32;
   const int fA = (rA0 >> 2) & 3, fB = (rB0 >> 2) & 3;
-  // persistent: workgroup b takes tiles b, b + gridDim.x, ...
+  // persistent: workgroup b takes tiles b, b + gridDim.x, ... The stages of
+  // its tiles form one stream through the ring: stage st of a tile sits in
+  // buffer (ring0 + st) % 4 and its scale group g in (grp0 + g) % 2, so when
+  // a next tile follows (and has at least eight stages) the last four steps
+  // of a tile load the next tile's first four stages, and the next tile
+  // starts on a full ring (pf_in) with its first stages already landed.
+  int ring0 = 0, grp0 = 0;
+  bool pf_in = false;
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     int tm, tn;
     tile_coords_of(tm, tn, tile, ntiles, mtiles, ntiles_n);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const bool pf_out = tile + (int)gridDim.x < ntiles && nst >= 8;
+    int64_t m0n = 0, n0n = 0;
+    if (pf_out) {
+      int tmn, tnn;
+      tile_coords_of(tmn, tnn, tile + (int)gridDim.x, ntiles, mtiles, ntiles_n);
+      m0n = (int64_t)tmn * BM;
+      n0n = (int64_t)tnn * BN;
+    }
 
     // per-lane load offsets (bytes, below 2^31 by the host's check): code unit
     // of row r = q / 4 of this wave's blocks, and the scale word of row
@@ -930,7 +945,7 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     const uint32_t offSA = (uint32_t)(min(m0 + rs, M - 1) * nb), offSB = (uint32_t)(min(n0 + rs, N - 1) * nb);
 
     auto issue_main = [&](int st) {  // eight loads per wave: codes of FP4 stage st
-      uint8_t *sbuf = smem + (st % kDmaStages) * DMA_STAGE;
+      uint8_t *sbuf = smem + ((st + ring0) & (kDmaStages - 1)) * DMA_STAGE;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         buf_dma16(rA, offA[i], (uint32_t)st * 64, sbuf + (4 * wave + i) * 1024);
@@ -945,7 +960,7 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
       offL2[i] = (uint32_t)(min(n0 + r, N - 1) * rp * 2 + u * 16);
     }
     auto issue_corr = [&](int st) {  // eight loads per wave: panel columns of correction stage st
-      uint8_t *sbuf = smem + (st % kDmaStages) * DMA_STAGE;
+      uint8_t *sbuf = smem + ((st + ring0) & (kDmaStages - 1)) * DMA_STAGE;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         buf_dma16(rL1, offL1[i], (uint32_t)(st - nst) * 64, sbuf + (4 * wave + i) * 1024);
@@ -957,9 +972,27 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
       else issue_corr(st);
     };
     auto issue_scales = [&](int g) {  // two loads per wave: scales of stages 4 g .. 4 g + 3
-      uint8_t *sg = smem + DMA_SCALE_BASE + (g % 2) * DMA_SCALE_GROUP;
+      uint8_t *sg = smem + DMA_SCALE_BASE + ((g + grp0) & 1) * DMA_SCALE_GROUP;
       buf_dma16(rSA, offSA, (uint32_t)g * 16, sg + wave * 1024);
       buf_dma16(rSB, offSB, (uint32_t)g * 16, sg + BM * 16 + wave * 1024);
+    };
+    // stage j < 4 of the next tile (FP4: nst >= 8), its scale group 0 first,
+    // into the buffers that follow this tile's last stage in the ring
+    auto issue_next = [&](int j) {
+      uint8_t *sbuf = smem + ((ring0 + ntot + j) & (kDmaStages - 1)) * DMA_STAGE;
+      if (j == 0) {
+        uint8_t *sg = smem + DMA_SCALE_BASE + ((grp0 + nst / 4) & 1) * DMA_SCALE_GROUP;
+        buf_dma16(rSA, (uint32_t)(min(m0n + rs, M - 1) * nb), 0u, sg + wave * 1024);
+        buf_dma16(rSB, (uint32_t)(min(n0n + rs, N - 1) * nb), 0u, sg + BM * 16 + wave * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = 64 * (4 * wave + i) + lane, r = q >> 2, u = (q & 3) ^ ((r >> 2) & 3);
+        buf_dma16(rA, (uint32_t)(min(m0n + r, M - 1) * (T / 2) + u * 16), (uint32_t)j * 64,
+                  sbuf + (4 * wave + i) * 1024);
+        buf_dma16(rB, (uint32_t)(min(n0n + r, N - 1) * (T / 2) + u * 16), (uint32_t)j * 64,
+                  sbuf + DMA_CODE_BYTES + (4 * wave + i) * 1024);
+      }
     };
     // Wait until the codes of stage s (and the scales of its group, issued
     // before them) have landed: at most the 8 loads of each later stage
@@ -979,7 +1012,7 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     auto load_frags_k = [&](int st, int ks, auto corr, u32x4 (&af)[MXW], u32x4 (&bf)[MXW], int (&sa)[MXW],
                             int (&sb)[MXW]) {
       constexpr bool CORR = decltype(corr)::value;
-      const uint8_t *base = smem + (st % kDmaStages) * DMA_STAGE;
+      const uint8_t *base = smem + ((st + ring0) & (kDmaStages - 1)) * DMA_STAGE;
       const int un = CORR ? 2 * ks + h : 2 * h + ks;
       const uint8_t *pa = base + rA0 * 64 + ((un ^ fA) << 4);
       const uint8_t *pb = base + DMA_CODE_BYTES + rB0 * 64 + ((un ^ fB) << 4);
@@ -989,7 +1022,7 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
         bf[i] = *(const u32x4 *)(pb + i * 2048);
       }
       if (!CORR && ks == 0) {
-        const uint8_t *sbase = smem + DMA_SCALE_BASE + ((st / 4) % 2) * DMA_SCALE_GROUP + (st % 4) * 4;
+        const uint8_t *sbase = smem + DMA_SCALE_BASE + ((st / 4 + grp0) & 1) * DMA_SCALE_GROUP + (st % 4) * 4;
 #pragma unroll
         for (int i = 0; i < MXW; ++i) {
           sa[i] = *(const int *)(sbase + (rA0 + 32 * i) * 16);
@@ -1039,14 +1072,22 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     // right after codes(4 g - 1), scales(g).
     u32x4 a0f[MXW], b0f[MXW], a1f[MXW], b1f[MXW];
     int s0a[MXW], s0b[MXW], s1a[MXW], s1b[MXW];
-    issue_scales(0);
-    issue(0);
-    if (ntot > 1) issue(1);
-    if (ntot > 2) issue(2);
-    wait_stage(0);
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    if (ntot > 3) issue(3);
+    if (pf_in) {
+      // stages 0 .. 2 landed before the previous tile's stores (each wave
+      // waited for its own loads; the barrier covers the others'), stage 3
+      // is in flight
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+    } else {
+      issue_scales(0);
+      issue(0);
+      if (ntot > 1) issue(1);
+      if (ntot > 2) issue(2);
+      wait_stage(0);
+      __builtin_amdgcn_s_barrier();
+      __asm__ volatile("" ::: "memory");
+      if (ntot > 3) issue(3);
+    }
     if (4 < nst) issue_scales(1);
     load_frags(0, 0, a0f, b0f, s0a, s0b);
     // One pipeline step; the FP4 stages and the bf16 correction stages run
@@ -1059,7 +1100,7 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     // due, follows the MFMAs. (Scheduling barriers keep the parts in order:
     // the compiler would otherwise gather both MFMA halves behind one wait
     // for all reads.)
-    auto step = [&](int st, auto corr, auto steady, auto nextc, auto dmac) {
+    auto step = [&](int st, auto corr, auto steady, auto nextc, auto dmac, auto landed) {
       constexpr bool STEADY = decltype(steady)::value;
       // half 0 (read during the previous MFMA half) is complete before half
       // 1's reads are issued, so the MFMAs below wait for nothing
@@ -1089,8 +1130,15 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
                        "+a"(acc[3][3]));
       __builtin_amdgcn_sched_barrier(0);
       __asm__ volatile("" ::: "memory");
-      if constexpr (STEADY) {
+      if constexpr (decltype(landed)::value) {
+        METIS_WAIT_LDS0();  // stage st + 1 landed before the previous tile's stores
+      } else if constexpr (STEADY) {
         METIS_WAIT_VMCNT_LDS(16);
+      } else if (pf_out) {
+        // the stream goes on into the next tile: at most the two stages after
+        // st + 1 (and a scale group) are pending
+        if (st + 1 < ntot) METIS_WAIT_VMCNT_LDS(16);
+        else METIS_WAIT_LDS0();
       } else {
         if (st + 1 < ntot) wait_stage(st + 1);
         else METIS_WAIT_VMCNT_LDS(0);
@@ -1105,6 +1153,7 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
         load_frags_k(st + 1, 0, nextc, a0f, b0f, s0a, s0b);
       } else {
         if (st + 4 < ntot) issue(st + 4);
+        else if (pf_out) issue_next(st + 4 - ntot);
         if ((st + 1) % 4 == 0 && 4 * ((st + 1) / 4 + 1) < nst) issue_scales((st + 1) / 4 + 1);
         if (st + 1 < ntot) load_frags(st + 1, 0, a0f, b0f, s0a, s0b);
       }
@@ -1130,27 +1179,42 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     using F = std::false_type;
     using Tt = std::true_type;
     int st = 0;
+    if (pf_in) {
+      // nst >= 8: the first group is steady; stages 1 and 2 need no wait
+      step(0, F{}, Tt{}, F{}, F{}, Tt{});
+      step(1, F{}, Tt{}, F{}, F{}, Tt{});
+      step(2, F{}, Tt{}, F{}, F{}, F{});
+      step(3, F{}, Tt{}, F{}, F{}, F{});
+      st = 4;
+    }
     // FP4 stages whose next four stages are FP4 stages too, four per group
     for (; st + 7 < nst; st += 4) {
-      step(st, F{}, Tt{}, F{}, F{});
-      step(st + 1, F{}, Tt{}, F{}, F{});
-      step(st + 2, F{}, Tt{}, F{}, F{});
-      step(st + 3, F{}, Tt{}, F{}, F{});
+      step(st, F{}, Tt{}, F{}, F{}, F{});
+      step(st + 1, F{}, Tt{}, F{}, F{}, F{});
+      step(st + 2, F{}, Tt{}, F{}, F{}, F{});
+      step(st + 3, F{}, Tt{}, F{}, F{}, F{});
     }
     if (ncs >= 4 && st + 4 == nst) {
       // the last four FP4 stages issue the first correction stages
-      step(st, F{}, Tt{}, F{}, Tt{});
-      step(st + 1, F{}, Tt{}, F{}, Tt{});
-      step(st + 2, F{}, Tt{}, F{}, Tt{});
-      step(st + 3, F{}, Tt{}, Tt{}, Tt{});
+      step(st, F{}, Tt{}, F{}, Tt{}, F{});
+      step(st + 1, F{}, Tt{}, F{}, Tt{}, F{});
+      step(st + 2, F{}, Tt{}, F{}, Tt{}, F{});
+      step(st + 3, F{}, Tt{}, Tt{}, Tt{}, F{});
       st += 4;
     }
-    for (; st < nst; ++st) step(st, F{}, F{}, F{}, F{});
-    for (; st + 4 < ntot; ++st) step(st, Tt{}, Tt{}, Tt{}, Tt{});
-    for (; st < ntot; ++st) step(st, Tt{}, F{}, F{}, F{});
-    // every LDS read of the tile finished before the last barrier, so the
-    // next tile's first loads may refill the ring while these stores drain
+    for (; st < nst; ++st) step(st, F{}, F{}, F{}, F{}, F{});
+    for (; st + 4 < ntot; ++st) step(st, Tt{}, Tt{}, Tt{}, Tt{}, F{});
+    for (; st < ntot; ++st) step(st, Tt{}, F{}, F{}, F{}, F{});
+    // every LDS read of the tile finished before the last barrier. With a
+    // next tile in the stream, its stages 0 .. 2 (and scale group 0) are
+    // waited for before the stores, since a wait issued after them would also
+    // wait for the stores; stage 3 may stay in flight. Otherwise the next
+    // tile's first loads refill the ring while these stores drain.
+    if (pf_out) METIS_WAIT_VMCNT_LDS(8);
     store_acc_mx4(acc, m0, n0, M, N, C, ldc);
+    ring0 = (ring0 + ntot) & (kDmaStages - 1);
+    grp0 = (grp0 + nst / 4) & 1;
+    pf_in = pf_out;
   }
 }
 
