@@ -102,22 +102,27 @@ def test_linear_deterministic():
     assert torch.equal(a, b)
 
 
-def test_linear_persistent_grid_with_ragged_tiles():
+@pytest.mark.parametrize("K", [1024, 1536, 2560])
+def test_linear_persistent_grid_with_ragged_tiles(K):
     """More output tiles than the MXFP4 kernel's persistent grid of 256
     workgroups (17 x 17 = 289), the last tile row and column ragged: the
-    workgroups that take a second tile take the ragged ones. Rows of the
-    first and of the last two tile rows are checked against the oracle."""
-    Mt, K, N = 4128, 1024, 4160
+    workgroups that take a second tile take the ragged ones, and the last
+    stages of their first tile load the first stages of the second. K = 1536
+    and 2560 give an odd number of four-stage scale groups per tile, so the
+    second tile's scale groups sit in the other buffer of each pair. Rows of
+    the first tile row, of tile row 8 (whose last two tiles are second
+    tiles) and of the last two tile rows are checked against the oracle."""
+    Mt, N = 4128, 4160
     X = _small(211, Mt, K, 8, 16)
     W = _small(212, N, K, 8, 16, kind="powerlaw")
     rx, rw = _operand(X, ("n",)), _operand(W, ("n",))
     Y = M.spectral_fp4_linear_fwd(rx, rw)
     torch.cuda.synchronize()
-    rows = np.concatenate([np.arange(0, 64), np.arange(Mt - 96, Mt)])
+    rows = np.concatenate([np.arange(0, 64), np.arange(2048, 2112), np.arange(Mt - 96, Mt)])
     got = Y[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
     want = OL.gemm_nt(G.record_to_dict(rx), "n", G.record_to_dict(rw), "n", rows=rows)
     err = _rel(got, want)
-    print("persistent ragged rel err %.3e" % err, flush=True)
+    print("persistent ragged K=%d rel err %.3e" % (K, err), flush=True)
     assert err <= 1e-5
 
 
