@@ -1073,9 +1073,8 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     u32x4 a0f[MXW], b0f[MXW], a1f[MXW], b1f[MXW];
     int s0a[MXW], s0b[MXW], s1a[MXW], s1b[MXW];
     if (pf_in) {
-      // stages 0 .. 2 landed before the previous tile's stores (each wave
-      // waited for its own loads; the barrier covers the others'), stage 3
-      // is in flight
+      // stages 0 .. 3 landed before the previous tile's stores (each wave
+      // waited for its own loads; the barrier covers the others')
       __builtin_amdgcn_s_barrier();
       __asm__ volatile("" ::: "memory");
     } else {
@@ -1180,10 +1179,10 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     using Tt = std::true_type;
     int st = 0;
     if (pf_in) {
-      // nst >= 8: the first group is steady; stages 1 and 2 need no wait
+      // nst >= 8: the first group is steady; stages 1 .. 3 need no wait
       step(0, F{}, Tt{}, F{}, F{}, Tt{});
       step(1, F{}, Tt{}, F{}, F{}, Tt{});
-      step(2, F{}, Tt{}, F{}, F{}, F{});
+      step(2, F{}, Tt{}, F{}, F{}, Tt{});
       step(3, F{}, Tt{}, F{}, F{}, F{});
       st = 4;
     }
@@ -1206,11 +1205,11 @@ __global__ void __launch_bounds__(kMxThreads, 1) __attribute__((amdgpu_waves_per
     for (; st + 4 < ntot; ++st) step(st, Tt{}, Tt{}, Tt{}, Tt{}, F{});
     for (; st < ntot; ++st) step(st, Tt{}, F{}, F{}, F{}, F{});
     // every LDS read of the tile finished before the last barrier. With a
-    // next tile in the stream, its stages 0 .. 2 (and scale group 0) are
+    // next tile in the stream, its stages 0 .. 3 (and scale group 0) are
     // waited for before the stores, since a wait issued after them would also
-    // wait for the stores; stage 3 may stay in flight. Otherwise the next
-    // tile's first loads refill the ring while these stores drain.
-    if (pf_out) METIS_WAIT_VMCNT_LDS(8);
+    // wait for the stores. Otherwise the next tile's first loads refill the
+    // ring while these stores drain.
+    if (pf_out) METIS_WAIT_VMCNT_LDS(0);
     store_acc_mx4(acc, m0, n0, M, N, C, ldc);
     ring0 = (ring0 + ntot) & (kDmaStages - 1);
     grp0 = (grp0 + nst / 4) & 1;
